@@ -1,0 +1,153 @@
+/*
+ * rmsnorm_quant.h -- C ABI of librmsnorm_quant.so, the MI355X (gfx950) library
+ * for the fused residual-add -> RMSNorm -> activation-quantization step and the
+ * QK GemmaRMSNorm + gate de-interleave step of LLM decoder layers.
+ *
+ * What is computed (per row = per token, row-major tensors):
+ *
+ *   residual_out = bf16(x + residual)                      (one rounding)
+ *   rstd         = 1 / sqrt(mean(residual_out^2) + eps)    (mean over H)
+ *   y            = bf16(residual_out * rstd * weight)      (one rounding)
+ *   then y is quantized in one of three formats.
+ *
+ * sglang PR #29723 (fused AllReduce + RMSNorm + per-token FP8 / MXFP4 quant on
+ * AMD), Motivation: the unfused sequence is residual add -> RMSNorm ->
+ * quantize in separate launches with bf16 tensors between them; Accuracy
+ * Tests: the fused kernel is numerically equivalent to that sequence; Key
+ * changes: the call returns (codes, residual_out, per-token scale of shape
+ * (M, 1)) or tells the caller it cannot fuse.  The all-reduce the page fuses in
+ * front of the residual add is not part of this library (one GPU); x is the
+ * already-reduced activation.
+ *
+ * Conventions shared by every entry point:
+ *  - bf16 tensors are passed as uint16_t bit patterns.  Only bf16 in/out is
+ *    supported; there is no silent promotion of other dtypes.
+ *  - All tensor pointers are DEVICE pointers owned by the caller.  The library
+ *    allocates nothing, never synchronizes the host and keeps no state besides
+ *    a per-device cache of the architecture check.  Every call only enqueues
+ *    kernels on `stream` (a hipStream_t; NULL = the null stream), so calls may
+ *    be captured into a hipGraph.
+ *  - Inputs x and residual may be strided views (row stride ldx / ldr in
+ *    elements); every output is contiguous.  residual_out may alias residual
+ *    exactly (in place) when ldr == H; any other overlap between an output and
+ *    any other buffer is rejected.
+ *  - Errors are decided by deterministic checks before anything is enqueued,
+ *    so on any error return nothing has been written:
+ *      RQ_ERR_INVALID      a null pointer with M > 0, a negative size,
+ *                          ld < row length, eps negative or NaN, overlapping
+ *                          buffers;
+ *      RQ_ERR_UNSUPPORTED  the device is not gfx950, a row start is not
+ *                          16-byte aligned, H % 8 != 0, H above
+ *                          RQ_MAX_HIDDEN, a granule that does not divide H,
+ *                          or an unsupported group size.  This is the "cannot
+ *                          fuse, use the unfused path" answer of PR #29723.
+ *      RQ_ERR_HIP          the kernel launch itself failed.
+ *    Faults inside a kernel surface at the caller's next synchronization.
+ *  - M == 0 (or T == 0) returns RQ_OK and launches nothing.
+ */
+#ifndef RMSNORM_QUANT_H
+#define RMSNORM_QUANT_H
+
+#include <stdint.h>
+
+#ifdef __cplusplus
+extern "C" {
+#endif
+
+typedef enum rq_status {
+  RQ_OK = 0,
+  RQ_ERR_INVALID = 1,
+  RQ_ERR_UNSUPPORTED = 2,
+  RQ_ERR_HIP = 3
+} rq_status;
+
+/* Largest row length the fused row kernels accept (the row is held in
+ * registers).  Larger H returns RQ_ERR_UNSUPPORTED. */
+#define RQ_MAX_HIDDEN 16384
+/* Largest head dimension of qk_gemma_rmsnorm_gate. */
+#define RQ_MAX_HEAD_DIM 512
+
+/* Fused residual add + RMSNorm + per-token FP8 quantization.
+ * sglang PR #29723, Key changes: tensor_model_parallel_fused_allreduce_
+ * rmsnorm_quant_per_token returns (fp8_output, residual_out,
+ * per_token_scale (M, 1)); review notes and "Applicability": an optional bf16
+ * side output for consumers that cannot take the quantized tuple.
+ *
+ *  x          [M, ldx] bf16, first H columns used (the reduced activation)
+ *  residual   [M, ldr] bf16
+ *  weight     [H] bf16 (RMSNorm gamma)
+ *  eps        added to the mean of squares inside the square root
+ *  residual_out [M, H] bf16 out: bf16(x + residual)
+ *  q_out      [M, H] uint8 out: OCP FP8 E4M3FN codes of y / scale
+ *             (nearest-even; y / scale is an IEEE fp32 quotient)
+ *  scale_out  [M] fp32 out: scale = fp32(max |y| over the row) / 448;
+ *             an all-zero row has scale 0 and codes 0x00 / 0x80 (sign of zero)
+ *  y_out      [M, H] bf16 out or NULL: the normalized row y
+ *  stream     hipStream_t
+ */
+rq_status rmsnorm_quant_fp8_per_token(
+    const uint16_t* x, int64_t ldx, const uint16_t* residual, int64_t ldr,
+    const uint16_t* weight, int64_t M, int64_t H, float eps,
+    uint16_t* residual_out, uint8_t* q_out, float* scale_out, uint16_t* y_out,
+    void* stream);
+
+/* Fused residual add + RMSNorm + per-group FP8 quantization (the pre-existing
+ * per-group variant of sglang PR #29723, Motivation).  As the per-token call,
+ * but one scale per `group` consecutive elements of a row, groups starting at
+ * column 0:
+ *  group      one of 32, 64, 128, 256, 512; must divide H
+ *  scale_out  [M, H / group] fp32 row-major
+ */
+rq_status rmsnorm_quant_fp8_per_group(
+    const uint16_t* x, int64_t ldx, const uint16_t* residual, int64_t ldr,
+    const uint16_t* weight, int64_t M, int64_t H, float eps, int64_t group,
+    uint16_t* residual_out, uint8_t* q_out, float* scale_out, uint16_t* y_out,
+    void* stream);
+
+/* Fused residual add + RMSNorm + MXFP4 quantization (sglang PR #29723: the
+ * MXFP4 variant with a direct MXFP4 epilogue; sgl-amd-mono PR #26 commit notes:
+ * the MXFP4 blocks are a pure function of the bf16 normalized row).
+ *  H          must be a multiple of 32
+ *  q_out      [M, H / 2] uint8 out: FP4 E2M1 codes, two per byte, element 2j
+ *             in the low nibble of byte j; code = E2M1(y * 2^-(s - 127)),
+ *             nearest-even, saturating at 6
+ *  scale_out  [M, H / 32] uint8 out: E8M0 byte s per 32-element block,
+ *             s = clamp(floor(log2 max|y|) - 2 + 127, 0, 254); an all-zero
+ *             block has s = 0 and codes 0x0 / 0x8 (sign of zero); a block
+ *             holding NaN has s = 255 and unspecified codes
+ */
+rq_status rmsnorm_quant_mxfp4(
+    const uint16_t* x, int64_t ldx, const uint16_t* residual, int64_t ldr,
+    const uint16_t* weight, int64_t M, int64_t H, float eps,
+    uint16_t* residual_out, uint8_t* q_out, uint8_t* scale_out, uint16_t* y_out,
+    void* stream);
+
+/* QK GemmaRMSNorm + gate de-interleave.  sglang PR #27656 ("Fuse QK RMSNorm +
+ * gate extraction Triton kernel for Qwen3.5 on HIP"), Motivation and
+ * Modifications: reads q and gate from the interleaved per-token layout
+ * [q_h0 | gate_h0 | q_h1 | gate_h1 | ...], applies GemmaRMSNorm
+ * (v * rstd * (1 + w)) to every head of q and k, writes contiguous q, k and
+ * gate; the review asks for k to be read through its stride, not copied.
+ *
+ *  qg        [T, ld_qg] bf16, ld_qg >= 2 * Hq * D; head h of token t has q at
+ *            columns [2Dh, 2Dh + D) and gate at [2Dh + D, 2D(h + 1))
+ *  k         [T, ld_k] bf16, ld_k >= Hk * D; head h at columns [Dh, D(h + 1))
+ *  q_w, k_w  [D] bf16 weights, applied as (1 + w)
+ *  D         head dimension: a multiple of 8, at most RQ_MAX_HEAD_DIM
+ *  q_out     [T, Hq, D] bf16 out; k_out [T, Hk, D]; gate_out [T, Hq, D]
+ *            (gate is copied bit for bit)
+ */
+rq_status qk_gemma_rmsnorm_gate(
+    const uint16_t* qg, int64_t ld_qg, const uint16_t* k, int64_t ld_k,
+    const uint16_t* q_w, const uint16_t* k_w, int64_t T, int64_t Hq, int64_t Hk,
+    int64_t D, float eps, uint16_t* q_out, uint16_t* k_out, uint16_t* gate_out,
+    void* stream);
+
+/* Static, human-readable name of a status code. */
+const char* rq_status_string(rq_status status);
+
+#ifdef __cplusplus
+}
+#endif
+
+#endif /* RMSNORM_QUANT_H */

@@ -1,0 +1,527 @@
+"""Pins of the CPU oracle against facts fixed outside the oracle itself.
+
+Each ``pin_*`` function takes an ``oracle.Oracle`` and raises AssertionError
+when the oracle disagrees with:
+  - library routines that define a format (torch's bf16 and float8_e4m3fn
+    casts), or the format's value set enumerated independently here;
+  - hand-derived values stored under tests/golden/ (each file says how);
+  - closed forms (a constant row, power-of-two amax);
+  - an independent vectorised numpy float64 formulation of the whole step
+    (nearest-value search over the formats' value sets instead of the
+    oracle's exponent arithmetic);
+  - invariants any correct result satisfies.
+The functions are plain so that tests/test_oracle_negative_controls.py can run
+them against deliberately broken copies of the oracle and show that each
+planted mistake is caught.
+"""
+
+from __future__ import annotations
+
+import os
+
+import numpy as np
+import torch
+
+from rmsnorm_activation_quantization_amd import inputs
+
+GOLDEN = os.path.join(os.path.dirname(os.path.abspath(__file__)), "golden")
+
+# ----------------------------------------------------------------------------
+# Independent value sets
+# ----------------------------------------------------------------------------
+
+_ALL16 = np.arange(65536, dtype=np.uint32)
+# bf16 is the upper half of an IEEE binary32 (decoded through numpy's float32).
+with np.errstate(invalid="ignore"):
+    BF16_VALUE = (_ALL16 << 16).view(np.float32).astype(np.float64)
+# Non-negative finite bf16 values in pattern order 0x0000..0x7F7F (increasing).
+BF16_GRID = BF16_VALUE[:0x7F80]
+
+# E4M3FN values as torch decodes them (codes 0x00..0x7E, increasing).
+E4M3_GRID = torch.arange(0, 0x7F, dtype=torch.uint8).view(torch.float8_e4m3fn).to(torch.float64).numpy()
+
+
+def _load_e2m1_table():
+    codes, values = [], []
+    with open(os.path.join(GOLDEN, "e2m1_codes.txt")) as f:
+        for line in f:
+            line = line.split("#")[0].strip()
+            if line:
+                c, v = line.split()[:2]
+                codes.append(int(c, 16))
+                values.append(float(v))
+    return np.array(codes), np.array(values)
+
+
+E2M1_CODES, E2M1_VALUES = _load_e2m1_table()
+E2M1_GRID = E2M1_VALUES[:8]  # 0, .5, 1, 1.5, 2, 3, 4, 6 for codes 0..7
+
+
+def nearest_even(a: np.ndarray, grid: np.ndarray) -> np.ndarray:
+    """Index of the nearest grid value to each a >= 0 (a <= grid[-1]); a tie
+    goes to the even index.  Grid values are a format's codes in order, so an
+    even index is an even mantissa."""
+    a = np.asarray(a, dtype=np.float64)
+    hi = np.searchsorted(grid, a, side="left")
+    hi = np.clip(hi, 1, len(grid) - 1)
+    lo = hi - 1
+    d_lo = a - grid[lo]   # exact: adjacent values of one format (Sterbenz)
+    d_hi = grid[hi] - a
+    pick = np.where(d_lo < d_hi, lo, hi)
+    tie = d_lo == d_hi
+    pick = np.where(tie, np.where(lo % 2 == 0, lo, hi), pick)
+    pick = np.where(a == grid[0], 0, pick)
+    return pick
+
+
+def np_bf16_round(v: np.ndarray) -> np.ndarray:
+    """bf16 bit pattern nearest to each finite double (ties to even), by search."""
+    v = np.asarray(v, dtype=np.float64)
+    idx = nearest_even(np.abs(v), BF16_GRID).astype(np.uint16)
+    return np.where(np.signbit(v), idx | np.uint16(0x8000), idx).astype(np.uint16)
+
+
+def np_bf16_value(bits: np.ndarray) -> np.ndarray:
+    return BF16_VALUE[np.asarray(bits, dtype=np.uint16)]
+
+
+def np_e4m3(q: np.ndarray) -> np.ndarray:
+    q = np.asarray(q, dtype=np.float64)
+    a = np.minimum(np.abs(q), 448.0)
+    idx = nearest_even(a, E4M3_GRID).astype(np.uint8)
+    return np.where(np.signbit(q), idx | np.uint8(0x80), idx).astype(np.uint8)
+
+
+def np_e2m1(v: np.ndarray) -> np.ndarray:
+    v = np.asarray(v, dtype=np.float64)
+    a = np.minimum(np.abs(v), 6.0)
+    idx = nearest_even(a, E2M1_GRID).astype(np.uint8)
+    return np.where(np.signbit(v), idx | np.uint8(0x8), idx).astype(np.uint8)
+
+
+def torch_bf16_add(x_bits: np.ndarray, r_bits: np.ndarray) -> np.ndarray:
+    """torch's CPU bf16 addition (an independent library routine)."""
+    return inputs.bits(inputs.from_bits(x_bits) + inputs.from_bits(r_bits))
+
+
+# ----------------------------------------------------------------------------
+# Independent formulation of the whole step (numpy float64, vectorised)
+# ----------------------------------------------------------------------------
+
+def np_norm(x_bits, r_bits, w_bits, eps):
+    res = torch_bf16_add(x_bits, r_bits)
+    r = np_bf16_value(res)
+    ms = np.mean(r * r, axis=1, keepdims=True)
+    rstd = 1.0 / np.sqrt(ms + eps)
+    y = np_bf16_round(r * rstd * np_bf16_value(w_bits)[None, :])
+    return res, y
+
+
+def np_fp8(y_bits, granule):
+    M, H = y_bits.shape
+    y = np_bf16_value(y_bits).reshape(M, H // granule, granule)
+    amax = np.abs(y).max(axis=2)
+    scale = amax.astype(np.float32) / np.float32(448.0)
+    with np.errstate(divide="ignore", invalid="ignore"):
+        quotient = y.astype(np.float32) / scale[:, :, None]
+    codes = np_e4m3(quotient)
+    zero = (amax == 0)[:, :, None]
+    codes = np.where(zero, np.where(np.signbit(y), 0x80, 0x00), codes).astype(np.uint8)
+    return codes.reshape(M, H), scale
+
+
+def np_mxfp4(y_bits):
+    M, H = y_bits.shape
+    y = np_bf16_value(y_bits).reshape(M, H // 32, 32)
+    amax = np.abs(y).max(axis=2)
+    _, e = np.frexp(amax)           # amax = f * 2^e, f in [0.5, 1): floor(log2 amax) = e - 1
+    byte = np.where(amax == 0, 0, np.clip(e - 1 - 2 + 127, 0, 254)).astype(np.uint8)
+    scaled = np.ldexp(y, -(byte.astype(np.int64) - 127)[:, :, None])
+    codes = np_e2m1(scaled).reshape(M, H)
+    packed = (codes[:, 0::2] | (codes[:, 1::2] << 4)).astype(np.uint8)
+    return packed, byte
+
+
+def np_qk(qg_bits, k_bits, qw_bits, kw_bits, Hq, Hk, D, eps):
+    T = qg_bits.shape[0]
+    qg = qg_bits[:, : 2 * Hq * D].reshape(T, Hq, 2, D)
+    q, gate = qg[:, :, 0, :], qg[:, :, 1, :]
+    k = k_bits[:, : Hk * D].reshape(T, Hk, D)
+
+    def gemma(v_bits, w_bits):
+        v = np_bf16_value(v_bits)
+        rstd = 1.0 / np.sqrt(np.mean(v * v, axis=2, keepdims=True) + eps)
+        return np_bf16_round(v * rstd * (1.0 + np_bf16_value(w_bits)))
+
+    return gemma(q, qw_bits), gemma(k, kw_bits), gate.copy()
+
+
+# ----------------------------------------------------------------------------
+# Pins
+# ----------------------------------------------------------------------------
+
+def pin_bf16_decode(ref):
+    got = ref.bf16_value(_ALL16.astype(np.uint16))
+    want = torch.from_numpy(_ALL16.astype(np.uint16).view(np.int16)).view(torch.bfloat16).double().numpy()
+    same = (got == want) | (np.isnan(got) & np.isnan(want))
+    assert same.all(), "bf16 decode differs from torch's"
+
+
+def pin_bf16_round_vs_torch(ref):
+    """Rounding of fp32 values to bf16 equals torch's RNE cast."""
+    rng = np.random.default_rng(11)
+    f = rng.integers(0, 2**32, size=20000, dtype=np.uint64).astype(np.uint32).view(np.float32)
+    f = f[np.isfinite(f)]
+    # plus exact midpoints and their neighbours
+    mids = ((rng.integers(0, 0x7F00, 3000).astype(np.uint32) << 16) | 0x8000).view(np.float32)
+    f = np.concatenate([f, mids, np.nextafter(mids, np.float32(0)), np.nextafter(mids, np.float32(np.inf))])
+    f = np.concatenate([f, -f])
+    got = ref.bf16_round(f.astype(np.float64))
+    want = inputs.bits(torch.from_numpy(f).to(torch.bfloat16))
+    assert (got == want).all(), f"bf16 rounding differs from torch at {f[got != want][:5]}"
+
+
+def pin_bf16_round_vs_search(ref):
+    """Rounding of doubles (more bits than fp32) to bf16 equals the nearest-even search."""
+    rng = np.random.default_rng(12)
+    v = np.ldexp(rng.uniform(1, 2, 30000), rng.integers(-133, 127, 30000))
+    lo_idx = rng.integers(1, 0x7F7E, 5000)
+    mids = (BF16_GRID[lo_idx] + BF16_GRID[lo_idx + 1]) / 2
+    v = np.concatenate([v, mids, np.nextafter(mids, 0), np.nextafter(mids, np.inf)])
+    v = np.concatenate([v, -v])
+    got = ref.bf16_round(v)
+    want = np_bf16_round(v)
+    assert (got == want).all(), f"bf16 rounding of doubles wrong at {v[got != want][:5]}"
+    assert ref.bf16_round(np.array([np.inf]))[0] == 0x7F80
+    assert ref.bf16_round(np.array([2.0**128]))[0] == 0x7F80
+    assert ref.bf16_round(np.array([-0.0]))[0] == 0x8000
+
+
+def pin_e4m3_table(ref):
+    codes = np.arange(256, dtype=np.uint8)
+    got = ref.e4m3fn_value(codes)
+    want = torch.from_numpy(codes).view(torch.float8_e4m3fn).to(torch.float64).numpy()
+    same = (got == want) | (np.isnan(got) & np.isnan(want))
+    assert same.all(), "E4M3FN decode differs from torch"
+    finite = codes[~np.isnan(want)]
+    assert len(finite) == 254
+    back = ref.e4m3fn(ref.e4m3fn_value(finite))
+    assert (back == finite).all(), "E4M3FN encode(decode(c)) != c"
+    assert ref.e4m3fn_value(np.array([0x7E]))[0] == 448.0
+
+
+def pin_e4m3_bruteforce(ref):
+    """Every bf16 value up to 448 in magnitude: nearest-even search and torch's cast agree."""
+    v = BF16_VALUE[: 0x43E1]            # 0 .. 448 (0x43E0 = 448)
+    assert v[-1] == 448.0
+    v = np.concatenate([v, -v])
+    got = ref.e4m3fn(v)
+    assert (got == np_e4m3(v)).all(), "E4M3FN rounding differs from nearest-even search"
+    want_torch = torch.from_numpy(v).to(torch.float8_e4m3fn).view(torch.uint8).numpy()
+    assert (got == want_torch).all(), "E4M3FN rounding differs from torch's cast"
+    # saturation beyond 448, and NaN
+    big = np.array([449.0, 464.0, 480.0, 1e6, np.inf, -500.0, -np.inf])
+    assert (ref.e4m3fn(big) == np.array([0x7E] * 5 + [0xFE] * 2, np.uint8)).all()
+    assert ref.e4m3fn(np.array([np.nan]))[0] == 0x7F
+
+
+def pin_e4m3_fp32_quotients(ref):
+    """fp32-precision inputs (as the quotient y/scale is) against the search."""
+    rng = np.random.default_rng(13)
+    v = rng.uniform(-460, 460, 40000).astype(np.float32).astype(np.float64)
+    mids = (E4M3_GRID[:-1] + E4M3_GRID[1:]) / 2
+    near = np.concatenate([mids, np.nextafter(mids.astype(np.float32), np.float32(0)).astype(np.float64),
+                           np.nextafter(mids.astype(np.float32), np.float32(np.inf)).astype(np.float64)])
+    v = np.concatenate([v, near, -near])
+    assert (ref.e4m3fn(v) == np_e4m3(v)).all(), "E4M3FN rounding of fp32 values wrong"
+
+
+def pin_e2m1_table(ref):
+    got = ref.e2m1_value(E2M1_CODES.astype(np.uint8))
+    assert (got == E2M1_VALUES).all() and (np.signbit(got) == np.signbit(E2M1_VALUES)).all(), \
+        "E2M1 decode differs from tests/golden/e2m1_codes.txt"
+    assert (ref.e2m1(E2M1_VALUES) == E2M1_CODES).all(), "E2M1 encode(value) != code"
+
+
+def pin_e2m1_bruteforce(ref):
+    """Every bf16 value below 8 in magnitude against the nearest-even search."""
+    v = BF16_VALUE[: 0x4100]             # 0 .. just below 8
+    assert v[-1] < 8.0 and BF16_VALUE[0x4100] == 8.0
+    v = np.concatenate([v, -v, [8.0, 100.0, np.inf, -7.0]])
+    assert (ref.e2m1(v) == np_e2m1(v)).all(), "E2M1 rounding differs from nearest-even search"
+
+
+def pin_e8m0(ref):
+    # power-of-two amax 2^k: floor(log2) = k, byte = k - 2 + 127
+    k = np.arange(-125, 128)
+    assert (ref.e8m0(np.ldexp(1.0, k)) == (k + 125).astype(np.uint8)).all()
+    # every positive finite bf16 value, floor(log2) through frexp
+    v = BF16_VALUE[1:0x7F80]
+    _, e = np.frexp(v)
+    want = np.clip(e - 1 - 2 + 127, 0, 254).astype(np.uint8)
+    assert (ref.e8m0(v) == want).all(), "E8M0 rule wrong"
+    assert ref.e8m0(np.array([6.0]))[0] == 127 and ref.e8m0(np.array([448.0]))[0] == 133
+    assert ref.e8m0(np.array([0.0]))[0] == 0
+    assert (ref.e8m0(np.array([np.nan, np.inf])) == 255).all()
+    # the largest magnitude of a block lands in [4, 8) after scaling (when not clamped)
+    mid = v[(v > 2.0**-120) & (v < 2.0**120)]
+    scaled = mid * ref.e8m0_value(ref.e8m0(mid)) ** -1
+    assert ((scaled >= 4.0) & (scaled < 8.0)).all()
+    assert ref.e8m0_value(np.array([127]))[0] == 1.0
+
+
+def _probe_rows(values_per_row, H, fill):
+    """x = residual = 512 and a weight row per probe row: y == weight exactly when eps = 0."""
+    M = len(values_per_row)
+    w = np.full((M, H), fill, dtype=np.float64)
+    for m, vals in enumerate(values_per_row):
+        w[m, : len(vals)] = vals
+    return w
+
+
+def _golden_fp8():
+    vals, codes = [], []
+    with open(os.path.join(GOLDEN, "fp8_weight_probe.txt")) as f:
+        for line in f:
+            line = line.split("#")[0].strip()
+            if line:
+                parts = line.split()
+                vals.append(float(parts[0]))
+                codes.append(int(parts[1], 16))
+    return np.array(vals), np.array(codes, dtype=np.uint8)
+
+
+def _golden_mxfp4():
+    blocks = []
+    with open(os.path.join(GOLDEN, "mxfp4_weight_probe.txt")) as f:
+        for line in f:
+            line = line.split("#")[0].strip()
+            if not line:
+                continue
+            parts = line.split()
+            if parts[0] == "block":
+                blocks.append(dict(amax=float(parts[1]), byte=int(parts[2]), vals=[], codes=[]))
+            else:
+                blocks[-1]["vals"].append(float(parts[0]))
+                blocks[-1]["codes"].append(int(parts[1], 16))
+    return blocks
+
+
+def fp8_probe_case():
+    """(x, residual, weight) bits with y == weight, and the expected codes and scale."""
+    vals, codes = _golden_fp8()
+    H = 64
+    w = np.ones(H)
+    w[: len(vals)] = vals
+    w_bits = np_bf16_round(w)
+    assert (np_bf16_value(w_bits) == w).all(), "probe values must be bf16 values"
+    x = np.full((1, H), 512.0)
+    xb = np_bf16_round(x)
+    want = np_e4m3(w)  # the filler 1.0 -> 0x38
+    want[: len(vals)] = codes
+    return xb, xb.copy(), w_bits, want, np.float32(1.0)
+
+
+def mxfp4_probe_case():
+    blocks = _golden_mxfp4()
+    H = 32 * len(blocks)
+    w = np.zeros(H)
+    want_codes = np.zeros(H, np.uint8)
+    want_bytes = np.zeros(len(blocks), np.uint8)
+    for b, blk in enumerate(blocks):
+        w[32 * b: 32 * b + len(blk["vals"])] = blk["vals"]
+        want_codes[32 * b: 32 * b + len(blk["codes"])] = blk["codes"]
+        want_bytes[b] = blk["byte"]
+        assert np.abs(w[32 * b: 32 * b + 32]).max() == blk["amax"]
+    w_bits = np_bf16_round(w)
+    assert (np_bf16_value(w_bits) == w).all()
+    x = np_bf16_round(np.full((1, H), 512.0))
+    packed = (want_codes[0::2] | (want_codes[1::2] << 4)).astype(np.uint8)
+    return x, x.copy(), w_bits, packed[None, :], want_bytes[None, :]
+
+
+def pin_fp8_weight_probe(ref):
+    x, r, w, want, scale = fp8_probe_case()
+    out = ref.fp8_per_token(x, r, w, 0.0, emit_y=True)
+    assert (out["y"][0] == w).all(), "probe: y must equal the weight"
+    assert out["scale"][0] == scale, "probe: scale must be 1"
+    bad = np.nonzero(out["q"][0] != want)[0]
+    assert len(bad) == 0, f"probe FP8 codes wrong at {bad[:8]}: {out['q'][0][bad[:8]]} vs {want[bad[:8]]}"
+    assert (out["residual_out"] == np_bf16_round(np.full(x.shape, 1024.0))).all()
+
+
+def pin_mxfp4_weight_probe(ref):
+    x, r, w, packed, bytes_ = mxfp4_probe_case()
+    out = ref.mxfp4(x, r, w, 0.0, emit_y=True)
+    assert (out["y"][0] == w).all()
+    assert (out["scale"] == bytes_).all(), f"probe E8M0 {out['scale']} vs {bytes_}"
+    assert (out["q"] == packed).all(), "probe MXFP4 codes wrong"
+
+
+def pin_group_weight_probe(ref):
+    """Per-group FP8: groups of 32 with amax 448, 224, 1.75 (scales 1, 0.5, 2^-8)."""
+    H = 96
+    w = np.ones(H)
+    w[0], w[1] = 448.0, 1.0625                 # scale 1: codes 0x7E, 0x38
+    w[32:64] = 0.25
+    w[32], w[33] = 224.0, 0.53125              # scale 0.5: 224 -> 448 (0x7E), 0.53125 -> 1.0625 (0x38)
+    w[64:96] = 0.0078125                       # 2^-7
+    w[64] = 1.75                               # scale 1.75 / 448 = 2^-8: 2^-7 -> 2.0 (0x40)
+    w_bits = np_bf16_round(w)
+    x = np_bf16_round(np.full((1, H), 512.0))
+    out = ref.fp8_per_group(x, x.copy(), w_bits, 0.0, 32)
+    assert (out["scale"][0] == np.array([1.0, 0.5, 2.0**-8], np.float32)).all(), out["scale"]
+    q = out["q"][0]
+    assert q[0] == 0x7E and q[1] == 0x38 and q[2] == 0x38
+    assert q[32] == 0x7E and q[33] == 0x38 and q[34] == 0x30   # 0.25 / 0.5 = 0.5 -> 0x30
+    assert q[64] == 0x7E and q[65] == 0x40
+
+
+def pin_constant_row(ref):
+    """x = residual = c/2: residual_out = c and rstd = 1/sqrt(c^2 + eps); with
+    w = 1 and c = +-1, y = +-1 (1/sqrt(1 + 1e-6) rounds back to 1 in bf16)."""
+    for c in (1.0, -1.0):
+        H = 256
+        xb = np_bf16_round(np.full((2, H), c / 2))
+        w = np_bf16_round(np.ones(H))
+        o = ref.fp8_per_token(xb, xb.copy(), w, 1e-6, emit_y=True)
+        assert (o["residual_out"] == np_bf16_round(np.full((2, H), c))).all()
+        assert (o["y"] == np_bf16_round(np.full((2, H), c))).all()
+        assert (o["scale"] == np.float32(1.0) / np.float32(448.0)).all()
+        assert (o["q"] == (0x7E if c > 0 else 0xFE)).all()
+        m = ref.mxfp4(xb, xb.copy(), w, 1e-6)
+        assert (m["scale"] == 125).all()
+        assert (m["q"] == (0x66 if c > 0 else 0xEE)).all()
+        g = ref.fp8_per_group(xb, xb.copy(), w, 1e-6, 128)
+        assert (g["q"] == (0x7E if c > 0 else 0xFE)).all()
+    # a large constant: rstd = 1/sqrt(c^2 + eps) with eps negligible, y = w
+    H = 64
+    xb = np_bf16_round(np.full((1, H), 3.0))          # c = 6
+    w = np_bf16_round(np.linspace(0.5, 1.5, H))
+    o = ref.fp8_per_token(xb, xb.copy(), w, 1e-6, emit_y=True)
+    want = np_bf16_round(6.0 / np.sqrt(36.0 + 1e-6) * np_bf16_value(w))
+    assert (o["y"][0] == want).all()
+
+
+def pin_zero_and_sign(ref):
+    """All-zero granules: scale 0 / byte 0 and codes keeping the sign of zero."""
+    H = 64
+    x = np.zeros((1, H), np.uint16)
+    x[0, 1::2] = 0x8000        # -0
+    r = x.copy()               # -0 + -0 = -0; 0 + 0 = 0
+    w = np_bf16_round(np.ones(H))
+    o = ref.fp8_per_token(x, r, w, 1e-6)
+    assert o["scale"][0] == 0.0
+    assert (o["q"][0, 0::2] == 0x00).all() and (o["q"][0, 1::2] == 0x80).all()
+    m = ref.mxfp4(x, r, w, 1e-6)
+    assert (m["scale"] == 0).all()
+    assert (m["q"] == 0x80).all()          # low nibble +0 (0x0), high nibble -0 (0x8)
+
+
+def pin_independent_rows(ref):
+    """The whole step against the independent numpy formulation on small rows
+    (several shapes, random data with ±0 and large values mixed in)."""
+    rng = np.random.default_rng(21)
+    for (M, H) in [(1, 32), (2, 64), (3, 96), (3, 128), (2, 544), (4, 2048)]:
+        d = inputs.random_rows(M, H, seed=100 + H + M)
+        xb, rb, wb = inputs.bits(d["x"]), inputs.bits(d["residual"]), inputs.bits(d["weight"])
+        xb = xb.copy()
+        xb[rng.random(xb.shape) < 0.05] = 0x8000
+        big = rng.random(xb.shape) < 0.02
+        xb[big] = np_bf16_round(np_bf16_value(xb[big]) * 300)
+        for eps in (1e-6, 0.5):
+            res, y = np_norm(xb, rb, wb, eps)
+            o = ref.fp8_per_token(xb, rb, wb, eps, emit_y=True)
+            assert (o["residual_out"] == res).all(), "residual_out differs from torch's bf16 add"
+            assert (o["y"] == y).all(), f"y differs from the numpy formulation at {M}x{H}"
+            q, s = np_fp8(y, H)
+            assert (o["scale"] == s[:, 0]).all() and (o["q"] == q).all(), "per-token FP8 differs"
+            for g in (32, 128):
+                if H % g == 0:
+                    og = ref.fp8_per_group(xb, rb, wb, eps, g)
+                    q, s = np_fp8(y, g)
+                    assert (og["scale"] == s).all() and (og["q"] == q).all(), f"group {g} differs"
+            om = ref.mxfp4(xb, rb, wb, eps)
+            packed, byte = np_mxfp4(y)
+            assert (om["scale"] == byte).all(), "E8M0 bytes differ"
+            assert (om["q"] == packed).all(), "MXFP4 codes differ"
+
+
+def pin_strided_inputs(ref):
+    d = inputs.random_rows(3, 128, seed=5)
+    xb, rb, wb = inputs.bits(d["x"]), inputs.bits(d["residual"]), inputs.bits(d["weight"])
+    wide = np.zeros((3, 200), np.uint16)
+    wide[:, 40:168] = xb
+    a = ref.fp8_per_token(xb, rb, wb, 1e-6)
+    b = ref.fp8_per_token(wide[:, 40:168], rb, wb, 1e-6)
+    for key in ("residual_out", "q", "scale"):
+        assert (a[key] == b[key]).all()
+
+
+def pin_qk(ref):
+    w = inputs.QKWorkload("qk_small", 3, 4, 2, 64, seed=77)
+    d = inputs.qk_inputs(w, ld_k=2 * 64 + 24)
+    qg, k, qw, kw = (inputs.bits(d[n]) for n in ("qg", "k", "q_w", "k_w"))
+    o = ref.qk_gemma_rmsnorm_gate(qg, k, qw, kw, w.Hq, w.Hk, w.D, w.eps)
+    q2, k2, g2 = np_qk(qg, k, qw, kw, w.Hq, w.Hk, w.D, w.eps)
+    assert (o["gate"] == g2).all(), "gate must be copied bit for bit from the odd D-slices"
+    assert (o["q"] == q2).all() and (o["k"] == k2).all(), "QK GemmaRMSNorm differs from numpy"
+    # probe: every value 1024 and eps = 0 gives rstd = 2^-10 exactly, out = bf16(1 + w)
+    T, Hq, Hk, D = 2, 2, 1, 64
+    qg = np_bf16_round(np.full((T, 2 * Hq * D), 1024.0))
+    k = np_bf16_round(np.full((T, Hk * D), -1024.0))
+    rng = np.random.default_rng(3)
+    qw = np_bf16_round(rng.normal(0, 0.3, D))
+    kw = np_bf16_round(rng.normal(0, 0.3, D))
+    o = ref.qk_gemma_rmsnorm_gate(qg, k, qw, kw, Hq, Hk, D, 0.0)
+    one_plus = lambda wb: inputs.bits((1.0 + inputs.from_bits(wb).float()).to(torch.bfloat16))
+    assert (o["q"] == one_plus(qw)[None, None, :]).all()
+    assert (o["k"] == (one_plus(kw) ^ np.uint16(0x8000))[None, None, :]).all()
+
+
+def pin_invariants_on_workloads(ref):
+    """On the C1..C3 workloads: the max-|y| element of each granule encodes at
+    the top of the format, dequantized codes stay within half a step of y, and
+    residual_out is torch's bf16 add."""
+    for wl, kind in ((inputs.FP8_TOKEN_SMALL, "token"), (inputs.FP8_GROUP_DECODE, "group"),
+                     (inputs.MXFP4_DECODE, "mx")):
+        d = inputs.row_inputs(wl)
+        xb, rb, wb = inputs.bits(d["x"]), inputs.bits(d["residual"]), inputs.bits(d["weight"])
+        if kind == "token":
+            o = ref.fp8_per_token(xb, rb, wb, wl.eps, emit_y=True)
+            gran = wl.H
+        elif kind == "group":
+            o = ref.fp8_per_group(xb, rb, wb, wl.eps, 128, emit_y=True)
+            gran = 128
+        else:
+            o = ref.mxfp4(xb, rb, wb, wl.eps, emit_y=True)
+            gran = 32
+        assert (o["residual_out"] == torch_bf16_add(xb, rb)).all()
+        y = np_bf16_value(o["y"]).reshape(wl.M, -1, gran)
+        amax_idx = np.abs(y).argmax(axis=2)
+        if kind != "mx":
+            q = o["q"].reshape(wl.M, -1, gran)
+            top = np.take_along_axis(q, amax_idx[:, :, None], 2)[:, :, 0]
+            assert ((top & 0x7F) == 0x7E).all(), "the granule's max must encode as +-448"
+            deq = ref.e4m3fn_value(q.reshape(-1)).reshape(q.shape) * o["scale"].reshape(wl.M, -1, 1)
+            step = np.maximum(np.abs(y), 2.0**-6 * o["scale"].reshape(wl.M, -1, 1)) * 2.0**-4
+            assert (np.abs(deq - y) <= step * 1.0001 + 1e-30).all(), "dequantized FP8 off by > half step"
+        else:
+            codes = np.stack([o["q"] & 0xF, o["q"] >> 4], axis=2).reshape(wl.M, -1, 32)
+            top = np.take_along_axis(codes, amax_idx[:, :, None], 2)[:, :, 0]
+            assert ((top & 0x7) >= 6).all(), "the block's max must encode as 4 or 6"
+            sc = ref.e8m0_value(o["scale"].reshape(-1)).reshape(wl.M, -1, 1)
+            deq = ref.e2m1_value(codes.reshape(-1)).reshape(codes.shape) * sc
+            half = np.where(np.abs(y) / sc < 2, 0.25, np.where(np.abs(y) / sc < 4, 0.5, 1.0)) * sc
+            ok = (np.abs(deq - y) <= half) | (np.abs(y) / sc > 6)
+            assert ok.all(), "dequantized E2M1 off by more than half a step"
+
+
+ALL_PINS = [
+    pin_bf16_decode, pin_bf16_round_vs_torch, pin_bf16_round_vs_search,
+    pin_e4m3_table, pin_e4m3_bruteforce, pin_e4m3_fp32_quotients,
+    pin_e2m1_table, pin_e2m1_bruteforce, pin_e8m0,
+    pin_fp8_weight_probe, pin_mxfp4_weight_probe, pin_group_weight_probe,
+    pin_constant_row, pin_zero_and_sign, pin_independent_rows,
+    pin_strided_inputs, pin_qk, pin_invariants_on_workloads,
+]
