@@ -1,0 +1,326 @@
+"""Benchmark of the fused residual-add -> RMSNorm -> quantization path on one MI355X.
+
+One step = one pass of every step of the hot path over one batch of synthetic
+rows resident in HBM:
+  rmsnorm_quant_fp8_per_token   [8192, 4096]
+  rmsnorm_quant_fp8_per_group   [8192, 4096], group 128
+  rmsnorm_quant_mxfp4           [8192, 4096]
+  qk_gemma_rmsnorm_gate         64 tokens, 16 q heads, 2 k heads, head dim 256
+Each step reads a different input set (4 sets rotate, 512 MiB of inputs in all,
+twice the 256 MB Infinity Cache), so every call reads cold rows from HBM.
+
+value = algorithmic bytes of the step / step time (GB/s).  Algorithmic bytes
+count every tensor once: x, residual, weight read; residual_out, codes, scales
+written (the optional bf16 side output is not requested here).
+
+Also reported: per-kernel time and GB/s (HIP events on the launch stream),
+decode-size microseconds per call (M = 16, H = 4096, all formats; graph replay
+of back-to-back calls over rotating inputs, as the pages time kernels) next to
+the launch floor of a one-element kernel timed the same way, and the CPU oracle
+timed on the host cores as the CPU baseline.
+"""
+
+from __future__ import annotations
+
+import argparse
+import json
+import os
+import sys
+import time
+
+ROOT = os.path.dirname(os.path.abspath(__file__))
+if ROOT not in sys.path:
+    sys.path.insert(0, ROOT)
+
+HBM_PEAK_GBS = 8000.0
+METRIC = "achieved HBM GB/s (% of peak) + µs/call at M=16 and M=8192, H=4096"
+
+
+def row_bytes(fmt: str, M: int, H: int, group: int = 128) -> int:
+    base = 2 * M * H * 3 + 2 * H  # x, residual, residual_out, weight
+    if fmt == "fp8_token":
+        return base + M * H + 4 * M
+    if fmt == "fp8_group":
+        return base + M * H + 4 * M * (H // group)
+    return base + M * H // 2 + M * H // 32
+
+
+def qk_bytes(T: int, Hq: int, Hk: int, D: int) -> int:
+    return 2 * (T * 2 * Hq * D + T * Hk * D + 2 * D) + 2 * (2 * T * Hq * D + T * Hk * D)
+
+
+def parse():
+    p = argparse.ArgumentParser()
+    p.add_argument("--gpus", type=int, default=1)
+    p.add_argument("--steps", type=int, default=50)
+    p.add_argument("--warmup", type=int, default=10)
+    p.add_argument("--sets", type=int, default=4, help="rotating input sets for the prefill rows")
+    p.add_argument("--no-cpu-baseline", action="store_true")
+    p.add_argument("--no-decode", action="store_true")
+    p.add_argument("--profile-pass", action="store_true",
+                   help="short run for rocprofv3: warmup + steps only, plus a 256 MiB device copy for calibration")
+    return p.parse_args()
+
+
+def main():
+    args = parse()
+    world = int(os.environ.get("WORLD_SIZE", "1"))
+    if args.gpus != 1 or world != 1:
+        print(f"bench.py runs on one GPU only (asked for {max(args.gpus, world)}): this path has no multi-GPU "
+              "part; rows shard across GPUs without communication, see DESIGN.md.", file=sys.stderr)
+        sys.exit(2)
+
+    import torch
+
+    import rmsnorm_activation_quantization_amd as rq
+    from rmsnorm_activation_quantization_amd import inputs
+
+    dev = torch.device("cuda:0")
+    rq.lib()
+    stream = torch.cuda.current_stream()
+
+    # ---- inputs resident in HBM ----
+    wl = inputs.PREFILL
+    M, H = wl.M, wl.H
+    sets = []
+    for s in range(args.sets):
+        d = inputs.row_inputs(wl, set_index=s)
+        sets.append({k: v.to(dev) for k, v in d.items()})
+    outs = []
+    for s in range(args.sets):
+        outs.append(dict(
+            t=(torch.empty((M, H), dtype=torch.uint8, device=dev), torch.empty((M, H), dtype=torch.bfloat16, device=dev),
+               torch.empty((M,), dtype=torch.float32, device=dev)),
+            g=(torch.empty((M, H), dtype=torch.uint8, device=dev), torch.empty((M, H), dtype=torch.bfloat16, device=dev),
+               torch.empty((M, H // 128), dtype=torch.float32, device=dev)),
+            m=(torch.empty((M, H // 2), dtype=torch.uint8, device=dev),
+               torch.empty((M, H), dtype=torch.bfloat16, device=dev),
+               torch.empty((M, H // 32), dtype=torch.uint8, device=dev)),
+        ))
+    qw = inputs.QK_DECODE
+    qd = {k: v.to(dev) for k, v in inputs.qk_inputs(qw).items()}
+    qk_out = (torch.empty((qw.T, qw.Hq, qw.D), dtype=torch.bfloat16, device=dev),
+              torch.empty((qw.T, qw.Hk, qw.D), dtype=torch.bfloat16, device=dev),
+              torch.empty((qw.T, qw.Hq, qw.D), dtype=torch.bfloat16, device=dev))
+
+    kernels = ["fp8_token", "fp8_group", "mxfp4", "qk"]
+    nbytes = {"fp8_token": row_bytes("fp8_token", M, H), "fp8_group": row_bytes("fp8_group", M, H),
+              "mxfp4": row_bytes("mxfp4", M, H), "qk": qk_bytes(qw.T, qw.Hq, qw.Hk, qw.D)}
+
+    def call(name, s):
+        i, o = sets[s], outs[s]
+        if name == "fp8_token":
+            q, ro, sc = o["t"]
+            r = rq.rmsnorm_quant_fp8_per_token(i["x"], i["residual"], i["weight"], wl.eps, q_out=q, residual_out=ro,
+                                               scale_out=sc)
+        elif name == "fp8_group":
+            q, ro, sc = o["g"]
+            r = rq.rmsnorm_quant_fp8_per_group(i["x"], i["residual"], i["weight"], wl.eps, 128, q_out=q,
+                                               residual_out=ro, scale_out=sc)
+        elif name == "mxfp4":
+            q, ro, sc = o["m"]
+            r = rq.rmsnorm_quant_mxfp4(i["x"], i["residual"], i["weight"], wl.eps, q_out=q, residual_out=ro,
+                                       scale_out=sc)
+        else:
+            r = rq.qk_gemma_rmsnorm_gate(qd["qg"], qd["k"], qd["q_w"], qd["k_w"], qw.Hq, qw.Hk, qw.D, qw.eps,
+                                         q_out=qk_out[0], k_out=qk_out[1], gate_out=qk_out[2])
+        if r is None:
+            raise RuntimeError(f"{name}: the library refused a supported shape")
+
+    # ---- warmup ----
+    for w in range(args.warmup):
+        for name in kernels:
+            call(name, w % args.sets)
+    torch.cuda.synchronize()
+
+    # ---- timed region: K steps, events around every kernel on the launch stream ----
+    ev = {name: [(torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True))
+                 for _ in range(args.steps)] for name in kernels}
+    start, stop = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+    torch.cuda.synchronize()
+    t0 = time.perf_counter()
+    start.record(stream)
+    for k in range(args.steps):
+        s = k % args.sets
+        for name in kernels:
+            ev[name][k][0].record(stream)
+            call(name, s)
+            ev[name][k][1].record(stream)
+    stop.record(stream)
+    torch.cuda.synchronize()
+    wall = time.perf_counter() - t0
+    total_ms = start.elapsed_time(stop)
+    ms_per_step = total_ms / args.steps
+    per_kernel_us = {name: 1000.0 * sum(a.elapsed_time(b) for a, b in ev[name]) / args.steps for name in kernels}
+    step_bytes = sum(nbytes.values())
+    value = step_bytes / (ms_per_step * 1e-3) / 1e9
+
+    if args.profile_pass:
+        # A plain device copy of known size, for scaling the HBM byte counters.
+        src = torch.empty(256 << 20, dtype=torch.uint8, device=dev)
+        dst = torch.empty_like(src)
+        for _ in range(3):
+            dst.copy_(src)
+        torch.cuda.synchronize()
+
+    kernels_out = {}
+    for name in kernels:
+        us = per_kernel_us[name]
+        gbs = nbytes[name] / (us * 1e-6) / 1e9
+        kernels_out[name] = {"us": round(us, 3), "bytes": nbytes[name], "GBps": round(gbs, 1),
+                             "frac_of_peak": round(gbs / HBM_PEAK_GBS, 4)}
+
+    dom = max(("fp8_token", "fp8_group", "mxfp4"), key=lambda n: nbytes[n])
+    roofline = {"bound": "hbm", "kernel": f"rmsnorm_quant_{dom} [{M}, {H}]",
+                "achieved": kernels_out[dom]["GBps"], "peak": HBM_PEAK_GBS, "unit": "GB/s",
+                "frac": kernels_out[dom]["frac_of_peak"], "traffic": measured_traffic(dom)}
+
+    result = {
+        "metric": METRIC, "value": round(value, 1), "unit": "GB/s", "n_gpus": 1, "steps": args.steps,
+        "warmup": args.warmup, "ms_per_step": round(ms_per_step, 5), "higher_is_better": True, "scaling": "weak",
+        "vs_baseline": None, "dtype": "f32", "data": "synthetic",
+        "config": {"workload": f"prefill rows [{M}, {H}] bf16 (per-token FP8, per-group-128 FP8, MXFP4) + "
+                               f"QK GemmaRMSNorm+gate T={qw.T} Hq={qw.Hq} Hk={qw.Hk} D={qw.D}",
+                   "M": M, "H": H, "eps": wl.eps, "rotating_input_sets": args.sets, "step_bytes": step_bytes},
+        "frac_of_peak": round(value / HBM_PEAK_GBS, 4),
+        "kernels": kernels_out,
+        "roofline": roofline,
+        "wall_s_timed": round(wall, 4),
+    }
+    if not args.no_decode and not args.profile_pass:
+        result["decode"] = decode_latency(torch, rq, inputs, dev)
+    if not args.no_cpu_baseline and not args.profile_pass:
+        result["cpu_baseline"] = cpu_baseline(inputs, wl, qw, nbytes)
+    print(json.dumps(result), flush=True)
+
+
+def measured_traffic(kernel: str):
+    """HBM bytes per launch from the committed rocprofv3 counter summary, or
+    None when the kernel source changed since the counters were taken."""
+    import hashlib
+    path = os.path.join(ROOT, "profiles", "hbm_traffic_prefill_8192x4096.md")
+    src = os.path.join(ROOT, "rmsnorm_activation_quantization_amd", "csrc", "rmsnorm_quant.hip")
+    if not os.path.exists(path):
+        return None
+    digest = hashlib.sha256(open(src, "rb").read()).hexdigest()[:16]
+    for line in open(path):
+        if line.startswith("traffic-json:"):
+            rec = json.loads(line.split(":", 1)[1])
+            if rec.get("source_sha256_16") == digest and kernel in rec.get("bytes_per_launch", {}):
+                return rec["bytes_per_launch"][kernel]
+    return None
+
+
+def decode_latency(torch, rq, inputs, dev, calls: int = 200, replays: int = 7):
+    """Per-call microseconds at decode sizes: a graph of `calls` back-to-back
+    calls over rotating inputs (more bytes than the Infinity Cache), replayed;
+    the median replay divided by `calls`.  The launch floor is a one-element
+    fill kernel timed the same way."""
+    import statistics
+    res = {}
+    cases = [("fp8_token", inputs.DECODE_4096), ("fp8_group", inputs.DECODE_4096), ("mxfp4", inputs.DECODE_4096),
+             ("fp8_token", inputs.FP8_TOKEN_SMALL), ("fp8_group", inputs.FP8_GROUP_DECODE),
+             ("mxfp4", inputs.MXFP4_DECODE)]
+    nsets = 1024  # decode sets of 256 KiB to 450 KiB: 256 MiB or more of rows in rotation
+
+    def graph_us(fn):
+        s = torch.cuda.Stream()
+        s.wait_stream(torch.cuda.current_stream())
+        with torch.cuda.stream(s):
+            for i in range(3):
+                fn(i)
+        torch.cuda.current_stream().wait_stream(s)
+        torch.cuda.synchronize()
+        g = torch.cuda.CUDAGraph()
+        with torch.cuda.graph(g):
+            for i in range(calls):
+                fn(i)
+        times = []
+        for _ in range(replays):
+            a, b = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+            a.record()
+            g.replay()
+            b.record()
+            torch.cuda.synchronize()
+            times.append(1000.0 * a.elapsed_time(b) / calls)
+        return statistics.median(times)
+
+    one = torch.zeros(1, device=dev)
+    res["launch_floor_us"] = round(graph_us(lambda i: one.fill_(float(i))), 3)
+    for fmt, wl in cases:
+        M, H = wl.M, wl.H
+        base = inputs.row_inputs(wl)
+        # distinct rotating copies: a pool of distinct rows, sliced per set
+        x = torch.randn(nsets, M, H, device=dev).to(torch.bfloat16)
+        r = torch.randn(nsets, M, H, device=dev).to(torch.bfloat16)
+        x[0].copy_(base["x"])
+        r[0].copy_(base["residual"])
+        w = base["weight"].to(dev)
+        ro = torch.empty((M, H), dtype=torch.bfloat16, device=dev)
+        if fmt == "mxfp4":
+            q = torch.empty((M, H // 2), dtype=torch.uint8, device=dev)
+            sc = torch.empty((M, H // 32), dtype=torch.uint8, device=dev)
+            fn = lambda i: rq.rmsnorm_quant_mxfp4(x[i % nsets], r[i % nsets], w, wl.eps, q_out=q, residual_out=ro,
+                                                  scale_out=sc)
+        elif fmt == "fp8_group":
+            q = torch.empty((M, H), dtype=torch.uint8, device=dev)
+            sc = torch.empty((M, H // 128), dtype=torch.float32, device=dev)
+            fn = lambda i: rq.rmsnorm_quant_fp8_per_group(x[i % nsets], r[i % nsets], w, wl.eps, 128, q_out=q,
+                                                          residual_out=ro, scale_out=sc)
+        else:
+            q = torch.empty((M, H), dtype=torch.uint8, device=dev)
+            sc = torch.empty((M,), dtype=torch.float32, device=dev)
+            fn = lambda i: rq.rmsnorm_quant_fp8_per_token(x[i % nsets], r[i % nsets], w, wl.eps, q_out=q,
+                                                          residual_out=ro, scale_out=sc)
+        us = graph_us(fn)
+        res[f"{fmt}_{M}x{H}_us"] = round(us, 3)
+        del x, r
+    qw = inputs.QK_DECODE
+    qd = {k: v.to(dev) for k, v in inputs.qk_inputs(qw).items()}
+    nq = 256
+    qg = qd["qg"].unsqueeze(0).repeat(nq, 1, 1)
+    kk = qd["k"].unsqueeze(0).repeat(nq, 1, 1)
+    outs = [torch.empty((qw.T, h, qw.D), dtype=torch.bfloat16, device=dev) for h in (qw.Hq, qw.Hk, qw.Hq)]
+    res[f"qk_{qw.T}x{qw.Hq}x{qw.Hk}x{qw.D}_us"] = round(graph_us(
+        lambda i: rq.qk_gemma_rmsnorm_gate(qg[i % nq], kk[i % nq], qd["q_w"], qd["k_w"], qw.Hq, qw.Hk, qw.D, qw.eps,
+                                           q_out=outs[0], k_out=outs[1], gate_out=outs[2])), 3)
+    res["pages_context_us"] = {"qk_gemma_rmsnorm_gate_kernel_mi355x_tp2": 4.6, "launch_floor_gfx950": 4.2}
+    return res
+
+
+def cpu_baseline(inputs, wl, qw, nbytes):
+    """The oracle as it stands, threaded over row slices (ctypes releases the
+    GIL), on the host of the GPU machine.  Sample: the same step on the first
+    `rows` rows of the prefill set (all 8192 when time allows), plus the QK case."""
+    import concurrent.futures as cf
+
+    import oracle
+    ref = oracle.get()
+    rows = 2048
+    d = inputs.row_inputs(wl)
+    xb, rb, wb = (inputs.bits(d[k])[:rows] if k != "weight" else inputs.bits(d[k]) for k in
+                  ("x", "residual", "weight"))
+    qd = inputs.qk_inputs(qw)
+    qargs = [inputs.bits(qd[n]) for n in ("qg", "k", "q_w", "k_w")]
+    threads = max(1, min(16, len(os.sched_getaffinity(0))))
+    bounds = [(i * rows // threads, (i + 1) * rows // threads) for i in range(threads)]
+
+    def part(lo, hi):
+        ref.fp8_per_token(xb[lo:hi], rb[lo:hi], wb, wl.eps)
+        ref.fp8_per_group(xb[lo:hi], rb[lo:hi], wb, wl.eps, 128)
+        ref.mxfp4(xb[lo:hi], rb[lo:hi], wb, wl.eps)
+
+    t0 = time.perf_counter()
+    with cf.ThreadPoolExecutor(threads) as ex:
+        list(ex.map(lambda b: part(*b), bounds))
+    ref.qk_gemma_rmsnorm_gate(*qargs, qw.Hq, qw.Hk, qw.D, qw.eps)
+    elapsed = time.perf_counter() - t0
+    sample_bytes = (row_bytes("fp8_token", rows, wl.H) + row_bytes("fp8_group", rows, wl.H) +
+                    row_bytes("mxfp4", rows, wl.H) + nbytes["qk"])
+    return {"value": round(sample_bytes / elapsed / 1e9, 3), "unit": "GB/s", "cores": threads, "kind": "oracle",
+            "sample": f"one step on the first {rows} of {wl.M} rows (H={wl.H}, three formats) plus the QK case",
+            "seconds": round(elapsed, 3)}
+
+
+if __name__ == "__main__":
+    main()

@@ -88,14 +88,17 @@ class Oracle:
         lib.rq_ref_qk_gemma_rmsnorm_gate.argtypes = [
             _u16p, _i64, _u16p, _i64, _u16p, _u16p, _i64, _i64, _i64, _i64, ctypes.c_float,
             _u16p, _u16p, _u16p]
-        for name in ("rq_ref_rmsnorm_quant_fp8_per_token", "rq_ref_rmsnorm_quant_fp8_per_group",
+        lib.rq_ref_quantize_fp8.argtypes = [_u16p, _i64, _i64, _i64, _u8p, _f32p]
+        lib.rq_ref_quantize_mxfp4.argtypes = [_u16p, _i64, _i64, _u8p, _u8p]
+        for name in ("rq_ref_quantize_fp8", "rq_ref_quantize_mxfp4",
+                     "rq_ref_rmsnorm_quant_fp8_per_token", "rq_ref_rmsnorm_quant_fp8_per_group",
                      "rq_ref_rmsnorm_quant_mxfp4", "rq_ref_qk_gemma_rmsnorm_gate"):
             getattr(lib, name).restype = ctypes.c_int
 
     # ---- scalar format functions (element-wise over arrays) ----
     def bf16_value(self, bits) -> np.ndarray:
         with np.errstate(invalid="ignore"):
-                return np.vectorize(self.lib.rq_ref_f64_from_bf16, otypes=[np.float64])(
+            return np.vectorize(self.lib.rq_ref_f64_from_bf16, otypes=[np.float64])(
                 np.asarray(bits, dtype=np.uint16))
 
     def bf16_round(self, v) -> np.ndarray:
@@ -171,6 +174,28 @@ class Oracle:
             _ptr(x, _u16p), ldx, _ptr(residual, _u16p), ldr, _ptr(weight, _u16p), M, H, eps,
             _ptr(out["residual_out"], _u16p), _ptr(out["q"], _u8p), _ptr(out["scale"], _u8p),
             _ptr(out["y"], _u16p))
+        if rc != 0:
+            raise ValueError("oracle rejected the arguments")
+        return out
+
+    # ---- the quantize step alone ----
+    def quantize_fp8(self, y, group=None) -> dict:
+        y = np.ascontiguousarray(y, dtype=np.uint16)
+        M, H = y.shape
+        group = H if group is None else group
+        out = dict(q=np.zeros((M, H), np.uint8), scale=np.zeros((M, H // group), np.float32))
+        rc = self.lib.rq_ref_quantize_fp8(_ptr(y, _u16p), M, H, group, _ptr(out["q"], _u8p),
+                                          _ptr(out["scale"], _f32p))
+        if rc != 0:
+            raise ValueError("oracle rejected the arguments")
+        return out
+
+    def quantize_mxfp4(self, y) -> dict:
+        y = np.ascontiguousarray(y, dtype=np.uint16)
+        M, H = y.shape
+        out = dict(q=np.zeros((M, H // 2), np.uint8), scale=np.zeros((M, H // 32), np.uint8))
+        rc = self.lib.rq_ref_quantize_mxfp4(_ptr(y, _u16p), M, H, _ptr(out["q"], _u8p),
+                                            _ptr(out["scale"], _u8p))
         if rc != 0:
             raise ValueError("oracle rejected the arguments")
         return out

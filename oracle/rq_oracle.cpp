@@ -271,6 +271,31 @@ int rq_ref_rmsnorm_quant_mxfp4(
   return 0;
 }
 
+int rq_ref_quantize_fp8(const uint16_t* y, int64_t M, int64_t H, int64_t group,
+                        uint8_t* q_out, float* scale_out) {
+  if (M < 0 || H <= 0 || group <= 0 || H % group != 0) return 1;
+  if (M > 0 && (!y || !q_out || !scale_out)) return 1;
+  const int64_t G = H / group;
+  for (int64_t m = 0; m < M; ++m)
+    for (int64_t g = 0; g < G; ++g)
+      quant_fp8_granule(y + m * H + g * group, group, q_out + m * H + g * group, scale_out + m * G + g);
+  return 0;
+}
+
+int rq_ref_quantize_mxfp4(const uint16_t* y, int64_t M, int64_t H, uint8_t* q_out, uint8_t* scale_out) {
+  if (M < 0 || H <= 0 || H % 32 != 0) return 1;
+  if (M > 0 && (!y || !q_out || !scale_out)) return 1;
+  const int64_t B = H / 32;
+  uint8_t codes[32];
+  for (int64_t m = 0; m < M; ++m)
+    for (int64_t b = 0; b < B; ++b) {
+      quant_mxfp4_block(y + m * H + b * 32, codes, scale_out + m * B + b);
+      for (int j = 0; j < 16; ++j)
+        q_out[m * (H / 2) + b * 16 + j] = (uint8_t)(codes[2 * j] | (codes[2 * j + 1] << 4));
+    }
+  return 0;
+}
+
 int rq_ref_qk_gemma_rmsnorm_gate(
     const uint16_t* qg, int64_t ld_qg, const uint16_t* k, int64_t ld_k,
     const uint16_t* q_w, const uint16_t* k_w, int64_t T, int64_t Hq, int64_t Hk,

@@ -89,6 +89,16 @@ int rq_ref_rmsnorm_quant_mxfp4(
     const uint16_t* weight, int64_t M, int64_t H, float eps,
     uint16_t* residual_out, uint8_t* q_out, uint8_t* scale_out, uint16_t* y_out);
 
+/* ---- the quantize step alone (the last launch of the unfused sequence) ---- */
+
+/* FP8 quantization of a bf16 tensor y [M, H]: one scale per `group`
+ * consecutive elements (group == H: per token), same rules as above. */
+int rq_ref_quantize_fp8(const uint16_t* y, int64_t M, int64_t H, int64_t group,
+                        uint8_t* q_out, float* scale_out);
+/* MXFP4 quantization of a bf16 tensor y [M, H], same rules as above. */
+int rq_ref_quantize_mxfp4(const uint16_t* y, int64_t M, int64_t H,
+                          uint8_t* q_out, uint8_t* scale_out);
+
 /* ---- the QK variant ---- */
 
 /* qg: [T, ld_qg] with per-token layout [q_0 | gate_0 | q_1 | gate_1 | ...],

@@ -1,1 +1,21 @@
-"""MI355X (gfx950) fused residual-add -> RMSNorm -> activation quantization."""
+"""MI355X (gfx950) fused residual-add -> RMSNorm -> activation quantization.
+
+The compute lives in librmsnorm_quant.so (hand-written HIP kernels behind a C
+ABI, include/rmsnorm_quant.h); this package only marshals torch tensors into
+that ABI.  Entry points keep the C names:
+
+  rmsnorm_quant_fp8_per_token   residual add + RMSNorm + per-token FP8 E4M3FN
+  rmsnorm_quant_fp8_per_group   ... + per-group FP8 (group 32..512)
+  rmsnorm_quant_mxfp4           ... + MXFP4 (E2M1 codes, E8M0 scale per 32)
+  qk_gemma_rmsnorm_gate         QK GemmaRMSNorm + gate de-interleave
+"""
+
+from .binding import (RQ_ERR_HIP, RQ_ERR_INVALID, RQ_ERR_UNSUPPORTED, RQ_MAX_HEAD_DIM, RQ_MAX_HIDDEN, RQ_OK,
+                      lib, library_path, qk_gemma_rmsnorm_gate, rmsnorm_quant_fp8_per_group,
+                      rmsnorm_quant_fp8_per_token, rmsnorm_quant_mxfp4, status_string)
+
+__all__ = [
+    "rmsnorm_quant_fp8_per_token", "rmsnorm_quant_fp8_per_group", "rmsnorm_quant_mxfp4", "qk_gemma_rmsnorm_gate",
+    "lib", "library_path", "status_string", "RQ_OK", "RQ_ERR_INVALID", "RQ_ERR_UNSUPPORTED", "RQ_ERR_HIP",
+    "RQ_MAX_HIDDEN", "RQ_MAX_HEAD_DIM",
+]

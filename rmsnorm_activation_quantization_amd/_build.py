@@ -1,0 +1,31 @@
+"""Build librmsnorm_quant.so in-tree with hipcc for gfx950."""
+
+from __future__ import annotations
+
+import os
+import subprocess
+
+PKG = os.path.dirname(os.path.abspath(__file__))
+ROOT = os.path.dirname(PKG)
+SOURCE = os.path.join(PKG, "csrc", "rmsnorm_quant.hip")
+INCLUDE = os.path.join(ROOT, "include")
+LIBRARY = os.path.join(PKG, "librmsnorm_quant.so")
+
+HIPCC = os.environ.get("HIPCC", "/opt/rocm/bin/hipcc")
+HIPCC_FLAGS = [
+    "--offload-arch=gfx950", "-O3", "-std=c++17", "-fPIC", "-shared",
+    # every rounding is the one written in the source: no FMA contraction
+    "-ffp-contract=off",
+    # no packed fp32 instructions (v_pk_*_f32) anywhere in the device code
+    "-Xclang", "-target-feature", "-Xclang", "-packed-fp32-ops",
+]
+
+
+def build(output: str = LIBRARY, extra_flags: tuple[str, ...] = ()) -> str:
+    tmp = output + ".tmp"
+    cmd = [HIPCC, *HIPCC_FLAGS, *extra_flags, "-I", INCLUDE, SOURCE, "-o", tmp]
+    proc = subprocess.run(cmd, capture_output=True, text=True)
+    if proc.returncode != 0:
+        raise RuntimeError(f"hipcc failed ({proc.returncode}):\n{proc.stderr}")
+    os.replace(tmp, output)
+    return output

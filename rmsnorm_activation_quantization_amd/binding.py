@@ -1,0 +1,194 @@
+"""Thin ctypes binding of librmsnorm_quant.so (argument marshalling only).
+
+Every entry point has the name of the C function it calls (include/rmsnorm_quant.h).
+torch supplies device memory and the current stream; every step of the
+computation runs in the library's HIP kernels.  There is no other code path:
+if the library is missing or the device is not an MI355X, calls fail loudly.
+
+Return convention, following sglang PR #29723 (Key changes: the fused call
+returns its tuple, or None when the backend cannot fuse so that the caller runs
+the unfused sequence): a tuple on success; None for RQ_ERR_UNSUPPORTED, which
+the library decides before enqueuing anything; ValueError for RQ_ERR_INVALID;
+RuntimeError for RQ_ERR_HIP.
+"""
+
+from __future__ import annotations
+
+import ctypes
+import os
+import threading
+
+import torch
+
+from . import _build
+
+RQ_OK, RQ_ERR_INVALID, RQ_ERR_UNSUPPORTED, RQ_ERR_HIP = 0, 1, 2, 3
+RQ_MAX_HIDDEN = 16384
+RQ_MAX_HEAD_DIM = 512
+
+_lib = None
+_lock = threading.Lock()
+
+_p = ctypes.c_void_p
+_i64 = ctypes.c_int64
+_f32 = ctypes.c_float
+
+_SIGNATURES = {
+    "rmsnorm_quant_fp8_per_token": [_p, _i64, _p, _i64, _p, _i64, _i64, _f32, _p, _p, _p, _p, _p],
+    "rmsnorm_quant_fp8_per_group": [_p, _i64, _p, _i64, _p, _i64, _i64, _f32, _i64, _p, _p, _p, _p, _p],
+    "rmsnorm_quant_mxfp4": [_p, _i64, _p, _i64, _p, _i64, _i64, _f32, _p, _p, _p, _p, _p],
+    "qk_gemma_rmsnorm_gate": [_p, _i64, _p, _i64, _p, _p, _i64, _i64, _i64, _i64, _f32, _p, _p, _p, _p],
+}
+
+
+def library_path() -> str:
+    return _build.LIBRARY
+
+
+def lib() -> ctypes.CDLL:
+    """The loaded C library.  Raises if it has not been built."""
+    global _lib
+    if _lib is None:
+        with _lock:
+            if _lib is None:
+                path = library_path()
+                if not os.path.exists(path):
+                    raise RuntimeError(
+                        f"{path} is missing: build it first (python -c 'import __graft_entry__ as g; g.build()')")
+                handle = ctypes.CDLL(path)
+                for name, argtypes in _SIGNATURES.items():
+                    fn = getattr(handle, name)
+                    fn.argtypes = argtypes
+                    fn.restype = ctypes.c_int
+                handle.rq_status_string.argtypes = [ctypes.c_int]
+                handle.rq_status_string.restype = ctypes.c_char_p
+                _lib = handle
+    return _lib
+
+
+def status_string(status: int) -> str:
+    return lib().rq_status_string(status).decode()
+
+
+def _check(status: int, name: str):
+    """Map a status code: True on success, False for 'cannot fuse', raise otherwise."""
+    if status == RQ_OK:
+        return True
+    if status == RQ_ERR_UNSUPPORTED:
+        return False
+    msg = f"{name}: {status_string(status)}"
+    if status == RQ_ERR_INVALID:
+        raise ValueError(msg)
+    raise RuntimeError(msg)
+
+
+def _ptr(t: torch.Tensor | None) -> int | None:
+    return None if t is None else t.data_ptr()
+
+
+def _stream(stream) -> int:
+    s = torch.cuda.current_stream() if stream is None else stream
+    return s.cuda_stream
+
+
+def _rows(t: torch.Tensor, name: str) -> int:
+    """Row stride (elements) of a 2-D bf16 CUDA tensor with unit column stride."""
+    if t.dim() != 2 or t.dtype != torch.bfloat16 or not t.is_cuda:
+        raise ValueError(f"{name} must be a 2-D bfloat16 CUDA tensor")
+    if t.shape[1] > 1 and t.stride(1) != 1:
+        raise ValueError(f"{name} must have unit column stride")
+    return t.stride(0) if t.shape[0] > 1 else t.shape[1]
+
+
+def _row_outputs(x, residual, weight, residual_out, y_out, emit_y):
+    M, H = x.shape
+    if residual.shape != (M, H) or weight.shape != (H,) or weight.dtype != torch.bfloat16:
+        raise ValueError("residual must be [M, H] and weight [H] bfloat16")
+    if not weight.is_contiguous():
+        raise ValueError("weight must be contiguous")
+    if residual_out is None:
+        residual_out = torch.empty((M, H), dtype=torch.bfloat16, device=x.device)
+    if y_out is None and emit_y:
+        y_out = torch.empty((M, H), dtype=torch.bfloat16, device=x.device)
+    for name, t in (("residual_out", residual_out), ("y_out", y_out)):
+        if t is not None and (t.shape != (M, H) or t.dtype != torch.bfloat16 or not t.is_contiguous()):
+            raise ValueError(f"{name} must be a contiguous [M, H] bfloat16 tensor")
+    return M, H, residual_out, y_out
+
+
+def rmsnorm_quant_fp8_per_token(x, residual, weight, eps: float = 1e-6, *, residual_out=None, q_out=None,
+                                scale_out=None, emit_y: bool = False, y_out=None, stream=None):
+    """-> (q [M, H] float8_e4m3fn, residual_out [M, H] bf16, scale [M, 1] fp32, y or None), or None."""
+    ldx, ldr = _rows(x, "x"), _rows(residual, "residual")
+    M, H, residual_out, y_out = _row_outputs(x, residual, weight, residual_out, y_out, emit_y)
+    if q_out is None:
+        q_out = torch.empty((M, H), dtype=torch.uint8, device=x.device)
+    if scale_out is None:
+        scale_out = torch.empty((M,), dtype=torch.float32, device=x.device)
+    st = lib().rmsnorm_quant_fp8_per_token(
+        _ptr(x), ldx, _ptr(residual), ldr, _ptr(weight), M, H, eps, _ptr(residual_out), _ptr(q_out),
+        _ptr(scale_out), _ptr(y_out), _stream(stream))
+    if not _check(st, "rmsnorm_quant_fp8_per_token"):
+        return None
+    return q_out.view(torch.float8_e4m3fn), residual_out, scale_out.view(M, 1), y_out
+
+
+def rmsnorm_quant_fp8_per_group(x, residual, weight, eps: float = 1e-6, group: int = 128, *, residual_out=None,
+                                q_out=None, scale_out=None, emit_y: bool = False, y_out=None, stream=None):
+    """-> (q [M, H] float8_e4m3fn, residual_out, scale [M, H/group] fp32, y or None), or None."""
+    ldx, ldr = _rows(x, "x"), _rows(residual, "residual")
+    M, H, residual_out, y_out = _row_outputs(x, residual, weight, residual_out, y_out, emit_y)
+    if q_out is None:
+        q_out = torch.empty((M, H), dtype=torch.uint8, device=x.device)
+    if scale_out is None:
+        scale_out = torch.empty((M, max(H // group, 1) if group > 0 else 1), dtype=torch.float32, device=x.device)
+    st = lib().rmsnorm_quant_fp8_per_group(
+        _ptr(x), ldx, _ptr(residual), ldr, _ptr(weight), M, H, eps, group, _ptr(residual_out), _ptr(q_out),
+        _ptr(scale_out), _ptr(y_out), _stream(stream))
+    if not _check(st, "rmsnorm_quant_fp8_per_group"):
+        return None
+    return q_out.view(torch.float8_e4m3fn), residual_out, scale_out, y_out
+
+
+def rmsnorm_quant_mxfp4(x, residual, weight, eps: float = 1e-6, *, residual_out=None, q_out=None,
+                        scale_out=None, emit_y: bool = False, y_out=None, stream=None):
+    """-> (q [M, H/2] uint8 packed E2M1, residual_out, scale [M, H/32] uint8 E8M0, y or None), or None."""
+    ldx, ldr = _rows(x, "x"), _rows(residual, "residual")
+    M, H, residual_out, y_out = _row_outputs(x, residual, weight, residual_out, y_out, emit_y)
+    if q_out is None:
+        q_out = torch.empty((M, H // 2), dtype=torch.uint8, device=x.device)
+    if scale_out is None:
+        scale_out = torch.empty((M, max(H // 32, 1)), dtype=torch.uint8, device=x.device)
+    st = lib().rmsnorm_quant_mxfp4(
+        _ptr(x), ldx, _ptr(residual), ldr, _ptr(weight), M, H, eps, _ptr(residual_out), _ptr(q_out),
+        _ptr(scale_out), _ptr(y_out), _stream(stream))
+    if not _check(st, "rmsnorm_quant_mxfp4"):
+        return None
+    return q_out, residual_out, scale_out, y_out
+
+
+def qk_gemma_rmsnorm_gate(qg, k, q_w, k_w, num_q_heads: int, num_k_heads: int, head_dim: int,
+                          eps: float = 1e-6, *, q_out=None, k_out=None, gate_out=None, stream=None):
+    """qg [T, >= 2*Hq*D] interleaved per head as [q | gate]; k [T, >= Hk*D] (row stride allowed).
+    -> (q [T, Hq, D], k [T, Hk, D], gate [T, Hq, D]) contiguous bf16, or None."""
+    ld_qg, ld_k = _rows(qg, "qg"), _rows(k, "k")
+    T = qg.shape[0]
+    Hq, Hk, D = num_q_heads, num_k_heads, head_dim
+    if k.shape[0] != T:
+        raise ValueError("qg and k must have the same number of tokens")
+    for name, w in (("q_w", q_w), ("k_w", k_w)):
+        if w.shape != (D,) or w.dtype != torch.bfloat16 or not w.is_contiguous():
+            raise ValueError(f"{name} must be a contiguous [head_dim] bfloat16 tensor")
+    dev = qg.device
+    q_out = torch.empty((T, Hq, D), dtype=torch.bfloat16, device=dev) if q_out is None else q_out
+    k_out = torch.empty((T, Hk, D), dtype=torch.bfloat16, device=dev) if k_out is None else k_out
+    gate_out = torch.empty((T, Hq, D), dtype=torch.bfloat16, device=dev) if gate_out is None else gate_out
+    for name, t, h in (("q_out", q_out, Hq), ("k_out", k_out, Hk), ("gate_out", gate_out, Hq)):
+        if t.shape != (T, h, D) or t.dtype != torch.bfloat16 or not t.is_contiguous():
+            raise ValueError(f"{name} must be a contiguous [T, heads, head_dim] bfloat16 tensor")
+    st = lib().qk_gemma_rmsnorm_gate(
+        _ptr(qg), ld_qg, _ptr(k), ld_k, _ptr(q_w), _ptr(k_w), T, Hq, Hk, D, eps, _ptr(q_out), _ptr(k_out),
+        _ptr(gate_out), _stream(stream))
+    if not _check(st, "qk_gemma_rmsnorm_gate"):
+        return None
+    return q_out, k_out, gate_out

@@ -1,0 +1,22 @@
+/* fp8_quotient.h -- the fp32 quotient y / sc used by the FP8 quantizer.
+ *
+ * q0 = y * inv is within about an ulp of y / sc when inv is the correctly
+ * rounded 1 / sc; one Markstein correction step (the residual e = sc*q0 - y is
+ * exact through the fused multiply-add) then yields the correctly rounded
+ * quotient.  The residual is formed as sc*q0 - y and subtracted so that
+ * y = -0 keeps its sign.  Plain C so the test suite can run it on the host
+ * over every bf16 significand and every fp32 significand of sc. */
+#ifndef RQ_FP8_QUOTIENT_H
+#define RQ_FP8_QUOTIENT_H
+
+#ifndef RQ_QUOTIENT_QUALIFIERS
+#define RQ_QUOTIENT_QUALIFIERS static inline
+#endif
+
+RQ_QUOTIENT_QUALIFIERS float rq_fp8_quotient(float y, float sc, float inv) {
+  float q0 = y * inv;
+  float e = __builtin_fmaf(sc, q0, -y);
+  return __builtin_fmaf(-e, inv, q0);
+}
+
+#endif /* RQ_FP8_QUOTIENT_H */

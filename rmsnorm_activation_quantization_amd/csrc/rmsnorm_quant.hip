@@ -1,0 +1,692 @@
+// rmsnorm_quant.hip -- gfx950 kernels and the C ABI of librmsnorm_quant.so.
+//
+// The fused step (sglang PR #29723, Motivation / Key changes / Accuracy
+// Tests): residual add -> RMSNorm -> quantize, equal to the unfused sequence
+// with bf16 tensors between its launches, in ONE pass over HBM:
+//   read x, residual (and the L2-resident weight) once, write residual_out,
+//   the codes and the scales once.  The row stays in VGPRs from load to store.
+// The QK variant (sglang PR #27656, Motivation / Modifications): GemmaRMSNorm
+// of q and k heads read through their strides plus the gate de-interleave, in
+// one launch.
+//
+// Work mapping (CDNA4: 64-lane waves, 16-byte loads):
+//   a lane owns 8 consecutive bf16 (one 16-byte load per tensor) per "chunk";
+//   the lanes of a row cover 8 * LANES consecutive columns per chunk, so every
+//   wave-level load and store is fully coalesced.  LANES = 64 (one wave per
+//   row, four rows per 256-thread workgroup: the prefill tiling, no LDS and no
+//   barrier) or 256 (the whole workgroup on one row: the decode tiling, one
+//   LDS exchange for the row sums).  NC = chunks per lane is a template
+//   parameter so the row lives in registers.
+// Reductions: the sum of squares over the row, and max |y| per token, per
+// group or per 32-element block, use DPP row operations inside 16-lane rows,
+// a swizzle across rows and readlane across wave halves.  Every butterfly step
+// is symmetric, so every lane ends with the bit-identical result.
+//
+// Arithmetic (matches the oracle's definition exactly except rstd, which is
+// fp32 here):
+//   residual_out = bf16_rne(f32(x) + f32(res))   exact: the fp32 sum of two
+//                  bf16 values rounded to bf16 is the correctly rounded sum
+//                  (24 >= 2*8 + 2, so the double rounding is innocuous).
+//   ss = sum of r^2 in fp32; rstd = 1 / sqrt(ss / H + eps) (IEEE div/sqrt).
+//   y = bf16_rne((r * rstd) * w).
+//   FP8: scale = amax / 448 (IEEE division); the quotient y / scale is formed
+//        with a correctly rounded reciprocal and one Markstein correction
+//        (q0 = y*inv, e = scale*q0 - y, q = q0 - e*inv), which equals the IEEE
+//        fp32 quotient for every bf16 y and fp32 scale >= 2^-64 (checked
+//        exhaustively on the host by the test suite); the hardware converter
+//        then rounds to E4M3FN (nearest-even).
+//   MXFP4: E8M0 byte from the exponent bits of amax; y * 2^(127 - byte) is
+//        exact, and the hardware converter rounds to E2M1 (nearest-even,
+//        saturating at 6).
+#include <hip/hip_runtime.h>
+
+#include <atomic>
+#include <cstdint>
+#include <cstring>
+#include <utility>
+
+#include "rmsnorm_quant.h"
+
+#define RQ_QUOTIENT_QUALIFIERS __device__ __forceinline__
+#include "fp8_quotient.h"
+
+namespace {
+
+typedef __bf16 bf16x2_t __attribute__((ext_vector_type(2)));
+typedef float f32x2_t __attribute__((ext_vector_type(2)));
+typedef unsigned short u16x2_t __attribute__((ext_vector_type(2)));
+
+constexpr int kWave = 64;
+constexpr int kBlock = 256;
+constexpr int kRowsPerWaveBlock = kBlock / kWave;  // prefill tiling: 4 rows a workgroup
+constexpr int kMaxChunksWave = 16;                 // one wave a row: H <= 16 * 512 = 8192
+constexpr int kMaxChunksBlock = 8;                 // a workgroup a row: H <= 8 * 2048 = 16384
+
+enum QuantMode { kFp8Token = 0, kFp8Group = 1, kMxfp4 = 2 };
+
+// ---------------------------------------------------------------------------
+// bf16 <-> fp32
+// ---------------------------------------------------------------------------
+__device__ __forceinline__ float bf_lo(uint32_t w) { return __uint_as_float(w << 16); }
+__device__ __forceinline__ float bf_hi(uint32_t w) { return __uint_as_float(w & 0xFFFF0000u); }
+// v_cvt_pk_bf16_f32: two fp32 -> packed bf16, round to nearest even.
+__device__ __forceinline__ uint32_t pack_bf16(float lo, float hi) {
+  f32x2_t v = {lo, hi};
+  return __builtin_bit_cast(uint32_t, __builtin_convertvector(v, bf16x2_t));
+}
+// Largest |bf16| bit pattern of a packed pair per half (integer max of the
+// magnitude bits orders finite < Inf < NaN, so a NaN propagates).
+__device__ __forceinline__ uint32_t abs_max2(uint32_t acc, uint32_t w) {
+  u16x2_t a = __builtin_bit_cast(u16x2_t, acc);
+  u16x2_t b = __builtin_bit_cast(u16x2_t, w & 0x7FFF7FFFu);
+  return __builtin_bit_cast(uint32_t, __builtin_elementwise_max(a, b));
+}
+__device__ __forceinline__ uint32_t halves_max(uint32_t w) {
+  uint32_t lo = w & 0xFFFFu, hi = w >> 16;
+  return lo > hi ? lo : hi;
+}
+
+// ---------------------------------------------------------------------------
+// Cross-lane exchange
+// ---------------------------------------------------------------------------
+template <int kCtrl>
+__device__ __forceinline__ uint32_t dpp(uint32_t v) {
+  return (uint32_t)__builtin_amdgcn_update_dpp(0, (int)v, kCtrl, 0xF, 0xF, false);
+}
+constexpr int kDppXor1 = 0xB1;        // quad_perm [1,0,3,2]
+constexpr int kDppXor2 = 0x4E;        // quad_perm [2,3,0,1]
+constexpr int kDppHalfMirror = 0x141; // lane i <-> 7 - i inside each 8
+constexpr int kDppMirror = 0x140;     // lane i <-> 15 - i inside each 16
+constexpr int kSwizzleXor16 = 0x401F; // ds_swizzle bit mode: lane ^ 16 inside each 32
+
+__device__ __forceinline__ uint32_t umax(uint32_t a, uint32_t b) { return a > b ? a : b; }
+__device__ __forceinline__ uint32_t swz16(uint32_t v) {
+  return (uint32_t)__builtin_amdgcn_ds_swizzle((int)v, kSwizzleXor16);
+}
+__device__ __forceinline__ uint32_t rdlane(uint32_t v, int l) {
+  return (uint32_t)__builtin_amdgcn_readlane((int)v, l);
+}
+
+// Max over aligned groups of 2^log2n lanes (log2n in 0..6, uniform).
+__device__ __forceinline__ uint32_t group_max(uint32_t v, int log2n) {
+  if (log2n >= 1) v = umax(v, dpp<kDppXor1>(v));
+  if (log2n >= 2) v = umax(v, dpp<kDppXor2>(v));
+  if (log2n >= 3) v = umax(v, dpp<kDppHalfMirror>(v));
+  if (log2n >= 4) v = umax(v, dpp<kDppMirror>(v));
+  if (log2n >= 5) v = umax(v, swz16(v));
+  if (log2n >= 6) v = umax(rdlane(v, 0), rdlane(v, 32));
+  return v;
+}
+template <int kLog2n>
+__device__ __forceinline__ uint32_t group_max_c(uint32_t v) { return group_max(v, kLog2n); }
+
+__device__ __forceinline__ float addf(float a, uint32_t b) { return a + __uint_as_float(b); }
+// Sum over aligned groups of 2^log2n lanes, identical in every lane of a group.
+__device__ __forceinline__ float group_sum(float v, int log2n) {
+  if (log2n >= 1) v = addf(v, dpp<kDppXor1>(__float_as_uint(v)));
+  if (log2n >= 2) v = addf(v, dpp<kDppXor2>(__float_as_uint(v)));
+  if (log2n >= 3) v = addf(v, dpp<kDppHalfMirror>(__float_as_uint(v)));
+  if (log2n >= 4) v = addf(v, dpp<kDppMirror>(__float_as_uint(v)));
+  if (log2n == 5) v = addf(v, swz16(__float_as_uint(v)));
+  if (log2n >= 6) {
+    float a = __uint_as_float(rdlane(__float_as_uint(v), 0));
+    float b = __uint_as_float(rdlane(__float_as_uint(v), 16));
+    float c = __uint_as_float(rdlane(__float_as_uint(v), 32));
+    float d = __uint_as_float(rdlane(__float_as_uint(v), 48));
+    v = (a + b) + (c + d);
+  }
+  return v;
+}
+
+// ---------------------------------------------------------------------------
+// Quantization helpers
+// ---------------------------------------------------------------------------
+// Per-granule constants of the FP8 quotient y / scale.
+struct Fp8Granule {
+  float scale;  // stored scale = amax / 448
+  float sc;     // divisor used by the correction step
+  float inv;    // correctly rounded 1 / sc
+  bool slow;    // scale below 2^-64: plain IEEE division per element
+};
+
+__device__ __forceinline__ Fp8Granule fp8_granule(uint32_t amax_bits) {
+  Fp8Granule g;
+  float amax = __uint_as_float(amax_bits << 16);
+  g.scale = amax / 448.0f;
+  g.slow = false;
+  if (amax_bits == 0) {
+    // All-zero granule: scale 0; q = y * 0 keeps the sign of each zero.
+    g.sc = 1.0f;
+    g.inv = 0.0f;
+  } else if (g.scale < 0x1p-64f) {
+    g.slow = true;  // keeps every intermediate of the correction step normal
+    g.sc = g.scale;
+    g.inv = 0.0f;
+  } else {
+    g.sc = g.scale;
+    g.inv = 1.0f / g.scale;
+  }
+  return g;
+}
+
+// fp32 quotient y / sc, correctly rounded (fp8_quotient.h).
+__device__ __forceinline__ float fp8_quotient(float y, const Fp8Granule& g) {
+  return rq_fp8_quotient(y, g.sc, g.inv);
+}
+
+// Eight bf16 values (packed in a uint4) -> eight E4M3FN codes (a uint2).
+__device__ __forceinline__ uint2 fp8_codes(const uint4& y, const Fp8Granule& g) {
+  const uint32_t w[4] = {y.x, y.y, y.z, y.w};
+  float q[8];
+  if (!g.slow) {
+#pragma unroll
+    for (int j = 0; j < 4; ++j) {
+      q[2 * j] = fp8_quotient(bf_lo(w[j]), g);
+      q[2 * j + 1] = fp8_quotient(bf_hi(w[j]), g);
+    }
+  } else {
+#pragma unroll
+    for (int j = 0; j < 4; ++j) {
+      q[2 * j] = bf_lo(w[j]) / g.sc;
+      q[2 * j + 1] = bf_hi(w[j]) / g.sc;
+    }
+  }
+  uint32_t d0 = (uint32_t)__builtin_amdgcn_cvt_pk_fp8_f32(q[0], q[1], 0, false);
+  d0 = (uint32_t)__builtin_amdgcn_cvt_pk_fp8_f32(q[2], q[3], (int)d0, true);
+  uint32_t d1 = (uint32_t)__builtin_amdgcn_cvt_pk_fp8_f32(q[4], q[5], 0, false);
+  d1 = (uint32_t)__builtin_amdgcn_cvt_pk_fp8_f32(q[6], q[7], (int)d1, true);
+  return make_uint2(d0, d1);
+}
+
+// E8M0 byte for a block whose largest magnitude has bf16 bits amax_bits:
+// floor(log2 amax) - 2 + 127 clamped to [0, 254] is (exponent field - 2) for
+// normal amax and 0 below (subnormal or zero amax); 255 for Inf / NaN.
+__device__ __forceinline__ uint32_t e8m0_byte(uint32_t amax_bits) {
+  uint32_t e = amax_bits >> 7;
+  if (e == 255u) return 255u;
+  return e >= 2u ? e - 2u : 0u;
+}
+
+// Eight bf16 values -> eight E2M1 codes (one uint32, element i in nibble i).
+// y * 2^(127 - byte) is exact (power-of-two scaling of a bf16 value); byte is
+// at most 252 for finite bf16 amax, so the factor is a normal fp32.
+__device__ __forceinline__ uint32_t mxfp4_codes(const uint4& y, uint32_t byte) {
+  const float f = __uint_as_float((254u - byte) << 23);
+  uint32_t d = 0;
+  d = (uint32_t)__builtin_amdgcn_cvt_scalef32_pk_fp4_f32(d, bf_lo(y.x) * f, bf_hi(y.x) * f, 1.0f, 0);
+  d = (uint32_t)__builtin_amdgcn_cvt_scalef32_pk_fp4_f32(d, bf_lo(y.y) * f, bf_hi(y.y) * f, 1.0f, 1);
+  d = (uint32_t)__builtin_amdgcn_cvt_scalef32_pk_fp4_f32(d, bf_lo(y.z) * f, bf_hi(y.z) * f, 1.0f, 2);
+  d = (uint32_t)__builtin_amdgcn_cvt_scalef32_pk_fp4_f32(d, bf_lo(y.w) * f, bf_hi(y.w) * f, 1.0f, 3);
+  return d;
+}
+
+__device__ __forceinline__ uint32_t chunk_abs_max(const uint4& y) {
+  uint32_t m = abs_max2(0u, y.x);
+  m = abs_max2(m, y.y);
+  m = abs_max2(m, y.z);
+  m = abs_max2(m, y.w);
+  return halves_max(m);
+}
+
+// ---------------------------------------------------------------------------
+// The fused row kernel
+// ---------------------------------------------------------------------------
+struct RowArgs {
+  const uint16_t* x;
+  const uint16_t* res;
+  const uint16_t* w;
+  uint16_t* res_out;
+  uint8_t* q;
+  void* scale;
+  uint16_t* y_out;
+  int64_t ldx;
+  int64_t ldr;
+  int M;
+  int H;
+  float eps;
+  int group_log2_lanes;  // per-group FP8: log2(group / 8)
+  int groups_per_row;    // per-group FP8: H / group
+};
+
+template <int kMode, int kNC, int kWPR>
+__global__ __launch_bounds__(kBlock) void fused_rows(const RowArgs a) {
+  constexpr int kLanes = kWave * kWPR;
+  constexpr int kChunk = kLanes * 8;
+  const int lane = threadIdx.x & (kWave - 1);
+  const int wave = threadIdx.x / kWave;
+  const int64_t row = (kWPR == 1) ? (int64_t)blockIdx.x * kRowsPerWaveBlock + wave : (int64_t)blockIdx.x;
+  const int t = (kWPR == 1) ? lane : (int)threadIdx.x;
+  if (kWPR == 1 && row >= a.M) return;  // whole waves only: no barrier in this tiling
+  const int H = a.H;
+
+  __shared__ float lds_sum[kWPR];
+  __shared__ uint32_t lds_max[kWPR];
+
+  const uint16_t* xr = a.x + row * a.ldx;
+  const uint16_t* rr = a.res + row * a.ldr;
+
+  // 1. Issue every load of the row before using any of it.
+  uint4 xv[kNC], rv[kNC], wv[kNC];
+#pragma unroll
+  for (int c = 0; c < kNC; ++c) {
+    const int col = c * kChunk + t * 8;
+    if (c < kNC - 1 || col < H) {
+      xv[c] = *reinterpret_cast<const uint4*>(xr + col);
+      rv[c] = *reinterpret_cast<const uint4*>(rr + col);
+      wv[c] = *reinterpret_cast<const uint4*>(a.w + col);
+    } else {
+      xv[c] = make_uint4(0, 0, 0, 0);
+      rv[c] = make_uint4(0, 0, 0, 0);
+      wv[c] = make_uint4(0, 0, 0, 0);
+    }
+  }
+
+  // 2. Residual add (one bf16 rounding), store residual_out, sum of squares.
+  uint4 rp[kNC];
+  float ss = 0.0f;
+#pragma unroll
+  for (int c = 0; c < kNC; ++c) {
+    const uint32_t xs[4] = {xv[c].x, xv[c].y, xv[c].z, xv[c].w};
+    const uint32_t rs[4] = {rv[c].x, rv[c].y, rv[c].z, rv[c].w};
+    uint32_t p[4];
+#pragma unroll
+    for (int j = 0; j < 4; ++j) {
+      p[j] = pack_bf16(bf_lo(xs[j]) + bf_lo(rs[j]), bf_hi(xs[j]) + bf_hi(rs[j]));
+      const float r0 = bf_lo(p[j]), r1 = bf_hi(p[j]);
+      ss = __builtin_fmaf(r0, r0, ss);
+      ss = __builtin_fmaf(r1, r1, ss);
+    }
+    rp[c] = make_uint4(p[0], p[1], p[2], p[3]);
+    const int col = c * kChunk + t * 8;
+    if (c < kNC - 1 || col < H) *reinterpret_cast<uint4*>(a.res_out + row * H + col) = rp[c];
+  }
+
+  // 3. rstd over the whole row.
+  ss = group_sum(ss, 6);
+  if (kWPR > 1) {
+    if (lane == 0) lds_sum[wave] = ss;
+    __syncthreads();
+    ss = (lds_sum[0] + lds_sum[1]) + (lds_sum[2] + lds_sum[3]);
+  }
+  const float rstd = 1.0f / __builtin_sqrtf(ss / (float)H + a.eps);
+
+  // 4. y = bf16((r * rstd) * w), optional bf16 side output.
+  uint4 yp[kNC];
+#pragma unroll
+  for (int c = 0; c < kNC; ++c) {
+    const uint32_t rs[4] = {rp[c].x, rp[c].y, rp[c].z, rp[c].w};
+    const uint32_t ws[4] = {wv[c].x, wv[c].y, wv[c].z, wv[c].w};
+    uint32_t p[4];
+#pragma unroll
+    for (int j = 0; j < 4; ++j)
+      p[j] = pack_bf16((bf_lo(rs[j]) * rstd) * bf_lo(ws[j]), (bf_hi(rs[j]) * rstd) * bf_hi(ws[j]));
+    yp[c] = make_uint4(p[0], p[1], p[2], p[3]);
+  }
+  if (a.y_out) {
+#pragma unroll
+    for (int c = 0; c < kNC; ++c) {
+      const int col = c * kChunk + t * 8;
+      if (c < kNC - 1 || col < H) *reinterpret_cast<uint4*>(a.y_out + row * H + col) = yp[c];
+    }
+  }
+
+  // 5. Absmax per granule, scale, quantize, pack, store.
+  if (kMode == kFp8Token) {
+    uint32_t m = 0;
+#pragma unroll
+    for (int c = 0; c < kNC; ++c) m = umax(m, chunk_abs_max(yp[c]));
+    m = group_max(m, 6);
+    if (kWPR > 1) {
+      if (lane == 0) lds_max[wave] = m;
+      __syncthreads();
+      m = umax(umax(lds_max[0], lds_max[1]), umax(lds_max[2], lds_max[3]));
+    }
+    const Fp8Granule g = fp8_granule(m);
+    if (t == 0) reinterpret_cast<float*>(a.scale)[row] = g.scale;
+#pragma unroll
+    for (int c = 0; c < kNC; ++c) {
+      const int col = c * kChunk + t * 8;
+      const uint2 codes = fp8_codes(yp[c], g);
+      if (c < kNC - 1 || col < H) *reinterpret_cast<uint2*>(a.q + row * H + col) = codes;
+    }
+  } else if (kMode == kFp8Group) {
+    const int gl = a.group_log2_lanes;
+#pragma unroll
+    for (int c = 0; c < kNC; ++c) {
+      const int col = c * kChunk + t * 8;
+      const uint32_t m = group_max(chunk_abs_max(yp[c]), gl);
+      const Fp8Granule g = fp8_granule(m);
+      const uint2 codes = fp8_codes(yp[c], g);
+      if (c < kNC - 1 || col < H) {
+        *reinterpret_cast<uint2*>(a.q + row * H + col) = codes;
+        if ((t & ((1 << gl) - 1)) == 0)
+          reinterpret_cast<float*>(a.scale)[row * a.groups_per_row + (col >> (gl + 3))] = g.scale;
+      }
+    }
+  } else {
+#pragma unroll
+    for (int c = 0; c < kNC; ++c) {
+      const int col = c * kChunk + t * 8;
+      const uint32_t m = group_max_c<2>(chunk_abs_max(yp[c]));
+      const uint32_t byte = e8m0_byte(m);
+      const uint32_t codes = mxfp4_codes(yp[c], byte);
+      if (c < kNC - 1 || col < H) {
+        *reinterpret_cast<uint32_t*>(a.q + row * (H / 2) + col / 2) = codes;
+        if ((t & 3) == 0) reinterpret_cast<uint8_t*>(a.scale)[row * (H / 32) + col / 32] = (uint8_t)byte;
+      }
+    }
+  }
+}
+
+// ---------------------------------------------------------------------------
+// QK GemmaRMSNorm + gate de-interleave
+// ---------------------------------------------------------------------------
+struct QKArgs {
+  const uint16_t* qg;
+  const uint16_t* k;
+  const uint16_t* qw;
+  const uint16_t* kw;
+  uint16_t* q_out;
+  uint16_t* k_out;
+  uint16_t* gate_out;
+  int64_t ld_qg;
+  int64_t ld_k;
+  int64_t units;  // T * (Hq + Hk) heads to normalize
+  int Hq;
+  int Hk;
+  int D;
+  float eps;
+};
+
+constexpr int kQKBlock = 64;  // one wave a workgroup: spreads a small decode batch over many CUs
+
+// kLog2Lanes: lanes per head = 2^kLog2Lanes >= D / 8; 64 >> kLog2Lanes heads a wave.
+template <int kLog2Lanes>
+__global__ __launch_bounds__(kQKBlock) void qk_gemma_gate(const QKArgs a) {
+  constexpr int kLanesPerHead = 1 << kLog2Lanes;
+  constexpr int kHeadsPerWave = kWave / kLanesPerHead;
+  const int lane = threadIdx.x;
+  const int64_t unit = (int64_t)blockIdx.x * kHeadsPerWave + lane / kLanesPerHead;
+  const int col = (lane % kLanesPerHead) * 8;
+  const int heads = a.Hq + a.Hk;
+  const bool active = unit < a.units && col < a.D;
+  const int64_t tok = active ? unit / heads : 0;
+  const int h = active ? (int)(unit % heads) : 0;
+  const bool is_q = h < a.Hq;
+
+  uint4 v = make_uint4(0, 0, 0, 0), w = make_uint4(0, 0, 0, 0), gate = make_uint4(0, 0, 0, 0);
+  const uint16_t* src;
+  if (is_q) {
+    src = a.qg + tok * a.ld_qg + (int64_t)2 * a.D * h + col;
+  } else {
+    src = a.k + tok * a.ld_k + (int64_t)a.D * (h - a.Hq) + col;
+  }
+  if (active) {
+    v = *reinterpret_cast<const uint4*>(src);
+    w = *reinterpret_cast<const uint4*>((is_q ? a.qw : a.kw) + col);
+    if (is_q) gate = *reinterpret_cast<const uint4*>(src + a.D);
+  }
+  const uint32_t vs[4] = {v.x, v.y, v.z, v.w};
+  const uint32_t ws[4] = {w.x, w.y, w.z, w.w};
+  float ss = 0.0f;
+#pragma unroll
+  for (int j = 0; j < 4; ++j) {
+    ss = __builtin_fmaf(bf_lo(vs[j]), bf_lo(vs[j]), ss);
+    ss = __builtin_fmaf(bf_hi(vs[j]), bf_hi(vs[j]), ss);
+  }
+  ss = group_sum(ss, kLog2Lanes);
+  const float rstd = 1.0f / __builtin_sqrtf(ss / (float)a.D + a.eps);
+  uint32_t p[4];
+#pragma unroll
+  for (int j = 0; j < 4; ++j)
+    p[j] = pack_bf16((bf_lo(vs[j]) * rstd) * (1.0f + bf_lo(ws[j])),
+                     (bf_hi(vs[j]) * rstd) * (1.0f + bf_hi(ws[j])));
+  if (active) {
+    const uint4 out = make_uint4(p[0], p[1], p[2], p[3]);
+    if (is_q) {
+      const int64_t o = (tok * a.Hq + h) * (int64_t)a.D + col;
+      *reinterpret_cast<uint4*>(a.q_out + o) = out;
+      *reinterpret_cast<uint4*>(a.gate_out + o) = gate;
+    } else {
+      *reinterpret_cast<uint4*>(a.k_out + (tok * a.Hk + (h - a.Hq)) * (int64_t)a.D + col) = out;
+    }
+  }
+}
+
+// ---------------------------------------------------------------------------
+// Kernel tables
+// ---------------------------------------------------------------------------
+using RowKernel = void (*)(RowArgs);
+using QKKernel = void (*)(QKArgs);
+
+template <int kMode, int kWPR, int... kNC>
+constexpr auto row_table(std::integer_sequence<int, kNC...>) {
+  struct T { RowKernel k[sizeof...(kNC)]; };
+  return T{{&fused_rows<kMode, kNC + 1, kWPR>...}};
+}
+template <int kMode>
+struct RowKernels {
+  static constexpr auto wave = row_table<kMode, 1>(std::make_integer_sequence<int, kMaxChunksWave>{});
+  static constexpr auto block = row_table<kMode, 4>(std::make_integer_sequence<int, kMaxChunksBlock>{});
+};
+constexpr QKKernel kQKKernels[7] = {&qk_gemma_gate<0>, &qk_gemma_gate<1>, &qk_gemma_gate<2>, &qk_gemma_gate<3>,
+                                    &qk_gemma_gate<4>, &qk_gemma_gate<5>, &qk_gemma_gate<6>};
+
+// ---------------------------------------------------------------------------
+// Host-side preflight
+// ---------------------------------------------------------------------------
+constexpr int kMaxDevices = 64;
+std::atomic<int> g_arch_state[kMaxDevices];  // 0 unknown, 1 gfx950, 2 other
+
+rq_status check_device() {
+  int dev = 0;
+  if (hipGetDevice(&dev) != hipSuccess) return RQ_ERR_HIP;
+  if (dev < 0 || dev >= kMaxDevices) return RQ_ERR_UNSUPPORTED;
+  int state = g_arch_state[dev].load(std::memory_order_relaxed);
+  if (state == 0) {
+    hipDeviceProp_t prop;
+    if (hipGetDeviceProperties(&prop, dev) != hipSuccess) return RQ_ERR_HIP;
+    state = std::strncmp(prop.gcnArchName, "gfx950", 6) == 0 ? 1 : 2;
+    g_arch_state[dev].store(state, std::memory_order_relaxed);
+  }
+  return state == 1 ? RQ_OK : RQ_ERR_UNSUPPORTED;
+}
+
+bool aligned(const void* p, uintptr_t n) { return (reinterpret_cast<uintptr_t>(p) & (n - 1)) == 0; }
+
+struct Span {
+  uintptr_t lo, hi;  // [lo, hi) in bytes; empty when lo == hi
+};
+Span span_of(const void* p, int64_t rows, int64_t ld, int64_t width, int64_t elem_bytes) {
+  if (!p || rows <= 0 || width <= 0) return {0, 0};
+  uintptr_t lo = reinterpret_cast<uintptr_t>(p);
+  return {lo, lo + (uintptr_t)(((rows - 1) * ld + width) * elem_bytes)};
+}
+bool overlap(const Span& a, const Span& b) { return a.lo < a.hi && b.lo < b.hi && a.lo < b.hi && b.lo < a.hi; }
+
+// Every output must be disjoint from every other buffer, except residual_out
+// aliasing residual exactly (ldr == H).
+bool outputs_disjoint(const Span* outs, int n_out, const Span* ins, int n_in, int inplace_out, int inplace_in) {
+  for (int i = 0; i < n_out; ++i) {
+    for (int j = i + 1; j < n_out; ++j)
+      if (overlap(outs[i], outs[j])) return false;
+    for (int j = 0; j < n_in; ++j) {
+      if (i == inplace_out && j == inplace_in && outs[i].lo == ins[j].lo && outs[i].hi == ins[j].hi) continue;
+      if (overlap(outs[i], ins[j])) return false;
+    }
+  }
+  return true;
+}
+
+// Shared checks of the three fused row entry points.  granule = elements per
+// scale; code_bytes_num / code_bytes_den = bytes per element of q_out.
+rq_status row_preflight(const uint16_t* x, int64_t ldx, const uint16_t* residual, int64_t ldr,
+                        const uint16_t* weight, int64_t M, int64_t H, float eps,
+                        const uint16_t* residual_out, const uint8_t* q_out, const void* scale_out,
+                        int64_t scale_count, int64_t scale_bytes, const uint16_t* y_out,
+                        int64_t granule, int code_bits) {
+  if (M < 0 || H <= 0 || !(eps >= 0.0f) || ldx < H || ldr < H) return RQ_ERR_INVALID;
+  if (M > 0 && (!x || !residual || !weight || !residual_out || !q_out || !scale_out)) return RQ_ERR_INVALID;
+  if (H % 8 != 0 || H > RQ_MAX_HIDDEN || M > INT32_MAX) return RQ_ERR_UNSUPPORTED;
+  if (granule <= 0 || H % granule != 0) return RQ_ERR_UNSUPPORTED;
+  if (M == 0) return RQ_OK;
+  if (ldx % 8 != 0 || ldr % 8 != 0 || !aligned(x, 16) || !aligned(residual, 16) || !aligned(weight, 16) ||
+      !aligned(residual_out, 16) || (y_out && !aligned(y_out, 16)) || !aligned(q_out, code_bits == 8 ? 8 : 4) ||
+      !aligned(scale_out, scale_bytes))
+    return RQ_ERR_UNSUPPORTED;
+  const Span ins[3] = {span_of(x, M, ldx, H, 2), span_of(residual, M, ldr, H, 2), span_of(weight, 1, H, H, 2)};
+  const Span outs[4] = {span_of(residual_out, M, H, H, 2), span_of(q_out, M, H * code_bits / 8, H * code_bits / 8, 1),
+                        span_of(scale_out, M, scale_count, scale_count, scale_bytes), span_of(y_out, M, H, H, 2)};
+  if (!outputs_disjoint(outs, 4, ins, 3, /*inplace_out=*/0, /*inplace_in=*/1)) return RQ_ERR_INVALID;
+  return check_device();
+}
+
+rq_status launch(const void* kernel, dim3 grid, dim3 block, void* args, void* stream) {
+  void* argv[1] = {args};
+  hipError_t err = hipLaunchKernel(kernel, grid, block, argv, 0, reinterpret_cast<hipStream_t>(stream));
+  return err == hipSuccess ? RQ_OK : RQ_ERR_HIP;
+}
+
+// Decode sizes (few rows) spread each row over a whole workgroup; prefill
+// sizes give each row one wave.  Rows longer than a wave's register budget
+// always take the workgroup tiling.
+template <int kMode>
+rq_status launch_rows(RowArgs& a, void* stream) {
+  const int H = a.H;
+  const bool block_tiling = (a.M <= 64) || H > kMaxChunksWave * kWave * 8;
+  if (block_tiling) {
+    const int nc = (H + kBlock * 8 - 1) / (kBlock * 8);
+    return launch(reinterpret_cast<const void*>(RowKernels<kMode>::block.k[nc - 1]), dim3(a.M), dim3(kBlock), &a,
+                  stream);
+  }
+  const int nc = (H + kWave * 8 - 1) / (kWave * 8);
+  const unsigned blocks = (unsigned)((a.M + kRowsPerWaveBlock - 1) / kRowsPerWaveBlock);
+  return launch(reinterpret_cast<const void*>(RowKernels<kMode>::wave.k[nc - 1]), dim3(blocks), dim3(kBlock), &a,
+                stream);
+}
+
+RowArgs make_row_args(const uint16_t* x, int64_t ldx, const uint16_t* residual, int64_t ldr, const uint16_t* weight,
+                      int64_t M, int64_t H, float eps, uint16_t* residual_out, uint8_t* q_out, void* scale_out,
+                      uint16_t* y_out) {
+  RowArgs a;
+  a.x = x;
+  a.res = residual;
+  a.w = weight;
+  a.res_out = residual_out;
+  a.q = q_out;
+  a.scale = scale_out;
+  a.y_out = y_out;
+  a.ldx = ldx;
+  a.ldr = ldr;
+  a.M = (int)M;
+  a.H = (int)H;
+  a.eps = eps;
+  a.group_log2_lanes = 0;
+  a.groups_per_row = 0;
+  return a;
+}
+
+}  // namespace
+
+extern "C" {
+
+rq_status rmsnorm_quant_fp8_per_token(const uint16_t* x, int64_t ldx, const uint16_t* residual, int64_t ldr,
+                                      const uint16_t* weight, int64_t M, int64_t H, float eps,
+                                      uint16_t* residual_out, uint8_t* q_out, float* scale_out, uint16_t* y_out,
+                                      void* stream) {
+  rq_status st = row_preflight(x, ldx, residual, ldr, weight, M, H, eps, residual_out, q_out, scale_out, 1, 4,
+                               y_out, H, 8);
+  if (st != RQ_OK || M == 0) return st;
+  RowArgs a = make_row_args(x, ldx, residual, ldr, weight, M, H, eps, residual_out, q_out, scale_out, y_out);
+  return launch_rows<kFp8Token>(a, stream);
+}
+
+rq_status rmsnorm_quant_fp8_per_group(const uint16_t* x, int64_t ldx, const uint16_t* residual, int64_t ldr,
+                                      const uint16_t* weight, int64_t M, int64_t H, float eps, int64_t group,
+                                      uint16_t* residual_out, uint8_t* q_out, float* scale_out, uint16_t* y_out,
+                                      void* stream) {
+  int log2_lanes = -1;
+  for (int l = 2; l <= 6; ++l)
+    if (group == (int64_t)8 << l) log2_lanes = l;
+  if (group <= 0) return RQ_ERR_INVALID;
+  const int64_t granule = log2_lanes < 0 ? -1 : group;
+  rq_status st = row_preflight(x, ldx, residual, ldr, weight, M, H, eps, residual_out, q_out, scale_out,
+                               log2_lanes < 0 ? 1 : H / group, 4, y_out, granule, 8);
+  if (st != RQ_OK || M == 0) return st;
+  RowArgs a = make_row_args(x, ldx, residual, ldr, weight, M, H, eps, residual_out, q_out, scale_out, y_out);
+  a.group_log2_lanes = log2_lanes;
+  a.groups_per_row = (int)(H / group);
+  return launch_rows<kFp8Group>(a, stream);
+}
+
+rq_status rmsnorm_quant_mxfp4(const uint16_t* x, int64_t ldx, const uint16_t* residual, int64_t ldr,
+                              const uint16_t* weight, int64_t M, int64_t H, float eps, uint16_t* residual_out,
+                              uint8_t* q_out, uint8_t* scale_out, uint16_t* y_out, void* stream) {
+  rq_status st = row_preflight(x, ldx, residual, ldr, weight, M, H, eps, residual_out, q_out, scale_out, H / 32, 1,
+                               y_out, 32, 4);
+  if (st != RQ_OK || M == 0) return st;
+  RowArgs a = make_row_args(x, ldx, residual, ldr, weight, M, H, eps, residual_out, q_out, scale_out, y_out);
+  return launch_rows<kMxfp4>(a, stream);
+}
+
+rq_status qk_gemma_rmsnorm_gate(const uint16_t* qg, int64_t ld_qg, const uint16_t* k, int64_t ld_k,
+                                const uint16_t* q_w, const uint16_t* k_w, int64_t T, int64_t Hq, int64_t Hk,
+                                int64_t D, float eps, uint16_t* q_out, uint16_t* k_out, uint16_t* gate_out,
+                                void* stream) {
+  if (T < 0 || Hq < 0 || Hk < 0 || D <= 0 || !(eps >= 0.0f)) return RQ_ERR_INVALID;
+  if (ld_qg < 2 * Hq * D || ld_k < Hk * D) return RQ_ERR_INVALID;
+  const bool any_q = T > 0 && Hq > 0, any_k = T > 0 && Hk > 0;
+  if (any_q && (!qg || !q_w || !q_out || !gate_out)) return RQ_ERR_INVALID;
+  if (any_k && (!k || !k_w || !k_out)) return RQ_ERR_INVALID;
+  if (D % 8 != 0 || D > RQ_MAX_HEAD_DIM || T > INT32_MAX) return RQ_ERR_UNSUPPORTED;
+  if (!any_q && !any_k) return RQ_OK;
+  if ((any_q && (ld_qg % 8 != 0 || !aligned(qg, 16) || !aligned(q_w, 16) || !aligned(q_out, 16) ||
+                 !aligned(gate_out, 16))) ||
+      (any_k && (ld_k % 8 != 0 || !aligned(k, 16) || !aligned(k_w, 16) || !aligned(k_out, 16))))
+    return RQ_ERR_UNSUPPORTED;
+  const Span ins[4] = {any_q ? span_of(qg, T, ld_qg, 2 * Hq * D, 2) : Span{0, 0},
+                       any_k ? span_of(k, T, ld_k, Hk * D, 2) : Span{0, 0},
+                       any_q ? span_of(q_w, 1, D, D, 2) : Span{0, 0}, any_k ? span_of(k_w, 1, D, D, 2) : Span{0, 0}};
+  const Span outs[3] = {any_q ? span_of(q_out, T, Hq * D, Hq * D, 2) : Span{0, 0},
+                        any_k ? span_of(k_out, T, Hk * D, Hk * D, 2) : Span{0, 0},
+                        any_q ? span_of(gate_out, T, Hq * D, Hq * D, 2) : Span{0, 0}};
+  if (!outputs_disjoint(outs, 3, ins, 4, -1, -1)) return RQ_ERR_INVALID;
+  rq_status st = check_device();
+  if (st != RQ_OK) return st;
+
+  int log2_lanes = 0;
+  while ((8 << log2_lanes) < D) ++log2_lanes;
+  QKArgs a;
+  a.qg = qg;
+  a.k = k;
+  a.qw = q_w;
+  a.kw = k_w;
+  a.q_out = q_out;
+  a.k_out = k_out;
+  a.gate_out = gate_out;
+  a.ld_qg = ld_qg;
+  a.ld_k = ld_k;
+  a.units = T * (Hq + Hk);
+  a.Hq = (int)Hq;
+  a.Hk = (int)Hk;
+  a.D = (int)D;
+  a.eps = eps;
+  const int64_t heads_per_wave = kWave >> log2_lanes;
+  const int64_t blocks = (a.units + heads_per_wave - 1) / heads_per_wave;
+  if (blocks > INT32_MAX) return RQ_ERR_UNSUPPORTED;
+  return launch(reinterpret_cast<const void*>(kQKKernels[log2_lanes]), dim3((unsigned)blocks), dim3(kQKBlock), &a,
+                stream);
+}
+
+const char* rq_status_string(rq_status status) {
+  switch (status) {
+    case RQ_OK: return "RQ_OK";
+    case RQ_ERR_INVALID: return "RQ_ERR_INVALID: invalid argument (null pointer, size, stride, eps or overlap)";
+    case RQ_ERR_UNSUPPORTED:
+      return "RQ_ERR_UNSUPPORTED: not gfx950, misaligned rows, or a shape this library does not fuse";
+    case RQ_ERR_HIP: return "RQ_ERR_HIP: the HIP runtime rejected the launch";
+  }
+  return "unknown rq_status";
+}
+
+}  // extern "C"

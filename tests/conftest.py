@@ -18,3 +18,15 @@ def pytest_configure(config):
 def ref():
     import oracle
     return oracle.get()
+
+
+def pytest_collection_modifyitems(config, items):
+    gpu_items = [it for it in items if "gpu" in it.keywords]
+    if not gpu_items:
+        return
+    import torch
+    if torch.cuda.is_available():
+        return
+    skip = pytest.mark.skip(reason="no GPU visible")
+    for it in gpu_items:
+        it.add_marker(skip)

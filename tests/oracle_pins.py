@@ -517,11 +517,38 @@ def pin_invariants_on_workloads(ref):
             assert ok.all(), "dequantized E2M1 off by more than half a step"
 
 
+def pin_quantize_step(ref):
+    """The quantize-only entry points equal the independent numpy quantizers
+    on random and special bf16 rows, and the fused step equals norm followed by
+    quantize (the unfused sequence)."""
+    rng = np.random.default_rng(31)
+    y = np_bf16_round(rng.normal(0, 1, (5, 256)) * np.exp(rng.normal(0, 3, (5, 1))))
+    y[0, :64] = 0
+    y[0, 64:96] = 0x8000
+    y[1, 5] = np_bf16_round(np.array([1e-39]))[0]      # a bf16 subnormal
+    y[2, :] = np_bf16_round(rng.normal(0, 1e-30, 256))  # a tiny row (scale far below 2^-64)
+    for g in (32, 128, 256):
+        o = ref.quantize_fp8(y, g)
+        q, s = np_fp8(y, g)
+        assert (o["q"] == q).all() and (o["scale"] == s).all(), f"quantize_fp8 group {g}"
+    m = ref.quantize_mxfp4(y)
+    packed, byte = np_mxfp4(y)
+    assert (m["q"] == packed).all() and (m["scale"] == byte).all(), "quantize_mxfp4"
+    d = inputs.random_rows(3, 512, seed=8)
+    xb, rb, wb = inputs.bits(d["x"]), inputs.bits(d["residual"]), inputs.bits(d["weight"])
+    f = ref.fp8_per_token(xb, rb, wb, 1e-6, emit_y=True)
+    q = ref.quantize_fp8(f["y"])
+    assert (q["q"] == f["q"]).all() and (q["scale"][:, 0] == f["scale"]).all()
+    f = ref.mxfp4(xb, rb, wb, 1e-6, emit_y=True)
+    q = ref.quantize_mxfp4(f["y"])
+    assert (q["q"] == f["q"]).all() and (q["scale"] == f["scale"]).all()
+
+
 ALL_PINS = [
     pin_bf16_decode, pin_bf16_round_vs_torch, pin_bf16_round_vs_search,
     pin_e4m3_table, pin_e4m3_bruteforce, pin_e4m3_fp32_quotients,
     pin_e2m1_table, pin_e2m1_bruteforce, pin_e8m0,
     pin_fp8_weight_probe, pin_mxfp4_weight_probe, pin_group_weight_probe,
     pin_constant_row, pin_zero_and_sign, pin_independent_rows,
-    pin_strided_inputs, pin_qk, pin_invariants_on_workloads,
+    pin_strided_inputs, pin_qk, pin_invariants_on_workloads, pin_quantize_step,
 ]

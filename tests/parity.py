@@ -1,0 +1,106 @@
+"""Comparison of the HIP path against the oracle (used by the GPU tests).
+
+Tolerances (the method statement's, written here):
+  residual_out              bit-exact (a correctly rounded bf16 sum on both sides)
+  y (bf16 normalized row)   within 1 bf16 ulp; the flip rate is reported.  The
+                            kernel computes rstd in fp32, the oracle in fp64, so
+                            y can differ where r * rstd * w lies next to a bf16
+                            rounding boundary.
+  codes                     identical on >= 99.9 % of elements, the rest at most
+                            one code step apart;
+  scales                    equal, or moved by the one-ulp change of the
+                            granule's amax (FP8: scale from amax +- 1 bf16 ulp;
+                            E8M0: +- 1).
+  Stronger, exact check: the kernel's codes and scales are bit-identical to the
+  oracle's quantization of the kernel's own y (the quantizer is a pure function
+  of the bf16 row, so nothing excuses a difference there).
+QK: q and k within 1 bf16 ulp, gate bit-exact.
+"""
+
+from __future__ import annotations
+
+import numpy as np
+
+from rmsnorm_activation_quantization_amd import inputs
+
+Y_FLIP_RATE_MAX = 1e-3
+CODE_MATCH_MIN = 0.999
+
+
+def signed_key(bits: np.ndarray, sign_bit: int) -> np.ndarray:
+    """Sign-magnitude codes mapped onto a monotonic integer line (+0 and -0 both 0)."""
+    b = np.asarray(bits).astype(np.int64)
+    mag = b & (sign_bit - 1)
+    return np.where(b & sign_bit, -mag, mag)
+
+
+def bf16_ulps(a, b) -> np.ndarray:
+    return np.abs(signed_key(a, 0x8000) - signed_key(b, 0x8000))
+
+
+def check_bf16_close(got, want, what: str, max_flip_rate: float = Y_FLIP_RATE_MAX) -> dict:
+    d = bf16_ulps(got, want)
+    assert d.max(initial=0) <= 1, f"{what}: {int(d.max())} bf16 ulps apart at {np.argwhere(d > 1)[:5].tolist()}"
+    rate = float((d != 0).mean()) if d.size else 0.0
+    assert rate <= max_flip_rate, f"{what}: {rate:.2e} of values flipped by one ulp"
+    return {"flips": int((d != 0).sum()), "flip_rate": rate}
+
+
+def to_np(out: dict) -> dict:
+    import torch
+    res = {}
+    for k, v in out.items():
+        if v is None:
+            res[k] = None
+        elif v.dtype == torch.bfloat16:
+            res[k] = inputs.bits(v)
+        elif v.dtype == torch.float8_e4m3fn:
+            res[k] = v.view(torch.uint8).cpu().numpy()
+        else:
+            res[k] = v.cpu().numpy()
+    return res
+
+
+def check_fp8(gpu: dict, ref: dict, requant: dict, granule: int, what: str) -> dict:
+    """gpu/ref: residual_out, y, q [M,H] uint8, scale [M,G] fp32; requant: oracle quantize(gpu y)."""
+    M, H = gpu["q"].shape
+    assert (gpu["residual_out"] == ref["residual_out"]).all(), f"{what}: residual_out not bit-exact"
+    stats = check_bf16_close(gpu["y"], ref["y"], f"{what}: y")
+    # exact: the kernel quantized its own y exactly as the oracle would
+    assert (gpu["q"] == requant["q"]).all(), f"{what}: codes differ from quantize(y_gpu)"
+    assert np.array_equal(gpu["scale"].view(np.uint32), requant["scale"].reshape(gpu["scale"].shape).view(np.uint32)), \
+        f"{what}: scales differ from quantize(y_gpu)"
+    # tolerance against the oracle's full result
+    same = gpu["q"] == ref["q"]
+    match = float(same.mean())
+    assert match >= CODE_MATCH_MIN, f"{what}: only {match:.5f} of codes identical"
+    nan = ((ref["q"] & 0x7F) == 0x7F) | ((gpu["q"] & 0x7F) == 0x7F)
+    steps = np.abs(signed_key(gpu["q"], 0x80) - signed_key(ref["q"], 0x80))[~nan]
+    assert steps.max(initial=0) <= 1, f"{what}: a code is {int(steps.max())} steps from the oracle's"
+    gs = gpu["scale"].reshape(M, H // granule)
+    rs = ref["scale"].reshape(M, H // granule)
+    diff = gs.view(np.uint32) != rs.view(np.uint32)
+    if diff.any():
+        ya = np.abs(signed_key(gpu["y"], 0x8000)).reshape(M, H // granule, granule).max(axis=2)
+        yr = np.abs(signed_key(ref["y"], 0x8000)).reshape(M, H // granule, granule).max(axis=2)
+        assert (np.abs(ya - yr)[diff] <= 1).all(), f"{what}: a scale differs without a one-ulp amax change"
+    stats.update(code_match=match, scale_diffs=int(diff.sum()))
+    return stats
+
+
+def check_mxfp4(gpu: dict, ref: dict, requant: dict, what: str) -> dict:
+    M = gpu["q"].shape[0]
+    assert (gpu["residual_out"] == ref["residual_out"]).all(), f"{what}: residual_out not bit-exact"
+    stats = check_bf16_close(gpu["y"], ref["y"], f"{what}: y")
+    assert (gpu["q"] == requant["q"]).all(), f"{what}: codes differ from quantize(y_gpu)"
+    assert (gpu["scale"] == requant["scale"]).all(), f"{what}: E8M0 bytes differ from quantize(y_gpu)"
+    nib = lambda q: np.stack([q & 0xF, q >> 4], axis=-1).reshape(M, -1)
+    g, r = nib(gpu["q"]), nib(ref["q"])
+    match = float((g == r).mean())
+    assert match >= CODE_MATCH_MIN, f"{what}: only {match:.5f} of codes identical"
+    steps = np.abs(signed_key(g, 0x8) - signed_key(r, 0x8))
+    assert steps.max(initial=0) <= 1, f"{what}: a code is {int(steps.max())} steps from the oracle's"
+    bd = np.abs(gpu["scale"].astype(int) - ref["scale"].astype(int))
+    assert bd.max(initial=0) <= 1, f"{what}: an E8M0 byte differs by {int(bd.max())}"
+    stats.update(code_match=match, scale_diffs=int((bd != 0).sum()))
+    return stats

@@ -1,0 +1,69 @@
+"""The entry points enqueue only kernels, so they can be captured into a HIP
+graph: replays (with eager work and synchronizations between them) must
+reproduce the eager results bit for bit."""
+
+from __future__ import annotations
+
+import pytest
+import torch
+
+import rmsnorm_activation_quantization_amd as rq
+from rmsnorm_activation_quantization_amd import inputs
+
+pytestmark = pytest.mark.gpu
+DEV = "cuda:0"
+
+
+def test_graph_replay_matches_eager():
+    d = inputs.row_inputs(inputs.DECODE_4096)
+    x, r, w = (d[k].to(DEV) for k in ("x", "residual", "weight"))
+    qd = inputs.qk_inputs(inputs.QK_DECODE)
+    qg, k, qw, kw = (qd[n].to(DEV) for n in ("qg", "k", "q_w", "k_w"))
+    M, H = x.shape
+    bufs = dict(
+        t=(torch.empty((M, H), dtype=torch.uint8, device=DEV), torch.empty((M, H), dtype=torch.bfloat16, device=DEV),
+           torch.empty((M,), dtype=torch.float32, device=DEV)),
+        g=(torch.empty((M, H), dtype=torch.uint8, device=DEV), torch.empty((M, H), dtype=torch.bfloat16, device=DEV),
+           torch.empty((M, H // 128), dtype=torch.float32, device=DEV)),
+        m=(torch.empty((M, H // 2), dtype=torch.uint8, device=DEV),
+           torch.empty((M, H), dtype=torch.bfloat16, device=DEV),
+           torch.empty((M, H // 32), dtype=torch.uint8, device=DEV)),
+    )
+    qk_out = (torch.empty((64, 16, 256), dtype=torch.bfloat16, device=DEV),
+              torch.empty((64, 2, 256), dtype=torch.bfloat16, device=DEV),
+              torch.empty((64, 16, 256), dtype=torch.bfloat16, device=DEV))
+
+    def step():
+        q, ro, s = bufs["t"]
+        assert rq.rmsnorm_quant_fp8_per_token(x, r, w, 1e-6, q_out=q, residual_out=ro, scale_out=s) is not None
+        q, ro, s = bufs["g"]
+        assert rq.rmsnorm_quant_fp8_per_group(x, r, w, 1e-6, 128, q_out=q, residual_out=ro, scale_out=s) is not None
+        q, ro, s = bufs["m"]
+        assert rq.rmsnorm_quant_mxfp4(x, r, w, 1e-6, q_out=q, residual_out=ro, scale_out=s) is not None
+        assert rq.qk_gemma_rmsnorm_gate(qg, k, qw, kw, 16, 2, 256, 1e-6, q_out=qk_out[0], k_out=qk_out[1],
+                                        gate_out=qk_out[2]) is not None
+
+    def snapshot():
+        return [t.clone() for group in bufs.values() for t in group] + [t.clone() for t in qk_out]
+
+    step()
+    torch.cuda.synchronize()
+    eager = snapshot()
+
+    s = torch.cuda.Stream()
+    s.wait_stream(torch.cuda.current_stream())
+    with torch.cuda.stream(s):
+        step()  # warm-up on the capture stream
+    torch.cuda.current_stream().wait_stream(s)
+    torch.cuda.synchronize()
+    g = torch.cuda.CUDAGraph()
+    with torch.cuda.graph(g):
+        step()
+    for i in range(4):
+        for t in [t for group in bufs.values() for t in group] + list(qk_out):
+            t.zero_()
+        _ = (x.float() * 2).sum().item()  # unrelated eager work between replays
+        g.replay()
+        torch.cuda.synchronize()
+        for a, b in zip(snapshot(), eager):
+            assert torch.equal(a.view(torch.uint8), b.view(torch.uint8)), f"replay {i} differs from eager"

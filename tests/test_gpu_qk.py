@@ -1,0 +1,75 @@
+"""GPU parity of qk_gemma_rmsnorm_gate against the CPU oracle."""
+
+from __future__ import annotations
+
+import numpy as np
+import pytest
+import torch
+
+import rmsnorm_activation_quantization_amd as rq
+from rmsnorm_activation_quantization_amd import inputs
+from oracle_pins import np_bf16_round
+from parity import check_bf16_close
+
+pytestmark = pytest.mark.gpu
+DEV = "cuda:0"
+
+
+def run_qk(ref, w: inputs.QKWorkload, ld_k=None, ld_qg_pad=0):
+    d = inputs.qk_inputs(w, ld_k=ld_k)
+    qg = d["qg"]
+    if ld_qg_pad:
+        wide = torch.zeros((w.T, qg.shape[1] + ld_qg_pad), dtype=torch.bfloat16)
+        wide[:, : qg.shape[1]] = qg
+        qg_dev = wide.to(DEV)[:, : qg.shape[1]]
+    else:
+        qg_dev = qg.to(DEV)
+    k_dev = d["k"].to(DEV)[:, : w.Hk * w.D] if ld_k else d["k"].to(DEV)
+    out = rq.qk_gemma_rmsnorm_gate(qg_dev, k_dev, d["q_w"].to(DEV), d["k_w"].to(DEV), w.Hq, w.Hk, w.D, w.eps)
+    assert out is not None
+    torch.cuda.synchronize()
+    q, k, gate = (inputs.bits(t) for t in out)
+    kb = inputs.bits(d["k"])
+    o = ref.qk_gemma_rmsnorm_gate(inputs.bits(qg), kb[:, : ld_k] if ld_k else kb, inputs.bits(d["q_w"]),
+                                  inputs.bits(d["k_w"]), w.Hq, w.Hk, w.D, w.eps)
+    assert (gate == o["gate"]).all(), "gate must be a bit-exact copy"
+    sq = check_bf16_close(q, o["q"], f"{w.name} q")
+    sk = check_bf16_close(k, o["k"], f"{w.name} k")
+    print(w.name, sq, sk, flush=True)
+
+
+def test_qk_workload(ref):
+    run_qk(ref, inputs.QK_DECODE)
+
+
+def test_qk_strided_k(ref):
+    w = inputs.QK_DECODE
+    run_qk(ref, w, ld_k=1024)
+
+
+def test_qk_strided_qg(ref):
+    run_qk(ref, inputs.QK_DECODE, ld_qg_pad=64)
+
+
+@pytest.mark.parametrize("T,Hq,Hk,D", [(1, 1, 1, 8), (3, 4, 1, 64), (5, 8, 2, 128), (7, 2, 2, 512), (9, 3, 0, 256),
+                                        (4, 0, 3, 256), (6, 5, 3, 40), (2, 7, 1, 200), (300, 16, 2, 256),
+                                        (1024, 8, 1, 128)])
+def test_qk_shapes(ref, T, Hq, Hk, D):
+    run_qk(ref, inputs.QKWorkload(f"qk_{T}x{Hq}x{Hk}x{D}", T, Hq, Hk, D, seed=T + Hq + D))
+
+
+def test_qk_weight_probe():
+    """Every value 1024 and eps = 0: rstd = 2^-10 exactly, so out = bf16(1 + w)."""
+    T, Hq, Hk, D = 3, 2, 1, 256
+    qg = torch.full((T, 2 * Hq * D), 1024.0, dtype=torch.bfloat16, device=DEV)
+    k = torch.full((T, Hk * D), -1024.0, dtype=torch.bfloat16, device=DEV)
+    rng = np.random.default_rng(4)
+    qw = inputs.from_bits(np_bf16_round(rng.normal(0, 0.3, D))).to(DEV)
+    kw = inputs.from_bits(np_bf16_round(rng.normal(0, 0.3, D))).to(DEV)
+    q, kk, gate = rq.qk_gemma_rmsnorm_gate(qg, k, qw, kw, Hq, Hk, D, 0.0)
+    torch.cuda.synchronize()
+    one_plus_q = (1.0 + qw.float()).to(torch.bfloat16)
+    one_plus_k = (1.0 + kw.float()).to(torch.bfloat16)
+    assert torch.equal(q, one_plus_q.expand(T, Hq, D))
+    assert torch.equal(kk, (-one_plus_k).expand(T, Hk, D))
+    assert (gate == 1024.0).all()

@@ -1,0 +1,293 @@
+"""GPU parity of the fused residual-add + RMSNorm + quantization entry points
+against the CPU oracle (calls go through the C ABI via the ctypes binding)."""
+
+from __future__ import annotations
+
+import numpy as np
+import pytest
+import torch
+
+import rmsnorm_activation_quantization_amd as rq
+from rmsnorm_activation_quantization_amd import inputs
+from oracle_pins import fp8_probe_case, mxfp4_probe_case, np_bf16_round, np_bf16_value, BF16_VALUE
+from parity import check_fp8, check_mxfp4, to_np
+
+pytestmark = pytest.mark.gpu
+DEV = "cuda:0"
+
+
+def gpu_call(fmt, x, r, w, eps, group=128, emit_y=True, **kw):
+    if fmt == "fp8_token":
+        out = rq.rmsnorm_quant_fp8_per_token(x, r, w, eps, emit_y=emit_y, **kw)
+    elif fmt == "fp8_group":
+        out = rq.rmsnorm_quant_fp8_per_group(x, r, w, eps, group, emit_y=emit_y, **kw)
+    else:
+        out = rq.rmsnorm_quant_mxfp4(x, r, w, eps, emit_y=emit_y, **kw)
+    assert out is not None, f"{fmt} returned 'cannot fuse' for a supported shape"
+    torch.cuda.synchronize()
+    q, res, scale, y = out
+    return to_np(dict(q=q, residual_out=res, scale=scale, y=y))
+
+
+def oracle_call(ref, fmt, xb, rb, wb, eps, group=128):
+    if fmt == "fp8_token":
+        o = ref.fp8_per_token(xb, rb, wb, eps, emit_y=True)
+    elif fmt == "fp8_group":
+        o = ref.fp8_per_group(xb, rb, wb, eps, group, emit_y=True)
+    else:
+        o = ref.mxfp4(xb, rb, wb, eps, emit_y=True)
+    return o
+
+
+def check(ref, fmt, gpu, o, group, what):
+    if fmt == "mxfp4":
+        return check_mxfp4(gpu, o, ref.quantize_mxfp4(gpu["y"]), what)
+    H = gpu["q"].shape[1]
+    granule = H if fmt == "fp8_token" else group
+    return check_fp8(gpu, o, ref.quantize_fp8(gpu["y"], granule), granule, what)
+
+
+def run_case(ref, fmt, d, eps, group=128, what=""):
+    x, r, w = (d[k].to(DEV) for k in ("x", "residual", "weight"))
+    gpu = gpu_call(fmt, x, r, w, eps, group)
+    o = oracle_call(ref, fmt, inputs.bits(d["x"]), inputs.bits(d["residual"]), inputs.bits(d["weight"]), eps, group)
+    stats = check(ref, fmt, gpu, o, group, what or fmt)
+    # the side output changes nothing else
+    plain = gpu_call(fmt, x, r, w, eps, group, emit_y=False)
+    for key in ("q", "residual_out", "scale"):
+        assert np.array_equal(plain[key], gpu[key]), f"{what}: {key} depends on emit_y"
+    print(f"{what or fmt}: {stats}", flush=True)
+    return gpu
+
+
+WORKLOADS = [
+    ("fp8_token", inputs.FP8_TOKEN_SMALL),
+    ("fp8_group", inputs.FP8_GROUP_DECODE),
+    ("mxfp4", inputs.MXFP4_DECODE),
+    ("fp8_token", inputs.DECODE_4096),
+    ("fp8_group", inputs.DECODE_4096),
+    ("mxfp4", inputs.DECODE_4096),
+    ("fp8_token", inputs.PREFILL),
+    ("fp8_group", inputs.PREFILL),
+    ("mxfp4", inputs.PREFILL),
+]
+
+
+@pytest.mark.parametrize("fmt,wl", WORKLOADS, ids=[f"{f}-{w.name}" for f, w in WORKLOADS])
+def test_workload_parity(ref, fmt, wl):
+    run_case(ref, fmt, inputs.row_inputs(wl), wl.eps, what=f"{fmt}-{wl.name}")
+
+
+SHAPES = [(1, 32), (1, 2048), (3, 520), (15, 4096), (16, 7168), (17, 1056), (63, 4096), (64, 4096), (65, 4096),
+          (65, 7168), (257, 2080), (33, 8192), (70, 8192), (5, 8224), (9, 16384), (100, 16384), (130, 64)]
+
+
+@pytest.mark.parametrize("fmt", ["fp8_token", "fp8_group", "mxfp4"])
+@pytest.mark.parametrize("M,H", SHAPES)
+def test_shapes(ref, fmt, M, H):
+    group = 32 if H % 128 else 128
+    if fmt != "fp8_token" and H % 32:
+        d = inputs.random_rows(M, H, seed=1)
+        x, r, w = (d[k].to(DEV) for k in ("x", "residual", "weight"))
+        fn = rq.rmsnorm_quant_mxfp4 if fmt == "mxfp4" else rq.rmsnorm_quant_fp8_per_group
+        args = (x, r, w, 1e-6) if fmt == "mxfp4" else (x, r, w, 1e-6, group)
+        assert fn(*args) is None, "a granule that does not divide H must be refused"
+        return
+    run_case(ref, fmt, inputs.random_rows(M, H, seed=7 * M + H), 1e-6, group, what=f"{fmt}-{M}x{H}")
+
+
+@pytest.mark.parametrize("group", [32, 64, 128, 256, 512])
+@pytest.mark.parametrize("M", [5, 300])
+def test_group_sizes(ref, group, M):
+    run_case(ref, "fp8_group", inputs.random_rows(M, 4096, seed=group + M), 1e-6, group, what=f"group{group}-M{M}")
+
+
+@pytest.mark.parametrize("fmt", ["fp8_token", "fp8_group", "mxfp4"])
+def test_strided_inputs(ref, fmt):
+    M, H = 40, 2048
+    d = inputs.random_rows(M, H, seed=99)
+    xw = torch.zeros((M, H + 64), dtype=torch.bfloat16)
+    rw = torch.zeros((M, H + 128), dtype=torch.bfloat16)
+    xw[:, 8:8 + H] = d["x"]
+    rw[:, 64:64 + H] = d["residual"]
+    xg, rg = xw.to(DEV)[:, 8:8 + H], rw.to(DEV)[:, 64:64 + H]
+    assert xg.stride(0) == H + 64 and rg.stride(0) == H + 128
+    gpu = gpu_call(fmt, xg, rg, d["weight"].to(DEV), 1e-6)
+    o = oracle_call(ref, fmt, inputs.bits(d["x"]), inputs.bits(d["residual"]), inputs.bits(d["weight"]), 1e-6)
+    check(ref, fmt, gpu, o, 128, f"strided-{fmt}")
+
+
+@pytest.mark.parametrize("fmt", ["fp8_token", "mxfp4"])
+def test_in_place_residual(ref, fmt):
+    M, H = 70, 4096
+    d = inputs.random_rows(M, H, seed=5)
+    x, w = d["x"].to(DEV), d["weight"].to(DEV)
+    r1, r2 = d["residual"].to(DEV), d["residual"].to(DEV)
+    a = gpu_call(fmt, x, r1, w, 1e-6)
+    b = gpu_call(fmt, x, r2, w, 1e-6, residual_out=r2)
+    for key in ("q", "scale", "y", "residual_out"):
+        assert np.array_equal(a[key], b[key]), f"in-place {key}"
+    assert np.array_equal(inputs.bits(r2), a["residual_out"])
+
+
+def _probe_tensors(xb, rb, wb):
+    return (inputs.from_bits(xb).to(DEV), inputs.from_bits(rb).to(DEV), inputs.from_bits(wb).to(DEV))
+
+
+def test_fp8_weight_probe_goldens():
+    xb, rb, wb, want, scale = fp8_probe_case()
+    gpu = gpu_call("fp8_token", *_probe_tensors(xb, rb, wb), 0.0)
+    assert (gpu["y"][0] == wb).all(), "probe: y must equal the weight"
+    assert gpu["scale"][0, 0] == scale
+    assert (gpu["q"][0] == want).all(), np.nonzero(gpu["q"][0] != want)
+
+
+def test_mxfp4_weight_probe_goldens():
+    xb, rb, wb, packed, bytes_ = mxfp4_probe_case()
+    gpu = gpu_call("mxfp4", *_probe_tensors(xb, rb, wb), 0.0)
+    assert (gpu["y"][0] == wb).all()
+    assert (gpu["scale"] == bytes_).all(), (gpu["scale"], bytes_)
+    assert (gpu["q"] == packed).all()
+
+
+def _probe_rows(values: np.ndarray, H: int, leader: float) -> np.ndarray:
+    """Rows of H weights: element 0 of every granule-sized row is `leader`, the
+    rest are the values to convert (zero-padded)."""
+    per_row = H - 1
+    n_rows = -(-len(values) // per_row)
+    w = np.zeros((n_rows, H))
+    w[:, 0] = leader
+    flat = np.zeros(n_rows * per_row)
+    flat[: len(values)] = values
+    w[:, 1:] = flat.reshape(n_rows, per_row)
+    return w
+
+
+def test_fp8_conversion_exhaustive(ref):
+    """Every bf16 value in [-448, 448] through the fused kernel with scale 1
+    (x = residual = 512, eps = 0 makes y equal the weight bit for bit)."""
+    vals = BF16_VALUE[:0x43E1]
+    vals = np.concatenate([vals, -vals])
+    H = 4096
+    w = _probe_rows(vals, H, 448.0)
+    xb = np_bf16_round(np.full((1, H), 512.0))
+    for i in range(w.shape[0]):
+        wb = np_bf16_round(w[i])
+        gpu = gpu_call("fp8_token", *_probe_tensors(xb, xb.copy(), wb), 0.0)
+        assert (gpu["y"][0] == wb).all()
+        o = ref.fp8_per_token(xb, xb.copy(), wb, 0.0)
+        assert gpu["scale"][0, 0] == 1.0 and o["scale"][0] == 1.0
+        bad = np.nonzero(gpu["q"][0] != o["q"][0])[0]
+        assert len(bad) == 0, f"E4M3 codes differ for {np_bf16_value(wb[bad[:8]])}"
+
+
+@pytest.mark.parametrize("k", [-100, -20, 0, 5, 60, 120])
+def test_mxfp4_conversion_exhaustive(ref, k):
+    """Every bf16 magnitude below 8 (times 2^k) with a block maximum 7.5 * 2^k,
+    so the E8M0 byte is 127 + k and every E2M1 rounding case is exercised."""
+    vals = np.ldexp(BF16_VALUE[:0x4100], k)
+    vals = np.concatenate([vals, -vals])
+    vals = vals[(vals != 0) & (np_bf16_value(np_bf16_round(vals)) == vals)]  # exact bf16 values only
+    blocks = -(-len(vals) // 31)
+    w = np.zeros((blocks, 32))
+    w[:, 0] = np.ldexp(7.5, k)
+    flat = np.zeros(blocks * 31)
+    flat[: len(vals)] = vals
+    w[:, 1:] = flat.reshape(blocks, 31)
+    H = 4096
+    w = np.concatenate([w.reshape(-1), np.zeros((-w.size) % H)]).reshape(-1, H)
+    w = np.where(w == 0, np.ldexp(1.0, k), w)  # padding blocks keep a normal amax
+    xb = np_bf16_round(np.full((1, H), 512.0))
+    for i in range(w.shape[0]):
+        wb = np_bf16_round(w[i])
+        assert (np_bf16_value(wb) == w[i]).all()
+        gpu = gpu_call("mxfp4", *_probe_tensors(xb, xb.copy(), wb), 0.0)
+        o = ref.mxfp4(xb, xb.copy(), wb, 0.0)
+        assert (gpu["scale"] == o["scale"]).all()
+        assert (gpu["q"] == o["q"]).all(), f"E2M1 codes differ in row {i} at k={k}"
+
+
+def test_zero_sign_tiny_and_nan(ref):
+    H = 1024
+    rows = []
+    z = np.zeros(H, np.uint16)
+    z[1::2] = 0x8000
+    rows.append((z, z.copy()))                                       # +0 / -0 row
+    d = inputs.random_rows(4, H, seed=1)
+    xb, rb = inputs.bits(d["x"]), inputs.bits(d["residual"])
+    rows.append((xb[0], rb[0]))
+    nan_x = xb[1].copy()
+    nan_x[17] = 0x7FC0                                               # NaN in the row
+    rows.append((nan_x, rb[1]))
+    xs = np.stack([r[0] for r in rows])
+    rs = np.stack([r[1] for r in rows])
+    wt = np_bf16_round(np.random.default_rng(2).normal(0, 1e-25, H))  # tiny weights: scale < 2^-64
+    w1 = inputs.bits(d["weight"])
+    for wb, label in ((w1, "normal"), (wt, "tiny")):
+        for fmt in ("fp8_token", "fp8_group", "mxfp4"):
+            gpu = gpu_call(fmt, *_probe_tensors(xs, rs, wb), 1e-6)
+            o = oracle_call(ref, fmt, xs, rs, wb, 1e-6)
+            assert (gpu["residual_out"] == o["residual_out"]).all()
+            # zero row: exact, signs of zero kept
+            assert (gpu["y"][0] == o["y"][0]).all()
+            if fmt == "mxfp4":
+                assert (gpu["scale"][0] == 0).all() and (gpu["q"][0] == o["q"][0]).all()
+                assert (gpu["scale"][2] == 255).any(), "NaN block must carry E8M0 255"
+                req = ref.quantize_mxfp4(gpu["y"][1:2])
+                assert (gpu["q"][1] == req["q"][0]).all() and (gpu["scale"][1] == req["scale"][0]).all()
+            else:
+                assert (gpu["scale"][0] == 0).all() and (gpu["q"][0] == o["q"][0]).all()
+                assert np.isnan(gpu["scale"][2]).any(), "NaN row must give a NaN scale"
+                granule = H if fmt == "fp8_token" else 128
+                req = ref.quantize_fp8(gpu["y"][1:2], granule)
+                assert (gpu["q"][1] == req["q"][0]).all(), f"{label} {fmt}: codes differ from quantize(y)"
+                assert np.array_equal(gpu["scale"][1].reshape(-1).view(np.uint32),
+                                      req["scale"][0].view(np.uint32))
+
+
+def test_determinism():
+    d = inputs.row_inputs(inputs.PREFILL)
+    x, r, w = (d[k].to(DEV) for k in ("x", "residual", "weight"))
+    for fmt in ("fp8_token", "mxfp4"):
+        a = gpu_call(fmt, x, r, w, 1e-6)
+        b = gpu_call(fmt, x, r, w, 1e-6)
+        for key in a:
+            assert np.array_equal(a[key], b[key]), f"{fmt} {key} not deterministic"
+
+
+def test_unsupported_returns_none_and_writes_nothing():
+    M, H = 4, rq.RQ_MAX_HIDDEN + 8
+    x = torch.randn(M, H, device=DEV).to(torch.bfloat16)
+    ro = torch.full((M, H), 7.0, dtype=torch.bfloat16, device=DEV)
+    assert rq.rmsnorm_quant_fp8_per_token(x, x, x[0].contiguous(), residual_out=ro) is None
+    torch.cuda.synchronize()
+    assert (ro == 7.0).all()
+    # a row start that is not 16-byte aligned
+    base = torch.randn(M, 2048 + 8, device=DEV).to(torch.bfloat16)
+    xs = base[:, 1:2049]
+    w = torch.ones(2048, dtype=torch.bfloat16, device=DEV)
+    q = torch.full((M, 2048), 5, dtype=torch.uint8, device=DEV)
+    assert rq.rmsnorm_quant_mxfp4(xs, xs, w) is None
+    assert rq.rmsnorm_quant_fp8_per_token(xs, xs, w, q_out=q) is None
+    torch.cuda.synchronize()
+    assert (q == 5).all()
+
+
+def test_invalid_raises():
+    M, H = 4, 256
+    x = torch.randn(M, H, device=DEV).to(torch.bfloat16)
+    w = torch.ones(H, dtype=torch.bfloat16, device=DEV)
+    ro = torch.empty((M, H), dtype=torch.bfloat16, device=DEV)
+    with pytest.raises(ValueError):
+        rq.rmsnorm_quant_fp8_per_token(x, x, w, residual_out=ro, q_out=ro.view(torch.uint8)[:, :H])
+    with pytest.raises(ValueError):
+        rq.rmsnorm_quant_fp8_per_token(x, x, w, eps=-1.0)
+
+
+def test_empty_batch():
+    x = torch.empty((0, 4096), dtype=torch.bfloat16, device=DEV)
+    w = torch.ones(4096, dtype=torch.bfloat16, device=DEV)
+    out = rq.rmsnorm_quant_fp8_per_token(x, x, w)
+    assert out is not None and out[0].shape == (0, 4096)
+    out = rq.rmsnorm_quant_mxfp4(x, x, w)
+    assert out is not None and out[2].shape == (0, 128)
