@@ -11,12 +11,15 @@
 //
 // Work mapping (CDNA4: 64-lane waves, 16-byte loads):
 //   a lane owns 8 consecutive bf16 (one 16-byte load per tensor) per "chunk";
-//   the lanes of a row cover 8 * LANES consecutive columns per chunk, so every
-//   wave-level load and store is fully coalesced.  LANES = 64 (one wave per
-//   row, four rows per 256-thread workgroup: the prefill tiling, no LDS and no
-//   barrier) or 256 (the whole workgroup on one row: the decode tiling, one
-//   LDS exchange for the row sums).  NC = chunks per lane is a template
-//   parameter so the row lives in registers.
+//   the lanes of a row cover 8 * lanes consecutive columns per chunk, so every
+//   wave-level load and store is fully coalesced.  A row is spread over WPR
+//   waves (1, 2, 4, 8 or 16) of one workgroup, and NC = chunks per lane is a
+//   template parameter, so the row lives in registers from load to store and is
+//   never re-read.  The host picks WPR so that a lane holds at most two chunks:
+//   few registers, hence up to 8 waves per SIMD in flight, which measured best
+//   on MI355X at prefill sizes (a wave per row with the row in 115 VGPRs ran at
+//   68 % of HBM peak, a workgroup per row at 74 %).  Waves of a row combine
+//   their partial sums and maxima through LDS with one barrier each.
 // Reductions: the sum of squares over the row, and max |y| per token, per
 // group or per 32-element block, use DPP row operations inside 16-lane rows,
 // a swizzle across rows and readlane across wave halves.  Every butterfly step
@@ -59,10 +62,7 @@ typedef unsigned int u32x4_t __attribute__((ext_vector_type(4)));
 typedef unsigned int u32x2_t __attribute__((ext_vector_type(2)));
 
 constexpr int kWave = 64;
-constexpr int kBlock = 256;
-constexpr int kRowsPerWaveBlock = kBlock / kWave;  // prefill tiling: 4 rows a workgroup
-constexpr int kMaxChunksWave = 16;                 // one wave a row: H <= 16 * 512 = 8192
-constexpr int kMaxChunksBlock = 8;                 // a workgroup a row: H <= 8 * 2048 = 16384
+constexpr int kMaxChunks = 2;  // chunks per lane; rows need at most 16 waves * 64 lanes * 8 * 2 = 16384
 
 enum QuantMode { kFp8Token = 0, kFp8Group = 1, kMxfp4 = 2 };
 
@@ -90,8 +90,9 @@ __device__ __forceinline__ uint32_t halves_max(uint32_t w) {
 
 // ---------------------------------------------------------------------------
 // Global memory.  Streaming rows (read once, written once) use non-temporal
-// loads and stores in the prefill tiling: measured on MI355X they raise the
-// sustained bandwidth of this read-2 / write-1.5 pattern by about 5 % of peak.
+// loads and stores: measured on MI355X they raise the sustained bandwidth of
+// this read-2 / write-1.5 pattern by about 5 % of peak.  The weight, re-read by
+// every row, uses ordinary cached loads.
 // ---------------------------------------------------------------------------
 template <bool kNT>
 __device__ __forceinline__ uint4 load16(const uint16_t* p) {
@@ -288,30 +289,42 @@ struct RowArgs {
   int groups_per_row;    // per-group FP8: H / group
 };
 
+// Rows a workgroup holds for a given number of waves per row (4 waves a
+// workgroup at least, so a small row still fills a 256-thread workgroup).
+template <int kWPR>
+constexpr int rows_per_block() { return kWPR >= 4 ? 1 : 4 / kWPR; }
+template <int kWPR>
+constexpr int block_threads() { return kWave * kWPR * rows_per_block<kWPR>(); }
+
 template <int kMode, int kNC, int kWPR>
-__global__ __launch_bounds__(kBlock) void fused_rows(const RowArgs a) {
+__global__ __launch_bounds__(block_threads<kWPR>()) void fused_rows(const RowArgs a) {
   constexpr int kLanes = kWave * kWPR;
   constexpr int kChunk = kLanes * 8;
-  constexpr bool kNT = (kWPR == 1);  // streaming tiling
+  constexpr int kRPB = rows_per_block<kWPR>();
+  constexpr bool kNT = true;
   const int lane = threadIdx.x & (kWave - 1);
-  const int wave = threadIdx.x / kWave;
-  const int64_t row = (kWPR == 1) ? (int64_t)blockIdx.x * kRowsPerWaveBlock + wave : (int64_t)blockIdx.x;
-  const int t = (kWPR == 1) ? lane : (int)threadIdx.x;
-  if (kWPR == 1 && row >= a.M) return;  // whole waves only: no barrier in this tiling
+  const int wave = threadIdx.x / kWave;            // wave in the workgroup
+  const int rloc = wave / kWPR;                     // row in the workgroup
+  const int wrow = wave % kWPR;                     // wave in the row
+  const int64_t row = (int64_t)blockIdx.x * kRPB + rloc;
+  const int t = (int)threadIdx.x % kLanes;          // lane in the row
+  // A row past the end only happens in the last workgroup of the few-waves
+  // tilings; its waves still reach every barrier (loads and stores are masked).
+  const bool live = row < a.M;
   const int H = a.H;
 
-  __shared__ float lds_sum[kWPR];
-  __shared__ uint32_t lds_max[kWPR];
+  __shared__ float lds_sum[kRPB][kWPR];
+  __shared__ uint32_t lds_max[kRPB][kWPR];
 
-  const uint16_t* xr = a.x + row * a.ldx;
-  const uint16_t* rr = a.res + row * a.ldr;
+  const uint16_t* xr = a.x + (live ? row : 0) * a.ldx;
+  const uint16_t* rr = a.res + (live ? row : 0) * a.ldr;
 
   // 1. Issue every load of the row before using any of it.
   uint4 xv[kNC], rv[kNC], wv[kNC];
 #pragma unroll
   for (int c = 0; c < kNC; ++c) {
     const int col = c * kChunk + t * 8;
-    if (c < kNC - 1 || col < H) {
+    if (live && (c < kNC - 1 || col < H)) {
       xv[c] = load16<kNT>(xr + col);
       rv[c] = load16<kNT>(rr + col);
       wv[c] = load16<false>(a.w + col);  // the weight is re-read by every row: keep it cached
@@ -339,15 +352,17 @@ __global__ __launch_bounds__(kBlock) void fused_rows(const RowArgs a) {
     }
     rp[c] = make_uint4(p[0], p[1], p[2], p[3]);
     const int col = c * kChunk + t * 8;
-    if (c < kNC - 1 || col < H) store16<kNT>(a.res_out + row * H + col, rp[c]);
+    if (live && (c < kNC - 1 || col < H)) store16<kNT>(a.res_out + row * H + col, rp[c]);
   }
 
   // 3. rstd over the whole row.
   ss = group_sum(ss, 6);
   if (kWPR > 1) {
-    if (lane == 0) lds_sum[wave] = ss;
+    if (lane == 0) lds_sum[rloc][wrow] = ss;
     __syncthreads();
-    ss = (lds_sum[0] + lds_sum[1]) + (lds_sum[2] + lds_sum[3]);
+    ss = lds_sum[rloc][0];
+#pragma unroll
+    for (int w = 1; w < kWPR; ++w) ss += lds_sum[rloc][w];  // one fixed order: every lane agrees
   }
   const float rstd = 1.0f / __builtin_sqrtf(ss / (float)H + a.eps);
 
@@ -367,7 +382,7 @@ __global__ __launch_bounds__(kBlock) void fused_rows(const RowArgs a) {
 #pragma unroll
     for (int c = 0; c < kNC; ++c) {
       const int col = c * kChunk + t * 8;
-      if (c < kNC - 1 || col < H) store16<kNT>(a.y_out + row * H + col, yp[c]);
+      if (live && (c < kNC - 1 || col < H)) store16<kNT>(a.y_out + row * H + col, yp[c]);
     }
   }
 
@@ -378,17 +393,18 @@ __global__ __launch_bounds__(kBlock) void fused_rows(const RowArgs a) {
     for (int c = 0; c < kNC; ++c) m = umax(m, chunk_abs_max(yp[c]));
     m = group_max(m, 6);
     if (kWPR > 1) {
-      if (lane == 0) lds_max[wave] = m;
+      if (lane == 0) lds_max[rloc][wrow] = m;
       __syncthreads();
-      m = umax(umax(lds_max[0], lds_max[1]), umax(lds_max[2], lds_max[3]));
+#pragma unroll
+      for (int w = 0; w < kWPR; ++w) m = umax(m, lds_max[rloc][w]);
     }
     const Fp8Granule g = fp8_granule(m);
-    if (t == 0) reinterpret_cast<float*>(a.scale)[row] = g.scale;
+    if (live && t == 0) reinterpret_cast<float*>(a.scale)[row] = g.scale;
 #pragma unroll
     for (int c = 0; c < kNC; ++c) {
       const int col = c * kChunk + t * 8;
       const uint2 codes = fp8_codes(yp[c], g);
-      if (c < kNC - 1 || col < H) store8<kNT>(a.q + row * H + col, codes);
+      if (live && (c < kNC - 1 || col < H)) store8<kNT>(a.q + row * H + col, codes);
     }
   } else if (kMode == kFp8Group) {
     const int gl = a.group_log2_lanes;
@@ -398,7 +414,7 @@ __global__ __launch_bounds__(kBlock) void fused_rows(const RowArgs a) {
       const uint32_t m = group_max(chunk_abs_max(yp[c]), gl);
       const Fp8Granule g = fp8_granule(m);
       const uint2 codes = fp8_codes(yp[c], g);
-      if (c < kNC - 1 || col < H) {
+      if (live && (c < kNC - 1 || col < H)) {
         store8<kNT>(a.q + row * H + col, codes);
         if ((t & ((1 << gl) - 1)) == 0)
           reinterpret_cast<float*>(a.scale)[row * a.groups_per_row + (col >> (gl + 3))] = g.scale;
@@ -411,7 +427,7 @@ __global__ __launch_bounds__(kBlock) void fused_rows(const RowArgs a) {
       const uint32_t m = group_max_c<2>(chunk_abs_max(yp[c]));
       const uint32_t byte = e8m0_byte(m);
       const uint32_t codes = mxfp4_codes(yp[c], byte);
-      if (c < kNC - 1 || col < H) {
+      if (live && (c < kNC - 1 || col < H)) {
         store4<kNT>(a.q + row * (H / 2) + col / 2, codes);
         if ((t & 3) == 0) reinterpret_cast<uint8_t*>(a.scale)[row * (H / 32) + col / 32] = (uint8_t)byte;
       }
@@ -500,15 +516,16 @@ __global__ __launch_bounds__(kQKBlock) void qk_gemma_gate(const QKArgs a) {
 using RowKernel = void (*)(RowArgs);
 using QKKernel = void (*)(QKArgs);
 
-template <int kMode, int kWPR, int... kNC>
-constexpr auto row_table(std::integer_sequence<int, kNC...>) {
-  struct T { RowKernel k[sizeof...(kNC)]; };
-  return T{{&fused_rows<kMode, kNC + 1, kWPR>...}};
-}
+template <int kMode, int kWPR>
+struct RowKernelsW {
+  static constexpr RowKernel k[kMaxChunks] = {&fused_rows<kMode, 1, kWPR>, &fused_rows<kMode, 2, kWPR>};
+};
 template <int kMode>
 struct RowKernels {
-  static constexpr auto wave = row_table<kMode, 1>(std::make_integer_sequence<int, kMaxChunksWave>{});
-  static constexpr auto block = row_table<kMode, 4>(std::make_integer_sequence<int, kMaxChunksBlock>{});
+  // [log2 waves per row][chunks per lane - 1]
+  static constexpr const RowKernel* k[5] = {RowKernelsW<kMode, 1>::k, RowKernelsW<kMode, 2>::k,
+                                           RowKernelsW<kMode, 4>::k, RowKernelsW<kMode, 8>::k,
+                                           RowKernelsW<kMode, 16>::k};
 };
 constexpr QKKernel kQKKernels[7] = {&qk_gemma_gate<0>, &qk_gemma_gate<1>, &qk_gemma_gate<2>, &qk_gemma_gate<3>,
                                     &qk_gemma_gate<4>, &qk_gemma_gate<5>, &qk_gemma_gate<6>};
@@ -588,22 +605,24 @@ rq_status launch(const void* kernel, dim3 grid, dim3 block, void* args, void* st
   return err == hipSuccess ? RQ_OK : RQ_ERR_HIP;
 }
 
-// Decode sizes (few rows) spread each row over a whole workgroup; prefill
-// sizes give each row one wave.  Rows longer than a wave's register budget
-// always take the workgroup tiling.
+// Waves per row: the fewest (a power of two, 1..16) for which a lane holds at
+// most kMaxChunks chunks of 8 elements.
+int waves_per_row_log2(int H) {
+  int l = 0;
+  while (l < 4 && (int64_t)kWave * (1 << l) * 8 * kMaxChunks < H) ++l;
+  return l;
+}
+
 template <int kMode>
 rq_status launch_rows(RowArgs& a, void* stream) {
-  const int H = a.H;
-  const bool block_tiling = (a.M <= 64) || H > kMaxChunksWave * kWave * 8;
-  if (block_tiling) {
-    const int nc = (H + kBlock * 8 - 1) / (kBlock * 8);
-    return launch(reinterpret_cast<const void*>(RowKernels<kMode>::block.k[nc - 1]), dim3(a.M), dim3(kBlock), &a,
-                  stream);
-  }
-  const int nc = (H + kWave * 8 - 1) / (kWave * 8);
-  const unsigned blocks = (unsigned)((a.M + kRowsPerWaveBlock - 1) / kRowsPerWaveBlock);
-  return launch(reinterpret_cast<const void*>(RowKernels<kMode>::wave.k[nc - 1]), dim3(blocks), dim3(kBlock), &a,
-                stream);
+  const int l = waves_per_row_log2(a.H);
+  const int wpr = 1 << l;
+  const int lanes = kWave * wpr;
+  const int nc = (a.H + lanes * 8 - 1) / (lanes * 8);
+  const int rpb = wpr >= 4 ? 1 : 4 / wpr;
+  const unsigned blocks = (unsigned)((a.M + rpb - 1) / rpb);
+  return launch(reinterpret_cast<const void*>(RowKernels<kMode>::k[l][nc - 1]), dim3(blocks),
+                dim3((unsigned)(lanes * rpb)), &a, stream);
 }
 
 RowArgs make_row_args(const uint16_t* x, int64_t ldx, const uint16_t* residual, int64_t ldr, const uint16_t* weight,
