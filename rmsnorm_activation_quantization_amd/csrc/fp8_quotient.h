@@ -19,4 +19,19 @@ RQ_QUOTIENT_QUALIFIERS float rq_fp8_quotient(float y, float sc, float inv) {
   return __builtin_fmaf(-e, inv, q0);
 }
 
+/* The FP8 scale amax / 448 for a bf16 amax: the same correction step with the
+ * correctly rounded constant 1/448, exact for every bf16 amax in the normal
+ * range. */
+#define RQ_INV_448 (1.0f / 448.0f)
+RQ_QUOTIENT_QUALIFIERS float rq_fp8_scale(float amax) { return rq_fp8_quotient(amax, 448.0f, RQ_INV_448); }
+
+/* One Newton step on an approximate reciprocal r0 of sc.  For the scales that
+ * occur (sc = amax / 448 rounded, amax a bf16 value: 128 significands) it
+ * returns the correctly rounded 1 / sc from any r0 within 2 ulp of it; the
+ * test suite checks every one of those significands and every such start. */
+RQ_QUOTIENT_QUALIFIERS float rq_recip_refine(float sc, float r0) {
+  float e = __builtin_fmaf(-sc, r0, 1.0f);
+  return __builtin_fmaf(e, r0, r0);
+}
+
 #endif /* RQ_FP8_QUOTIENT_H */

@@ -30,14 +30,16 @@
 //   residual_out = bf16_rne(f32(x) + f32(res))   exact: the fp32 sum of two
 //                  bf16 values rounded to bf16 is the correctly rounded sum
 //                  (24 >= 2*8 + 2, so the double rounding is innocuous).
-//   ss = sum of r^2 in fp32; rstd = 1 / sqrt(ss / H + eps) (IEEE div/sqrt).
+//   ss = sum of r^2 in fp32; rstd = rsq(ss * (1/H) + eps) (hardware
+//        reciprocal square root; the oracle's rstd is fp64, and y may differ
+//        by one bf16 ulp where r * rstd * w lies next to a rounding boundary).
 //   y = bf16_rne((r * rstd) * w).
-//   FP8: scale = amax / 448 (IEEE division); the quotient y / scale is formed
-//        with a correctly rounded reciprocal and one Markstein correction
-//        (q0 = y*inv, e = scale*q0 - y, q = q0 - e*inv), which equals the IEEE
-//        fp32 quotient for every bf16 y and fp32 scale >= 2^-64 (checked
-//        exhaustively on the host by the test suite); the hardware converter
-//        then rounds to E4M3FN (nearest-even).
+//   FP8: scale = amax / 448 exactly (IEEE-equal); the quotient y / scale is
+//        formed with the correctly rounded reciprocal of the scale and one
+//        Markstein correction (q0 = y*inv, e = scale*q0 - y, q = q0 - e*inv),
+//        which equals the IEEE fp32 quotient for every bf16 y and fp32 scale
+//        >= 2^-64 (checked exhaustively on the host by the test suite); the
+//        hardware converter then rounds to E4M3FN (nearest-even).
 //   MXFP4: E8M0 byte from the exponent bits of amax; y * 2^(127 - byte) is
 //        exact, and the hardware converter rounds to E2M1 (nearest-even,
 //        saturating at 6).
@@ -187,25 +189,33 @@ struct Fp8Granule {
   float scale;  // stored scale = amax / 448
   float sc;     // divisor used by the correction step
   float inv;    // correctly rounded 1 / sc
-  bool slow;    // scale below 2^-64: plain IEEE division per element
+  bool slow;    // scale below 2^-62 or amax not finite: plain IEEE division
 };
 
+// No division on the fast path: the scale is the exact quotient amax / 448
+// (correction step with the constant 1/448), and its reciprocal is the hardware
+// estimate refined by one Newton step, which is the correctly rounded value for
+// every scale that can occur (fp8_quotient.h).  Both depend only on amax, so
+// they issue in parallel: two short chains instead of two IEEE divisions.
 __device__ __forceinline__ Fp8Granule fp8_granule(uint32_t amax_bits) {
   Fp8Granule g;
-  float amax = __uint_as_float(amax_bits << 16);
-  g.scale = amax / 448.0f;
+  const float amax = __uint_as_float(amax_bits << 16);
+  const uint32_t e = amax_bits >> 7;  // exponent field of the bf16 amax
   g.slow = false;
   if (amax_bits == 0) {
     // All-zero granule: scale 0; q = y * 0 keeps the sign of each zero.
+    g.scale = 0.0f;
     g.sc = 1.0f;
     g.inv = 0.0f;
-  } else if (g.scale < 0x1p-64f) {
-    g.slow = true;  // keeps every intermediate of the correction step normal
+  } else if (e >= 73u && e < 255u) {  // amax >= 2^-54: the scale and every intermediate stay normal
+    g.scale = rq_fp8_scale(amax);
+    g.sc = g.scale;
+    g.inv = rq_recip_refine(g.scale, __builtin_amdgcn_rcpf(g.scale));
+  } else {
+    g.scale = amax / 448.0f;
     g.sc = g.scale;
     g.inv = 0.0f;
-  } else {
-    g.sc = g.scale;
-    g.inv = 1.0f / g.scale;
+    g.slow = true;
   }
   return g;
 }
@@ -225,7 +235,7 @@ __device__ __forceinline__ uint2 fp8_codes(const uint4& y, const Fp8Granule& g) 
       q[2 * j] = fp8_quotient(bf_lo(w[j]), g);
       q[2 * j + 1] = fp8_quotient(bf_hi(w[j]), g);
     }
-  } else {
+  } else {  // tiny or non-finite granule
 #pragma unroll
     for (int j = 0; j < 4; ++j) {
       q[2 * j] = bf_lo(w[j]) / g.sc;
@@ -285,14 +295,15 @@ struct RowArgs {
   int M;
   int H;
   float eps;
+  float inv_h;           // 1 / H, rounded on the host
   int group_log2_lanes;  // per-group FP8: log2(group / 8)
   int groups_per_row;    // per-group FP8: H / group
 };
 
-// Rows a workgroup holds for a given number of waves per row (4 waves a
-// workgroup at least, so a small row still fills a 256-thread workgroup).
+// Rows a workgroup holds: four one-wave rows, or one row of several waves (so
+// every barrier of a multi-wave row is uniform over its workgroup).
 template <int kWPR>
-constexpr int rows_per_block() { return kWPR >= 4 ? 1 : 4 / kWPR; }
+constexpr int rows_per_block() { return kWPR == 1 ? 4 : 1; }
 template <int kWPR>
 constexpr int block_threads() { return kWave * kWPR * rows_per_block<kWPR>(); }
 
@@ -314,6 +325,7 @@ __global__ __launch_bounds__(block_threads<kWPR>()) void fused_rows(const RowArg
   const int H = a.H;
 
   __shared__ float lds_sum[kRPB][kWPR];
+  __shared__ float lds_sum_tiny[kRPB][kWPR];
   __shared__ uint32_t lds_max[kRPB][kWPR];
 
   const uint16_t* xr = a.x + (live ? row : 0) * a.ldx;
@@ -364,7 +376,38 @@ __global__ __launch_bounds__(block_threads<kWPR>()) void fused_rows(const RowArg
 #pragma unroll
     for (int w = 1; w < kWPR; ++w) ss += lds_sum[rloc][w];  // one fixed order: every lane agrees
   }
-  const float rstd = 1.0f / __builtin_sqrtf(ss / (float)H + a.eps);
+  // rstd need not be correctly rounded (the tolerance on y is one bf16 ulp):
+  // the hardware reciprocal square root keeps it off the critical path.
+  const float t_ms = __builtin_fmaf(ss, a.inv_h, a.eps);
+  float rstd;
+  if (!(t_ms < 0x1p-100f)) {
+    rstd = __builtin_amdgcn_rsqf(t_ms);  // NaN and Inf propagate through here
+  } else {
+    // Only with eps < 2^-100: the squares of a row this small underflow fp32,
+    // so sum them again with r scaled by 2^100 (exact; |r| < 2^-43 here, so the
+    // scaled squares lie in [2^-66, 2^114]).  Uniform over the row, and a
+    // multi-wave row has its workgroup to itself.
+    float s2 = 0.0f;
+#pragma unroll
+    for (int c = 0; c < kNC; ++c) {
+      const uint32_t rs[4] = {rp[c].x, rp[c].y, rp[c].z, rp[c].w};
+#pragma unroll
+      for (int j = 0; j < 4; ++j) {
+        const float r0 = bf_lo(rs[j]) * 0x1p100f, r1 = bf_hi(rs[j]) * 0x1p100f;
+        s2 = __builtin_fmaf(r0, r0, s2);
+        s2 = __builtin_fmaf(r1, r1, s2);
+      }
+    }
+    s2 = group_sum(s2, 6);
+    if (kWPR > 1) {
+      if (lane == 0) lds_sum_tiny[rloc][wrow] = s2;
+      __syncthreads();
+      s2 = lds_sum_tiny[rloc][0];
+#pragma unroll
+      for (int w = 1; w < kWPR; ++w) s2 += lds_sum_tiny[rloc][w];
+    }
+    rstd = __builtin_amdgcn_rsqf(__builtin_fmaf(s2, a.inv_h, a.eps * 0x1p100f * 0x1p100f)) * 0x1p100f;
+  }
 
   // 4. y = bf16((r * rstd) * w), optional bf16 side output.
   uint4 yp[kNC];
@@ -453,6 +496,7 @@ struct QKArgs {
   int Hk;
   int D;
   float eps;
+  float inv_d;  // 1 / D, rounded on the host
 };
 
 constexpr int kQKBlock = 64;  // one wave a workgroup: spreads a small decode batch over many CUs
@@ -492,7 +536,21 @@ __global__ __launch_bounds__(kQKBlock) void qk_gemma_gate(const QKArgs a) {
     ss = __builtin_fmaf(bf_hi(vs[j]), bf_hi(vs[j]), ss);
   }
   ss = group_sum(ss, kLog2Lanes);
-  const float rstd = 1.0f / __builtin_sqrtf(ss / (float)a.D + a.eps);
+  const float t_ms = __builtin_fmaf(ss, a.inv_d, a.eps);
+  float rstd;
+  if (!(t_ms < 0x1p-100f)) {
+    rstd = __builtin_amdgcn_rsqf(t_ms);
+  } else {  // a head this small with eps < 2^-100: sum the squares of v * 2^100 (exact)
+    float s2 = 0.0f;
+#pragma unroll
+    for (int j = 0; j < 4; ++j) {
+      const float v0 = bf_lo(vs[j]) * 0x1p100f, v1 = bf_hi(vs[j]) * 0x1p100f;
+      s2 = __builtin_fmaf(v0, v0, s2);
+      s2 = __builtin_fmaf(v1, v1, s2);
+    }
+    s2 = group_sum(s2, kLog2Lanes);
+    rstd = __builtin_amdgcn_rsqf(__builtin_fmaf(s2, a.inv_d, a.eps * 0x1p100f * 0x1p100f)) * 0x1p100f;
+  }
   uint32_t p[4];
 #pragma unroll
   for (int j = 0; j < 4; ++j)
@@ -619,7 +677,7 @@ rq_status launch_rows(RowArgs& a, void* stream) {
   const int wpr = 1 << l;
   const int lanes = kWave * wpr;
   const int nc = (a.H + lanes * 8 - 1) / (lanes * 8);
-  const int rpb = wpr >= 4 ? 1 : 4 / wpr;
+  const int rpb = wpr == 1 ? 4 : 1;
   const unsigned blocks = (unsigned)((a.M + rpb - 1) / rpb);
   return launch(reinterpret_cast<const void*>(RowKernels<kMode>::k[l][nc - 1]), dim3(blocks),
                 dim3((unsigned)(lanes * rpb)), &a, stream);
@@ -641,6 +699,7 @@ RowArgs make_row_args(const uint16_t* x, int64_t ldx, const uint16_t* residual, 
   a.M = (int)M;
   a.H = (int)H;
   a.eps = eps;
+  a.inv_h = 1.0f / (float)H;
   a.group_log2_lanes = 0;
   a.groups_per_row = 0;
   return a;
@@ -731,6 +790,7 @@ rq_status qk_gemma_rmsnorm_gate(const uint16_t* qg, int64_t ld_qg, const uint16_
   a.Hk = (int)Hk;
   a.D = (int)D;
   a.eps = eps;
+  a.inv_d = 1.0f / (float)D;
   const int64_t heads_per_wave = kWave >> log2_lanes;
   const int64_t blocks = (a.units + heads_per_wave - 1) / heads_per_wave;
   if (blocks > INT32_MAX) return RQ_ERR_UNSUPPORTED;

@@ -54,3 +54,40 @@ def test_quotient_is_correctly_rounded(tmp_path):
                    check=True)
     out = subprocess.run([str(exe)], capture_output=True, text=True, timeout=600)
     assert out.returncode == 0 and "mismatches 0" in out.stdout, out.stdout + out.stderr
+
+
+SCALE_PROGRAM = r"""
+#include <stdio.h>
+#include <string.h>
+#include <stdint.h>
+#include "fp8_quotient.h"
+static uint32_t bits(float f) { uint32_t u; memcpy(&u, &f, 4); return u; }
+static float from(uint32_t u) { float f; memcpy(&f, &u, 4); return f; }
+int main(void) {
+  long long bad = 0;
+  /* every bf16 amax from 2^-54 up to the largest finite bf16 (the kernel's fast path) */
+  for (uint32_t ab = (73u << 7); ab < 0x7F80u; ++ab) {
+    float amax = from(ab << 16);
+    float want = (float)((double)amax / 448.0);          /* RN(amax / 448) */
+    float scale = rq_fp8_scale(amax);
+    if (bits(scale) != bits(want)) ++bad;
+    float inv = (float)(1.0 / (double)want);              /* RN(1 / scale) */
+    for (int d = -2; d <= 2; ++d)                          /* any hardware estimate within 2 ulp */
+      if (bits(rq_recip_refine(want, from(bits(inv) + d))) != bits(inv)) ++bad;
+  }
+  printf("mismatches %lld\n", bad);
+  return bad != 0;
+}
+"""
+
+
+def test_scale_and_reciprocal_are_correctly_rounded(tmp_path):
+    """Every bf16 amax on the fast path: the division-free scale equals
+    RN(amax / 448), and one Newton step from any estimate within 2 ulp gives
+    RN(1 / scale) (the hardware reciprocal estimate is within 1 ulp)."""
+    src = tmp_path / "scale_check.c"
+    src.write_text(SCALE_PROGRAM)
+    exe = tmp_path / "scale_check"
+    subprocess.run(["gcc", "-O2", "-mfma", "-ffp-contract=off", "-I", PKG, str(src), "-o", str(exe)], check=True)
+    out = subprocess.run([str(exe)], capture_output=True, text=True, timeout=120)
+    assert out.returncode == 0 and "mismatches 0" in out.stdout, out.stdout + out.stderr

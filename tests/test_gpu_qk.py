@@ -73,3 +73,18 @@ def test_qk_weight_probe():
     assert torch.equal(q, one_plus_q.expand(T, Hq, D))
     assert torch.equal(kk, (-one_plus_k).expand(T, Hk, D))
     assert (gate == 1024.0).all()
+
+
+def test_qk_tiny_heads_without_eps(ref):
+    """eps = 0 and heads whose squares underflow fp32."""
+    w = inputs.QKWorkload("qk_tiny", 8, 4, 2, 128, seed=12, eps=0.0)
+    d = inputs.qk_inputs(w)
+    qg = inputs.from_bits(np_bf16_round(d["qg"].double().numpy() * 1e-25))
+    k = inputs.from_bits(np_bf16_round(d["k"].double().numpy() * 1e-30))
+    out = rq.qk_gemma_rmsnorm_gate(qg.to(DEV), k.to(DEV), d["q_w"].to(DEV), d["k_w"].to(DEV), w.Hq, w.Hk, w.D, 0.0)
+    torch.cuda.synchronize()
+    o = ref.qk_gemma_rmsnorm_gate(inputs.bits(qg), inputs.bits(k), inputs.bits(d["q_w"]), inputs.bits(d["k_w"]),
+                                  w.Hq, w.Hk, w.D, 0.0)
+    assert (inputs.bits(out[2]) == o["gate"]).all()
+    check_bf16_close(inputs.bits(out[0]), o["q"], "tiny q")
+    check_bf16_close(inputs.bits(out[1]), o["k"], "tiny k")

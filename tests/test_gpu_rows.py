@@ -291,3 +291,43 @@ def test_empty_batch():
     assert out is not None and out[0].shape == (0, 4096)
     out = rq.rmsnorm_quant_mxfp4(x, x, w)
     assert out is not None and out[2].shape == (0, 128)
+
+
+@pytest.mark.parametrize("exp_field", [40, 73, 100, 127, 160, 250])
+def test_every_fp8_scale_significand(ref, exp_field):
+    """Per-group FP8 with 32-element groups whose maxima take all 128 bf16
+    significands at one exponent (the fast division-free scale path from
+    exponent field 73 up, the IEEE-division path below); y equals the weight
+    exactly (x = residual = 512, eps = 0), and codes and scales must equal the
+    oracle's bit for bit."""
+    rng = np.random.default_rng(exp_field)
+    H, g = 4096, 32
+    amax_bits = ((exp_field << 7) | np.arange(128)).astype(np.uint16)
+    amax = np_bf16_value(amax_bits)
+    w = np.empty((128, g))
+    w[:, 0] = amax * np.where(rng.random(128) < 0.5, -1, 1)
+    w[:, 1:] = rng.uniform(-1, 1, (128, g - 1)) * amax[:, None]
+    wb = np_bf16_round(w.reshape(-1))
+    over = np.abs(np_bf16_value(wb)) > np.repeat(amax, g)
+    wb[over] = (wb[over] & 0x8000) | np.repeat(amax_bits, g)[over]  # keep every element within the group's amax
+    xb = np_bf16_round(np.full((1, H), 512.0))
+    gpu = gpu_call("fp8_group", *_probe_tensors(xb, xb.copy(), wb), 0.0, group=g)
+    o = ref.fp8_per_group(xb, xb.copy(), wb, 0.0, g)
+    assert (gpu["y"][0] == wb).all()
+    assert np.array_equal(gpu["scale"].view(np.uint32), o["scale"].view(np.uint32)), "scales differ"
+    assert (gpu["q"] == o["q"]).all(), f"codes differ in {np.count_nonzero(gpu['q'] != o['q'])} places"
+
+
+@pytest.mark.parametrize("fmt", ["fp8_token", "fp8_group", "mxfp4"])
+@pytest.mark.parametrize("M,H", [(4, 4096), (70, 4096), (3, 2048), (5, 512)])
+def test_tiny_rows_without_eps(ref, fmt, M, H):
+    """eps = 0 and rows so small that their squares underflow fp32: the
+    kernel's rescaled sum must still normalize them like the oracle."""
+    d = inputs.random_rows(M, H, seed=M + H)
+    scale = np.array([1e-22, 1e-30, 1e-36, 3e-39])[np.arange(M) % 4]
+    xb = np_bf16_round(np_bf16_value(inputs.bits(d["x"])) * scale[:, None])
+    rb = np_bf16_round(np_bf16_value(inputs.bits(d["residual"])) * scale[:, None])
+    wb = inputs.bits(d["weight"])
+    gpu = gpu_call(fmt, *_probe_tensors(xb, rb, wb), 0.0)
+    o = oracle_call(ref, fmt, xb, rb, wb, 0.0)
+    check(ref, fmt, gpu, o, 128, f"tiny-{fmt}-{M}x{H}")
