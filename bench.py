@@ -194,6 +194,7 @@ def main():
     }
     if not args.no_decode and not args.profile_pass:
         result["decode"] = decode_latency(torch, rq, inputs, dev)
+        result["unfused_vs_fused"] = unfused_comparison(torch, rq, inputs, dev, sets, outs, per_kernel_us, args)
     if not args.no_cpu_baseline and not args.profile_pass:
         result["cpu_baseline"] = cpu_baseline(inputs, wl, qw, nbytes)
     print(json.dumps(result), flush=True)
@@ -290,6 +291,99 @@ def decode_latency(torch, rq, inputs, dev, calls: int = 200, replays: int = 7):
         lambda i: rq.qk_gemma_rmsnorm_gate(qg[i % nq], kk[i % nq], qd["q_w"], qd["k_w"], qw.Hq, qw.Hk, qw.D, qw.eps,
                                            q_out=outs[0], k_out=outs[1], gate_out=outs[2])), 3)
     res["pages_context_us"] = {"qk_gemma_rmsnorm_gate_kernel_mi355x_tp2": 4.6, "launch_floor_gfx950": 4.2}
+    return res
+
+
+def unfused_comparison(torch, rq, inputs, dev, sets, outs, fused_us, args):
+    """The same work as the unfused sequence (rmsnorm_residual_bf16, then
+    quantize_*: two launches with the bf16 row y written and read back) next
+    to the fused call.  Prefill: K back-to-back pairs over the rotating sets,
+    timed like the fused phases.  Decode [16, 4096]: graph replay over
+    rotating cold inputs."""
+    import statistics
+    M, H = sets[0]["x"].shape
+    ys = [torch.empty((M, H), dtype=torch.bfloat16, device=dev) for _ in sets]
+    res = {"prefill_8192x4096": {}, "decode_16x4096": {}}
+
+    def quant(fmt, y, o):
+        if fmt == "fp8_token":
+            return rq.quantize_fp8_per_token(y, q_out=o["t"][0], scale_out=o["t"][2])
+        if fmt == "fp8_group":
+            return rq.quantize_fp8_per_group(y, 128, q_out=o["g"][0], scale_out=o["g"][2])
+        return rq.quantize_mxfp4(y, q_out=o["m"][0], scale_out=o["m"][2])
+
+    key = {"fp8_token": "t", "fp8_group": "g", "mxfp4": "m"}
+    for fmt in ("fp8_token", "fp8_group", "mxfp4"):
+        def pair(j):
+            i, o = sets[j % len(sets)], outs[j % len(sets)]
+            rq.rmsnorm_residual_bf16(i["x"], i["residual"], i["weight"], 1e-6, residual_out=o[key[fmt]][1],
+                                     y_out=ys[j % len(sets)])
+            quant(fmt, ys[j % len(sets)], o)
+        for j in range(4):
+            pair(j)
+        torch.cuda.synchronize()
+        a, b = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+        a.record()
+        for j in range(args.steps):
+            pair(j)
+        b.record()
+        torch.cuda.synchronize()
+        un = 1000.0 * a.elapsed_time(b) / args.steps
+        res["prefill_8192x4096"][fmt] = {"fused_us": round(fused_us[fmt], 3), "unfused_us": round(un, 3),
+                                         "fused_speedup": round(un / fused_us[fmt], 3)}
+
+    # decode
+    wl = inputs.DECODE_4096
+    nsets, calls = 1024, 200
+    x = torch.randn(nsets, wl.M, wl.H, device=dev).to(torch.bfloat16)
+    r = torch.randn(nsets, wl.M, wl.H, device=dev).to(torch.bfloat16)
+    w = inputs.row_inputs(wl)["weight"].to(dev)
+    o = dict(t=(torch.empty((wl.M, wl.H), dtype=torch.uint8, device=dev), None,
+                torch.empty((wl.M,), dtype=torch.float32, device=dev)),
+             g=(torch.empty((wl.M, wl.H), dtype=torch.uint8, device=dev), None,
+                torch.empty((wl.M, wl.H // 128), dtype=torch.float32, device=dev)),
+             m=(torch.empty((wl.M, wl.H // 2), dtype=torch.uint8, device=dev), None,
+                torch.empty((wl.M, wl.H // 32), dtype=torch.uint8, device=dev)))
+    ro = torch.empty((wl.M, wl.H), dtype=torch.bfloat16, device=dev)
+    y = torch.empty((wl.M, wl.H), dtype=torch.bfloat16, device=dev)
+
+    def graph_us(fn):
+        s = torch.cuda.Stream()
+        s.wait_stream(torch.cuda.current_stream())
+        with torch.cuda.stream(s):
+            fn(0)
+        torch.cuda.current_stream().wait_stream(s)
+        torch.cuda.synchronize()
+        g = torch.cuda.CUDAGraph()
+        with torch.cuda.graph(g):
+            for i in range(calls):
+                fn(i)
+        times = []
+        for _ in range(7):
+            a, b = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+            a.record()
+            g.replay()
+            b.record()
+            torch.cuda.synchronize()
+            times.append(1000.0 * a.elapsed_time(b) / calls)
+        return statistics.median(times)
+
+    fused_fn = {
+        "fp8_token": lambda i: rq.rmsnorm_quant_fp8_per_token(x[i % nsets], r[i % nsets], w, 1e-6, residual_out=ro,
+                                                              q_out=o["t"][0], scale_out=o["t"][2]),
+        "fp8_group": lambda i: rq.rmsnorm_quant_fp8_per_group(x[i % nsets], r[i % nsets], w, 1e-6, 128,
+                                                              residual_out=ro, q_out=o["g"][0], scale_out=o["g"][2]),
+        "mxfp4": lambda i: rq.rmsnorm_quant_mxfp4(x[i % nsets], r[i % nsets], w, 1e-6, residual_out=ro,
+                                                  q_out=o["m"][0], scale_out=o["m"][2]),
+    }
+    for fmt in ("fp8_token", "fp8_group", "mxfp4"):
+        def pair(i, fmt=fmt):
+            rq.rmsnorm_residual_bf16(x[i % nsets], r[i % nsets], w, 1e-6, residual_out=ro, y_out=y)
+            quant(fmt, y, o)
+        f = graph_us(fused_fn[fmt])
+        u = graph_us(pair)
+        res["decode_16x4096"][fmt] = {"fused_us": round(f, 3), "unfused_us": round(u, 3),
+                                      "fused_speedup": round(u / f, 3)}
     return res
 
 

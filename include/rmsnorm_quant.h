@@ -122,6 +122,38 @@ rq_status rmsnorm_quant_mxfp4(
     uint16_t* residual_out, uint8_t* q_out, uint8_t* scale_out, uint16_t* y_out,
     void* stream);
 
+/* ---- The unfused sequence, one launch per step ----
+ * sglang PR #29723, Motivation: without fusion the step runs as separate
+ * launches with bf16 tensors between them (the all-reduce, RMSNorm with the
+ * residual add, then the quantization); Speed Tests: the fused kernel is
+ * benchmarked against that sequence; "Applicability": a consumer that cannot
+ * take the quantized tuple needs the bf16 row.  These entry points are those
+ * launches on one GPU.  Their results equal the fused entry points' bit for
+ * bit: rmsnorm_residual_bf16 followed by quantize_* gives exactly the codes
+ * and scales of rmsnorm_quant_* (the same kernel code computes y).
+ */
+
+/* residual_out = bf16(x + residual); y_out = bf16(residual_out * rstd * weight).
+ * Arguments, layout, aliasing and errors as rmsnorm_quant_fp8_per_token;
+ * y_out [M, H] bf16 is required. */
+rq_status rmsnorm_residual_bf16(
+    const uint16_t* x, int64_t ldx, const uint16_t* residual, int64_t ldr,
+    const uint16_t* weight, int64_t M, int64_t H, float eps,
+    uint16_t* residual_out, uint16_t* y_out, void* stream);
+
+/* Quantize a bf16 tensor y [M, ldy] (first H columns) with the rules and
+ * output layouts of rmsnorm_quant_fp8_per_token / _fp8_per_group / _mxfp4.
+ * Outputs must not overlap y. */
+rq_status quantize_fp8_per_token(
+    const uint16_t* y, int64_t ldy, int64_t M, int64_t H,
+    uint8_t* q_out, float* scale_out, void* stream);
+rq_status quantize_fp8_per_group(
+    const uint16_t* y, int64_t ldy, int64_t M, int64_t H, int64_t group,
+    uint8_t* q_out, float* scale_out, void* stream);
+rq_status quantize_mxfp4(
+    const uint16_t* y, int64_t ldy, int64_t M, int64_t H,
+    uint8_t* q_out, uint8_t* scale_out, void* stream);
+
 /* QK GemmaRMSNorm + gate de-interleave.  sglang PR #27656 ("Fuse QK RMSNorm +
  * gate extraction Triton kernel for Qwen3.5 on HIP"), Motivation and
  * Modifications: reads q and gate from the interleaved per-token layout

@@ -8,14 +8,21 @@ that ABI.  Entry points keep the C names:
   rmsnorm_quant_fp8_per_group   ... + per-group FP8 (group 32..512)
   rmsnorm_quant_mxfp4           ... + MXFP4 (E2M1 codes, E8M0 scale per 32)
   qk_gemma_rmsnorm_gate         QK GemmaRMSNorm + gate de-interleave
+
+and the unfused sequence, one launch per step (bit-identical results):
+
+  rmsnorm_residual_bf16         residual add + RMSNorm -> bf16 y
+  quantize_fp8_per_token / quantize_fp8_per_group / quantize_mxfp4
 """
 
 from .binding import (RQ_ERR_HIP, RQ_ERR_INVALID, RQ_ERR_UNSUPPORTED, RQ_MAX_HEAD_DIM, RQ_MAX_HIDDEN, RQ_OK,
-                      lib, library_path, qk_gemma_rmsnorm_gate, rmsnorm_quant_fp8_per_group,
-                      rmsnorm_quant_fp8_per_token, rmsnorm_quant_mxfp4, status_string)
+                      lib, library_path, qk_gemma_rmsnorm_gate, quantize_fp8_per_group, quantize_fp8_per_token,
+                      quantize_mxfp4, rmsnorm_quant_fp8_per_group, rmsnorm_quant_fp8_per_token,
+                      rmsnorm_quant_mxfp4, rmsnorm_residual_bf16, status_string)
 
 __all__ = [
     "rmsnorm_quant_fp8_per_token", "rmsnorm_quant_fp8_per_group", "rmsnorm_quant_mxfp4", "qk_gemma_rmsnorm_gate",
+    "rmsnorm_residual_bf16", "quantize_fp8_per_token", "quantize_fp8_per_group", "quantize_mxfp4",
     "lib", "library_path", "status_string", "RQ_OK", "RQ_ERR_INVALID", "RQ_ERR_UNSUPPORTED", "RQ_ERR_HIP",
     "RQ_MAX_HIDDEN", "RQ_MAX_HEAD_DIM",
 ]

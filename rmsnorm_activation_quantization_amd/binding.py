@@ -38,6 +38,10 @@ _SIGNATURES = {
     "rmsnorm_quant_fp8_per_group": [_p, _i64, _p, _i64, _p, _i64, _i64, _f32, _i64, _p, _p, _p, _p, _p],
     "rmsnorm_quant_mxfp4": [_p, _i64, _p, _i64, _p, _i64, _i64, _f32, _p, _p, _p, _p, _p],
     "qk_gemma_rmsnorm_gate": [_p, _i64, _p, _i64, _p, _p, _i64, _i64, _i64, _i64, _f32, _p, _p, _p, _p],
+    "rmsnorm_residual_bf16": [_p, _i64, _p, _i64, _p, _i64, _i64, _f32, _p, _p, _p],
+    "quantize_fp8_per_token": [_p, _i64, _i64, _i64, _p, _p, _p],
+    "quantize_fp8_per_group": [_p, _i64, _i64, _i64, _i64, _p, _p, _p],
+    "quantize_mxfp4": [_p, _i64, _i64, _i64, _p, _p, _p],
 }
 
 
@@ -192,3 +196,56 @@ def qk_gemma_rmsnorm_gate(qg, k, q_w, k_w, num_q_heads: int, num_k_heads: int, h
     if not _check(st, "qk_gemma_rmsnorm_gate"):
         return None
     return q_out, k_out, gate_out
+
+
+# ---- the unfused sequence, one launch per step ----
+
+def rmsnorm_residual_bf16(x, residual, weight, eps: float = 1e-6, *, residual_out=None, y_out=None, stream=None):
+    """-> (residual_out [M, H] bf16, y [M, H] bf16), or None."""
+    ldx, ldr = _rows(x, "x"), _rows(residual, "residual")
+    M, H, residual_out, y_out = _row_outputs(x, residual, weight, residual_out, y_out, True)
+    st = lib().rmsnorm_residual_bf16(_ptr(x), ldx, _ptr(residual), ldr, _ptr(weight), M, H, eps,
+                                     _ptr(residual_out), _ptr(y_out), _stream(stream))
+    if not _check(st, "rmsnorm_residual_bf16"):
+        return None
+    return residual_out, y_out
+
+
+def _quant_input(y):
+    ldy = _rows(y, "y")
+    return ldy, y.shape[0], y.shape[1]
+
+
+def quantize_fp8_per_token(y, *, q_out=None, scale_out=None, stream=None):
+    """-> (q [M, H] float8_e4m3fn, scale [M, 1] fp32), or None."""
+    ldy, M, H = _quant_input(y)
+    q_out = torch.empty((M, H), dtype=torch.uint8, device=y.device) if q_out is None else q_out
+    scale_out = torch.empty((M,), dtype=torch.float32, device=y.device) if scale_out is None else scale_out
+    st = lib().quantize_fp8_per_token(_ptr(y), ldy, M, H, _ptr(q_out), _ptr(scale_out), _stream(stream))
+    if not _check(st, "quantize_fp8_per_token"):
+        return None
+    return q_out.view(torch.float8_e4m3fn), scale_out.view(M, 1)
+
+
+def quantize_fp8_per_group(y, group: int = 128, *, q_out=None, scale_out=None, stream=None):
+    """-> (q [M, H] float8_e4m3fn, scale [M, H/group] fp32), or None."""
+    ldy, M, H = _quant_input(y)
+    q_out = torch.empty((M, H), dtype=torch.uint8, device=y.device) if q_out is None else q_out
+    if scale_out is None:
+        scale_out = torch.empty((M, max(H // group, 1) if group > 0 else 1), dtype=torch.float32, device=y.device)
+    st = lib().quantize_fp8_per_group(_ptr(y), ldy, M, H, group, _ptr(q_out), _ptr(scale_out), _stream(stream))
+    if not _check(st, "quantize_fp8_per_group"):
+        return None
+    return q_out.view(torch.float8_e4m3fn), scale_out
+
+
+def quantize_mxfp4(y, *, q_out=None, scale_out=None, stream=None):
+    """-> (q [M, H/2] uint8 packed E2M1, scale [M, H/32] uint8 E8M0), or None."""
+    ldy, M, H = _quant_input(y)
+    q_out = torch.empty((M, H // 2), dtype=torch.uint8, device=y.device) if q_out is None else q_out
+    if scale_out is None:
+        scale_out = torch.empty((M, max(H // 32, 1)), dtype=torch.uint8, device=y.device)
+    st = lib().quantize_mxfp4(_ptr(y), ldy, M, H, _ptr(q_out), _ptr(scale_out), _stream(stream))
+    if not _check(st, "quantize_mxfp4"):
+        return None
+    return q_out, scale_out

@@ -67,6 +67,7 @@ constexpr int kWave = 64;
 constexpr int kMaxChunks = 2;  // chunks per lane; rows need at most 16 waves * 64 lanes * 8 * 2 = 16384
 
 enum QuantMode { kFp8Token = 0, kFp8Group = 1, kMxfp4 = 2 };
+enum Stage { kStageFused = 0, kStageNorm = 1, kStageQuantize = 2 };
 
 // ---------------------------------------------------------------------------
 // bf16 <-> fp32
@@ -307,7 +308,10 @@ constexpr int rows_per_block() { return kWPR == 1 ? 4 : 1; }
 template <int kWPR>
 constexpr int block_threads() { return kWave * kWPR * rows_per_block<kWPR>(); }
 
-template <int kMode, int kNC, int kWPR>
+// kStage selects what one launch does: the fused step (norm + quantize), or
+// one launch of the unfused sequence (norm alone writing y, or quantize alone
+// reading y from a.x with stride a.ldx).
+template <int kMode, int kNC, int kWPR, int kStage>
 __global__ __launch_bounds__(block_threads<kWPR>()) void fused_rows(const RowArgs a) {
   constexpr int kLanes = kWave * kWPR;
   constexpr int kChunk = kLanes * 8;
@@ -328,106 +332,117 @@ __global__ __launch_bounds__(block_threads<kWPR>()) void fused_rows(const RowArg
   __shared__ float lds_sum_tiny[kRPB][kWPR];
   __shared__ uint32_t lds_max[kRPB][kWPR];
 
-  const uint16_t* xr = a.x + (live ? row : 0) * a.ldx;
-  const uint16_t* rr = a.res + (live ? row : 0) * a.ldr;
-
-  // 1. Issue every load of the row before using any of it.
-  uint4 xv[kNC], rv[kNC], wv[kNC];
-#pragma unroll
-  for (int c = 0; c < kNC; ++c) {
-    const int col = c * kChunk + t * 8;
-    if (live && (c < kNC - 1 || col < H)) {
-      xv[c] = load16<kNT>(xr + col);
-      rv[c] = load16<kNT>(rr + col);
-      wv[c] = load16<false>(a.w + col);  // the weight is re-read by every row: keep it cached
-    } else {
-      xv[c] = make_uint4(0, 0, 0, 0);
-      rv[c] = make_uint4(0, 0, 0, 0);
-      wv[c] = make_uint4(0, 0, 0, 0);
-    }
-  }
-
-  // 2. Residual add (one bf16 rounding), store residual_out, sum of squares.
-  uint4 rp[kNC];
-  float ss = 0.0f;
-#pragma unroll
-  for (int c = 0; c < kNC; ++c) {
-    const uint32_t xs[4] = {xv[c].x, xv[c].y, xv[c].z, xv[c].w};
-    const uint32_t rs[4] = {rv[c].x, rv[c].y, rv[c].z, rv[c].w};
-    uint32_t p[4];
-#pragma unroll
-    for (int j = 0; j < 4; ++j) {
-      p[j] = pack_bf16(bf_lo(xs[j]) + bf_lo(rs[j]), bf_hi(xs[j]) + bf_hi(rs[j]));
-      const float r0 = bf_lo(p[j]), r1 = bf_hi(p[j]);
-      ss = __builtin_fmaf(r0, r0, ss);
-      ss = __builtin_fmaf(r1, r1, ss);
-    }
-    rp[c] = make_uint4(p[0], p[1], p[2], p[3]);
-    const int col = c * kChunk + t * 8;
-    if (live && (c < kNC - 1 || col < H)) store16<kNT>(a.res_out + row * H + col, rp[c]);
-  }
-
-  // 3. rstd over the whole row.
-  ss = group_sum(ss, 6);
-  if (kWPR > 1) {
-    if (lane == 0) lds_sum[rloc][wrow] = ss;
-    __syncthreads();
-    ss = lds_sum[rloc][0];
-#pragma unroll
-    for (int w = 1; w < kWPR; ++w) ss += lds_sum[rloc][w];  // one fixed order: every lane agrees
-  }
-  // rstd need not be correctly rounded (the tolerance on y is one bf16 ulp):
-  // the hardware reciprocal square root keeps it off the critical path.
-  const float t_ms = __builtin_fmaf(ss, a.inv_h, a.eps);
-  float rstd;
-  if (!(t_ms < 0x1p-100f)) {
-    rstd = __builtin_amdgcn_rsqf(t_ms);  // NaN and Inf propagate through here
-  } else {
-    // Only with eps < 2^-100: the squares of a row this small underflow fp32,
-    // so sum them again with r scaled by 2^100 (exact; |r| < 2^-43 here, so the
-    // scaled squares lie in [2^-66, 2^114]).  Uniform over the row, and a
-    // multi-wave row has its workgroup to itself.
-    float s2 = 0.0f;
-#pragma unroll
-    for (int c = 0; c < kNC; ++c) {
-      const uint32_t rs[4] = {rp[c].x, rp[c].y, rp[c].z, rp[c].w};
-#pragma unroll
-      for (int j = 0; j < 4; ++j) {
-        const float r0 = bf_lo(rs[j]) * 0x1p100f, r1 = bf_hi(rs[j]) * 0x1p100f;
-        s2 = __builtin_fmaf(r0, r0, s2);
-        s2 = __builtin_fmaf(r1, r1, s2);
-      }
-    }
-    s2 = group_sum(s2, 6);
-    if (kWPR > 1) {
-      if (lane == 0) lds_sum_tiny[rloc][wrow] = s2;
-      __syncthreads();
-      s2 = lds_sum_tiny[rloc][0];
-#pragma unroll
-      for (int w = 1; w < kWPR; ++w) s2 += lds_sum_tiny[rloc][w];
-    }
-    rstd = __builtin_amdgcn_rsqf(__builtin_fmaf(s2, a.inv_h, a.eps * 0x1p100f * 0x1p100f)) * 0x1p100f;
-  }
-
-  // 4. y = bf16((r * rstd) * w), optional bf16 side output.
   uint4 yp[kNC];
-#pragma unroll
-  for (int c = 0; c < kNC; ++c) {
-    const uint32_t rs[4] = {rp[c].x, rp[c].y, rp[c].z, rp[c].w};
-    const uint32_t ws[4] = {wv[c].x, wv[c].y, wv[c].z, wv[c].w};
-    uint32_t p[4];
-#pragma unroll
-    for (int j = 0; j < 4; ++j)
-      p[j] = pack_bf16((bf_lo(rs[j]) * rstd) * bf_lo(ws[j]), (bf_hi(rs[j]) * rstd) * bf_hi(ws[j]));
-    yp[c] = make_uint4(p[0], p[1], p[2], p[3]);
-  }
-  if (a.y_out) {
+  if constexpr (kStage == kStageQuantize) {
+    // The quantize launch of the unfused sequence: y comes from memory.
+    const uint16_t* yr = a.x + (live ? row : 0) * a.ldx;
 #pragma unroll
     for (int c = 0; c < kNC; ++c) {
       const int col = c * kChunk + t * 8;
-      if (live && (c < kNC - 1 || col < H)) store16<kNT>(a.y_out + row * H + col, yp[c]);
+      yp[c] = (live && (c < kNC - 1 || col < H)) ? load16<kNT>(yr + col) : make_uint4(0, 0, 0, 0);
+    }
+  } else {
+    const uint16_t* xr = a.x + (live ? row : 0) * a.ldx;
+    const uint16_t* rr = a.res + (live ? row : 0) * a.ldr;
+
+    // 1. Issue every load of the row before using any of it.
+    uint4 xv[kNC], rv[kNC], wv[kNC];
+  #pragma unroll
+    for (int c = 0; c < kNC; ++c) {
+      const int col = c * kChunk + t * 8;
+      if (live && (c < kNC - 1 || col < H)) {
+        xv[c] = load16<kNT>(xr + col);
+        rv[c] = load16<kNT>(rr + col);
+        wv[c] = load16<false>(a.w + col);  // the weight is re-read by every row: keep it cached
+      } else {
+        xv[c] = make_uint4(0, 0, 0, 0);
+        rv[c] = make_uint4(0, 0, 0, 0);
+        wv[c] = make_uint4(0, 0, 0, 0);
+      }
+    }
+
+    // 2. Residual add (one bf16 rounding), store residual_out, sum of squares.
+    uint4 rp[kNC];
+    float ss = 0.0f;
+  #pragma unroll
+    for (int c = 0; c < kNC; ++c) {
+      const uint32_t xs[4] = {xv[c].x, xv[c].y, xv[c].z, xv[c].w};
+      const uint32_t rs[4] = {rv[c].x, rv[c].y, rv[c].z, rv[c].w};
+      uint32_t p[4];
+  #pragma unroll
+      for (int j = 0; j < 4; ++j) {
+        p[j] = pack_bf16(bf_lo(xs[j]) + bf_lo(rs[j]), bf_hi(xs[j]) + bf_hi(rs[j]));
+        const float r0 = bf_lo(p[j]), r1 = bf_hi(p[j]);
+        ss = __builtin_fmaf(r0, r0, ss);
+        ss = __builtin_fmaf(r1, r1, ss);
+      }
+      rp[c] = make_uint4(p[0], p[1], p[2], p[3]);
+      const int col = c * kChunk + t * 8;
+      if (live && (c < kNC - 1 || col < H)) store16<kNT>(a.res_out + row * H + col, rp[c]);
+    }
+
+    // 3. rstd over the whole row.
+    ss = group_sum(ss, 6);
+    if (kWPR > 1) {
+      if (lane == 0) lds_sum[rloc][wrow] = ss;
+      __syncthreads();
+      ss = lds_sum[rloc][0];
+  #pragma unroll
+      for (int w = 1; w < kWPR; ++w) ss += lds_sum[rloc][w];  // one fixed order: every lane agrees
+    }
+    // rstd need not be correctly rounded (the tolerance on y is one bf16 ulp):
+    // the hardware reciprocal square root keeps it off the critical path.
+    const float t_ms = __builtin_fmaf(ss, a.inv_h, a.eps);
+    float rstd;
+    if (!(t_ms < 0x1p-100f)) {
+      rstd = __builtin_amdgcn_rsqf(t_ms);  // NaN and Inf propagate through here
+    } else {
+      // Only with eps < 2^-100: the squares of a row this small underflow fp32,
+      // so sum them again with r scaled by 2^100 (exact; |r| < 2^-43 here, so the
+      // scaled squares lie in [2^-66, 2^114]).  Uniform over the row, and a
+      // multi-wave row has its workgroup to itself.
+      float s2 = 0.0f;
+  #pragma unroll
+      for (int c = 0; c < kNC; ++c) {
+        const uint32_t rs[4] = {rp[c].x, rp[c].y, rp[c].z, rp[c].w};
+  #pragma unroll
+        for (int j = 0; j < 4; ++j) {
+          const float r0 = bf_lo(rs[j]) * 0x1p100f, r1 = bf_hi(rs[j]) * 0x1p100f;
+          s2 = __builtin_fmaf(r0, r0, s2);
+          s2 = __builtin_fmaf(r1, r1, s2);
+        }
+      }
+      s2 = group_sum(s2, 6);
+      if (kWPR > 1) {
+        if (lane == 0) lds_sum_tiny[rloc][wrow] = s2;
+        __syncthreads();
+        s2 = lds_sum_tiny[rloc][0];
+  #pragma unroll
+        for (int w = 1; w < kWPR; ++w) s2 += lds_sum_tiny[rloc][w];
+      }
+      rstd = __builtin_amdgcn_rsqf(__builtin_fmaf(s2, a.inv_h, a.eps * 0x1p100f * 0x1p100f)) * 0x1p100f;
+    }
+
+    // 4. y = bf16((r * rstd) * w), optional bf16 side output.
+  #pragma unroll
+    for (int c = 0; c < kNC; ++c) {
+      const uint32_t rs[4] = {rp[c].x, rp[c].y, rp[c].z, rp[c].w};
+      const uint32_t ws[4] = {wv[c].x, wv[c].y, wv[c].z, wv[c].w};
+      uint32_t p[4];
+  #pragma unroll
+      for (int j = 0; j < 4; ++j)
+        p[j] = pack_bf16((bf_lo(rs[j]) * rstd) * bf_lo(ws[j]), (bf_hi(rs[j]) * rstd) * bf_hi(ws[j]));
+      yp[c] = make_uint4(p[0], p[1], p[2], p[3]);
+    }
+    if (a.y_out) {
+  #pragma unroll
+      for (int c = 0; c < kNC; ++c) {
+        const int col = c * kChunk + t * 8;
+        if (live && (c < kNC - 1 || col < H)) store16<kNT>(a.y_out + row * H + col, yp[c]);
+      }
     }
   }
+  if constexpr (kStage == kStageNorm) return;
 
   // 5. Absmax per granule, scale, quantize, pack, store.
   if (kMode == kFp8Token) {
@@ -574,16 +589,16 @@ __global__ __launch_bounds__(kQKBlock) void qk_gemma_gate(const QKArgs a) {
 using RowKernel = void (*)(RowArgs);
 using QKKernel = void (*)(QKArgs);
 
-template <int kMode, int kWPR>
+template <int kMode, int kStage, int kWPR>
 struct RowKernelsW {
-  static constexpr RowKernel k[kMaxChunks] = {&fused_rows<kMode, 1, kWPR>, &fused_rows<kMode, 2, kWPR>};
+  static constexpr RowKernel k[kMaxChunks] = {&fused_rows<kMode, 1, kWPR, kStage>, &fused_rows<kMode, 2, kWPR, kStage>};
 };
-template <int kMode>
+template <int kMode, int kStage>
 struct RowKernels {
   // [log2 waves per row][chunks per lane - 1]
-  static constexpr const RowKernel* k[5] = {RowKernelsW<kMode, 1>::k, RowKernelsW<kMode, 2>::k,
-                                           RowKernelsW<kMode, 4>::k, RowKernelsW<kMode, 8>::k,
-                                           RowKernelsW<kMode, 16>::k};
+  static constexpr const RowKernel* k[5] = {RowKernelsW<kMode, kStage, 1>::k, RowKernelsW<kMode, kStage, 2>::k,
+                                           RowKernelsW<kMode, kStage, 4>::k, RowKernelsW<kMode, kStage, 8>::k,
+                                           RowKernelsW<kMode, kStage, 16>::k};
 };
 constexpr QKKernel kQKKernels[7] = {&qk_gemma_gate<0>, &qk_gemma_gate<1>, &qk_gemma_gate<2>, &qk_gemma_gate<3>,
                                     &qk_gemma_gate<4>, &qk_gemma_gate<5>, &qk_gemma_gate<6>};
@@ -657,6 +672,49 @@ rq_status row_preflight(const uint16_t* x, int64_t ldx, const uint16_t* residual
   return check_device();
 }
 
+// Checks of the norm launch of the unfused sequence (x, residual, weight in;
+// residual_out and y out).
+rq_status norm_preflight(const uint16_t* x, int64_t ldx, const uint16_t* residual, int64_t ldr,
+                         const uint16_t* weight, int64_t M, int64_t H, float eps, const uint16_t* residual_out,
+                         const uint16_t* y_out) {
+  if (M < 0 || H <= 0 || !(eps >= 0.0f) || ldx < H || ldr < H) return RQ_ERR_INVALID;
+  if (M > 0 && (!x || !residual || !weight || !residual_out || !y_out)) return RQ_ERR_INVALID;
+  if (H % 8 != 0 || H > RQ_MAX_HIDDEN || M > INT32_MAX) return RQ_ERR_UNSUPPORTED;
+  if (M == 0) return RQ_OK;
+  if (ldx % 8 != 0 || ldr % 8 != 0 || !aligned(x, 16) || !aligned(residual, 16) || !aligned(weight, 16) ||
+      !aligned(residual_out, 16) || !aligned(y_out, 16))
+    return RQ_ERR_UNSUPPORTED;
+  const Span ins[3] = {span_of(x, M, ldx, H, 2), span_of(residual, M, ldr, H, 2), span_of(weight, 1, H, H, 2)};
+  const Span outs[2] = {span_of(residual_out, M, H, H, 2), span_of(y_out, M, H, H, 2)};
+  if (!outputs_disjoint(outs, 2, ins, 3, /*inplace_out=*/0, /*inplace_in=*/1)) return RQ_ERR_INVALID;
+  return check_device();
+}
+
+// Checks of the quantize launch of the unfused sequence (y in; codes and
+// scales out).
+rq_status quant_preflight(const uint16_t* y, int64_t ldy, int64_t M, int64_t H, const uint8_t* q_out,
+                          const void* scale_out, int64_t scale_count, int64_t scale_bytes, int64_t granule,
+                          int code_bits) {
+  if (M < 0 || H <= 0 || ldy < H) return RQ_ERR_INVALID;
+  if (M > 0 && (!y || !q_out || !scale_out)) return RQ_ERR_INVALID;
+  if (H % 8 != 0 || H > RQ_MAX_HIDDEN || M > INT32_MAX) return RQ_ERR_UNSUPPORTED;
+  if (granule <= 0 || H % granule != 0) return RQ_ERR_UNSUPPORTED;
+  if (M == 0) return RQ_OK;
+  if (ldy % 8 != 0 || !aligned(y, 16) || !aligned(q_out, code_bits == 8 ? 8 : 4) || !aligned(scale_out, scale_bytes))
+    return RQ_ERR_UNSUPPORTED;
+  const Span ins[1] = {span_of(y, M, ldy, H, 2)};
+  const Span outs[2] = {span_of(q_out, M, H * code_bits / 8, H * code_bits / 8, 1),
+                        span_of(scale_out, M, scale_count, scale_count, scale_bytes)};
+  if (!outputs_disjoint(outs, 2, ins, 1, -1, -1)) return RQ_ERR_INVALID;
+  return check_device();
+}
+
+int group_log2_lanes(int64_t group) {
+  for (int l = 2; l <= 6; ++l)
+    if (group == (int64_t)8 << l) return l;
+  return -1;
+}
+
 rq_status launch(const void* kernel, dim3 grid, dim3 block, void* args, void* stream) {
   void* argv[1] = {args};
   hipError_t err = hipLaunchKernel(kernel, grid, block, argv, 0, reinterpret_cast<hipStream_t>(stream));
@@ -671,7 +729,7 @@ int waves_per_row_log2(int H) {
   return l;
 }
 
-template <int kMode>
+template <int kMode, int kStage = kStageFused>
 rq_status launch_rows(RowArgs& a, void* stream) {
   const int l = waves_per_row_log2(a.H);
   const int wpr = 1 << l;
@@ -679,7 +737,7 @@ rq_status launch_rows(RowArgs& a, void* stream) {
   const int nc = (a.H + lanes * 8 - 1) / (lanes * 8);
   const int rpb = wpr == 1 ? 4 : 1;
   const unsigned blocks = (unsigned)((a.M + rpb - 1) / rpb);
-  return launch(reinterpret_cast<const void*>(RowKernels<kMode>::k[l][nc - 1]), dim3(blocks),
+  return launch(reinterpret_cast<const void*>(RowKernels<kMode, kStage>::k[l][nc - 1]), dim3(blocks),
                 dim3((unsigned)(lanes * rpb)), &a, stream);
 }
 
@@ -724,10 +782,8 @@ rq_status rmsnorm_quant_fp8_per_group(const uint16_t* x, int64_t ldx, const uint
                                       const uint16_t* weight, int64_t M, int64_t H, float eps, int64_t group,
                                       uint16_t* residual_out, uint8_t* q_out, float* scale_out, uint16_t* y_out,
                                       void* stream) {
-  int log2_lanes = -1;
-  for (int l = 2; l <= 6; ++l)
-    if (group == (int64_t)8 << l) log2_lanes = l;
   if (group <= 0) return RQ_ERR_INVALID;
+  const int log2_lanes = group_log2_lanes(group);
   const int64_t granule = log2_lanes < 0 ? -1 : group;
   rq_status st = row_preflight(x, ldx, residual, ldr, weight, M, H, eps, residual_out, q_out, scale_out,
                                log2_lanes < 0 ? 1 : H / group, 4, y_out, granule, 8);
@@ -796,6 +852,43 @@ rq_status qk_gemma_rmsnorm_gate(const uint16_t* qg, int64_t ld_qg, const uint16_
   if (blocks > INT32_MAX) return RQ_ERR_UNSUPPORTED;
   return launch(reinterpret_cast<const void*>(kQKKernels[log2_lanes]), dim3((unsigned)blocks), dim3(kQKBlock), &a,
                 stream);
+}
+
+rq_status rmsnorm_residual_bf16(const uint16_t* x, int64_t ldx, const uint16_t* residual, int64_t ldr,
+                                const uint16_t* weight, int64_t M, int64_t H, float eps, uint16_t* residual_out,
+                                uint16_t* y_out, void* stream) {
+  rq_status st = norm_preflight(x, ldx, residual, ldr, weight, M, H, eps, residual_out, y_out);
+  if (st != RQ_OK || M == 0) return st;
+  RowArgs a = make_row_args(x, ldx, residual, ldr, weight, M, H, eps, residual_out, nullptr, nullptr, y_out);
+  return launch_rows<kFp8Token, kStageNorm>(a, stream);
+}
+
+rq_status quantize_fp8_per_token(const uint16_t* y, int64_t ldy, int64_t M, int64_t H, uint8_t* q_out,
+                                 float* scale_out, void* stream) {
+  rq_status st = quant_preflight(y, ldy, M, H, q_out, scale_out, 1, 4, H, 8);
+  if (st != RQ_OK || M == 0) return st;
+  RowArgs a = make_row_args(y, ldy, nullptr, 0, nullptr, M, H, 0.0f, nullptr, q_out, scale_out, nullptr);
+  return launch_rows<kFp8Token, kStageQuantize>(a, stream);
+}
+
+rq_status quantize_fp8_per_group(const uint16_t* y, int64_t ldy, int64_t M, int64_t H, int64_t group,
+                                 uint8_t* q_out, float* scale_out, void* stream) {
+  if (group <= 0) return RQ_ERR_INVALID;
+  const int l = group_log2_lanes(group);
+  rq_status st = quant_preflight(y, ldy, M, H, q_out, scale_out, l < 0 ? 1 : H / group, 4, l < 0 ? -1 : group, 8);
+  if (st != RQ_OK || M == 0) return st;
+  RowArgs a = make_row_args(y, ldy, nullptr, 0, nullptr, M, H, 0.0f, nullptr, q_out, scale_out, nullptr);
+  a.group_log2_lanes = l;
+  a.groups_per_row = (int)(H / group);
+  return launch_rows<kFp8Group, kStageQuantize>(a, stream);
+}
+
+rq_status quantize_mxfp4(const uint16_t* y, int64_t ldy, int64_t M, int64_t H, uint8_t* q_out, uint8_t* scale_out,
+                         void* stream) {
+  rq_status st = quant_preflight(y, ldy, M, H, q_out, scale_out, H / 32, 1, 32, 4);
+  if (st != RQ_OK || M == 0) return st;
+  RowArgs a = make_row_args(y, ldy, nullptr, 0, nullptr, M, H, 0.0f, nullptr, q_out, scale_out, nullptr);
+  return launch_rows<kMxfp4, kStageQuantize>(a, stream);
 }
 
 const char* rq_status_string(rq_status status) {

@@ -33,7 +33,8 @@ def lib():
 def test_every_declared_symbol_is_exported(lib):
     names = _declared(os.path.join(ROOT, "include", "rmsnorm_quant.h"))
     assert set(names) >= {"rmsnorm_quant_fp8_per_token", "rmsnorm_quant_fp8_per_group", "rmsnorm_quant_mxfp4",
-                          "qk_gemma_rmsnorm_gate", "rq_status_string"}
+                          "qk_gemma_rmsnorm_gate", "rq_status_string", "rmsnorm_residual_bf16",
+                          "quantize_fp8_per_token", "quantize_fp8_per_group", "quantize_mxfp4"}
     dyn = subprocess.run(["nm", "-D", "--defined-only", _build.LIBRARY], capture_output=True, text=True).stdout
     for n in names:
         assert re.search(rf"\bT {n}$", dyn, re.M), f"{n} not exported"
@@ -138,3 +139,39 @@ def test_qk_preflight(lib):
         rq.RQ_ERR_UNSUPPORTED
     assert f(qg + 2, 2 * Hq * D, k, Hk * D, qw, kw, T, Hq, Hk, D, 1e-6, qo, ko, go, None) == rq.RQ_ERR_UNSUPPORTED
     assert f(None, 2 * Hq * D, None, Hk * D, None, None, 0, Hq, Hk, D, 1e-6, None, None, None, None) == rq.RQ_OK
+
+
+def test_norm_preflight(lib):
+    f = lib.rmsnorm_residual_bf16
+    x, r, w, ro, y = BUF[:5]
+    assert f(x, 256, r, 256, w, 4, 256, 1e-6, ro, None, None) == rq.RQ_ERR_INVALID       # y_out required
+    assert f(x, 256, r, 256, w, -1, 256, 1e-6, ro, y, None) == rq.RQ_ERR_INVALID
+    assert f(x, 256, r, 256, w, 4, 256, 1e-6, ro, ro, None) == rq.RQ_ERR_INVALID         # outputs overlap
+    assert f(x, 256, r, 256, w, 4, 12, 1e-6, ro, y, None) == rq.RQ_ERR_UNSUPPORTED
+    assert f(x + 2, 256, r, 256, w, 4, 256, 1e-6, ro, y, None) == rq.RQ_ERR_UNSUPPORTED
+    assert f(None, 256, None, 256, None, 0, 256, 1e-6, None, None, None) == rq.RQ_OK
+
+
+@pytest.mark.parametrize("fn", ["quantize_fp8_per_token", "quantize_fp8_per_group", "quantize_mxfp4"])
+def test_quant_preflight(lib, fn):
+    y, q, s = BUF[:3]
+
+    def call(y=y, ldy=256, M=4, H=256, q=q, s=s, group=128):
+        if fn == "quantize_fp8_per_group":
+            return lib.quantize_fp8_per_group(y, ldy, M, H, group, q, s, None)
+        return getattr(lib, fn)(y, ldy, M, H, q, s, None)
+
+    assert call(M=-1) == rq.RQ_ERR_INVALID
+    assert call(ldy=128) == rq.RQ_ERR_INVALID
+    assert call(y=None) == rq.RQ_ERR_INVALID
+    assert call(q=None) == rq.RQ_ERR_INVALID
+    assert call(s=None) == rq.RQ_ERR_INVALID
+    assert call(q=y + 64) == rq.RQ_ERR_INVALID                                          # codes over the input
+    assert call(H=12) == rq.RQ_ERR_UNSUPPORTED
+    assert call(y=y + 2) == rq.RQ_ERR_UNSUPPORTED
+    assert call(M=0, y=None, q=None, s=None) == rq.RQ_OK
+    if fn == "quantize_mxfp4":
+        assert call(H=48) == rq.RQ_ERR_UNSUPPORTED
+    if fn == "quantize_fp8_per_group":
+        assert call(group=96) == rq.RQ_ERR_UNSUPPORTED
+        assert call(group=0) == rq.RQ_ERR_INVALID
