@@ -58,7 +58,8 @@ def _rows(a: np.ndarray) -> tuple[np.ndarray, int]:
 
 
 class Oracle:
-    """numpy front end of librq_oracle.so.  bf16 arrays are uint16 bit patterns."""
+    """numpy front end of librq_oracle.so.  bf16 and fp16 arrays are uint16 bit
+    patterns; the row functions take dtype="bf16" (default) or "fp16"."""
 
     def __init__(self, path: str = LIBRARY):
         if not os.path.exists(path):
@@ -81,19 +82,32 @@ class Oracle:
         lib.rq_ref_e8m0_from_amax.restype = ctypes.c_uint8
         lib.rq_ref_f64_from_e8m0.argtypes = [ctypes.c_uint8]
         lib.rq_ref_f64_from_e8m0.restype = ctypes.c_double
+        lib.rq_ref_f64_from_f16.argtypes = [ctypes.c_uint16]
+        lib.rq_ref_f64_from_f16.restype = ctypes.c_double
+        lib.rq_ref_f16_from_f64.argtypes = [ctypes.c_double]
+        lib.rq_ref_f16_from_f64.restype = ctypes.c_uint16
         row_args = [_u16p, _i64, _u16p, _i64, _u16p, _i64, _i64, ctypes.c_float]
-        lib.rq_ref_rmsnorm_quant_fp8_per_token.argtypes = row_args + [_u16p, _u8p, _f32p, _u16p]
-        lib.rq_ref_rmsnorm_quant_fp8_per_group.argtypes = row_args + [_i64, _u16p, _u8p, _f32p, _u16p]
-        lib.rq_ref_rmsnorm_quant_mxfp4.argtypes = row_args + [_u16p, _u8p, _u8p, _u16p]
+        for sfx in ("", "_f16"):
+            getattr(lib, "rq_ref_rmsnorm_quant_fp8_per_token" + sfx).argtypes = row_args + [_u16p, _u8p, _f32p, _u16p]
+            getattr(lib, "rq_ref_rmsnorm_quant_fp8_per_group" + sfx).argtypes = \
+                row_args + [_i64, _u16p, _u8p, _f32p, _u16p]
+            getattr(lib, "rq_ref_rmsnorm_quant_mxfp4" + sfx).argtypes = row_args + [_u16p, _u8p, _u8p, _u16p]
+            getattr(lib, "rq_ref_quantize_fp8" + sfx).argtypes = [_u16p, _i64, _i64, _i64, _u8p, _f32p]
+            getattr(lib, "rq_ref_quantize_mxfp4" + sfx).argtypes = [_u16p, _i64, _i64, _u8p, _u8p]
         lib.rq_ref_qk_gemma_rmsnorm_gate.argtypes = [
             _u16p, _i64, _u16p, _i64, _u16p, _u16p, _i64, _i64, _i64, _i64, ctypes.c_float,
             _u16p, _u16p, _u16p]
-        lib.rq_ref_quantize_fp8.argtypes = [_u16p, _i64, _i64, _i64, _u8p, _f32p]
-        lib.rq_ref_quantize_mxfp4.argtypes = [_u16p, _i64, _i64, _u8p, _u8p]
         for name in ("rq_ref_quantize_fp8", "rq_ref_quantize_mxfp4",
                      "rq_ref_rmsnorm_quant_fp8_per_token", "rq_ref_rmsnorm_quant_fp8_per_group",
-                     "rq_ref_rmsnorm_quant_mxfp4", "rq_ref_qk_gemma_rmsnorm_gate"):
+                     "rq_ref_rmsnorm_quant_mxfp4"):
             getattr(lib, name).restype = ctypes.c_int
+            getattr(lib, name + "_f16").restype = ctypes.c_int
+        lib.rq_ref_qk_gemma_rmsnorm_gate.restype = ctypes.c_int
+
+    def _fn(self, name, dtype):
+        if dtype not in ("bf16", "fp16"):
+            raise ValueError(f"unknown element type {dtype!r}")
+        return getattr(self.lib, name + ("_f16" if dtype == "fp16" else ""))
 
     # ---- scalar format functions (element-wise over arrays) ----
     def bf16_value(self, bits) -> np.ndarray:
@@ -103,6 +117,15 @@ class Oracle:
 
     def bf16_round(self, v) -> np.ndarray:
         return np.vectorize(self.lib.rq_ref_bf16_from_f64, otypes=[np.uint16])(
+            np.asarray(v, dtype=np.float64))
+
+    def f16_value(self, bits) -> np.ndarray:
+        with np.errstate(invalid="ignore"):
+            return np.vectorize(self.lib.rq_ref_f64_from_f16, otypes=[np.float64])(
+                np.asarray(bits, dtype=np.uint16))
+
+    def f16_round(self, v) -> np.ndarray:
+        return np.vectorize(self.lib.rq_ref_f16_from_f64, otypes=[np.uint16])(
             np.asarray(v, dtype=np.float64))
 
     def e4m3fn(self, v) -> np.ndarray:
@@ -138,12 +161,12 @@ class Oracle:
         assert residual.shape == (M, H) and weight.shape == (H,)
         return x, ldx, residual, ldr, weight, M, H
 
-    def fp8_per_token(self, x, residual, weight, eps, emit_y=False) -> dict:
+    def fp8_per_token(self, x, residual, weight, eps, emit_y=False, dtype="bf16") -> dict:
         x, ldx, residual, ldr, weight, M, H = self._row_inputs(x, residual, weight)
         out = dict(residual_out=np.zeros((M, H), np.uint16), q=np.zeros((M, H), np.uint8),
                    scale=np.zeros((M,), np.float32),
                    y=np.zeros((M, H), np.uint16) if emit_y else None)
-        rc = self.lib.rq_ref_rmsnorm_quant_fp8_per_token(
+        rc = self._fn("rq_ref_rmsnorm_quant_fp8_per_token", dtype)(
             _ptr(x, _u16p), ldx, _ptr(residual, _u16p), ldr, _ptr(weight, _u16p), M, H, eps,
             _ptr(out["residual_out"], _u16p), _ptr(out["q"], _u8p), _ptr(out["scale"], _f32p),
             _ptr(out["y"], _u16p))
@@ -151,13 +174,13 @@ class Oracle:
             raise ValueError("oracle rejected the arguments")
         return out
 
-    def fp8_per_group(self, x, residual, weight, eps, group, emit_y=False) -> dict:
+    def fp8_per_group(self, x, residual, weight, eps, group, emit_y=False, dtype="bf16") -> dict:
         x, ldx, residual, ldr, weight, M, H = self._row_inputs(x, residual, weight)
         G = H // group if group > 0 else 0
         out = dict(residual_out=np.zeros((M, H), np.uint16), q=np.zeros((M, H), np.uint8),
                    scale=np.zeros((M, G), np.float32),
                    y=np.zeros((M, H), np.uint16) if emit_y else None)
-        rc = self.lib.rq_ref_rmsnorm_quant_fp8_per_group(
+        rc = self._fn("rq_ref_rmsnorm_quant_fp8_per_group", dtype)(
             _ptr(x, _u16p), ldx, _ptr(residual, _u16p), ldr, _ptr(weight, _u16p), M, H, eps,
             group, _ptr(out["residual_out"], _u16p), _ptr(out["q"], _u8p),
             _ptr(out["scale"], _f32p), _ptr(out["y"], _u16p))
@@ -165,12 +188,12 @@ class Oracle:
             raise ValueError("oracle rejected the arguments")
         return out
 
-    def mxfp4(self, x, residual, weight, eps, emit_y=False) -> dict:
+    def mxfp4(self, x, residual, weight, eps, emit_y=False, dtype="bf16") -> dict:
         x, ldx, residual, ldr, weight, M, H = self._row_inputs(x, residual, weight)
         out = dict(residual_out=np.zeros((M, H), np.uint16), q=np.zeros((M, H // 2), np.uint8),
                    scale=np.zeros((M, H // 32), np.uint8),
                    y=np.zeros((M, H), np.uint16) if emit_y else None)
-        rc = self.lib.rq_ref_rmsnorm_quant_mxfp4(
+        rc = self._fn("rq_ref_rmsnorm_quant_mxfp4", dtype)(
             _ptr(x, _u16p), ldx, _ptr(residual, _u16p), ldr, _ptr(weight, _u16p), M, H, eps,
             _ptr(out["residual_out"], _u16p), _ptr(out["q"], _u8p), _ptr(out["scale"], _u8p),
             _ptr(out["y"], _u16p))
@@ -179,22 +202,22 @@ class Oracle:
         return out
 
     # ---- the quantize step alone ----
-    def quantize_fp8(self, y, group=None) -> dict:
+    def quantize_fp8(self, y, group=None, dtype="bf16") -> dict:
         y = np.ascontiguousarray(y, dtype=np.uint16)
         M, H = y.shape
         group = H if group is None else group
         out = dict(q=np.zeros((M, H), np.uint8), scale=np.zeros((M, H // group), np.float32))
-        rc = self.lib.rq_ref_quantize_fp8(_ptr(y, _u16p), M, H, group, _ptr(out["q"], _u8p),
+        rc = self._fn("rq_ref_quantize_fp8", dtype)(_ptr(y, _u16p), M, H, group, _ptr(out["q"], _u8p),
                                           _ptr(out["scale"], _f32p))
         if rc != 0:
             raise ValueError("oracle rejected the arguments")
         return out
 
-    def quantize_mxfp4(self, y) -> dict:
+    def quantize_mxfp4(self, y, dtype="bf16") -> dict:
         y = np.ascontiguousarray(y, dtype=np.uint16)
         M, H = y.shape
         out = dict(q=np.zeros((M, H // 2), np.uint8), scale=np.zeros((M, H // 32), np.uint8))
-        rc = self.lib.rq_ref_quantize_mxfp4(_ptr(y, _u16p), M, H, _ptr(out["q"], _u8p),
+        rc = self._fn("rq_ref_quantize_mxfp4", dtype)(_ptr(y, _u16p), M, H, _ptr(out["q"], _u8p),
                                             _ptr(out["scale"], _u8p))
         if rc != 0:
             raise ValueError("oracle rejected the arguments")

@@ -72,6 +72,41 @@ uint16_t bf16_round(double v) {
   return (uint16_t)(sign | (u >> 16));
 }
 
+double f16_value(uint16_t b) {
+  // IEEE binary16: sign, 5 exponent bits (bias 15), 10 mantissa bits.
+  const double s = (b & 0x8000) ? -1.0 : 1.0;
+  const int e = (b >> 10) & 0x1F, m = b & 0x3FF;
+  if (e == 31) return m ? std::nan("") : s * INFINITY;
+  if (e == 0) return s * std::ldexp((double)m, -24);
+  return s * std::ldexp(1.0 + m / 1024.0, e - 15);
+}
+
+uint16_t f16_round(double v) {
+  const uint16_t sign = std::signbit(v) ? 0x8000 : 0;
+  if (std::isnan(v)) return (uint16_t)(sign | 0x7E00);
+  double a = std::fabs(v);
+  if (a == 0.0) return sign;
+  if (std::isinf(a)) return (uint16_t)(sign | 0x7C00);
+  // 11 significant bits; normal exponents -14..15; below 2^-14 the spacing is 2^-24.
+  int e = std::ilogb(a);
+  int quantum_exp = (e < -14) ? -24 : e - 10;
+  double r = std::ldexp(std::nearbyint(std::ldexp(a, -quantum_exp)), quantum_exp);  // ties to even
+  if (r > 65504.0) return (uint16_t)(sign | 0x7C00);  // rounds past the largest finite half
+  if (r == 0.0) return sign;
+  if (r < 0x1p-14) return (uint16_t)(sign | (int)std::ldexp(r, 24));
+  int E = std::ilogb(r);
+  int mant = (int)((std::ldexp(r, -E) - 1.0) * 1024.0);
+  return (uint16_t)(sign | ((E + 15) << 10) | mant);
+}
+
+// The activation element type: bf16 (the pages' type) or fp16.
+struct Elem {
+  double (*value)(uint16_t);
+  uint16_t (*round)(double);
+};
+const Elem kBf16 = {bf16_value, bf16_round};
+const Elem kF16 = {f16_value, f16_round};
+
 uint8_t e4m3fn_round(double v) {
   if (std::isnan(v)) return 0x7F;
   const uint8_t sign = std::signbit(v) ? 0x80 : 0;
@@ -131,38 +166,38 @@ uint8_t e8m0_for_amax(double amax) {
   return (uint8_t)b;
 }
 
-// Largest |v| over a granule of bf16 values; NaN if any element is NaN.
-double granule_amax(const uint16_t* y, int64_t n) {
+// Largest |v| over a granule of values; NaN if any element is NaN.
+double granule_amax(const Elem& e, const uint16_t* y, int64_t n) {
   double amax = 0.0;
   for (int64_t i = 0; i < n; ++i) {
-    double a = std::fabs(bf16_value(y[i]));
+    double a = std::fabs(e.value(y[i]));
     if (std::isnan(a)) return a;
     if (a > amax) amax = a;
   }
   return amax;
 }
 
-// Residual add and RMSNorm of one row: fills r (the bf16 residual_out row)
-// and y (the bf16 normalized row).
-void add_and_norm_row(const uint16_t* x, const uint16_t* res, const uint16_t* w,
+// Residual add and RMSNorm of one row: fills r (the residual_out row) and y
+// (the normalized row), each rounded once to the element type.
+void add_and_norm_row(const Elem& e, const uint16_t* x, const uint16_t* res, const uint16_t* w,
                       int64_t H, float eps, uint16_t* r, uint16_t* y) {
-  for (int64_t i = 0; i < H; ++i) r[i] = bf16_round(bf16_value(x[i]) + bf16_value(res[i]));
+  for (int64_t i = 0; i < H; ++i) r[i] = e.round(e.value(x[i]) + e.value(res[i]));
   double ss = 0.0;
   for (int64_t i = 0; i < H; ++i) {
-    double v = bf16_value(r[i]);
+    double v = e.value(r[i]);
     ss += v * v;
   }
   double rstd = 1.0 / std::sqrt(ss / (double)H + (double)eps);
-  for (int64_t i = 0; i < H; ++i) y[i] = bf16_round(bf16_value(r[i]) * rstd * bf16_value(w[i]));
+  for (int64_t i = 0; i < H; ++i) y[i] = e.round(e.value(r[i]) * rstd * e.value(w[i]));
 }
 
-// FP8 quantization of one granule of the bf16 normalized row.
-void quant_fp8_granule(const uint16_t* y, int64_t n, uint8_t* q, float* scale) {
-  double amax = granule_amax(y, n);
-  float s = (float)amax / 448.0f;  // amax is a bf16 value: the cast is exact
+// FP8 quantization of one granule of the normalized row.
+void quant_fp8_granule(const Elem& e, const uint16_t* y, int64_t n, uint8_t* q, float* scale) {
+  double amax = granule_amax(e, y, n);
+  float s = (float)amax / 448.0f;  // amax is a bf16 or fp16 value: the cast is exact
   *scale = s;
   for (int64_t i = 0; i < n; ++i) {
-    double v = bf16_value(y[i]);
+    double v = e.value(y[i]);
     if (amax == 0.0) {
       q[i] = std::signbit(v) ? 0x80 : 0x00;
     } else {
@@ -174,15 +209,15 @@ void quant_fp8_granule(const uint16_t* y, int64_t n, uint8_t* q, float* scale) {
 
 // MXFP4 quantization of one 32-element block; codes[i] is the 4-bit code of
 // element i (packed by the caller).
-void quant_mxfp4_block(const uint16_t* y, uint8_t* codes, uint8_t* scale_byte) {
-  double amax = granule_amax(y, 32);
+void quant_mxfp4_block(const Elem& e, const uint16_t* y, uint8_t* codes, uint8_t* scale_byte) {
+  double amax = granule_amax(e, y, 32);
   uint8_t b = e8m0_for_amax(amax);
   *scale_byte = b;
   for (int i = 0; i < 32; ++i) {
     if (b == 0xFF) {
       codes[i] = 0;  // non-finite block: codes unspecified, written as 0
     } else {
-      codes[i] = e2m1_round(std::ldexp(bf16_value(y[i]), -((int)b - 127)));  // exact scaling
+      codes[i] = e2m1_round(std::ldexp(e.value(y[i]), -((int)b - 127)));  // exact scaling
     }
   }
 }
@@ -195,6 +230,78 @@ bool bad_row_args(const void* x, int64_t ldx, const void* residual, int64_t ldr,
   if (ldx < H || ldr < H) return true;
   if (M > 0 && (!x || !residual || !weight || !residual_out || !q_out || !scale_out)) return true;
   return false;
+}
+
+// The fused step for FP8 with one scale per `group` elements (group == H:
+// per token), on rows of element type e.
+int fused_fp8(const Elem& e, const uint16_t* x, int64_t ldx, const uint16_t* residual, int64_t ldr,
+              const uint16_t* weight, int64_t M, int64_t H, float eps, int64_t group,
+              uint16_t* residual_out, uint8_t* q_out, float* scale_out, uint16_t* y_out) {
+  if (bad_row_args(x, ldx, residual, ldr, weight, M, H, eps, residual_out, q_out, scale_out))
+    return 1;
+  if (group <= 0 || H % group != 0) return 1;
+  const int64_t G = H / group;
+  std::vector<uint16_t> r(H), y(H);
+  for (int64_t m = 0; m < M; ++m) {
+    add_and_norm_row(e, x + m * ldx, residual + m * ldr, weight, H, eps, r.data(), y.data());
+    for (int64_t g = 0; g < G; ++g)
+      quant_fp8_granule(e, y.data() + g * group, group, q_out + m * H + g * group,
+                        scale_out + m * G + g);
+    std::memcpy(residual_out + m * H, r.data(), H * sizeof(uint16_t));
+    if (y_out) std::memcpy(y_out + m * H, y.data(), H * sizeof(uint16_t));
+  }
+  return 0;
+}
+
+// Packs the 4-bit codes of one 32-element block into 16 bytes.
+void pack_block(const uint8_t* codes, uint8_t* out) {
+  for (int j = 0; j < 16; ++j) out[j] = (uint8_t)(codes[2 * j] | (codes[2 * j + 1] << 4));
+}
+
+int fused_mxfp4(const Elem& e, const uint16_t* x, int64_t ldx, const uint16_t* residual, int64_t ldr,
+                const uint16_t* weight, int64_t M, int64_t H, float eps,
+                uint16_t* residual_out, uint8_t* q_out, uint8_t* scale_out, uint16_t* y_out) {
+  if (bad_row_args(x, ldx, residual, ldr, weight, M, H, eps, residual_out, q_out, scale_out))
+    return 1;
+  if (H % 32 != 0) return 1;
+  const int64_t B = H / 32;
+  std::vector<uint16_t> r(H), y(H);
+  uint8_t codes[32];
+  for (int64_t m = 0; m < M; ++m) {
+    add_and_norm_row(e, x + m * ldx, residual + m * ldr, weight, H, eps, r.data(), y.data());
+    for (int64_t b = 0; b < B; ++b) {
+      quant_mxfp4_block(e, y.data() + b * 32, codes, scale_out + m * B + b);
+      pack_block(codes, q_out + m * (H / 2) + b * 16);
+    }
+    std::memcpy(residual_out + m * H, r.data(), H * sizeof(uint16_t));
+    if (y_out) std::memcpy(y_out + m * H, y.data(), H * sizeof(uint16_t));
+  }
+  return 0;
+}
+
+int quantize_fp8_rows(const Elem& e, const uint16_t* y, int64_t M, int64_t H, int64_t group,
+                      uint8_t* q_out, float* scale_out) {
+  if (M < 0 || H <= 0 || group <= 0 || H % group != 0) return 1;
+  if (M > 0 && (!y || !q_out || !scale_out)) return 1;
+  const int64_t G = H / group;
+  for (int64_t m = 0; m < M; ++m)
+    for (int64_t g = 0; g < G; ++g)
+      quant_fp8_granule(e, y + m * H + g * group, group, q_out + m * H + g * group, scale_out + m * G + g);
+  return 0;
+}
+
+int quantize_mxfp4_rows(const Elem& e, const uint16_t* y, int64_t M, int64_t H, uint8_t* q_out,
+                        uint8_t* scale_out) {
+  if (M < 0 || H <= 0 || H % 32 != 0) return 1;
+  if (M > 0 && (!y || !q_out || !scale_out)) return 1;
+  const int64_t B = H / 32;
+  uint8_t codes[32];
+  for (int64_t m = 0; m < M; ++m)
+    for (int64_t b = 0; b < B; ++b) {
+      quant_mxfp4_block(e, y + m * H + b * 32, codes, scale_out + m * B + b);
+      pack_block(codes, q_out + m * (H / 2) + b * 16);
+    }
+  return 0;
 }
 
 }  // namespace
@@ -212,89 +319,43 @@ double rq_ref_f64_from_e8m0(uint8_t b) {
   return b == 0xFF ? std::nan("") : std::ldexp(1.0, (int)b - 127);
 }
 
-int rq_ref_rmsnorm_quant_fp8_per_token(
-    const uint16_t* x, int64_t ldx, const uint16_t* residual, int64_t ldr,
-    const uint16_t* weight, int64_t M, int64_t H, float eps,
-    uint16_t* residual_out, uint8_t* q_out, float* scale_out, uint16_t* y_out) {
-  if (bad_row_args(x, ldx, residual, ldr, weight, M, H, eps, residual_out, q_out, scale_out))
-    return 1;
-  std::vector<uint16_t> r(H), y(H);
-  for (int64_t m = 0; m < M; ++m) {
-    add_and_norm_row(x + m * ldx, residual + m * ldr, weight, H, eps, r.data(), y.data());
-    quant_fp8_granule(y.data(), H, q_out + m * H, scale_out + m);
-    std::memcpy(residual_out + m * H, r.data(), H * sizeof(uint16_t));
-    if (y_out) std::memcpy(y_out + m * H, y.data(), H * sizeof(uint16_t));
+
+double rq_ref_f64_from_f16(uint16_t b) { return f16_value(b); }
+uint16_t rq_ref_f16_from_f64(double v) { return f16_round(v); }
+
+#define RQ_REF_ROW_EXPORTS(SUFFIX, ELEM)                                                            \
+  int rq_ref_rmsnorm_quant_fp8_per_token##SUFFIX(                                                   \
+      const uint16_t* x, int64_t ldx, const uint16_t* residual, int64_t ldr, const uint16_t* weight, \
+      int64_t M, int64_t H, float eps, uint16_t* residual_out, uint8_t* q_out, float* scale_out,    \
+      uint16_t* y_out) {                                                                           \
+    return fused_fp8(ELEM, x, ldx, residual, ldr, weight, M, H, eps, H, residual_out, q_out,        \
+                     scale_out, y_out);                                                            \
+  }                                                                                                \
+  int rq_ref_rmsnorm_quant_fp8_per_group##SUFFIX(                                                   \
+      const uint16_t* x, int64_t ldx, const uint16_t* residual, int64_t ldr, const uint16_t* weight, \
+      int64_t M, int64_t H, float eps, int64_t group, uint16_t* residual_out, uint8_t* q_out,       \
+      float* scale_out, uint16_t* y_out) {                                                         \
+    return fused_fp8(ELEM, x, ldx, residual, ldr, weight, M, H, eps, group, residual_out, q_out,    \
+                     scale_out, y_out);                                                            \
+  }                                                                                                \
+  int rq_ref_rmsnorm_quant_mxfp4##SUFFIX(                                                           \
+      const uint16_t* x, int64_t ldx, const uint16_t* residual, int64_t ldr, const uint16_t* weight, \
+      int64_t M, int64_t H, float eps, uint16_t* residual_out, uint8_t* q_out, uint8_t* scale_out,  \
+      uint16_t* y_out) {                                                                           \
+    return fused_mxfp4(ELEM, x, ldx, residual, ldr, weight, M, H, eps, residual_out, q_out,         \
+                       scale_out, y_out);                                                          \
+  }                                                                                                \
+  int rq_ref_quantize_fp8##SUFFIX(const uint16_t* y, int64_t M, int64_t H, int64_t group,           \
+                                  uint8_t* q_out, float* scale_out) {                              \
+    return quantize_fp8_rows(ELEM, y, M, H, group, q_out, scale_out);                              \
+  }                                                                                                \
+  int rq_ref_quantize_mxfp4##SUFFIX(const uint16_t* y, int64_t M, int64_t H, uint8_t* q_out,        \
+                                    uint8_t* scale_out) {                                          \
+    return quantize_mxfp4_rows(ELEM, y, M, H, q_out, scale_out);                                   \
   }
-  return 0;
-}
 
-int rq_ref_rmsnorm_quant_fp8_per_group(
-    const uint16_t* x, int64_t ldx, const uint16_t* residual, int64_t ldr,
-    const uint16_t* weight, int64_t M, int64_t H, float eps, int64_t group,
-    uint16_t* residual_out, uint8_t* q_out, float* scale_out, uint16_t* y_out) {
-  if (bad_row_args(x, ldx, residual, ldr, weight, M, H, eps, residual_out, q_out, scale_out))
-    return 1;
-  if (group <= 0 || H % group != 0) return 1;
-  const int64_t G = H / group;
-  std::vector<uint16_t> r(H), y(H);
-  for (int64_t m = 0; m < M; ++m) {
-    add_and_norm_row(x + m * ldx, residual + m * ldr, weight, H, eps, r.data(), y.data());
-    for (int64_t g = 0; g < G; ++g)
-      quant_fp8_granule(y.data() + g * group, group, q_out + m * H + g * group,
-                        scale_out + m * G + g);
-    std::memcpy(residual_out + m * H, r.data(), H * sizeof(uint16_t));
-    if (y_out) std::memcpy(y_out + m * H, y.data(), H * sizeof(uint16_t));
-  }
-  return 0;
-}
-
-int rq_ref_rmsnorm_quant_mxfp4(
-    const uint16_t* x, int64_t ldx, const uint16_t* residual, int64_t ldr,
-    const uint16_t* weight, int64_t M, int64_t H, float eps,
-    uint16_t* residual_out, uint8_t* q_out, uint8_t* scale_out, uint16_t* y_out) {
-  if (bad_row_args(x, ldx, residual, ldr, weight, M, H, eps, residual_out, q_out, scale_out))
-    return 1;
-  if (H % 32 != 0) return 1;
-  const int64_t B = H / 32;
-  std::vector<uint16_t> r(H), y(H);
-  uint8_t codes[32];
-  for (int64_t m = 0; m < M; ++m) {
-    add_and_norm_row(x + m * ldx, residual + m * ldr, weight, H, eps, r.data(), y.data());
-    for (int64_t b = 0; b < B; ++b) {
-      quant_mxfp4_block(y.data() + b * 32, codes, scale_out + m * B + b);
-      for (int j = 0; j < 16; ++j)
-        q_out[m * (H / 2) + b * 16 + j] = (uint8_t)(codes[2 * j] | (codes[2 * j + 1] << 4));
-    }
-    std::memcpy(residual_out + m * H, r.data(), H * sizeof(uint16_t));
-    if (y_out) std::memcpy(y_out + m * H, y.data(), H * sizeof(uint16_t));
-  }
-  return 0;
-}
-
-int rq_ref_quantize_fp8(const uint16_t* y, int64_t M, int64_t H, int64_t group,
-                        uint8_t* q_out, float* scale_out) {
-  if (M < 0 || H <= 0 || group <= 0 || H % group != 0) return 1;
-  if (M > 0 && (!y || !q_out || !scale_out)) return 1;
-  const int64_t G = H / group;
-  for (int64_t m = 0; m < M; ++m)
-    for (int64_t g = 0; g < G; ++g)
-      quant_fp8_granule(y + m * H + g * group, group, q_out + m * H + g * group, scale_out + m * G + g);
-  return 0;
-}
-
-int rq_ref_quantize_mxfp4(const uint16_t* y, int64_t M, int64_t H, uint8_t* q_out, uint8_t* scale_out) {
-  if (M < 0 || H <= 0 || H % 32 != 0) return 1;
-  if (M > 0 && (!y || !q_out || !scale_out)) return 1;
-  const int64_t B = H / 32;
-  uint8_t codes[32];
-  for (int64_t m = 0; m < M; ++m)
-    for (int64_t b = 0; b < B; ++b) {
-      quant_mxfp4_block(y + m * H + b * 32, codes, scale_out + m * B + b);
-      for (int j = 0; j < 16; ++j)
-        q_out[m * (H / 2) + b * 16 + j] = (uint8_t)(codes[2 * j] | (codes[2 * j + 1] << 4));
-    }
-  return 0;
-}
+RQ_REF_ROW_EXPORTS(, kBf16)
+RQ_REF_ROW_EXPORTS(_f16, kF16)
 
 int rq_ref_qk_gemma_rmsnorm_gate(
     const uint16_t* qg, int64_t ld_qg, const uint16_t* k, int64_t ld_k,

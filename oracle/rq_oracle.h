@@ -48,6 +48,11 @@ double rq_ref_f64_from_bf16(uint16_t b);
 /* Round a double to the nearest bf16 (ties to even), overflow -> +-Inf, NaN -> 0x7FC0|sign. */
 uint16_t rq_ref_bf16_from_f64(double v);
 
+/* IEEE binary16 (fp16) bits -> exact value, and rounding of a double to the
+ * nearest fp16 (ties to even, |v| rounding past 65504 -> +-Inf). */
+double rq_ref_f64_from_f16(uint16_t b);
+uint16_t rq_ref_f16_from_f64(double v);
+
 /* OCP FP8 E4M3FN: bias 7, no infinities, 0x7F/0xFF NaN, max 448.
  * Nearest, ties to even; |v| > 448 saturates to +-448; NaN -> 0x7F. */
 uint8_t rq_ref_e4m3fn_from_f64(double v);
@@ -98,6 +103,28 @@ int rq_ref_quantize_fp8(const uint16_t* y, int64_t M, int64_t H, int64_t group,
 /* MXFP4 quantization of a bf16 tensor y [M, H], same rules as above. */
 int rq_ref_quantize_mxfp4(const uint16_t* y, int64_t M, int64_t H,
                           uint8_t* q_out, uint8_t* scale_out);
+
+/* ---- fp16 rows ----
+ * The same functions on IEEE fp16 activations (x, residual, weight,
+ * residual_out and y are fp16; every rounding is to fp16 instead of bf16),
+ * the activation dtype carried through the step as the review of sglang
+ * PR #29723 asks.  Same arguments and results otherwise. */
+int rq_ref_rmsnorm_quant_fp8_per_token_f16(
+    const uint16_t* x, int64_t ldx, const uint16_t* residual, int64_t ldr,
+    const uint16_t* weight, int64_t M, int64_t H, float eps,
+    uint16_t* residual_out, uint8_t* q_out, float* scale_out, uint16_t* y_out);
+int rq_ref_rmsnorm_quant_fp8_per_group_f16(
+    const uint16_t* x, int64_t ldx, const uint16_t* residual, int64_t ldr,
+    const uint16_t* weight, int64_t M, int64_t H, float eps, int64_t group,
+    uint16_t* residual_out, uint8_t* q_out, float* scale_out, uint16_t* y_out);
+int rq_ref_rmsnorm_quant_mxfp4_f16(
+    const uint16_t* x, int64_t ldx, const uint16_t* residual, int64_t ldr,
+    const uint16_t* weight, int64_t M, int64_t H, float eps,
+    uint16_t* residual_out, uint8_t* q_out, uint8_t* scale_out, uint16_t* y_out);
+int rq_ref_quantize_fp8_f16(const uint16_t* y, int64_t M, int64_t H, int64_t group,
+                            uint8_t* q_out, float* scale_out);
+int rq_ref_quantize_mxfp4_f16(const uint16_t* y, int64_t M, int64_t H,
+                              uint8_t* q_out, uint8_t* scale_out);
 
 /* ---- the QK variant ---- */
 

@@ -85,6 +85,20 @@ def np_bf16_value(bits: np.ndarray) -> np.ndarray:
     return BF16_VALUE[np.asarray(bits, dtype=np.uint16)]
 
 
+def np_f16_round(v: np.ndarray) -> np.ndarray:
+    """numpy's correctly rounded float64 -> float16 cast, as bit patterns."""
+    with np.errstate(over="ignore"):
+        return np.asarray(v, dtype=np.float64).astype(np.float16).view(np.uint16)
+
+
+def np_f16_value(bits: np.ndarray) -> np.ndarray:
+    return np.asarray(bits, dtype=np.uint16).view(np.float16).astype(np.float64)
+
+
+NP_CODEC = {"bf16": (np_bf16_round, np_bf16_value), "fp16": (np_f16_round, np_f16_value)}
+TORCH_DTYPE = {"bf16": torch.bfloat16, "fp16": torch.float16}
+
+
 def np_e4m3(q: np.ndarray) -> np.ndarray:
     q = np.asarray(q, dtype=np.float64)
     a = np.minimum(np.abs(q), 448.0)
@@ -99,27 +113,31 @@ def np_e2m1(v: np.ndarray) -> np.ndarray:
     return np.where(np.signbit(v), idx | np.uint8(0x8), idx).astype(np.uint8)
 
 
-def torch_bf16_add(x_bits: np.ndarray, r_bits: np.ndarray) -> np.ndarray:
-    """torch's CPU bf16 addition (an independent library routine)."""
-    return inputs.bits(inputs.from_bits(x_bits) + inputs.from_bits(r_bits))
+def torch_bf16_add(x_bits: np.ndarray, r_bits: np.ndarray, dtype: str = "bf16") -> np.ndarray:
+    """torch's CPU bf16 (or fp16) addition (an independent library routine)."""
+    td = TORCH_DTYPE[dtype]
+    a = torch.from_numpy(np.ascontiguousarray(x_bits, dtype=np.uint16).view(np.int16)).view(td)
+    b = torch.from_numpy(np.ascontiguousarray(r_bits, dtype=np.uint16).view(np.int16)).view(td)
+    return (a + b).view(torch.int16).numpy().view(np.uint16)
 
 
 # ----------------------------------------------------------------------------
 # Independent formulation of the whole step (numpy float64, vectorised)
 # ----------------------------------------------------------------------------
 
-def np_norm(x_bits, r_bits, w_bits, eps):
-    res = torch_bf16_add(x_bits, r_bits)
-    r = np_bf16_value(res)
+def np_norm(x_bits, r_bits, w_bits, eps, dtype="bf16"):
+    rnd, val = NP_CODEC[dtype]
+    res = torch_bf16_add(x_bits, r_bits, dtype)
+    r = val(res)
     ms = np.mean(r * r, axis=1, keepdims=True)
     rstd = 1.0 / np.sqrt(ms + eps)
-    y = np_bf16_round(r * rstd * np_bf16_value(w_bits)[None, :])
+    y = rnd(r * rstd * val(w_bits)[None, :])
     return res, y
 
 
-def np_fp8(y_bits, granule):
+def np_fp8(y_bits, granule, dtype="bf16"):
     M, H = y_bits.shape
-    y = np_bf16_value(y_bits).reshape(M, H // granule, granule)
+    y = NP_CODEC[dtype][1](y_bits).reshape(M, H // granule, granule)
     amax = np.abs(y).max(axis=2)
     scale = amax.astype(np.float32) / np.float32(448.0)
     with np.errstate(divide="ignore", invalid="ignore"):
@@ -130,9 +148,9 @@ def np_fp8(y_bits, granule):
     return codes.reshape(M, H), scale
 
 
-def np_mxfp4(y_bits):
+def np_mxfp4(y_bits, dtype="bf16"):
     M, H = y_bits.shape
-    y = np_bf16_value(y_bits).reshape(M, H // 32, 32)
+    y = NP_CODEC[dtype][1](y_bits).reshape(M, H // 32, 32)
     amax = np.abs(y).max(axis=2)
     _, e = np.frexp(amax)           # amax = f * 2^e, f in [0.5, 1): floor(log2 amax) = e - 1
     byte = np.where(amax == 0, 0, np.clip(e - 1 - 2 + 127, 0, 254)).astype(np.uint8)
@@ -544,6 +562,76 @@ def pin_quantize_step(ref):
     assert (q["q"] == f["q"]).all() and (q["scale"] == f["scale"]).all()
 
 
+def pin_f16_decode(ref):
+    allb = np.arange(65536, dtype=np.uint32).astype(np.uint16)
+    got = ref.f16_value(allb)
+    want = np_f16_value(allb)
+    same = (got == want) | (np.isnan(got) & np.isnan(want))
+    signs = (np.signbit(got) == np.signbit(want)) | np.isnan(want)
+    assert same.all() and signs.all(), "fp16 decode differs from numpy"
+
+
+def pin_f16_round(ref):
+    """Rounding of doubles to fp16 equals numpy's correctly rounded cast, at
+    random values, at every midpoint between adjacent fp16 values and next to
+    them, and through the subnormal and overflow ranges."""
+    rng = np.random.default_rng(14)
+    v = np.ldexp(rng.uniform(1, 2, 20000), rng.integers(-26, 17, 20000))
+    grid = np_f16_value(np.arange(0x7C00, dtype=np.uint16))
+    mids = (grid[:-1] + grid[1:]) / 2
+    v = np.concatenate([v, mids, np.nextafter(mids, 0), np.nextafter(mids, np.inf),
+                        [65504.0, 65519.0, 65520.0, 1e6, 2.0 ** -25, 2.0 ** -26, 3 * 2.0 ** -26]])
+    v = np.concatenate([v, -v])
+    got = ref.f16_round(v)
+    assert (got == np_f16_round(v)).all(), f"fp16 rounding differs from numpy at {v[got != np_f16_round(v)][:5]}"
+    f = rng.normal(0, 100, 20000).astype(np.float32)
+    want = torch.from_numpy(f).to(torch.float16).view(torch.int16).numpy().view(np.uint16)
+    assert (ref.f16_round(f.astype(np.float64)) == want).all(), "fp16 rounding differs from torch's cast"
+
+
+def pin_f16_rows(ref):
+    """The fp16 step against the independent numpy formulation (numpy's float16
+    cast for every rounding, torch's half addition for residual_out)."""
+    rng = np.random.default_rng(41)
+    for (M, H) in [(1, 32), (3, 128), (2, 544), (4, 2048)]:
+        x = rng.normal(0, 1, (M, H)) * np.exp(rng.normal(0, 2, (M, 1)))
+        xb = np_f16_round(x)
+        rb = np_f16_round(rng.normal(0, 1, (M, H)))
+        wb = np_f16_round(rng.normal(1, 0.1, H))
+        xb[rng.random(xb.shape) < 0.05] = 0x8000
+        for eps in (1e-6, 0.25):
+            res, y = np_norm(xb, rb, wb, eps, "fp16")
+            o = ref.fp8_per_token(xb, rb, wb, eps, emit_y=True, dtype="fp16")
+            assert (o["residual_out"] == res).all(), "fp16 residual_out differs from torch's half add"
+            assert (o["y"] == y).all(), f"fp16 y differs from the numpy formulation at {M}x{H}"
+            q, sc = np_fp8(y, H, "fp16")
+            assert (o["scale"] == sc[:, 0]).all() and (o["q"] == q).all(), "fp16 per-token FP8 differs"
+            if H % 32 == 0:
+                og = ref.fp8_per_group(xb, rb, wb, eps, 32, dtype="fp16")
+                q, sc = np_fp8(y, 32, "fp16")
+                assert (og["scale"] == sc).all() and (og["q"] == q).all(), "fp16 group FP8 differs"
+                om = ref.mxfp4(xb, rb, wb, eps, dtype="fp16")
+                packed, byte = np_mxfp4(y, "fp16")
+                assert (om["scale"] == byte).all() and (om["q"] == packed).all(), "fp16 MXFP4 differs"
+            qq = ref.quantize_fp8(y, dtype="fp16")
+            assert (qq["q"] == o["q"]).all()
+
+
+def pin_f16_weight_probe(ref):
+    """The FP8 and MXFP4 goldens hold for fp16 rows too (every probe value is an
+    fp16 value; x = residual = 512, eps = 0 gives y == weight)."""
+    xb, rb, wb, want, scale = fp8_probe_case()
+    w16 = np_f16_round(np_bf16_value(wb))
+    x16 = np_f16_round(np.full(xb.shape, 512.0))
+    o = ref.fp8_per_token(x16, x16.copy(), w16, 0.0, emit_y=True, dtype="fp16")
+    assert (o["y"][0] == w16).all() and o["scale"][0] == scale and (o["q"][0] == want).all()
+    xb, rb, wb, packed, bytes_ = mxfp4_probe_case()
+    w16 = np_f16_round(np_bf16_value(wb))
+    x16 = np_f16_round(np.full(xb.shape, 512.0))
+    m = ref.mxfp4(x16, x16.copy(), w16, 0.0, dtype="fp16")
+    assert (m["scale"] == bytes_).all() and (m["q"] == packed).all()
+
+
 ALL_PINS = [
     pin_bf16_decode, pin_bf16_round_vs_torch, pin_bf16_round_vs_search,
     pin_e4m3_table, pin_e4m3_bruteforce, pin_e4m3_fp32_quotients,
@@ -551,4 +639,5 @@ ALL_PINS = [
     pin_fp8_weight_probe, pin_mxfp4_weight_probe, pin_group_weight_probe,
     pin_constant_row, pin_zero_and_sign, pin_independent_rows,
     pin_strided_inputs, pin_qk, pin_invariants_on_workloads, pin_quantize_step,
+    pin_f16_decode, pin_f16_round, pin_f16_rows, pin_f16_weight_probe,
 ]

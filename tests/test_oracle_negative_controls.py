@@ -27,12 +27,16 @@ MUTATIONS = {
                        "int quantum_exp = (e < 0) ? -1 : e - 1;\n  double r = std::ldexp(std::round("),
     "bf16_ties_away": ("double n = std::nearbyint(std::ldexp(a, -quantum_exp));  // ties to even",
                        "double n = std::round(std::ldexp(a, -quantum_exp));"),
-    "residual_sign": ("bf16_value(x[i]) + bf16_value(res[i])", "bf16_value(x[i]) - bf16_value(res[i])"),
+    "residual_sign": ("e.value(x[i]) + e.value(res[i])", "e.value(x[i]) - e.value(res[i])"),
     "norm_reads_unrounded_sum": (
-        "    double v = bf16_value(r[i]);\n    ss += v * v;",
-        "    double v = bf16_value(x[i]) + bf16_value(res[i]);\n    ss += v * v;"),
-    "weight_index_reversed": ("bf16_value(r[i]) * rstd * bf16_value(w[i])",
-                              "bf16_value(r[i]) * rstd * bf16_value(w[H - 1 - i])"),
+        "    double v = e.value(r[i]);\n    ss += v * v;",
+        "    double v = e.value(x[i]) + e.value(res[i]);\n    ss += v * v;"),
+    "weight_index_reversed": ("e.value(r[i]) * rstd * e.value(w[i])",
+                              "e.value(r[i]) * rstd * e.value(w[H - 1 - i])"),
+    "f16_subnormal_quantum": ("(e < -14) ? -24 : e - 10", "(e < -14) ? -25 : e - 10"),
+    "f16_saturates_instead_of_inf": ("if (r > 65504.0) return (uint16_t)(sign | 0x7C00);",
+                                     "if (r > 65504.0) return (uint16_t)(sign | 0x7BFF);"),
+    "f16_exponent_bias": ("return s * std::ldexp(1.0 + m / 1024.0, e - 15);", "return s * std::ldexp(1.0 + m / 1024.0, e - 14);"),
     "zero_sign_dropped": ("q[i] = std::signbit(v) ? 0x80 : 0x00;", "q[i] = 0x00;"),
     "gemma_without_one": ("(1.0 + bf16_value(w[i]))", "bf16_value(w[i])"),
     "qk_interleave_stride": ("qg + t * ld_qg + 2 * D * h", "qg + t * ld_qg + D * h"),
