@@ -20,8 +20,9 @@
  * already-reduced activation.
  *
  * Conventions shared by every entry point:
- *  - bf16 tensors are passed as uint16_t bit patterns.  Only bf16 in/out is
- *    supported; there is no silent promotion of other dtypes.
+ *  - bf16 tensors are passed as uint16_t bit patterns.  The calls with an
+ *    _f16 suffix take and return IEEE fp16 instead; no call promotes one type
+ *    to the other.
  *  - All tensor pointers are DEVICE pointers owned by the caller.  The library
  *    allocates nothing, never synchronizes the host and keeps no state besides
  *    a per-device cache of the architecture check.  Every call only enqueues
@@ -151,6 +152,42 @@ rq_status quantize_fp8_per_group(
     const uint16_t* y, int64_t ldy, int64_t M, int64_t H, int64_t group,
     uint8_t* q_out, float* scale_out, void* stream);
 rq_status quantize_mxfp4(
+    const uint16_t* y, int64_t ldy, int64_t M, int64_t H,
+    uint8_t* q_out, uint8_t* scale_out, void* stream);
+
+/* ---- fp16 activations ----
+ * The review of sglang PR #29723 asks that the activation dtype be carried
+ * through the fused tuple rather than silently promoted to bf16.  These take
+ * IEEE fp16 x, residual and weight (as uint16_t bits) and return fp16
+ * residual_out and y, with every rounding to fp16 instead of bf16; codes,
+ * scales, layouts, aliasing and errors are exactly those of the bf16 calls of
+ * the same name without the suffix. */
+rq_status rmsnorm_quant_fp8_per_token_f16(
+    const uint16_t* x, int64_t ldx, const uint16_t* residual, int64_t ldr,
+    const uint16_t* weight, int64_t M, int64_t H, float eps,
+    uint16_t* residual_out, uint8_t* q_out, float* scale_out, uint16_t* y_out,
+    void* stream);
+rq_status rmsnorm_quant_fp8_per_group_f16(
+    const uint16_t* x, int64_t ldx, const uint16_t* residual, int64_t ldr,
+    const uint16_t* weight, int64_t M, int64_t H, float eps, int64_t group,
+    uint16_t* residual_out, uint8_t* q_out, float* scale_out, uint16_t* y_out,
+    void* stream);
+rq_status rmsnorm_quant_mxfp4_f16(
+    const uint16_t* x, int64_t ldx, const uint16_t* residual, int64_t ldr,
+    const uint16_t* weight, int64_t M, int64_t H, float eps,
+    uint16_t* residual_out, uint8_t* q_out, uint8_t* scale_out, uint16_t* y_out,
+    void* stream);
+rq_status rmsnorm_residual_f16(
+    const uint16_t* x, int64_t ldx, const uint16_t* residual, int64_t ldr,
+    const uint16_t* weight, int64_t M, int64_t H, float eps,
+    uint16_t* residual_out, uint16_t* y_out, void* stream);
+rq_status quantize_fp8_per_token_f16(
+    const uint16_t* y, int64_t ldy, int64_t M, int64_t H,
+    uint8_t* q_out, float* scale_out, void* stream);
+rq_status quantize_fp8_per_group_f16(
+    const uint16_t* y, int64_t ldy, int64_t M, int64_t H, int64_t group,
+    uint8_t* q_out, float* scale_out, void* stream);
+rq_status quantize_mxfp4_f16(
     const uint16_t* y, int64_t ldy, int64_t M, int64_t H,
     uint8_t* q_out, uint8_t* scale_out, void* stream);
 

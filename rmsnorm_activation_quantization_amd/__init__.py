@@ -13,16 +13,23 @@ and the unfused sequence, one launch per step (bit-identical results):
 
   rmsnorm_residual_bf16         residual add + RMSNorm -> bf16 y
   quantize_fp8_per_token / quantize_fp8_per_group / quantize_mxfp4
+
+Row functions take bf16 or fp16 tensors and return their rows in the same
+dtype (the _f16 names are the same functions, named after the C entry points).
 """
 
 from .binding import (RQ_ERR_HIP, RQ_ERR_INVALID, RQ_ERR_UNSUPPORTED, RQ_MAX_HEAD_DIM, RQ_MAX_HIDDEN, RQ_OK,
-                      lib, library_path, qk_gemma_rmsnorm_gate, quantize_fp8_per_group, quantize_fp8_per_token,
-                      quantize_mxfp4, rmsnorm_quant_fp8_per_group, rmsnorm_quant_fp8_per_token,
-                      rmsnorm_quant_mxfp4, rmsnorm_residual_bf16, status_string)
+                      lib, library_path, qk_gemma_rmsnorm_gate, quantize_fp8_per_group, quantize_fp8_per_group_f16,
+                      quantize_fp8_per_token, quantize_fp8_per_token_f16, quantize_mxfp4, quantize_mxfp4_f16,
+                      rmsnorm_quant_fp8_per_group, rmsnorm_quant_fp8_per_group_f16, rmsnorm_quant_fp8_per_token,
+                      rmsnorm_quant_fp8_per_token_f16, rmsnorm_quant_mxfp4, rmsnorm_quant_mxfp4_f16,
+                      rmsnorm_residual_bf16, rmsnorm_residual_f16, status_string)
 
 __all__ = [
     "rmsnorm_quant_fp8_per_token", "rmsnorm_quant_fp8_per_group", "rmsnorm_quant_mxfp4", "qk_gemma_rmsnorm_gate",
     "rmsnorm_residual_bf16", "quantize_fp8_per_token", "quantize_fp8_per_group", "quantize_mxfp4",
+    "rmsnorm_quant_fp8_per_token_f16", "rmsnorm_quant_fp8_per_group_f16", "rmsnorm_quant_mxfp4_f16",
+    "rmsnorm_residual_f16", "quantize_fp8_per_token_f16", "quantize_fp8_per_group_f16", "quantize_mxfp4_f16",
     "lib", "library_path", "status_string", "RQ_OK", "RQ_ERR_INVALID", "RQ_ERR_UNSUPPORTED", "RQ_ERR_HIP",
     "RQ_MAX_HIDDEN", "RQ_MAX_HEAD_DIM",
 ]

@@ -5,6 +5,11 @@ torch supplies device memory and the current stream; every step of the
 computation runs in the library's HIP kernels.  There is no other code path:
 if the library is missing or the device is not an MI355X, calls fail loudly.
 
+bf16 and fp16 rows: every row function dispatches on the dtype of x (or y):
+bf16 tensors run the bf16 kernels, fp16 tensors the _f16 ones, and the row
+outputs come back in the input's dtype (the activation dtype is carried
+through the step).  Mixing dtypes raises ValueError.
+
 Return convention, following sglang PR #29723 (Key changes: the fused call
 returns its tuple, or None when the backend cannot fuse so that the caller runs
 the unfused sequence): a tuple on success; None for RQ_ERR_UNSUPPORTED, which
@@ -43,6 +48,21 @@ _SIGNATURES = {
     "quantize_fp8_per_group": [_p, _i64, _i64, _i64, _i64, _p, _p, _p],
     "quantize_mxfp4": [_p, _i64, _i64, _i64, _p, _p, _p],
 }
+# fp16 variants of the row entry points (same arguments)
+for _name in ("rmsnorm_quant_fp8_per_token", "rmsnorm_quant_fp8_per_group", "rmsnorm_quant_mxfp4",
+              "quantize_fp8_per_token", "quantize_fp8_per_group", "quantize_mxfp4"):
+    _SIGNATURES[_name + "_f16"] = _SIGNATURES[_name]
+_SIGNATURES["rmsnorm_residual_f16"] = _SIGNATURES["rmsnorm_residual_bf16"]
+
+_ELEMENT_TYPES = (torch.bfloat16, torch.float16)
+
+
+def _fn(name: str, dtype):
+    """The C entry point for an element type: bf16 -> name (rmsnorm_residual_bf16
+    for the norm launch), fp16 -> name_f16."""
+    if dtype == torch.float16:
+        return getattr(lib(), name + "_f16")
+    return getattr(lib(), name + ("_bf16" if name == "rmsnorm_residual" else ""))
 
 
 def library_path() -> str:
@@ -95,41 +115,47 @@ def _stream(stream) -> int:
     return s.cuda_stream
 
 
-def _rows(t: torch.Tensor, name: str) -> int:
-    """Row stride (elements) of a 2-D bf16 CUDA tensor with unit column stride."""
-    if t.dim() != 2 or t.dtype != torch.bfloat16 or not t.is_cuda:
-        raise ValueError(f"{name} must be a 2-D bfloat16 CUDA tensor")
+def _rows(t: torch.Tensor, name: str, dtype=None) -> int:
+    """Row stride (elements) of a 2-D bf16 or fp16 CUDA tensor with unit column
+    stride (and the given dtype, when one is given)."""
+    if t.dim() != 2 or t.dtype not in _ELEMENT_TYPES or not t.is_cuda:
+        raise ValueError(f"{name} must be a 2-D bfloat16 or float16 CUDA tensor")
+    if dtype is not None and t.dtype != dtype:
+        raise ValueError(f"{name} must have the dtype of x ({dtype})")
     if t.shape[1] > 1 and t.stride(1) != 1:
         raise ValueError(f"{name} must have unit column stride")
     return t.stride(0) if t.shape[0] > 1 else t.shape[1]
 
 
 def _row_outputs(x, residual, weight, residual_out, y_out, emit_y):
+    """Checks the row inputs (one element type for all) and allocates the
+    missing row outputs in that type."""
     M, H = x.shape
-    if residual.shape != (M, H) or weight.shape != (H,) or weight.dtype != torch.bfloat16:
-        raise ValueError("residual must be [M, H] and weight [H] bfloat16")
+    dt = x.dtype
+    if residual.shape != (M, H) or weight.shape != (H,) or residual.dtype != dt or weight.dtype != dt:
+        raise ValueError(f"residual must be [M, H] and weight [H], both {dt} like x")
     if not weight.is_contiguous():
         raise ValueError("weight must be contiguous")
     if residual_out is None:
-        residual_out = torch.empty((M, H), dtype=torch.bfloat16, device=x.device)
+        residual_out = torch.empty((M, H), dtype=dt, device=x.device)
     if y_out is None and emit_y:
-        y_out = torch.empty((M, H), dtype=torch.bfloat16, device=x.device)
+        y_out = torch.empty((M, H), dtype=dt, device=x.device)
     for name, t in (("residual_out", residual_out), ("y_out", y_out)):
-        if t is not None and (t.shape != (M, H) or t.dtype != torch.bfloat16 or not t.is_contiguous()):
-            raise ValueError(f"{name} must be a contiguous [M, H] bfloat16 tensor")
+        if t is not None and (t.shape != (M, H) or t.dtype != dt or not t.is_contiguous()):
+            raise ValueError(f"{name} must be a contiguous [M, H] {dt} tensor")
     return M, H, residual_out, y_out
 
 
 def rmsnorm_quant_fp8_per_token(x, residual, weight, eps: float = 1e-6, *, residual_out=None, q_out=None,
                                 scale_out=None, emit_y: bool = False, y_out=None, stream=None):
     """-> (q [M, H] float8_e4m3fn, residual_out [M, H] bf16, scale [M, 1] fp32, y or None), or None."""
-    ldx, ldr = _rows(x, "x"), _rows(residual, "residual")
+    ldx, ldr = _rows(x, "x"), _rows(residual, "residual", x.dtype)
     M, H, residual_out, y_out = _row_outputs(x, residual, weight, residual_out, y_out, emit_y)
     if q_out is None:
         q_out = torch.empty((M, H), dtype=torch.uint8, device=x.device)
     if scale_out is None:
         scale_out = torch.empty((M,), dtype=torch.float32, device=x.device)
-    st = lib().rmsnorm_quant_fp8_per_token(
+    st = _fn("rmsnorm_quant_fp8_per_token", x.dtype)(
         _ptr(x), ldx, _ptr(residual), ldr, _ptr(weight), M, H, eps, _ptr(residual_out), _ptr(q_out),
         _ptr(scale_out), _ptr(y_out), _stream(stream))
     if not _check(st, "rmsnorm_quant_fp8_per_token"):
@@ -140,13 +166,13 @@ def rmsnorm_quant_fp8_per_token(x, residual, weight, eps: float = 1e-6, *, resid
 def rmsnorm_quant_fp8_per_group(x, residual, weight, eps: float = 1e-6, group: int = 128, *, residual_out=None,
                                 q_out=None, scale_out=None, emit_y: bool = False, y_out=None, stream=None):
     """-> (q [M, H] float8_e4m3fn, residual_out, scale [M, H/group] fp32, y or None), or None."""
-    ldx, ldr = _rows(x, "x"), _rows(residual, "residual")
+    ldx, ldr = _rows(x, "x"), _rows(residual, "residual", x.dtype)
     M, H, residual_out, y_out = _row_outputs(x, residual, weight, residual_out, y_out, emit_y)
     if q_out is None:
         q_out = torch.empty((M, H), dtype=torch.uint8, device=x.device)
     if scale_out is None:
         scale_out = torch.empty((M, max(H // group, 1) if group > 0 else 1), dtype=torch.float32, device=x.device)
-    st = lib().rmsnorm_quant_fp8_per_group(
+    st = _fn("rmsnorm_quant_fp8_per_group", x.dtype)(
         _ptr(x), ldx, _ptr(residual), ldr, _ptr(weight), M, H, eps, group, _ptr(residual_out), _ptr(q_out),
         _ptr(scale_out), _ptr(y_out), _stream(stream))
     if not _check(st, "rmsnorm_quant_fp8_per_group"):
@@ -157,13 +183,13 @@ def rmsnorm_quant_fp8_per_group(x, residual, weight, eps: float = 1e-6, group: i
 def rmsnorm_quant_mxfp4(x, residual, weight, eps: float = 1e-6, *, residual_out=None, q_out=None,
                         scale_out=None, emit_y: bool = False, y_out=None, stream=None):
     """-> (q [M, H/2] uint8 packed E2M1, residual_out, scale [M, H/32] uint8 E8M0, y or None), or None."""
-    ldx, ldr = _rows(x, "x"), _rows(residual, "residual")
+    ldx, ldr = _rows(x, "x"), _rows(residual, "residual", x.dtype)
     M, H, residual_out, y_out = _row_outputs(x, residual, weight, residual_out, y_out, emit_y)
     if q_out is None:
         q_out = torch.empty((M, H // 2), dtype=torch.uint8, device=x.device)
     if scale_out is None:
         scale_out = torch.empty((M, max(H // 32, 1)), dtype=torch.uint8, device=x.device)
-    st = lib().rmsnorm_quant_mxfp4(
+    st = _fn("rmsnorm_quant_mxfp4", x.dtype)(
         _ptr(x), ldx, _ptr(residual), ldr, _ptr(weight), M, H, eps, _ptr(residual_out), _ptr(q_out),
         _ptr(scale_out), _ptr(y_out), _stream(stream))
     if not _check(st, "rmsnorm_quant_mxfp4"):
@@ -175,12 +201,12 @@ def qk_gemma_rmsnorm_gate(qg, k, q_w, k_w, num_q_heads: int, num_k_heads: int, h
                           eps: float = 1e-6, *, q_out=None, k_out=None, gate_out=None, stream=None):
     """qg [T, >= 2*Hq*D] interleaved per head as [q | gate]; k [T, >= Hk*D] (row stride allowed).
     -> (q [T, Hq, D], k [T, Hk, D], gate [T, Hq, D]) contiguous bf16, or None."""
-    ld_qg, ld_k = _rows(qg, "qg"), _rows(k, "k")
+    ld_qg, ld_k = _rows(qg, "qg", torch.bfloat16), _rows(k, "k", torch.bfloat16)
     T = qg.shape[0]
     Hq, Hk, D = num_q_heads, num_k_heads, head_dim
     if k.shape[0] != T:
         raise ValueError("qg and k must have the same number of tokens")
-    for name, w in (("q_w", q_w), ("k_w", k_w)):
+    for name, w in (("q_w", q_w), ("k_w", k_w)):  # this variant is bf16 only
         if w.shape != (D,) or w.dtype != torch.bfloat16 or not w.is_contiguous():
             raise ValueError(f"{name} must be a contiguous [head_dim] bfloat16 tensor")
     dev = qg.device
@@ -202,9 +228,9 @@ def qk_gemma_rmsnorm_gate(qg, k, q_w, k_w, num_q_heads: int, num_k_heads: int, h
 
 def rmsnorm_residual_bf16(x, residual, weight, eps: float = 1e-6, *, residual_out=None, y_out=None, stream=None):
     """-> (residual_out [M, H] bf16, y [M, H] bf16), or None."""
-    ldx, ldr = _rows(x, "x"), _rows(residual, "residual")
+    ldx, ldr = _rows(x, "x"), _rows(residual, "residual", x.dtype)
     M, H, residual_out, y_out = _row_outputs(x, residual, weight, residual_out, y_out, True)
-    st = lib().rmsnorm_residual_bf16(_ptr(x), ldx, _ptr(residual), ldr, _ptr(weight), M, H, eps,
+    st = _fn("rmsnorm_residual", x.dtype)(_ptr(x), ldx, _ptr(residual), ldr, _ptr(weight), M, H, eps,
                                      _ptr(residual_out), _ptr(y_out), _stream(stream))
     if not _check(st, "rmsnorm_residual_bf16"):
         return None
@@ -221,7 +247,7 @@ def quantize_fp8_per_token(y, *, q_out=None, scale_out=None, stream=None):
     ldy, M, H = _quant_input(y)
     q_out = torch.empty((M, H), dtype=torch.uint8, device=y.device) if q_out is None else q_out
     scale_out = torch.empty((M,), dtype=torch.float32, device=y.device) if scale_out is None else scale_out
-    st = lib().quantize_fp8_per_token(_ptr(y), ldy, M, H, _ptr(q_out), _ptr(scale_out), _stream(stream))
+    st = _fn("quantize_fp8_per_token", y.dtype)(_ptr(y), ldy, M, H, _ptr(q_out), _ptr(scale_out), _stream(stream))
     if not _check(st, "quantize_fp8_per_token"):
         return None
     return q_out.view(torch.float8_e4m3fn), scale_out.view(M, 1)
@@ -233,7 +259,7 @@ def quantize_fp8_per_group(y, group: int = 128, *, q_out=None, scale_out=None, s
     q_out = torch.empty((M, H), dtype=torch.uint8, device=y.device) if q_out is None else q_out
     if scale_out is None:
         scale_out = torch.empty((M, max(H // group, 1) if group > 0 else 1), dtype=torch.float32, device=y.device)
-    st = lib().quantize_fp8_per_group(_ptr(y), ldy, M, H, group, _ptr(q_out), _ptr(scale_out), _stream(stream))
+    st = _fn("quantize_fp8_per_group", y.dtype)(_ptr(y), ldy, M, H, group, _ptr(q_out), _ptr(scale_out), _stream(stream))
     if not _check(st, "quantize_fp8_per_group"):
         return None
     return q_out.view(torch.float8_e4m3fn), scale_out
@@ -245,7 +271,19 @@ def quantize_mxfp4(y, *, q_out=None, scale_out=None, stream=None):
     q_out = torch.empty((M, H // 2), dtype=torch.uint8, device=y.device) if q_out is None else q_out
     if scale_out is None:
         scale_out = torch.empty((M, max(H // 32, 1)), dtype=torch.uint8, device=y.device)
-    st = lib().quantize_mxfp4(_ptr(y), ldy, M, H, _ptr(q_out), _ptr(scale_out), _stream(stream))
+    st = _fn("quantize_mxfp4", y.dtype)(_ptr(y), ldy, M, H, _ptr(q_out), _ptr(scale_out), _stream(stream))
     if not _check(st, "quantize_mxfp4"):
         return None
     return q_out, scale_out
+
+
+# The fp16 entry points under their C names.  Every function above already
+# dispatches on the tensors' dtype (bf16 or fp16), so these are the same
+# functions; calling one with bf16 tensors runs the bf16 kernels.
+rmsnorm_quant_fp8_per_token_f16 = rmsnorm_quant_fp8_per_token
+rmsnorm_quant_fp8_per_group_f16 = rmsnorm_quant_fp8_per_group
+rmsnorm_quant_mxfp4_f16 = rmsnorm_quant_mxfp4
+rmsnorm_residual_f16 = rmsnorm_residual_bf16
+quantize_fp8_per_token_f16 = quantize_fp8_per_token
+quantize_fp8_per_group_f16 = quantize_fp8_per_group
+quantize_mxfp4_f16 = quantize_mxfp4

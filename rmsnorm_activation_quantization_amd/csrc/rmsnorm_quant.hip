@@ -60,6 +60,7 @@ namespace {
 typedef __bf16 bf16x2_t __attribute__((ext_vector_type(2)));
 typedef float f32x2_t __attribute__((ext_vector_type(2)));
 typedef unsigned short u16x2_t __attribute__((ext_vector_type(2)));
+typedef _Float16 f16x2_t __attribute__((ext_vector_type(2)));
 typedef unsigned int u32x4_t __attribute__((ext_vector_type(4)));
 typedef unsigned int u32x2_t __attribute__((ext_vector_type(2)));
 
@@ -79,7 +80,28 @@ __device__ __forceinline__ uint32_t pack_bf16(float lo, float hi) {
   f32x2_t v = {lo, hi};
   return __builtin_bit_cast(uint32_t, __builtin_convertvector(v, bf16x2_t));
 }
-// Largest |bf16| bit pattern of a packed pair per half (integer max of the
+// Element types of the activation rows, two 16-bit values packed per 32-bit
+// word (element 2j in the low half).  bf16 is the pages' type; fp16 rows are
+// carried through the step unchanged in type (fp16 in, fp16 residual_out and
+// y out) for consumers that hold fp16 activations.
+struct Bf16 {
+  __device__ static float lo(uint32_t w) { return bf_lo(w); }
+  __device__ static float hi(uint32_t w) { return bf_hi(w); }
+  __device__ static uint32_t pack(float a, float b) { return pack_bf16(a, b); }
+  __device__ static float value(uint32_t h) { return __uint_as_float(h << 16); }  // one element's bits
+};
+struct F16 {
+  __device__ static float lo(uint32_t w) { return (float)__builtin_bit_cast(_Float16, (uint16_t)(w & 0xFFFFu)); }
+  __device__ static float hi(uint32_t w) { return (float)__builtin_bit_cast(_Float16, (uint16_t)(w >> 16)); }
+  // v_cvt_pk_f16_f32: round to nearest even
+  __device__ static uint32_t pack(float a, float b) {
+    f32x2_t v = {a, b};
+    return __builtin_bit_cast(uint32_t, __builtin_convertvector(v, f16x2_t));
+  }
+  __device__ static float value(uint32_t h) { return (float)__builtin_bit_cast(_Float16, (uint16_t)h); }
+};
+
+// Largest |bf16| or |fp16| bit pattern of a packed pair per half (integer max of the
 // magnitude bits orders finite < Inf < NaN, so a NaN propagates).
 __device__ __forceinline__ uint32_t abs_max2(uint32_t acc, uint32_t w) {
   u16x2_t a = __builtin_bit_cast(u16x2_t, acc);
@@ -198,10 +220,11 @@ struct Fp8Granule {
 // estimate refined by one Newton step, which is the correctly rounded value for
 // every scale that can occur (fp8_quotient.h).  Both depend only on amax, so
 // they issue in parallel: two short chains instead of two IEEE divisions.
+template <typename E>
 __device__ __forceinline__ Fp8Granule fp8_granule(uint32_t amax_bits) {
   Fp8Granule g;
-  const float amax = __uint_as_float(amax_bits << 16);
-  const uint32_t e = amax_bits >> 7;  // exponent field of the bf16 amax
+  const float amax = E::value(amax_bits);     // exact: every bf16 and fp16 value is an fp32 value
+  const uint32_t e = __float_as_uint(amax) >> 23;  // its fp32 exponent field (sign is clear)
   g.slow = false;
   if (amax_bits == 0) {
     // All-zero granule: scale 0; q = y * 0 keeps the sign of each zero.
@@ -226,21 +249,22 @@ __device__ __forceinline__ float fp8_quotient(float y, const Fp8Granule& g) {
   return rq_fp8_quotient(y, g.sc, g.inv);
 }
 
-// Eight bf16 values (packed in a uint4) -> eight E4M3FN codes (a uint2).
+// Eight values (packed in a uint4) -> eight E4M3FN codes (a uint2).
+template <typename E>
 __device__ __forceinline__ uint2 fp8_codes(const uint4& y, const Fp8Granule& g) {
   const uint32_t w[4] = {y.x, y.y, y.z, y.w};
   float q[8];
   if (!g.slow) {
 #pragma unroll
     for (int j = 0; j < 4; ++j) {
-      q[2 * j] = fp8_quotient(bf_lo(w[j]), g);
-      q[2 * j + 1] = fp8_quotient(bf_hi(w[j]), g);
+      q[2 * j] = fp8_quotient(E::lo(w[j]), g);
+      q[2 * j + 1] = fp8_quotient(E::hi(w[j]), g);
     }
   } else {  // tiny or non-finite granule
 #pragma unroll
     for (int j = 0; j < 4; ++j) {
-      q[2 * j] = bf_lo(w[j]) / g.sc;
-      q[2 * j + 1] = bf_hi(w[j]) / g.sc;
+      q[2 * j] = E::lo(w[j]) / g.sc;
+      q[2 * j + 1] = E::hi(w[j]) / g.sc;
     }
   }
   uint32_t d0 = (uint32_t)__builtin_amdgcn_cvt_pk_fp8_f32(q[0], q[1], 0, false);
@@ -250,25 +274,27 @@ __device__ __forceinline__ uint2 fp8_codes(const uint4& y, const Fp8Granule& g) 
   return make_uint2(d0, d1);
 }
 
-// E8M0 byte for a block whose largest magnitude has bf16 bits amax_bits:
-// floor(log2 amax) - 2 + 127 clamped to [0, 254] is (exponent field - 2) for
-// normal amax and 0 below (subnormal or zero amax); 255 for Inf / NaN.
-__device__ __forceinline__ uint32_t e8m0_byte(uint32_t amax_bits) {
-  uint32_t e = amax_bits >> 7;
+// E8M0 byte for a block whose largest magnitude is amax (a bf16 or fp16 value,
+// exact in fp32): floor(log2 amax) - 2 + 127 clamped to [0, 254] is the fp32
+// exponent field minus 2, and 0 below that (fp32-subnormal or zero amax); 255
+// for Inf / NaN.
+__device__ __forceinline__ uint32_t e8m0_byte(float amax) {
+  const uint32_t e = __float_as_uint(amax) >> 23;
   if (e == 255u) return 255u;
   return e >= 2u ? e - 2u : 0u;
 }
 
-// Eight bf16 values -> eight E2M1 codes (one uint32, element i in nibble i).
-// y * 2^(127 - byte) is exact (power-of-two scaling of a bf16 value); byte is
-// at most 252 for finite bf16 amax, so the factor is a normal fp32.
+// Eight values -> eight E2M1 codes (one uint32, element i in nibble i).
+// y * 2^(127 - byte) is exact (power-of-two scaling of a bf16 or fp16 value);
+// byte is at most 252 for a finite amax, so the factor is a normal fp32.
+template <typename E>
 __device__ __forceinline__ uint32_t mxfp4_codes(const uint4& y, uint32_t byte) {
   const float f = __uint_as_float((254u - byte) << 23);
   uint32_t d = 0;
-  d = (uint32_t)__builtin_amdgcn_cvt_scalef32_pk_fp4_f32(d, bf_lo(y.x) * f, bf_hi(y.x) * f, 1.0f, 0);
-  d = (uint32_t)__builtin_amdgcn_cvt_scalef32_pk_fp4_f32(d, bf_lo(y.y) * f, bf_hi(y.y) * f, 1.0f, 1);
-  d = (uint32_t)__builtin_amdgcn_cvt_scalef32_pk_fp4_f32(d, bf_lo(y.z) * f, bf_hi(y.z) * f, 1.0f, 2);
-  d = (uint32_t)__builtin_amdgcn_cvt_scalef32_pk_fp4_f32(d, bf_lo(y.w) * f, bf_hi(y.w) * f, 1.0f, 3);
+  d = (uint32_t)__builtin_amdgcn_cvt_scalef32_pk_fp4_f32(d, E::lo(y.x) * f, E::hi(y.x) * f, 1.0f, 0);
+  d = (uint32_t)__builtin_amdgcn_cvt_scalef32_pk_fp4_f32(d, E::lo(y.y) * f, E::hi(y.y) * f, 1.0f, 1);
+  d = (uint32_t)__builtin_amdgcn_cvt_scalef32_pk_fp4_f32(d, E::lo(y.z) * f, E::hi(y.z) * f, 1.0f, 2);
+  d = (uint32_t)__builtin_amdgcn_cvt_scalef32_pk_fp4_f32(d, E::lo(y.w) * f, E::hi(y.w) * f, 1.0f, 3);
   return d;
 }
 
@@ -311,7 +337,7 @@ constexpr int block_threads() { return kWave * kWPR * rows_per_block<kWPR>(); }
 // kStage selects what one launch does: the fused step (norm + quantize), or
 // one launch of the unfused sequence (norm alone writing y, or quantize alone
 // reading y from a.x with stride a.ldx).
-template <int kMode, int kNC, int kWPR, int kStage>
+template <typename E, int kMode, int kNC, int kWPR, int kStage>
 __global__ __launch_bounds__(block_threads<kWPR>()) void fused_rows(const RowArgs a) {
   constexpr int kLanes = kWave * kWPR;
   constexpr int kChunk = kLanes * 8;
@@ -371,8 +397,8 @@ __global__ __launch_bounds__(block_threads<kWPR>()) void fused_rows(const RowArg
       uint32_t p[4];
   #pragma unroll
       for (int j = 0; j < 4; ++j) {
-        p[j] = pack_bf16(bf_lo(xs[j]) + bf_lo(rs[j]), bf_hi(xs[j]) + bf_hi(rs[j]));
-        const float r0 = bf_lo(p[j]), r1 = bf_hi(p[j]);
+        p[j] = E::pack(E::lo(xs[j]) + E::lo(rs[j]), E::hi(xs[j]) + E::hi(rs[j]));
+        const float r0 = E::lo(p[j]), r1 = E::hi(p[j]);
         ss = __builtin_fmaf(r0, r0, ss);
         ss = __builtin_fmaf(r1, r1, ss);
       }
@@ -407,7 +433,7 @@ __global__ __launch_bounds__(block_threads<kWPR>()) void fused_rows(const RowArg
         const uint32_t rs[4] = {rp[c].x, rp[c].y, rp[c].z, rp[c].w};
   #pragma unroll
         for (int j = 0; j < 4; ++j) {
-          const float r0 = bf_lo(rs[j]) * 0x1p100f, r1 = bf_hi(rs[j]) * 0x1p100f;
+          const float r0 = E::lo(rs[j]) * 0x1p100f, r1 = E::hi(rs[j]) * 0x1p100f;
           s2 = __builtin_fmaf(r0, r0, s2);
           s2 = __builtin_fmaf(r1, r1, s2);
         }
@@ -431,7 +457,7 @@ __global__ __launch_bounds__(block_threads<kWPR>()) void fused_rows(const RowArg
       uint32_t p[4];
   #pragma unroll
       for (int j = 0; j < 4; ++j)
-        p[j] = pack_bf16((bf_lo(rs[j]) * rstd) * bf_lo(ws[j]), (bf_hi(rs[j]) * rstd) * bf_hi(ws[j]));
+        p[j] = E::pack((E::lo(rs[j]) * rstd) * E::lo(ws[j]), (E::hi(rs[j]) * rstd) * E::hi(ws[j]));
       yp[c] = make_uint4(p[0], p[1], p[2], p[3]);
     }
     if (a.y_out) {
@@ -456,12 +482,12 @@ __global__ __launch_bounds__(block_threads<kWPR>()) void fused_rows(const RowArg
 #pragma unroll
       for (int w = 0; w < kWPR; ++w) m = umax(m, lds_max[rloc][w]);
     }
-    const Fp8Granule g = fp8_granule(m);
+    const Fp8Granule g = fp8_granule<E>(m);
     if (live && t == 0) reinterpret_cast<float*>(a.scale)[row] = g.scale;
 #pragma unroll
     for (int c = 0; c < kNC; ++c) {
       const int col = c * kChunk + t * 8;
-      const uint2 codes = fp8_codes(yp[c], g);
+      const uint2 codes = fp8_codes<E>(yp[c], g);
       if (live && (c < kNC - 1 || col < H)) store8<kNT>(a.q + row * H + col, codes);
     }
   } else if (kMode == kFp8Group) {
@@ -470,8 +496,8 @@ __global__ __launch_bounds__(block_threads<kWPR>()) void fused_rows(const RowArg
     for (int c = 0; c < kNC; ++c) {
       const int col = c * kChunk + t * 8;
       const uint32_t m = group_max(chunk_abs_max(yp[c]), gl);
-      const Fp8Granule g = fp8_granule(m);
-      const uint2 codes = fp8_codes(yp[c], g);
+      const Fp8Granule g = fp8_granule<E>(m);
+      const uint2 codes = fp8_codes<E>(yp[c], g);
       if (live && (c < kNC - 1 || col < H)) {
         store8<kNT>(a.q + row * H + col, codes);
         if ((t & ((1 << gl) - 1)) == 0)
@@ -483,8 +509,8 @@ __global__ __launch_bounds__(block_threads<kWPR>()) void fused_rows(const RowArg
     for (int c = 0; c < kNC; ++c) {
       const int col = c * kChunk + t * 8;
       const uint32_t m = group_max_c<2>(chunk_abs_max(yp[c]));
-      const uint32_t byte = e8m0_byte(m);
-      const uint32_t codes = mxfp4_codes(yp[c], byte);
+      const uint32_t byte = e8m0_byte(E::value(m));
+      const uint32_t codes = mxfp4_codes<E>(yp[c], byte);
       if (live && (c < kNC - 1 || col < H)) {
         store4<kNT>(a.q + row * (H / 2) + col / 2, codes);
         if ((t & 3) == 0) reinterpret_cast<uint8_t*>(a.scale)[row * (H / 32) + col / 32] = (uint8_t)byte;
@@ -589,16 +615,17 @@ __global__ __launch_bounds__(kQKBlock) void qk_gemma_gate(const QKArgs a) {
 using RowKernel = void (*)(RowArgs);
 using QKKernel = void (*)(QKArgs);
 
-template <int kMode, int kStage, int kWPR>
+template <typename E, int kMode, int kStage, int kWPR>
 struct RowKernelsW {
-  static constexpr RowKernel k[kMaxChunks] = {&fused_rows<kMode, 1, kWPR, kStage>, &fused_rows<kMode, 2, kWPR, kStage>};
+  static constexpr RowKernel k[kMaxChunks] = {&fused_rows<E, kMode, 1, kWPR, kStage>,
+                                              &fused_rows<E, kMode, 2, kWPR, kStage>};
 };
-template <int kMode, int kStage>
+template <typename E, int kMode, int kStage>
 struct RowKernels {
   // [log2 waves per row][chunks per lane - 1]
-  static constexpr const RowKernel* k[5] = {RowKernelsW<kMode, kStage, 1>::k, RowKernelsW<kMode, kStage, 2>::k,
-                                           RowKernelsW<kMode, kStage, 4>::k, RowKernelsW<kMode, kStage, 8>::k,
-                                           RowKernelsW<kMode, kStage, 16>::k};
+  static constexpr const RowKernel* k[5] = {
+      RowKernelsW<E, kMode, kStage, 1>::k, RowKernelsW<E, kMode, kStage, 2>::k, RowKernelsW<E, kMode, kStage, 4>::k,
+      RowKernelsW<E, kMode, kStage, 8>::k, RowKernelsW<E, kMode, kStage, 16>::k};
 };
 constexpr QKKernel kQKKernels[7] = {&qk_gemma_gate<0>, &qk_gemma_gate<1>, &qk_gemma_gate<2>, &qk_gemma_gate<3>,
                                     &qk_gemma_gate<4>, &qk_gemma_gate<5>, &qk_gemma_gate<6>};
@@ -729,7 +756,7 @@ int waves_per_row_log2(int H) {
   return l;
 }
 
-template <int kMode, int kStage = kStageFused>
+template <typename E, int kMode, int kStage = kStageFused>
 rq_status launch_rows(RowArgs& a, void* stream) {
   const int l = waves_per_row_log2(a.H);
   const int wpr = 1 << l;
@@ -737,7 +764,7 @@ rq_status launch_rows(RowArgs& a, void* stream) {
   const int nc = (a.H + lanes * 8 - 1) / (lanes * 8);
   const int rpb = wpr == 1 ? 4 : 1;
   const unsigned blocks = (unsigned)((a.M + rpb - 1) / rpb);
-  return launch(reinterpret_cast<const void*>(RowKernels<kMode, kStage>::k[l][nc - 1]), dim3(blocks),
+  return launch(reinterpret_cast<const void*>(RowKernels<E, kMode, kStage>::k[l][nc - 1]), dim3(blocks),
                 dim3((unsigned)(lanes * rpb)), &a, stream);
 }
 
@@ -763,25 +790,23 @@ RowArgs make_row_args(const uint16_t* x, int64_t ldx, const uint16_t* residual, 
   return a;
 }
 
-}  // namespace
-
-extern "C" {
-
-rq_status rmsnorm_quant_fp8_per_token(const uint16_t* x, int64_t ldx, const uint16_t* residual, int64_t ldr,
-                                      const uint16_t* weight, int64_t M, int64_t H, float eps,
-                                      uint16_t* residual_out, uint8_t* q_out, float* scale_out, uint16_t* y_out,
-                                      void* stream) {
+// One implementation per entry point, for either element type.
+template <typename E>
+rq_status fp8_per_token_impl(const uint16_t* x, int64_t ldx, const uint16_t* residual, int64_t ldr,
+                             const uint16_t* weight, int64_t M, int64_t H, float eps, uint16_t* residual_out,
+                             uint8_t* q_out, float* scale_out, uint16_t* y_out, void* stream) {
   rq_status st = row_preflight(x, ldx, residual, ldr, weight, M, H, eps, residual_out, q_out, scale_out, 1, 4,
                                y_out, H, 8);
   if (st != RQ_OK || M == 0) return st;
   RowArgs a = make_row_args(x, ldx, residual, ldr, weight, M, H, eps, residual_out, q_out, scale_out, y_out);
-  return launch_rows<kFp8Token>(a, stream);
+  return launch_rows<E, kFp8Token>(a, stream);
 }
 
-rq_status rmsnorm_quant_fp8_per_group(const uint16_t* x, int64_t ldx, const uint16_t* residual, int64_t ldr,
-                                      const uint16_t* weight, int64_t M, int64_t H, float eps, int64_t group,
-                                      uint16_t* residual_out, uint8_t* q_out, float* scale_out, uint16_t* y_out,
-                                      void* stream) {
+template <typename E>
+rq_status fp8_per_group_impl(const uint16_t* x, int64_t ldx, const uint16_t* residual, int64_t ldr,
+                             const uint16_t* weight, int64_t M, int64_t H, float eps, int64_t group,
+                             uint16_t* residual_out, uint8_t* q_out, float* scale_out, uint16_t* y_out,
+                             void* stream) {
   if (group <= 0) return RQ_ERR_INVALID;
   const int log2_lanes = group_log2_lanes(group);
   const int64_t granule = log2_lanes < 0 ? -1 : group;
@@ -791,17 +816,111 @@ rq_status rmsnorm_quant_fp8_per_group(const uint16_t* x, int64_t ldx, const uint
   RowArgs a = make_row_args(x, ldx, residual, ldr, weight, M, H, eps, residual_out, q_out, scale_out, y_out);
   a.group_log2_lanes = log2_lanes;
   a.groups_per_row = (int)(H / group);
-  return launch_rows<kFp8Group>(a, stream);
+  return launch_rows<E, kFp8Group>(a, stream);
 }
 
-rq_status rmsnorm_quant_mxfp4(const uint16_t* x, int64_t ldx, const uint16_t* residual, int64_t ldr,
-                              const uint16_t* weight, int64_t M, int64_t H, float eps, uint16_t* residual_out,
-                              uint8_t* q_out, uint8_t* scale_out, uint16_t* y_out, void* stream) {
+template <typename E>
+rq_status mxfp4_impl(const uint16_t* x, int64_t ldx, const uint16_t* residual, int64_t ldr, const uint16_t* weight,
+                     int64_t M, int64_t H, float eps, uint16_t* residual_out, uint8_t* q_out, uint8_t* scale_out,
+                     uint16_t* y_out, void* stream) {
   rq_status st = row_preflight(x, ldx, residual, ldr, weight, M, H, eps, residual_out, q_out, scale_out, H / 32, 1,
                                y_out, 32, 4);
   if (st != RQ_OK || M == 0) return st;
   RowArgs a = make_row_args(x, ldx, residual, ldr, weight, M, H, eps, residual_out, q_out, scale_out, y_out);
-  return launch_rows<kMxfp4>(a, stream);
+  return launch_rows<E, kMxfp4>(a, stream);
+}
+
+template <typename E>
+rq_status norm_impl(const uint16_t* x, int64_t ldx, const uint16_t* residual, int64_t ldr, const uint16_t* weight,
+                    int64_t M, int64_t H, float eps, uint16_t* residual_out, uint16_t* y_out, void* stream) {
+  rq_status st = norm_preflight(x, ldx, residual, ldr, weight, M, H, eps, residual_out, y_out);
+  if (st != RQ_OK || M == 0) return st;
+  RowArgs a = make_row_args(x, ldx, residual, ldr, weight, M, H, eps, residual_out, nullptr, nullptr, y_out);
+  return launch_rows<E, kFp8Token, kStageNorm>(a, stream);
+}
+
+template <typename E>
+rq_status quant_fp8_token_impl(const uint16_t* y, int64_t ldy, int64_t M, int64_t H, uint8_t* q_out,
+                               float* scale_out, void* stream) {
+  rq_status st = quant_preflight(y, ldy, M, H, q_out, scale_out, 1, 4, H, 8);
+  if (st != RQ_OK || M == 0) return st;
+  RowArgs a = make_row_args(y, ldy, nullptr, 0, nullptr, M, H, 0.0f, nullptr, q_out, scale_out, nullptr);
+  return launch_rows<E, kFp8Token, kStageQuantize>(a, stream);
+}
+
+template <typename E>
+rq_status quant_fp8_group_impl(const uint16_t* y, int64_t ldy, int64_t M, int64_t H, int64_t group, uint8_t* q_out,
+                               float* scale_out, void* stream) {
+  if (group <= 0) return RQ_ERR_INVALID;
+  const int l = group_log2_lanes(group);
+  rq_status st = quant_preflight(y, ldy, M, H, q_out, scale_out, l < 0 ? 1 : H / group, 4, l < 0 ? -1 : group, 8);
+  if (st != RQ_OK || M == 0) return st;
+  RowArgs a = make_row_args(y, ldy, nullptr, 0, nullptr, M, H, 0.0f, nullptr, q_out, scale_out, nullptr);
+  a.group_log2_lanes = l;
+  a.groups_per_row = (int)(H / group);
+  return launch_rows<E, kFp8Group, kStageQuantize>(a, stream);
+}
+
+template <typename E>
+rq_status quant_mxfp4_impl(const uint16_t* y, int64_t ldy, int64_t M, int64_t H, uint8_t* q_out,
+                           uint8_t* scale_out, void* stream) {
+  rq_status st = quant_preflight(y, ldy, M, H, q_out, scale_out, H / 32, 1, 32, 4);
+  if (st != RQ_OK || M == 0) return st;
+  RowArgs a = make_row_args(y, ldy, nullptr, 0, nullptr, M, H, 0.0f, nullptr, q_out, scale_out, nullptr);
+  return launch_rows<E, kMxfp4, kStageQuantize>(a, stream);
+}
+
+}  // namespace
+
+extern "C" {
+
+#define RQ_ROW_EXPORTS(SUFFIX, E)                                                                                  \
+  rq_status rmsnorm_quant_fp8_per_token##SUFFIX(                                                                   \
+      const uint16_t* x, int64_t ldx, const uint16_t* residual, int64_t ldr, const uint16_t* weight, int64_t M,    \
+      int64_t H, float eps, uint16_t* residual_out, uint8_t* q_out, float* scale_out, uint16_t* y_out,             \
+      void* stream) {                                                                                              \
+    return fp8_per_token_impl<E>(x, ldx, residual, ldr, weight, M, H, eps, residual_out, q_out, scale_out, y_out,  \
+                                 stream);                                                                          \
+  }                                                                                                                \
+  rq_status rmsnorm_quant_fp8_per_group##SUFFIX(                                                                   \
+      const uint16_t* x, int64_t ldx, const uint16_t* residual, int64_t ldr, const uint16_t* weight, int64_t M,    \
+      int64_t H, float eps, int64_t group, uint16_t* residual_out, uint8_t* q_out, float* scale_out,               \
+      uint16_t* y_out, void* stream) {                                                                             \
+    return fp8_per_group_impl<E>(x, ldx, residual, ldr, weight, M, H, eps, group, residual_out, q_out, scale_out,  \
+                                 y_out, stream);                                                                   \
+  }                                                                                                                \
+  rq_status rmsnorm_quant_mxfp4##SUFFIX(const uint16_t* x, int64_t ldx, const uint16_t* residual, int64_t ldr,     \
+                                        const uint16_t* weight, int64_t M, int64_t H, float eps,                  \
+                                        uint16_t* residual_out, uint8_t* q_out, uint8_t* scale_out,               \
+                                        uint16_t* y_out, void* stream) {                                          \
+    return mxfp4_impl<E>(x, ldx, residual, ldr, weight, M, H, eps, residual_out, q_out, scale_out, y_out, stream); \
+  }                                                                                                                \
+  rq_status quantize_fp8_per_token##SUFFIX(const uint16_t* y, int64_t ldy, int64_t M, int64_t H, uint8_t* q_out,  \
+                                           float* scale_out, void* stream) {                                      \
+    return quant_fp8_token_impl<E>(y, ldy, M, H, q_out, scale_out, stream);                                        \
+  }                                                                                                                \
+  rq_status quantize_fp8_per_group##SUFFIX(const uint16_t* y, int64_t ldy, int64_t M, int64_t H, int64_t group,   \
+                                           uint8_t* q_out, float* scale_out, void* stream) {                      \
+    return quant_fp8_group_impl<E>(y, ldy, M, H, group, q_out, scale_out, stream);                                 \
+  }                                                                                                                \
+  rq_status quantize_mxfp4##SUFFIX(const uint16_t* y, int64_t ldy, int64_t M, int64_t H, uint8_t* q_out,          \
+                                   uint8_t* scale_out, void* stream) {                                            \
+    return quant_mxfp4_impl<E>(y, ldy, M, H, q_out, scale_out, stream);                                            \
+  }
+
+RQ_ROW_EXPORTS(, Bf16)
+RQ_ROW_EXPORTS(_f16, F16)
+
+rq_status rmsnorm_residual_bf16(const uint16_t* x, int64_t ldx, const uint16_t* residual, int64_t ldr,
+                                const uint16_t* weight, int64_t M, int64_t H, float eps, uint16_t* residual_out,
+                                uint16_t* y_out, void* stream) {
+  return norm_impl<Bf16>(x, ldx, residual, ldr, weight, M, H, eps, residual_out, y_out, stream);
+}
+
+rq_status rmsnorm_residual_f16(const uint16_t* x, int64_t ldx, const uint16_t* residual, int64_t ldr,
+                               const uint16_t* weight, int64_t M, int64_t H, float eps, uint16_t* residual_out,
+                               uint16_t* y_out, void* stream) {
+  return norm_impl<F16>(x, ldx, residual, ldr, weight, M, H, eps, residual_out, y_out, stream);
 }
 
 rq_status qk_gemma_rmsnorm_gate(const uint16_t* qg, int64_t ld_qg, const uint16_t* k, int64_t ld_k,
@@ -852,43 +971,6 @@ rq_status qk_gemma_rmsnorm_gate(const uint16_t* qg, int64_t ld_qg, const uint16_
   if (blocks > INT32_MAX) return RQ_ERR_UNSUPPORTED;
   return launch(reinterpret_cast<const void*>(kQKKernels[log2_lanes]), dim3((unsigned)blocks), dim3(kQKBlock), &a,
                 stream);
-}
-
-rq_status rmsnorm_residual_bf16(const uint16_t* x, int64_t ldx, const uint16_t* residual, int64_t ldr,
-                                const uint16_t* weight, int64_t M, int64_t H, float eps, uint16_t* residual_out,
-                                uint16_t* y_out, void* stream) {
-  rq_status st = norm_preflight(x, ldx, residual, ldr, weight, M, H, eps, residual_out, y_out);
-  if (st != RQ_OK || M == 0) return st;
-  RowArgs a = make_row_args(x, ldx, residual, ldr, weight, M, H, eps, residual_out, nullptr, nullptr, y_out);
-  return launch_rows<kFp8Token, kStageNorm>(a, stream);
-}
-
-rq_status quantize_fp8_per_token(const uint16_t* y, int64_t ldy, int64_t M, int64_t H, uint8_t* q_out,
-                                 float* scale_out, void* stream) {
-  rq_status st = quant_preflight(y, ldy, M, H, q_out, scale_out, 1, 4, H, 8);
-  if (st != RQ_OK || M == 0) return st;
-  RowArgs a = make_row_args(y, ldy, nullptr, 0, nullptr, M, H, 0.0f, nullptr, q_out, scale_out, nullptr);
-  return launch_rows<kFp8Token, kStageQuantize>(a, stream);
-}
-
-rq_status quantize_fp8_per_group(const uint16_t* y, int64_t ldy, int64_t M, int64_t H, int64_t group,
-                                 uint8_t* q_out, float* scale_out, void* stream) {
-  if (group <= 0) return RQ_ERR_INVALID;
-  const int l = group_log2_lanes(group);
-  rq_status st = quant_preflight(y, ldy, M, H, q_out, scale_out, l < 0 ? 1 : H / group, 4, l < 0 ? -1 : group, 8);
-  if (st != RQ_OK || M == 0) return st;
-  RowArgs a = make_row_args(y, ldy, nullptr, 0, nullptr, M, H, 0.0f, nullptr, q_out, scale_out, nullptr);
-  a.group_log2_lanes = l;
-  a.groups_per_row = (int)(H / group);
-  return launch_rows<kFp8Group, kStageQuantize>(a, stream);
-}
-
-rq_status quantize_mxfp4(const uint16_t* y, int64_t ldy, int64_t M, int64_t H, uint8_t* q_out, uint8_t* scale_out,
-                         void* stream) {
-  rq_status st = quant_preflight(y, ldy, M, H, q_out, scale_out, H / 32, 1, 32, 4);
-  if (st != RQ_OK || M == 0) return st;
-  RowArgs a = make_row_args(y, ldy, nullptr, 0, nullptr, M, H, 0.0f, nullptr, q_out, scale_out, nullptr);
-  return launch_rows<kMxfp4, kStageQuantize>(a, stream);
 }
 
 const char* rq_status_string(rq_status status) {

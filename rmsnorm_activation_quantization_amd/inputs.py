@@ -57,8 +57,9 @@ def _normal(gen: torch.Generator, shape, mean: float, std: float) -> torch.Tenso
     return torch.randn(shape, generator=gen, dtype=torch.float32) * std + mean
 
 
-def row_inputs(w: RowWorkload, set_index: int = 0) -> dict:
-    """x, residual [M, H] and weight [H] as CPU bf16 tensors."""
+def row_inputs(w: RowWorkload, set_index: int = 0, dtype: torch.dtype = torch.bfloat16) -> dict:
+    """x, residual [M, H] and weight [H] as CPU tensors of `dtype` (bf16 or fp16;
+    the same fp32 draws, rounded once to that type)."""
     gen = torch.Generator().manual_seed(w.seed + 7919 * set_index)
     x = _normal(gen, (w.M, w.H), 0.0, 1.0)
     residual = _normal(gen, (w.M, w.H), 0.0, 1.0)
@@ -66,8 +67,7 @@ def row_inputs(w: RowWorkload, set_index: int = 0) -> dict:
     if w.outliers:
         x = torch.where(torch.rand((w.M, w.H), generator=gen) < 0.01, x * 20.0, x)
         residual = torch.where(torch.rand((w.M, w.H), generator=gen) < 0.01, residual * 20.0, residual)
-    return dict(x=x.to(torch.bfloat16), residual=residual.to(torch.bfloat16),
-                weight=weight.to(torch.bfloat16))
+    return dict(x=x.to(dtype), residual=residual.to(dtype), weight=weight.to(dtype))
 
 
 def qk_inputs(w: QKWorkload, ld_k: int | None = None) -> dict:
@@ -82,26 +82,17 @@ def qk_inputs(w: QKWorkload, ld_k: int | None = None) -> dict:
                 q_w=q_w.to(torch.bfloat16), k_w=k_w.to(torch.bfloat16))
 
 
-def random_rows(M: int, H: int, seed: int, std: float = 1.0) -> dict:
+def random_rows(M: int, H: int, seed: int, dtype: torch.dtype = torch.bfloat16) -> dict:
     """Generic seeded rows for edge-case shapes (same distributions)."""
-    return row_inputs(RowWorkload(f"rows_{M}x{H}", M, H, seed), 0) if std == 1.0 else _scaled(M, H, seed, std)
-
-
-def _scaled(M: int, H: int, seed: int, std: float) -> dict:
-    gen = torch.Generator().manual_seed(seed)
-    x = _normal(gen, (M, H), 0.0, std)
-    residual = _normal(gen, (M, H), 0.0, std)
-    weight = _normal(gen, (H,), 1.0, 0.1)
-    return dict(x=x.to(torch.bfloat16), residual=residual.to(torch.bfloat16),
-                weight=weight.to(torch.bfloat16))
+    return row_inputs(RowWorkload(f"rows_{M}x{H}", M, H, seed), 0, dtype)
 
 
 def bits(t: torch.Tensor) -> np.ndarray:
-    """The uint16 bit patterns of a bf16 tensor (any device), as numpy."""
-    assert t.dtype == torch.bfloat16
+    """The uint16 bit patterns of a bf16 or fp16 tensor (any device), as numpy."""
+    assert t.dtype in (torch.bfloat16, torch.float16)
     return t.detach().cpu().contiguous().view(torch.int16).numpy().view(np.uint16)
 
 
-def from_bits(a: np.ndarray) -> torch.Tensor:
-    """A CPU bf16 tensor from uint16 bit patterns."""
-    return torch.from_numpy(np.ascontiguousarray(a, dtype=np.uint16).view(np.int16)).view(torch.bfloat16)
+def from_bits(a: np.ndarray, dtype: torch.dtype = torch.bfloat16) -> torch.Tensor:
+    """A CPU bf16 (or fp16) tensor from uint16 bit patterns."""
+    return torch.from_numpy(np.ascontiguousarray(a, dtype=np.uint16).view(np.int16)).view(dtype)

@@ -52,7 +52,7 @@ def to_np(out: dict) -> dict:
     for k, v in out.items():
         if v is None:
             res[k] = None
-        elif v.dtype == torch.bfloat16:
+        elif v.dtype in (torch.bfloat16, torch.float16):
             res[k] = inputs.bits(v)
         elif v.dtype == torch.float8_e4m3fn:
             res[k] = v.view(torch.uint8).cpu().numpy()

@@ -1,0 +1,148 @@
+"""GPU parity of the fp16 row entry points (the activation dtype carried through
+the step) against the oracle's fp16 functions."""
+
+from __future__ import annotations
+
+import numpy as np
+import pytest
+import torch
+
+import rmsnorm_activation_quantization_amd as rq
+from rmsnorm_activation_quantization_amd import inputs
+from oracle_pins import np_f16_round, np_f16_value
+from parity import check_fp8, check_mxfp4, to_np
+
+pytestmark = pytest.mark.gpu
+DEV = "cuda:0"
+F16 = torch.float16
+
+
+def gpu_call(fmt, x, r, w, eps, group=128, emit_y=True):
+    if fmt == "fp8_token":
+        out = rq.rmsnorm_quant_fp8_per_token(x, r, w, eps, emit_y=emit_y)
+    elif fmt == "fp8_group":
+        out = rq.rmsnorm_quant_fp8_per_group(x, r, w, eps, group, emit_y=emit_y)
+    else:
+        out = rq.rmsnorm_quant_mxfp4(x, r, w, eps, emit_y=emit_y)
+    assert out is not None
+    torch.cuda.synchronize()
+    q, res, scale, y = out
+    assert res.dtype == F16 and (y is None or y.dtype == F16), "fp16 rows must come back as fp16"
+    return to_np(dict(q=q, residual_out=res, scale=scale, y=y))
+
+
+def oracle_and_check(ref, fmt, gpu, xb, rb, wb, eps, group, what):
+    H = xb.shape[1]
+    if fmt == "fp8_token":
+        o = ref.fp8_per_token(xb, rb, wb, eps, emit_y=True, dtype="fp16")
+        return check_fp8(gpu, o, ref.quantize_fp8(gpu["y"], H, dtype="fp16"), H, what)
+    if fmt == "fp8_group":
+        o = ref.fp8_per_group(xb, rb, wb, eps, group, emit_y=True, dtype="fp16")
+        return check_fp8(gpu, o, ref.quantize_fp8(gpu["y"], group, dtype="fp16"), group, what)
+    o = ref.mxfp4(xb, rb, wb, eps, emit_y=True, dtype="fp16")
+    return check_mxfp4(gpu, o, ref.quantize_mxfp4(gpu["y"], dtype="fp16"), what)
+
+
+WORKLOADS = [("fp8_token", inputs.FP8_TOKEN_SMALL), ("fp8_group", inputs.FP8_GROUP_DECODE),
+             ("mxfp4", inputs.MXFP4_DECODE), ("fp8_token", inputs.PREFILL), ("fp8_group", inputs.PREFILL),
+             ("mxfp4", inputs.PREFILL)]
+
+
+@pytest.mark.parametrize("fmt,wl", WORKLOADS, ids=[f"{f}-{w.name}" for f, w in WORKLOADS])
+def test_fp16_workload_parity(ref, fmt, wl):
+    d = inputs.row_inputs(wl, dtype=F16)
+    xb, rb, wb = (inputs.bits(d[k]) for k in ("x", "residual", "weight"))
+    gpu = gpu_call(fmt, *(d[k].to(DEV) for k in ("x", "residual", "weight")), wl.eps)
+    stats = oracle_and_check(ref, fmt, gpu, xb, rb, wb, wl.eps, 128, f"fp16-{fmt}-{wl.name}")
+    print(f"fp16 {fmt} {wl.name}: {stats}", flush=True)
+
+
+@pytest.mark.parametrize("M,H", [(1, 32), (3, 544), (17, 4096), (70, 7168), (9, 16384)])
+def test_fp16_shapes_and_unfused(ref, M, H):
+    d = inputs.random_rows(M, H, seed=M * 7 + H, dtype=F16)
+    x, r, w = (d[k].to(DEV) for k in ("x", "residual", "weight"))
+    xb, rb, wb = (inputs.bits(d[k]) for k in ("x", "residual", "weight"))
+    ro, y = rq.rmsnorm_residual_f16(x, r, w, 1e-6)
+    torch.cuda.synchronize()
+    assert ro.dtype == F16 and y.dtype == F16
+    for fmt in ("fp8_token", "fp8_group", "mxfp4"):
+        if fmt == "fp8_group" and H % 128:
+            continue
+        gpu = gpu_call(fmt, x, r, w, 1e-6)
+        oracle_and_check(ref, fmt, gpu, xb, rb, wb, 1e-6, 128, f"fp16-{fmt}-{M}x{H}")
+        assert (gpu["y"] == inputs.bits(y)).all() and (gpu["residual_out"] == inputs.bits(ro)).all()
+        if fmt == "fp8_token":
+            q, s = rq.quantize_fp8_per_token(y)
+        elif fmt == "fp8_group":
+            q, s = rq.quantize_fp8_per_group(y, 128)
+        else:
+            q, s = rq.quantize_mxfp4(y)
+        torch.cuda.synchronize()
+        qn = q.view(torch.uint8).cpu().numpy() if q.dtype != torch.uint8 else q.cpu().numpy()
+        assert (qn == gpu["q"]).all(), f"fp16 {fmt}: fused codes differ from norm + quantize"
+        assert np.array_equal(s.cpu().numpy().reshape(-1).view(np.uint8), gpu["scale"].reshape(-1).view(np.uint8))
+
+
+def _probe(values, H, leader):
+    per = H - 1
+    n = -(-len(values) // per)
+    w = np.zeros((n, H))
+    w[:, 0] = leader
+    flat = np.zeros(n * per)
+    flat[: len(values)] = values
+    w[:, 1:] = flat.reshape(n, per)
+    return w
+
+
+def test_fp16_fp8_conversion_exhaustive(ref):
+    """Every fp16 value in [-448, 448] through the fused kernel at scale 1."""
+    vals = np_f16_value(np.arange(0, 0x5F01, dtype=np.uint16))
+    assert vals[-1] == 448.0
+    vals = np.concatenate([vals, -vals])
+    H = 4096
+    w = _probe(vals, H, 448.0)
+    xb = np_f16_round(np.full((1, H), 512.0))
+    x = inputs.from_bits(xb, F16).to(DEV)
+    for i in range(w.shape[0]):
+        wb = np_f16_round(w[i])
+        gpu = gpu_call("fp8_token", x, x.clone(), inputs.from_bits(wb, F16).to(DEV), 0.0)
+        assert (gpu["y"][0] == wb).all()
+        o = ref.fp8_per_token(xb, xb.copy(), wb, 0.0, dtype="fp16")
+        assert gpu["scale"][0, 0] == 1.0
+        assert (gpu["q"][0] == o["q"][0]).all(), f"E4M3 codes differ in probe row {i}"
+
+
+@pytest.mark.parametrize("k", [-12, 0, 5])
+def test_fp16_mxfp4_conversion_exhaustive(ref, k):
+    """Every fp16 magnitude below 8 (times 2^k) in blocks led by 7.5 * 2^k."""
+    vals = np.ldexp(np_f16_value(np.arange(0, 0x4800, dtype=np.uint16)), k)
+    vals = np.concatenate([vals, -vals])
+    vals = vals[(vals != 0) & (np_f16_value(np_f16_round(vals)) == vals)]
+    blocks = -(-len(vals) // 31)
+    w = np.full((blocks, 32), np.ldexp(1.0, k))
+    w[:, 0] = np.ldexp(7.5, k)
+    flat = np.full(blocks * 31, np.ldexp(1.0, k))
+    flat[: len(vals)] = vals
+    w[:, 1:] = flat.reshape(blocks, 31)
+    H = 4096
+    w = np.concatenate([w.reshape(-1), np.full((-w.size) % H, np.ldexp(1.0, k))]).reshape(-1, H)
+    xb = np_f16_round(np.full((1, H), 512.0))
+    x = inputs.from_bits(xb, F16).to(DEV)
+    for i in range(w.shape[0]):
+        wb = np_f16_round(w[i])
+        gpu = gpu_call("mxfp4", x, x.clone(), inputs.from_bits(wb, F16).to(DEV), 0.0)
+        o = ref.mxfp4(xb, xb.copy(), wb, 0.0, dtype="fp16")
+        assert (gpu["scale"] == o["scale"]).all()
+        assert (gpu["q"] == o["q"]).all(), f"E2M1 codes differ in row {i} at k={k}"
+
+
+def test_mixed_dtypes_are_rejected():
+    x = torch.randn(4, 256, device=DEV).to(F16)
+    r = torch.randn(4, 256, device=DEV).to(torch.bfloat16)
+    w = torch.ones(256, dtype=F16, device=DEV)
+    with pytest.raises(ValueError):
+        rq.rmsnorm_quant_fp8_per_token(x, r, w)
+    with pytest.raises(ValueError):
+        rq.rmsnorm_quant_mxfp4(x, x, w.to(torch.bfloat16))
+    with pytest.raises(ValueError):
+        rq.qk_gemma_rmsnorm_gate(x, x, w, w, 1, 0, 128)
