@@ -10,6 +10,9 @@ ROOT = os.path.dirname(PKG)
 SOURCE = os.path.join(PKG, "csrc", "rmsnorm_quant.hip")
 INCLUDE = os.path.join(ROOT, "include")
 LIBRARY = os.path.join(PKG, "librmsnorm_quant.so")
+EXAMPLE_SOURCE = os.path.join(PKG, "csrc", "abi_example.c")
+EXAMPLE = os.path.join(PKG, "rq_abi_example")
+ROCM = os.environ.get("ROCM_PATH", "/opt/rocm")
 
 HIPCC = os.environ.get("HIPCC", "/opt/rocm/bin/hipcc")
 HIPCC_FLAGS = [
@@ -28,4 +31,16 @@ def build(output: str = LIBRARY, extra_flags: tuple[str, ...] = ()) -> str:
     if proc.returncode != 0:
         raise RuntimeError(f"hipcc failed ({proc.returncode}):\n{proc.stderr}")
     os.replace(tmp, output)
+    return output
+
+
+def build_example(output: str = EXAMPLE) -> str:
+    """The plain-C user of the ABI (gcc, HIP runtime API only), linked against
+    the library next to it."""
+    cmd = ["gcc", "-std=c11", "-O2", "-D__HIP_PLATFORM_AMD__", "-I", os.path.join(ROCM, "include"), "-I", INCLUDE,
+           EXAMPLE_SOURCE, "-o", output, "-L", os.path.join(ROCM, "lib"), "-lamdhip64", "-L", PKG,
+           "-l:librmsnorm_quant.so", "-Wl,-rpath,$ORIGIN", "-Wl,-rpath," + os.path.join(ROCM, "lib")]
+    proc = subprocess.run(cmd, capture_output=True, text=True)
+    if proc.returncode != 0:
+        raise RuntimeError(f"gcc failed ({proc.returncode}):\n{proc.stderr}")
     return output

@@ -5,21 +5,25 @@
 // with bf16 tensors between its launches, in ONE pass over HBM:
 //   read x, residual (and the L2-resident weight) once, write residual_out,
 //   the codes and the scales once.  The row stays in VGPRs from load to store.
+// The same kernel template also runs the two launches of the unfused sequence
+// (norm alone, quantize alone: a stage parameter), with bit-identical results,
+// and takes bf16 or fp16 rows (an element-type parameter).
 // The QK variant (sglang PR #27656, Motivation / Modifications): GemmaRMSNorm
 // of q and k heads read through their strides plus the gate de-interleave, in
 // one launch.
 //
 // Work mapping (CDNA4: 64-lane waves, 16-byte loads):
-//   a lane owns 8 consecutive bf16 (one 16-byte load per tensor) per "chunk";
-//   the lanes of a row cover 8 * lanes consecutive columns per chunk, so every
-//   wave-level load and store is fully coalesced.  A row is spread over WPR
-//   waves (1, 2, 4, 8 or 16) of one workgroup, and NC = chunks per lane is a
-//   template parameter, so the row lives in registers from load to store and is
-//   never re-read.  The host picks WPR so that a lane holds at most two chunks:
-//   few registers, hence up to 8 waves per SIMD in flight, which measured best
-//   on MI355X at prefill sizes (a wave per row with the row in 115 VGPRs ran at
-//   68 % of HBM peak, a workgroup per row at 74 %).  Waves of a row combine
-//   their partial sums and maxima through LDS with one barrier each.
+//   a lane owns 8 consecutive elements (one 16-byte load per tensor) per
+//   "chunk"; the lanes of a row cover 8 * lanes consecutive columns per chunk,
+//   so every wave-level load and store is fully coalesced.  A row is spread
+//   over WPR waves (1, 2, 4, 8 or 16) of one workgroup, and NC = chunks per
+//   lane is a template parameter, so the row lives in registers from load to
+//   store and is never re-read.  The host picks WPR so that a lane holds at most
+//   two chunks: few registers, hence up to 8 waves per SIMD in flight, which
+//   measured best on MI355X at prefill sizes (a wave per row with the row in
+//   115 VGPRs ran at 68 % of HBM peak, a workgroup per row at 74 %).  Waves of
+//   a row combine their partial sums and maxima through LDS with one barrier
+//   each.
 // Reductions: the sum of squares over the row, and max |y| per token, per
 // group or per 32-element block, use DPP row operations inside 16-lane rows,
 // a swizzle across rows and readlane across wave halves.  Every butterfly step
@@ -27,20 +31,21 @@
 //
 // Arithmetic (matches the oracle's definition exactly except rstd, which is
 // fp32 here):
-//   residual_out = bf16_rne(f32(x) + f32(res))   exact: the fp32 sum of two
-//                  bf16 values rounded to bf16 is the correctly rounded sum
-//                  (24 >= 2*8 + 2, so the double rounding is innocuous).
+//   residual_out = round(f32(x) + f32(res))   exact: the fp32 sum of two bf16
+//                  (fp16) values rounded to bf16 (fp16) is the correctly
+//                  rounded sum (24 >= 2*8 + 2 and 24 >= 2*11 + 2, so the
+//                  double rounding is innocuous).
 //   ss = sum of r^2 in fp32; rstd = rsq(ss * (1/H) + eps) (hardware
 //        reciprocal square root; the oracle's rstd is fp64, and y may differ
-//        by one bf16 ulp where r * rstd * w lies next to a rounding boundary).
-//   y = bf16_rne((r * rstd) * w).
+//        by one ulp where r * rstd * w lies next to a rounding boundary).
+//   y = round((r * rstd) * w), to nearest even.
 //   FP8: scale = amax / 448 exactly (IEEE-equal); the quotient y / scale is
 //        formed with the correctly rounded reciprocal of the scale and one
 //        Markstein correction (q0 = y*inv, e = scale*q0 - y, q = q0 - e*inv),
-//        which equals the IEEE fp32 quotient for every bf16 y and fp32 scale
-//        >= 2^-64 (checked exhaustively on the host by the test suite); the
-//        hardware converter then rounds to E4M3FN (nearest-even).
-//   MXFP4: E8M0 byte from the exponent bits of amax; y * 2^(127 - byte) is
+//        which equals the IEEE fp32 quotient for every bf16 or fp16 y and
+//        fp32 scale >= 2^-64 (checked exhaustively on the host by the test
+//        suite); the hardware converter then rounds to E4M3FN (nearest-even).
+//   MXFP4: E8M0 byte from the fp32 exponent of amax; y * 2^(127 - byte) is
 //        exact, and the hardware converter rounds to E2M1 (nearest-even,
 //        saturating at 6).
 #include <hip/hip_runtime.h>
@@ -677,7 +682,7 @@ bool outputs_disjoint(const Span* outs, int n_out, const Span* ins, int n_in, in
 }
 
 // Shared checks of the three fused row entry points.  granule = elements per
-// scale; code_bytes_num / code_bytes_den = bytes per element of q_out.
+// scale; code_bits = bits per element of q_out (8 for FP8, 4 for MXFP4).
 rq_status row_preflight(const uint16_t* x, int64_t ldx, const uint16_t* residual, int64_t ldr,
                         const uint16_t* weight, int64_t M, int64_t H, float eps,
                         const uint16_t* residual_out, const uint8_t* q_out, const void* scale_out,
