@@ -67,3 +67,45 @@ def test_graph_replay_matches_eager():
         torch.cuda.synchronize()
         for a, b in zip(snapshot(), eager):
             assert torch.equal(a.view(torch.uint8), b.view(torch.uint8)), f"replay {i} differs from eager"
+
+
+def test_graph_replay_unfused_and_fp16():
+    """The unfused launches and the fp16 rows inside one captured graph."""
+    d = inputs.row_inputs(inputs.DECODE_4096)
+    x, r, w = (d[k].to(DEV) for k in ("x", "residual", "weight"))
+    d16 = inputs.row_inputs(inputs.DECODE_4096, dtype=torch.float16)
+    x16, r16, w16 = (d16[k].to(DEV) for k in ("x", "residual", "weight"))
+    M, H = x.shape
+    ro, y = torch.empty_like(x), torch.empty_like(x)
+    q = torch.empty((M, H), dtype=torch.uint8, device=DEV)
+    s = torch.empty((M,), dtype=torch.float32, device=DEV)
+    ro16 = torch.empty_like(x16)
+    q16 = torch.empty((M, H // 2), dtype=torch.uint8, device=DEV)
+    s16 = torch.empty((M, H // 32), dtype=torch.uint8, device=DEV)
+    bufs = [ro, y, q, s, ro16, q16, s16]
+
+    def step():
+        assert rq.rmsnorm_residual_bf16(x, r, w, 1e-6, residual_out=ro, y_out=y) is not None
+        assert rq.quantize_fp8_per_token(y, q_out=q, scale_out=s) is not None
+        assert rq.rmsnorm_quant_mxfp4(x16, r16, w16, 1e-6, residual_out=ro16, q_out=q16, scale_out=s16) is not None
+
+    step()
+    torch.cuda.synchronize()
+    eager = [t.clone() for t in bufs]
+    st = torch.cuda.Stream()
+    st.wait_stream(torch.cuda.current_stream())
+    with torch.cuda.stream(st):
+        step()
+    torch.cuda.current_stream().wait_stream(st)
+    torch.cuda.synchronize()
+    g = torch.cuda.CUDAGraph()
+    with torch.cuda.graph(g):
+        step()
+    for i in range(3):
+        for t in bufs:
+            t.zero_()
+        torch.cuda.synchronize()
+        g.replay()
+        torch.cuda.synchronize()
+        for a, b in zip(bufs, eager):
+            assert torch.equal(a.view(torch.uint8), b.view(torch.uint8)), f"replay {i} differs from eager"
