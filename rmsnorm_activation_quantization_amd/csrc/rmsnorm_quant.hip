@@ -18,12 +18,15 @@
 //   so every wave-level load and store is fully coalesced.  A row is spread
 //   over WPR waves (1, 2, 4, 8 or 16) of one workgroup, and NC = chunks per
 //   lane is a template parameter, so the row lives in registers from load to
-//   store and is never re-read.  The host picks WPR so that a lane holds at most
-//   two chunks: few registers, hence up to 8 waves per SIMD in flight, which
-//   measured best on MI355X at prefill sizes (a wave per row with the row in
-//   115 VGPRs ran at 68 % of HBM peak, a workgroup per row at 74 %).  Waves of
-//   a row combine their partial sums and maxima through LDS with one barrier
-//   each.
+//   store and is never re-read.  For many rows the host picks WPR so that a
+//   lane holds at most two chunks: few registers, hence up to 8 waves per SIMD
+//   in flight, which measured best on MI355X at prefill sizes (a wave per row
+//   with the row in 115 VGPRs ran at 68 % of HBM peak, a workgroup per row at
+//   74 %).  For a decode batch, which cannot fill the chip, it picks one chunk
+//   per lane (more waves per row, a shorter chain per lane).  Waves of a row
+//   combine their partial sums and maxima through LDS with one barrier each;
+//   the row's sum of squares is added up in one order whatever the tiling, so
+//   a row gives the same bits in any batch.
 // Reductions: the sum of squares over the row, and max |y| per token, per
 // group or per 32-element block, use DPP row operations inside 16-lane rows,
 // a swizzle across rows and readlane across wave halves.  Every butterfly step
@@ -259,13 +262,15 @@ template <typename E>
 __device__ __forceinline__ uint2 fp8_codes(const uint4& y, const Fp8Granule& g) {
   const uint32_t w[4] = {y.x, y.y, y.z, y.w};
   float q[8];
-  if (!g.slow) {
 #pragma unroll
-    for (int j = 0; j < 4; ++j) {
-      q[2 * j] = fp8_quotient(E::lo(w[j]), g);
-      q[2 * j + 1] = fp8_quotient(E::hi(w[j]), g);
-    }
-  } else {  // tiny or non-finite granule
+  for (int j = 0; j < 4; ++j) {
+    q[2 * j] = fp8_quotient(E::lo(w[j]), g);
+    q[2 * j + 1] = fp8_quotient(E::hi(w[j]), g);
+  }
+  // Tiny or non-finite granule: plain IEEE division instead.  The branch is
+  // marked unlikely so that it stays a branch: evaluating the eight divisions
+  // unconditionally and selecting cost about 0.4 us a decode call.
+  if (__builtin_expect(g.slow, false)) {
 #pragma unroll
     for (int j = 0; j < 4; ++j) {
       q[2 * j] = E::lo(w[j]) / g.sc;
@@ -332,6 +337,32 @@ struct RowArgs {
   int groups_per_row;    // per-group FP8: H / group
 };
 
+// Sum of a row from per-lane piece sums (one per chunk): each 64-lane block
+// by the wave butterfly, then the blocks in column order (block b = chunk
+// b / kWPR of wave b % kWPR).  A multi-wave row exchanges the block sums
+// through LDS (one barrier); the loop runs over every block slot, and those
+// past the row's end hold +0, which leaves a sum of squares unchanged.
+template <int kNC, int kWPR>
+__device__ __forceinline__ float row_sum(float (&part)[kNC], float* lds, int lane, int wrow) {
+#pragma unroll
+  for (int c = 0; c < kNC; ++c) part[c] = group_sum(part[c], 6);  // independent chains
+  if (kWPR == 1) {
+    float s = part[0];
+#pragma unroll
+    for (int c = 1; c < kNC; ++c) s += part[c];
+    return s;
+  }
+  if (lane == 0) {
+#pragma unroll
+    for (int c = 0; c < kNC; ++c) lds[c * kWPR + wrow] = part[c];
+  }
+  __syncthreads();
+  float s = lds[0];
+#pragma unroll
+  for (int b = 1; b < kNC * kWPR; ++b) s += lds[b];  // one fixed order: every lane agrees
+  return s;
+}
+
 // Rows a workgroup holds: four one-wave rows, or one row of several waves (so
 // every barrier of a multi-wave row is uniform over its workgroup).
 template <int kWPR>
@@ -359,8 +390,8 @@ __global__ __launch_bounds__(block_threads<kWPR>()) void fused_rows(const RowArg
   const bool live = row < a.M;
   const int H = a.H;
 
-  __shared__ float lds_sum[kRPB][kWPR];
-  __shared__ float lds_sum_tiny[kRPB][kWPR];
+  __shared__ float lds_sum[kRPB][kWPR * kNC];
+  __shared__ float lds_sum_tiny[kRPB][kWPR * kNC];
   __shared__ uint32_t lds_max[kRPB][kWPR];
 
   uint4 yp[kNC];
@@ -376,51 +407,61 @@ __global__ __launch_bounds__(block_threads<kWPR>()) void fused_rows(const RowArg
     const uint16_t* xr = a.x + (live ? row : 0) * a.ldx;
     const uint16_t* rr = a.res + (live ? row : 0) * a.ldr;
 
-    // 1. Issue every load of the row before using any of it.
+    // 1. Issue every load of the row before using any of it, the weight
+    //    first.  Loads return in order, so by the time x and the residual have
+    //    arrived the weight has too, and no later wait for data can be made to
+    //    include the completion of a store (the one counter of vector memory
+    //    operations counts both, and a wait behind a store waits for all).
     uint4 xv[kNC], rv[kNC], wv[kNC];
+  #pragma unroll
+    for (int c = 0; c < kNC; ++c) {
+      const int col = c * kChunk + t * 8;
+      // the weight is re-read by every row: keep it cached
+      wv[c] = (live && (c < kNC - 1 || col < H)) ? load16<false>(a.w + col) : make_uint4(0, 0, 0, 0);
+    }
   #pragma unroll
     for (int c = 0; c < kNC; ++c) {
       const int col = c * kChunk + t * 8;
       if (live && (c < kNC - 1 || col < H)) {
         xv[c] = load16<kNT>(xr + col);
         rv[c] = load16<kNT>(rr + col);
-        wv[c] = load16<false>(a.w + col);  // the weight is re-read by every row: keep it cached
       } else {
         xv[c] = make_uint4(0, 0, 0, 0);
         rv[c] = make_uint4(0, 0, 0, 0);
-        wv[c] = make_uint4(0, 0, 0, 0);
       }
     }
 
-    // 2. Residual add (one bf16 rounding), store residual_out, sum of squares.
+    // 2. Residual add (one bf16 rounding) and the sum of squares of each
+    //    8-element piece; then the residual_out stores, after the last load.
     uint4 rp[kNC];
-    float ss = 0.0f;
+    float ssc[kNC];
   #pragma unroll
     for (int c = 0; c < kNC; ++c) {
       const uint32_t xs[4] = {xv[c].x, xv[c].y, xv[c].z, xv[c].w};
       const uint32_t rs[4] = {rv[c].x, rv[c].y, rv[c].z, rv[c].w};
       uint32_t p[4];
+      ssc[c] = 0.0f;
   #pragma unroll
       for (int j = 0; j < 4; ++j) {
         p[j] = E::pack(E::lo(xs[j]) + E::lo(rs[j]), E::hi(xs[j]) + E::hi(rs[j]));
         const float r0 = E::lo(p[j]), r1 = E::hi(p[j]);
-        ss = __builtin_fmaf(r0, r0, ss);
-        ss = __builtin_fmaf(r1, r1, ss);
+        ssc[c] = __builtin_fmaf(r0, r0, ssc[c]);
+        ssc[c] = __builtin_fmaf(r1, r1, ssc[c]);
       }
       rp[c] = make_uint4(p[0], p[1], p[2], p[3]);
+    }
+  #pragma unroll
+    for (int c = 0; c < kNC; ++c) {
       const int col = c * kChunk + t * 8;
       if (live && (c < kNC - 1 || col < H)) store16<kNT>(a.res_out + row * H + col, rp[c]);
     }
 
-    // 3. rstd over the whole row.
-    ss = group_sum(ss, 6);
-    if (kWPR > 1) {
-      if (lane == 0) lds_sum[rloc][wrow] = ss;
-      __syncthreads();
-      ss = lds_sum[rloc][0];
-  #pragma unroll
-      for (int w = 1; w < kWPR; ++w) ss += lds_sum[rloc][w];  // one fixed order: every lane agrees
-    }
+    // 3. rstd over the whole row, summed in an order that does not depend on
+    //    the tiling: the 64 pieces of each 512-column block by the wave
+    //    butterfly, then the blocks' sums left to right.  Block b is chunk
+    //    b / kWPR of wave b % kWPR, so every (kWPR, kNC) launch of a row gives
+    //    the same bits, and the host may pick the tiling from the batch size.
+    const float ss = row_sum<kNC, kWPR>(ssc, lds_sum[rloc], lane, wrow);
     // rstd need not be correctly rounded (the tolerance on y is one bf16 ulp):
     // the hardware reciprocal square root keeps it off the critical path.
     const float t_ms = __builtin_fmaf(ss, a.inv_h, a.eps);
@@ -432,25 +473,19 @@ __global__ __launch_bounds__(block_threads<kWPR>()) void fused_rows(const RowArg
       // so sum them again with r scaled by 2^100 (exact; |r| < 2^-43 here, so the
       // scaled squares lie in [2^-66, 2^114]).  Uniform over the row, and a
       // multi-wave row has its workgroup to itself.
-      float s2 = 0.0f;
+      float s2c[kNC];
   #pragma unroll
       for (int c = 0; c < kNC; ++c) {
         const uint32_t rs[4] = {rp[c].x, rp[c].y, rp[c].z, rp[c].w};
+        s2c[c] = 0.0f;
   #pragma unroll
         for (int j = 0; j < 4; ++j) {
           const float r0 = E::lo(rs[j]) * 0x1p100f, r1 = E::hi(rs[j]) * 0x1p100f;
-          s2 = __builtin_fmaf(r0, r0, s2);
-          s2 = __builtin_fmaf(r1, r1, s2);
+          s2c[c] = __builtin_fmaf(r0, r0, s2c[c]);
+          s2c[c] = __builtin_fmaf(r1, r1, s2c[c]);
         }
       }
-      s2 = group_sum(s2, 6);
-      if (kWPR > 1) {
-        if (lane == 0) lds_sum_tiny[rloc][wrow] = s2;
-        __syncthreads();
-        s2 = lds_sum_tiny[rloc][0];
-  #pragma unroll
-        for (int w = 1; w < kWPR; ++w) s2 += lds_sum_tiny[rloc][w];
-      }
+      const float s2 = row_sum<kNC, kWPR>(s2c, lds_sum_tiny[rloc], lane, wrow);
       rstd = __builtin_amdgcn_rsqf(__builtin_fmaf(s2, a.inv_h, a.eps * 0x1p100f * 0x1p100f)) * 0x1p100f;
     }
 
@@ -753,20 +788,33 @@ rq_status launch(const void* kernel, dim3 grid, dim3 block, void* args, void* st
   return err == hipSuccess ? RQ_OK : RQ_ERR_HIP;
 }
 
-// Waves per row: the fewest (a power of two, 1..16) for which a lane holds at
-// most kMaxChunks chunks of 8 elements.
-int waves_per_row_log2(int H) {
+// One wave per SIMD over the whole chip (256 CUs x 4 SIMDs).
+constexpr int64_t kChipSimds = 1024;
+
+int chunks_per_lane(int H, int l) {
+  const int lanes = kWave << l;
+  return (H + lanes * 8 - 1) / (lanes * 8);
+}
+
+// Waves per row (a power of two, 1..16).  Many rows: the fewest for which a
+// lane holds at most kMaxChunks chunks of 8 elements (few registers, many waves
+// in flight to cover HBM latency).  Few rows, where the launch cannot fill the
+// chip anyway: more waves, so that a lane holds one chunk, while the launch
+// stays within one wave per SIMD; a lane's dependent chain from load to store
+// is then as short as it gets.  The row's sum is the same for every tiling.
+int waves_per_row_log2(int64_t M, int H) {
   int l = 0;
-  while (l < 4 && (int64_t)kWave * (1 << l) * 8 * kMaxChunks < H) ++l;
+  while (l < 4 && chunks_per_lane(H, l) > kMaxChunks) ++l;
+  while (l < 4 && chunks_per_lane(H, l) > 1 && M * (int64_t)(2 << l) <= kChipSimds) ++l;
   return l;
 }
 
 template <typename E, int kMode, int kStage = kStageFused>
 rq_status launch_rows(RowArgs& a, void* stream) {
-  const int l = waves_per_row_log2(a.H);
+  const int l = waves_per_row_log2(a.M, a.H);
   const int wpr = 1 << l;
   const int lanes = kWave * wpr;
-  const int nc = (a.H + lanes * 8 - 1) / (lanes * 8);
+  const int nc = chunks_per_lane(a.H, l);
   const int rpb = wpr == 1 ? 4 : 1;
   const unsigned blocks = (unsigned)((a.M + rpb - 1) / rpb);
   return launch(reinterpret_cast<const void*>(RowKernels<E, kMode, kStage>::k[l][nc - 1]), dim3(blocks),

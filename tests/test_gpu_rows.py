@@ -255,6 +255,29 @@ def test_determinism():
             assert np.array_equal(a[key], b[key]), f"{fmt} {key} not deterministic"
 
 
+@pytest.mark.parametrize("H", [256, 544, 2048, 4096, 7168, 8192, 16384])
+def test_batch_invariance(H):
+    """A row gives the same bits alone in a decode batch (more waves per row,
+    one chunk a lane) and inside a prefill batch (fewer waves, two chunks a
+    lane): the row's sum of squares is added in one order for every tiling.
+    Also rows small enough for the rescaled re-sum (eps 0, |r| ~ 2^-60)."""
+    for mag, eps in ((1.0, 1e-6), (2.0 ** -60, 0.0)):
+        big = inputs.random_rows(2048, H, seed=H + 11, dtype=torch.bfloat16)
+        x, r, w = (big[k].to(DEV) for k in ("x", "residual", "weight"))
+        x, r = (x.float() * mag).to(torch.bfloat16), (r.float() * mag).to(torch.bfloat16)
+        for fmt in ("fp8_token", "fp8_group", "mxfp4"):
+            if fmt == "fp8_group" and H % 128:
+                continue
+            whole = gpu_call(fmt, x, r, w, eps)
+            for m in (1, 4, 16, 64):
+                part = gpu_call(fmt, x[:m].contiguous(), r[:m].contiguous(), w, eps)
+                for key in part:
+                    if part[key] is None:
+                        continue
+                    assert np.array_equal(part[key], whole[key][:m]), \
+                        f"{fmt} H={H} mag={mag}: {key} of the first {m} rows depends on the batch size"
+
+
 def test_unsupported_returns_none_and_writes_nothing():
     M, H = 4, rq.RQ_MAX_HIDDEN + 8
     x = torch.randn(M, H, device=DEV).to(torch.bfloat16)
