@@ -385,4 +385,25 @@ int rq_ref_qk_gemma_rmsnorm_gate(
   return 0;
 }
 
+// The QK step followed by FP8 quantization of the normalized q and k, one
+// scale per head of each token: the bf16 heads of the step above, each
+// quantized as one granule of D values by the per-token FP8 rule (scale =
+// amax / 448).  The pages fuse a downstream quantization of the attention
+// inputs without giving its granule; one head of one token is the plainest
+// granule of that data.
+int rq_ref_qk_gemma_rmsnorm_gate_fp8(
+    const uint16_t* qg, int64_t ld_qg, const uint16_t* k, int64_t ld_k,
+    const uint16_t* q_w, const uint16_t* k_w, int64_t T, int64_t Hq, int64_t Hk,
+    int64_t D, float eps, uint8_t* q_codes, float* q_scale, uint8_t* k_codes, float* k_scale,
+    uint16_t* gate_out) {
+  if (T > 0 && (!q_codes || !q_scale || !k_codes || !k_scale)) return 1;
+  std::vector<uint16_t> q_bf16((size_t)(T > 0 ? T : 0) * Hq * D), k_bf16((size_t)(T > 0 ? T : 0) * Hk * D);
+  int rc = rq_ref_qk_gemma_rmsnorm_gate(qg, ld_qg, k, ld_k, q_w, k_w, T, Hq, Hk, D, eps, q_bf16.data(),
+                                        k_bf16.data(), gate_out);
+  if (rc != 0) return rc;
+  rc = quantize_fp8_rows(kBf16, q_bf16.data(), T * Hq, D, D, q_codes, q_scale);
+  if (rc != 0) return rc;
+  return quantize_fp8_rows(kBf16, k_bf16.data(), T * Hk, D, D, k_codes, k_scale);
+}
+
 }  // extern "C"

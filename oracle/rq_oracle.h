@@ -138,6 +138,17 @@ int rq_ref_qk_gemma_rmsnorm_gate(
     const uint16_t* q_w, const uint16_t* k_w, int64_t T, int64_t Hq, int64_t Hk,
     int64_t D, float eps, uint16_t* q_out, uint16_t* k_out, uint16_t* gate_out);
 
+/* The QK step, then FP8 quantization of each normalized head: the bf16 q and
+ * k heads of rq_ref_qk_gemma_rmsnorm_gate, each one granule of D values with
+ * the per-token rule (scale = fp32(amax) / 448, q = e4m3fn(v / scale)).
+ * q_codes [T, Hq, D] and k_codes [T, Hk, D] E4M3FN bytes; q_scale [T, Hq] and
+ * k_scale [T, Hk] fp32; gate_out as above. */
+int rq_ref_qk_gemma_rmsnorm_gate_fp8(
+    const uint16_t* qg, int64_t ld_qg, const uint16_t* k, int64_t ld_k,
+    const uint16_t* q_w, const uint16_t* k_w, int64_t T, int64_t Hq, int64_t Hk,
+    int64_t D, float eps, uint8_t* q_codes, float* q_scale, uint8_t* k_codes, float* k_scale,
+    uint16_t* gate_out);
+
 #ifdef __cplusplus
 }
 #endif

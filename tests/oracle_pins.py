@@ -497,6 +497,40 @@ def pin_qk(ref):
     assert (o["k"] == (one_plus(kw) ^ np.uint16(0x8000))[None, None, :]).all()
 
 
+def pin_qk_fp8(ref):
+    """QK with per-head FP8 outputs against numpy (the QK formulation above, then
+    the FP8 rule with one granule per head), a closed form and the invariants."""
+    for D, ld_pad in ((64, 24), (96, 0), (256, 8)):
+        w = inputs.QKWorkload(f"qk_fp8_{D}", 5, 3, 2, D, seed=91 + D)
+        d = inputs.qk_inputs(w, ld_k=2 * D + ld_pad)
+        qg, k, qw, kw = (inputs.bits(d[n]) for n in ("qg", "k", "q_w", "k_w"))
+        o = ref.qk_gemma_rmsnorm_gate_fp8(qg, k, qw, kw, w.Hq, w.Hk, w.D, w.eps)
+        q2, k2, g2 = np_qk(qg, k, qw, kw, w.Hq, w.Hk, w.D, w.eps)
+        for name, heads, H in (("q", q2, w.Hq), ("k", k2, w.Hk)):
+            codes, scale = np_fp8(heads.reshape(-1, D), D)
+            assert (o[name].reshape(-1, D) == codes).all(), f"{name} codes differ from numpy at D={D}"
+            assert np.array_equal(o[name + "_scale"].reshape(-1).view(np.uint32),
+                                  scale.reshape(-1).view(np.uint32)), f"{name} scales differ from numpy at D={D}"
+            # every head with a nonzero value has its largest magnitude at code +-448
+            top = (o[name].reshape(-1, D) & 0x7F).max(axis=1)
+            assert (top[np.abs(np_bf16_value(heads.reshape(-1, D))).max(axis=1) > 0] == 0x7E).all()
+        assert (o["gate"] == g2).all()
+    # closed form: constant heads with w = 0 normalize to exactly 1 (-1 for k)
+    T, Hq, Hk, D = 2, 3, 1, 128
+    qg = np_bf16_round(np.full((T, 2 * Hq * D), 3.0))
+    k = np_bf16_round(np.full((T, Hk * D), -0.25))
+    z = np.zeros(D, np.uint16)
+    o = ref.qk_gemma_rmsnorm_gate_fp8(qg, k, z, z, Hq, Hk, D, 1e-6)
+    assert (o["q"] == 0x7E).all() and (o["k"] == 0xFE).all()
+    assert (o["q_scale"] == np.float32(1.0) / np.float32(448.0)).all()
+    assert (o["k_scale"] == np.float32(1.0) / np.float32(448.0)).all()
+    # a zero head: scale 0 and codes that only keep the sign of zero
+    o = ref.qk_gemma_rmsnorm_gate_fp8(np.zeros((1, 2 * D), np.uint16), np.zeros((1, D), np.uint16),
+                                      z, z, 1, 1, D, 1e-6)
+    assert (o["q_scale"] == 0).all() and (o["k_scale"] == 0).all()
+    assert ((o["q"] & 0x7F) == 0).all() and ((o["k"] & 0x7F) == 0).all()
+
+
 def pin_invariants_on_workloads(ref):
     """On the C1..C3 workloads: the max-|y| element of each granule encodes at
     the top of the format, dequantized codes stay within half a step of y, and
@@ -638,6 +672,6 @@ ALL_PINS = [
     pin_e2m1_table, pin_e2m1_bruteforce, pin_e8m0,
     pin_fp8_weight_probe, pin_mxfp4_weight_probe, pin_group_weight_probe,
     pin_constant_row, pin_zero_and_sign, pin_independent_rows,
-    pin_strided_inputs, pin_qk, pin_invariants_on_workloads, pin_quantize_step,
+    pin_strided_inputs, pin_qk, pin_qk_fp8, pin_invariants_on_workloads, pin_quantize_step,
     pin_f16_decode, pin_f16_round, pin_f16_rows, pin_f16_weight_probe,
 ]

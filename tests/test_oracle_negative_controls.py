@@ -42,6 +42,10 @@ MUTATIONS = {
     "qk_interleave_stride": ("qg + t * ld_qg + 2 * D * h", "qg + t * ld_qg + D * h"),
     "qk_gate_offset": ("const uint16_t* gate_part = q_part + D;", "const uint16_t* gate_part = q_part + D + 1;"),
     "quotient_by_reciprocal": ("float quotient = (float)v / s;", "float quotient = (float)v * (1.0f / s);"),
+    "qk_fp8_granule_per_token": ("quantize_fp8_rows(kBf16, q_bf16.data(), T * Hq, D, D, q_codes, q_scale)",
+                                 "quantize_fp8_rows(kBf16, q_bf16.data(), T, Hq * D, Hq * D, q_codes, q_scale)"),
+    "qk_fp8_k_from_q": ("quantize_fp8_rows(kBf16, k_bf16.data(), T * Hk, D, D, k_codes, k_scale)",
+                        "quantize_fp8_rows(kBf16, q_bf16.data(), T * Hk, D, D, k_codes, k_scale)"),
 }
 
 
