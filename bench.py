@@ -205,6 +205,7 @@ def main():
     if not args.no_decode and not args.profile_pass:
         result["decode"] = decode_latency(torch, rq, inputs, dev)
         result["unfused_vs_fused"] = unfused_comparison(torch, rq, inputs, dev, sets, outs, per_kernel_us, args)
+        result["qk_prefill"] = qk_prefill(torch, rq, dev)
     if not args.no_cpu_baseline and not args.profile_pass:
         result["cpu_baseline"] = cpu_baseline(inputs, wl, qw, nbytes)
     print(json.dumps(result), flush=True)
@@ -314,7 +315,65 @@ def decode_latency(torch, rq, inputs, dev, calls: int = 200, replays: int = 7):
     res[f"qk_{qw.T}x{qw.Hq}x{qw.Hk}x{qw.D}_us"] = round(graph_us(
         lambda i: rq.qk_gemma_rmsnorm_gate(qg[i % nq], kk[i % nq], qd["q_w"], qd["k_w"], qw.Hq, qw.Hk, qw.D, qw.eps,
                                            q_out=outs[0], k_out=outs[1], gate_out=outs[2])), 3)
+    o8 = (torch.empty((qw.T, qw.Hq, qw.D), dtype=torch.uint8, device=dev),
+          torch.empty((qw.T, qw.Hq), dtype=torch.float32, device=dev),
+          torch.empty((qw.T, qw.Hk, qw.D), dtype=torch.uint8, device=dev),
+          torch.empty((qw.T, qw.Hk), dtype=torch.float32, device=dev))
+    res[f"qk_fp8_{qw.T}x{qw.Hq}x{qw.Hk}x{qw.D}_us"] = round(graph_us(
+        lambda i: rq.qk_gemma_rmsnorm_gate_fp8(qg[i % nq], kk[i % nq], qd["q_w"], qd["k_w"], qw.Hq, qw.Hk, qw.D,
+                                               qw.eps, q_out=o8[0], q_scale_out=o8[1], k_out=o8[2],
+                                               k_scale_out=o8[3], gate_out=outs[2])), 3)
     res["pages_context_us"] = {"qk_gemma_rmsnorm_gate_kernel_mi355x_tp2": 4.6, "launch_floor_gfx950": 4.2}
+    return res
+
+
+def qk_fp8_bytes(T: int, Hq: int, Hk: int, D: int) -> int:
+    """qg, k and both weights read; FP8 q and k, their per-head fp32 scales and
+    the bf16 gate written."""
+    return 2 * (T * 2 * Hq * D + T * Hk * D + 2 * D) + T * (Hq + Hk) * D + 4 * T * (Hq + Hk) + 2 * T * Hq * D
+
+
+def qk_prefill(torch, rq, dev, T: int = 8192, Hq: int = 16, Hk: int = 2, D: int = 256, calls: int = 24):
+    """Both QK entry points at a prefill batch (T tokens), GB/s of algorithmic
+    bytes: a graph of `calls` back-to-back calls over 3 rotating input sets
+    (400 MiB, more than the Infinity Cache), one uploaded replay timed."""
+    nsets = 3
+    gen = torch.Generator(device="cpu").manual_seed(1007)
+    qg = [torch.randn((T, 2 * Hq * D), generator=gen).to(torch.bfloat16).to(dev) for _ in range(nsets)]
+    kk = [torch.randn((T, Hk * D), generator=gen).to(torch.bfloat16).to(dev) for _ in range(nsets)]
+    qw = (0.1 * torch.randn(D, generator=gen)).to(torch.bfloat16).to(dev)
+    kw = (0.1 * torch.randn(D, generator=gen)).to(torch.bfloat16).to(dev)
+    bf = [torch.empty((T, h, D), dtype=torch.bfloat16, device=dev) for h in (Hq, Hk, Hq)]
+    f8 = (torch.empty((T, Hq, D), dtype=torch.uint8, device=dev), torch.empty((T, Hq), dtype=torch.float32, device=dev),
+          torch.empty((T, Hk, D), dtype=torch.uint8, device=dev), torch.empty((T, Hk), dtype=torch.float32, device=dev))
+    fns = {
+        "qk_bf16": (lambda i: rq.qk_gemma_rmsnorm_gate(qg[i % nsets], kk[i % nsets], qw, kw, Hq, Hk, D, 1e-6,
+                                                       q_out=bf[0], k_out=bf[1], gate_out=bf[2]),
+                    qk_bytes(T, Hq, Hk, D)),
+        "qk_fp8": (lambda i: rq.qk_gemma_rmsnorm_gate_fp8(qg[i % nsets], kk[i % nsets], qw, kw, Hq, Hk, D, 1e-6,
+                                                          q_out=f8[0], q_scale_out=f8[1], k_out=f8[2],
+                                                          k_scale_out=f8[3], gate_out=bf[2]),
+                   qk_fp8_bytes(T, Hq, Hk, D)),
+    }
+    res = {"T": T, "Hq": Hq, "Hk": Hk, "D": D}
+    for name, (fn, nbytes) in fns.items():
+        for i in range(nsets):
+            fn(i)
+        torch.cuda.synchronize()
+        g = torch.cuda.CUDAGraph()
+        with torch.cuda.graph(g):
+            for i in range(calls):
+                fn(i)
+        upload_graphs(torch, [g], torch.cuda.current_stream())
+        a, b = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+        a.record()
+        g.replay()
+        b.record()
+        torch.cuda.synchronize()
+        us = 1000.0 * a.elapsed_time(b) / calls
+        gbs = nbytes / (us * 1e-6) / 1e9
+        res[name] = {"us": round(us, 3), "bytes": nbytes, "GBps": round(gbs, 1),
+                     "frac_of_peak": round(gbs / HBM_PEAK_GBS, 4)}
     return res
 
 

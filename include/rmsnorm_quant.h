@@ -212,6 +212,30 @@ rq_status qk_gemma_rmsnorm_gate(
     int64_t D, float eps, uint16_t* q_out, uint16_t* k_out, uint16_t* gate_out,
     void* stream);
 
+/* QK GemmaRMSNorm + gate de-interleave with FP8 q and k.  The step above,
+ * followed by the downstream quantization of the attention inputs that the
+ * pages fuse elsewhere into the step before a quantized consumer (sglang PR
+ * #29723, Motivation; sgl-amd-mono PR #26 commit notes on the FP8 copy of the
+ * next attention input).  Each normalized bf16 head (bit-identical to what
+ * qk_gemma_rmsnorm_gate writes) is one granule of the per-token FP8 rule:
+ * scale = amax / 448 (fp32, IEEE-equal), codes = E4M3FN(v / scale), nearest
+ * even, saturating; an all-zero head has scale 0 and codes +-0.
+ *
+ *  qg, k, q_w, k_w, T, Hq, Hk, D, eps   as for qk_gemma_rmsnorm_gate
+ *  q_codes   [T, Hq, D] uint8 out: E4M3FN codes (8-byte aligned)
+ *  q_scale   [T, Hq] fp32 out: one scale per head of each token
+ *  k_codes   [T, Hk, D] uint8 out; k_scale [T, Hk] fp32 out
+ *  gate_out  [T, Hq, D] bf16 out (copied bit for bit)
+ * Errors as for qk_gemma_rmsnorm_gate; a null or misaligned scale pointer is
+ * RQ_ERR_INVALID / RQ_ERR_UNSUPPORTED, and scales may not overlap any other
+ * buffer.
+ */
+rq_status qk_gemma_rmsnorm_gate_fp8(
+    const uint16_t* qg, int64_t ld_qg, const uint16_t* k, int64_t ld_k,
+    const uint16_t* q_w, const uint16_t* k_w, int64_t T, int64_t Hq, int64_t Hk,
+    int64_t D, float eps, uint8_t* q_codes, float* q_scale, uint8_t* k_codes,
+    float* k_scale, uint16_t* gate_out, void* stream);
+
 /* Static, human-readable name of a status code. */
 const char* rq_status_string(rq_status status);
 

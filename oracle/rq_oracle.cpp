@@ -397,7 +397,11 @@ int rq_ref_qk_gemma_rmsnorm_gate_fp8(
     int64_t D, float eps, uint8_t* q_codes, float* q_scale, uint8_t* k_codes, float* k_scale,
     uint16_t* gate_out) {
   if (T > 0 && (!q_codes || !q_scale || !k_codes || !k_scale)) return 1;
-  std::vector<uint16_t> q_bf16((size_t)(T > 0 ? T : 0) * Hq * D), k_bf16((size_t)(T > 0 ? T : 0) * Hk * D);
+  // At least one element each, so that a side with no heads still passes a
+  // non-null buffer to the step above.
+  const size_t nq = (size_t)(T > 0 ? T : 0) * (size_t)(Hq > 0 ? Hq : 0) * (size_t)D;
+  const size_t nk = (size_t)(T > 0 ? T : 0) * (size_t)(Hk > 0 ? Hk : 0) * (size_t)D;
+  std::vector<uint16_t> q_bf16(nq > 0 ? nq : 1), k_bf16(nk > 0 ? nk : 1);
   int rc = rq_ref_qk_gemma_rmsnorm_gate(qg, ld_qg, k, ld_k, q_w, k_w, T, Hq, Hk, D, eps, q_bf16.data(),
                                         k_bf16.data(), gate_out);
   if (rc != 0) return rc;

@@ -43,6 +43,8 @@ _SIGNATURES = {
     "rmsnorm_quant_fp8_per_group": [_p, _i64, _p, _i64, _p, _i64, _i64, _f32, _i64, _p, _p, _p, _p, _p],
     "rmsnorm_quant_mxfp4": [_p, _i64, _p, _i64, _p, _i64, _i64, _f32, _p, _p, _p, _p, _p],
     "qk_gemma_rmsnorm_gate": [_p, _i64, _p, _i64, _p, _p, _i64, _i64, _i64, _i64, _f32, _p, _p, _p, _p],
+    "qk_gemma_rmsnorm_gate_fp8": [_p, _i64, _p, _i64, _p, _p, _i64, _i64, _i64, _i64, _f32, _p, _p, _p, _p, _p,
+                                  _p],
     "rmsnorm_residual_bf16": [_p, _i64, _p, _i64, _p, _i64, _i64, _f32, _p, _p, _p],
     "quantize_fp8_per_token": [_p, _i64, _i64, _i64, _p, _p, _p],
     "quantize_fp8_per_group": [_p, _i64, _i64, _i64, _i64, _p, _p, _p],
@@ -239,6 +241,42 @@ def qk_gemma_rmsnorm_gate(qg, k, q_w, k_w, num_q_heads: int, num_k_heads: int, h
     if not _check(st, "qk_gemma_rmsnorm_gate"):
         return None
     return q_out, k_out, gate_out
+
+
+def qk_gemma_rmsnorm_gate_fp8(qg, k, q_w, k_w, num_q_heads: int, num_k_heads: int, head_dim: int,
+                              eps: float = 1e-6, *, q_out=None, q_scale_out=None, k_out=None, k_scale_out=None,
+                              gate_out=None, stream=None):
+    """As qk_gemma_rmsnorm_gate, with q and k quantized per head to FP8 E4M3FN.
+    -> (q [T, Hq, D] float8_e4m3fn, q_scale [T, Hq] fp32, k [T, Hk, D] float8_e4m3fn, k_scale [T, Hk] fp32,
+        gate [T, Hq, D] bf16), or None."""
+    ld_qg, ld_k = _rows(qg, "qg", torch.bfloat16), _rows(k, "k", torch.bfloat16)
+    T = qg.shape[0]
+    Hq, Hk, D = num_q_heads, num_k_heads, head_dim
+    if k.shape[0] != T:
+        raise ValueError("qg and k must have the same number of tokens")
+    for name, w in (("q_w", q_w), ("k_w", k_w)):
+        if w.shape != (D,) or w.dtype != torch.bfloat16 or not w.is_contiguous():
+            raise ValueError(f"{name} must be a contiguous [head_dim] bfloat16 tensor")
+    dev = qg.device
+    fp8 = torch.float8_e4m3fn
+    q_out = torch.empty((T, Hq, D), dtype=fp8, device=dev) if q_out is None else q_out
+    k_out = torch.empty((T, Hk, D), dtype=fp8, device=dev) if k_out is None else k_out
+    q_scale_out = torch.empty((T, Hq), dtype=torch.float32, device=dev) if q_scale_out is None else q_scale_out
+    k_scale_out = torch.empty((T, Hk), dtype=torch.float32, device=dev) if k_scale_out is None else k_scale_out
+    gate_out = torch.empty((T, Hq, D), dtype=torch.bfloat16, device=dev) if gate_out is None else gate_out
+    for name, t, shape, dts in (("q_out", q_out, (T, Hq, D), (fp8, torch.uint8)),
+                                ("k_out", k_out, (T, Hk, D), (fp8, torch.uint8)),
+                                ("q_scale_out", q_scale_out, (T, Hq), (torch.float32,)),
+                                ("k_scale_out", k_scale_out, (T, Hk), (torch.float32,)),
+                                ("gate_out", gate_out, (T, Hq, D), (torch.bfloat16,))):
+        if tuple(t.shape) != shape or t.dtype not in dts or not t.is_contiguous():
+            raise ValueError(f"{name} must be a contiguous {list(shape)} tensor of {dts[0]}")
+    st = lib().qk_gemma_rmsnorm_gate_fp8(
+        _ptr(qg), ld_qg, _ptr(k), ld_k, _ptr(q_w), _ptr(k_w), T, Hq, Hk, D, eps, _ptr(q_out), _ptr(q_scale_out),
+        _ptr(k_out), _ptr(k_scale_out), _ptr(gate_out), _stream(stream, qg))
+    if not _check(st, "qk_gemma_rmsnorm_gate_fp8"):
+        return None
+    return q_out, q_scale_out, k_out, k_scale_out, gate_out
 
 
 # ---- the unfused sequence, one launch per step ----

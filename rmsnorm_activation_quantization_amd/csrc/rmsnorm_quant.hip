@@ -567,9 +567,13 @@ struct QKArgs {
   const uint16_t* k;
   const uint16_t* qw;
   const uint16_t* kw;
-  uint16_t* q_out;
+  uint16_t* q_out;     // bf16 outputs (kFp8 false)
   uint16_t* k_out;
   uint16_t* gate_out;
+  uint8_t* q_codes;    // per-head FP8 outputs (kFp8 true)
+  uint8_t* k_codes;
+  float* q_scale;
+  float* k_scale;
   int64_t ld_qg;
   int64_t ld_k;
   int64_t units;  // T * (Hq + Hk) heads to normalize
@@ -583,7 +587,10 @@ struct QKArgs {
 constexpr int kQKBlock = 64;  // one wave a workgroup: spreads a small decode batch over many CUs
 
 // kLog2Lanes: lanes per head = 2^kLog2Lanes >= D / 8; 64 >> kLog2Lanes heads a wave.
-template <int kLog2Lanes>
+// kFp8: write each normalized q and k head as E4M3FN codes with one fp32 scale
+// (amax / 448) per head instead of bf16; the bf16 head it quantizes is the
+// one the bf16 variant writes, bit for bit.
+template <int kLog2Lanes, bool kFp8>
 __global__ __launch_bounds__(kQKBlock) void qk_gemma_gate(const QKArgs a) {
   constexpr int kLanesPerHead = 1 << kLog2Lanes;
   constexpr int kHeadsPerWave = kWave / kLanesPerHead;
@@ -637,14 +644,24 @@ __global__ __launch_bounds__(kQKBlock) void qk_gemma_gate(const QKArgs a) {
   for (int j = 0; j < 4; ++j)
     p[j] = pack_bf16((bf_lo(vs[j]) * rstd) * (1.0f + bf_lo(ws[j])),
                      (bf_hi(vs[j]) * rstd) * (1.0f + bf_hi(ws[j])));
-  if (active) {
-    const uint4 out = make_uint4(p[0], p[1], p[2], p[3]);
-    if (is_q) {
-      const int64_t o = (tok * a.Hq + h) * (int64_t)a.D + col;
-      *reinterpret_cast<uint4*>(a.q_out + o) = out;
-      *reinterpret_cast<uint4*>(a.gate_out + o) = gate;
-    } else {
-      *reinterpret_cast<uint4*>(a.k_out + (tok * a.Hk + (h - a.Hq)) * (int64_t)a.D + col) = out;
+  const uint4 out = make_uint4(p[0], p[1], p[2], p[3]);
+  const int64_t head = is_q ? tok * a.Hq + h : tok * a.Hk + (h - a.Hq);  // in the contiguous q or k output
+  const int64_t o = head * a.D + col;
+  if constexpr (!kFp8) {
+    if (active) {
+      *reinterpret_cast<uint4*>((is_q ? a.q_out : a.k_out) + o) = out;
+      if (is_q) *reinterpret_cast<uint4*>(a.gate_out + o) = gate;
+    }
+  } else {
+    // The head's lanes form an aligned group; lanes past D (and heads past
+    // the end) hold zeros, which leave the maximum unchanged.
+    const uint32_t m = group_max(chunk_abs_max(out), kLog2Lanes);
+    const Fp8Granule g = fp8_granule<Bf16>(m);
+    const uint2 codes = fp8_codes<Bf16>(out, g);
+    if (active) {
+      *reinterpret_cast<uint2*>((is_q ? a.q_codes : a.k_codes) + o) = codes;
+      if (is_q) *reinterpret_cast<uint4*>(a.gate_out + o) = gate;
+      if (col == 0) (is_q ? a.q_scale : a.k_scale)[head] = g.scale;
     }
   }
 }
@@ -667,8 +684,12 @@ struct RowKernels {
       RowKernelsW<E, kMode, kStage, 1>::k, RowKernelsW<E, kMode, kStage, 2>::k, RowKernelsW<E, kMode, kStage, 4>::k,
       RowKernelsW<E, kMode, kStage, 8>::k, RowKernelsW<E, kMode, kStage, 16>::k};
 };
-constexpr QKKernel kQKKernels[7] = {&qk_gemma_gate<0>, &qk_gemma_gate<1>, &qk_gemma_gate<2>, &qk_gemma_gate<3>,
-                                    &qk_gemma_gate<4>, &qk_gemma_gate<5>, &qk_gemma_gate<6>};
+template <bool kFp8>
+struct QKKernels {
+  static constexpr QKKernel k[7] = {&qk_gemma_gate<0, kFp8>, &qk_gemma_gate<1, kFp8>, &qk_gemma_gate<2, kFp8>,
+                                    &qk_gemma_gate<3, kFp8>, &qk_gemma_gate<4, kFp8>, &qk_gemma_gate<5, kFp8>,
+                                    &qk_gemma_gate<6, kFp8>};
+};
 
 // ---------------------------------------------------------------------------
 // Host-side preflight
@@ -923,6 +944,59 @@ rq_status quant_mxfp4_impl(const uint16_t* y, int64_t ldy, int64_t M, int64_t H,
   return launch_rows<E, kMxfp4, kStageQuantize>(a, stream);
 }
 
+// Checks and launch of both QK variants.  q_dst / k_dst are the q and k
+// outputs (bf16 rows, or FP8 codes with the scales already in `a`).
+template <bool kFp8>
+rq_status qk_impl(const uint16_t* qg, int64_t ld_qg, const uint16_t* k, int64_t ld_k, const uint16_t* q_w,
+                  const uint16_t* k_w, int64_t T, int64_t Hq, int64_t Hk, int64_t D, float eps, QKArgs& a,
+                  const void* q_dst, const void* k_dst, uint16_t* gate_out, void* stream) {
+  constexpr int kOutBytes = kFp8 ? 1 : 2;  // bytes per q or k output element
+  if (T < 0 || Hq < 0 || Hk < 0 || D <= 0 || !(eps >= 0.0f)) return RQ_ERR_INVALID;
+  if (ld_qg < 2 * Hq * D || ld_k < Hk * D) return RQ_ERR_INVALID;
+  const bool any_q = T > 0 && Hq > 0, any_k = T > 0 && Hk > 0;
+  if (any_q && (!qg || !q_w || !q_dst || !gate_out || (kFp8 && !a.q_scale))) return RQ_ERR_INVALID;
+  if (any_k && (!k || !k_w || !k_dst || (kFp8 && !a.k_scale))) return RQ_ERR_INVALID;
+  if (D % 8 != 0 || D > RQ_MAX_HEAD_DIM || T > INT32_MAX) return RQ_ERR_UNSUPPORTED;
+  if (!any_q && !any_k) return RQ_OK;
+  if ((any_q && (ld_qg % 8 != 0 || !aligned(qg, 16) || !aligned(q_w, 16) || !aligned(q_dst, 8 * kOutBytes) ||
+                 !aligned(gate_out, 16) || (kFp8 && !aligned(a.q_scale, 4)))) ||
+      (any_k && (ld_k % 8 != 0 || !aligned(k, 16) || !aligned(k_w, 16) || !aligned(k_dst, 8 * kOutBytes) ||
+                 (kFp8 && !aligned(a.k_scale, 4)))))
+    return RQ_ERR_UNSUPPORTED;
+  const Span ins[4] = {any_q ? span_of(qg, T, ld_qg, 2 * Hq * D, 2) : Span{0, 0},
+                       any_k ? span_of(k, T, ld_k, Hk * D, 2) : Span{0, 0},
+                       any_q ? span_of(q_w, 1, D, D, 2) : Span{0, 0}, any_k ? span_of(k_w, 1, D, D, 2) : Span{0, 0}};
+  const Span outs[5] = {any_q ? span_of(q_dst, T, Hq * D, Hq * D, kOutBytes) : Span{0, 0},
+                        any_k ? span_of(k_dst, T, Hk * D, Hk * D, kOutBytes) : Span{0, 0},
+                        any_q ? span_of(gate_out, T, Hq * D, Hq * D, 2) : Span{0, 0},
+                        kFp8 && any_q ? span_of(a.q_scale, T, Hq, Hq, 4) : Span{0, 0},
+                        kFp8 && any_k ? span_of(a.k_scale, T, Hk, Hk, 4) : Span{0, 0}};
+  if (!outputs_disjoint(outs, 5, ins, 4, -1, -1)) return RQ_ERR_INVALID;
+  rq_status st = check_device();
+  if (st != RQ_OK) return st;
+
+  int log2_lanes = 0;
+  while ((8 << log2_lanes) < D) ++log2_lanes;
+  a.qg = qg;
+  a.k = k;
+  a.qw = q_w;
+  a.kw = k_w;
+  a.gate_out = gate_out;
+  a.ld_qg = ld_qg;
+  a.ld_k = ld_k;
+  a.units = T * (Hq + Hk);
+  a.Hq = (int)Hq;
+  a.Hk = (int)Hk;
+  a.D = (int)D;
+  a.eps = eps;
+  a.inv_d = 1.0f / (float)D;
+  const int64_t heads_per_wave = kWave >> log2_lanes;
+  const int64_t blocks = (a.units + heads_per_wave - 1) / heads_per_wave;
+  if (blocks > INT32_MAX) return RQ_ERR_UNSUPPORTED;
+  return launch(reinterpret_cast<const void*>(QKKernels<kFp8>::k[log2_lanes]), dim3((unsigned)blocks),
+                dim3(kQKBlock), &a, stream);
+}
+
 }  // namespace
 
 extern "C" {
@@ -980,50 +1054,22 @@ rq_status qk_gemma_rmsnorm_gate(const uint16_t* qg, int64_t ld_qg, const uint16_
                                 const uint16_t* q_w, const uint16_t* k_w, int64_t T, int64_t Hq, int64_t Hk,
                                 int64_t D, float eps, uint16_t* q_out, uint16_t* k_out, uint16_t* gate_out,
                                 void* stream) {
-  if (T < 0 || Hq < 0 || Hk < 0 || D <= 0 || !(eps >= 0.0f)) return RQ_ERR_INVALID;
-  if (ld_qg < 2 * Hq * D || ld_k < Hk * D) return RQ_ERR_INVALID;
-  const bool any_q = T > 0 && Hq > 0, any_k = T > 0 && Hk > 0;
-  if (any_q && (!qg || !q_w || !q_out || !gate_out)) return RQ_ERR_INVALID;
-  if (any_k && (!k || !k_w || !k_out)) return RQ_ERR_INVALID;
-  if (D % 8 != 0 || D > RQ_MAX_HEAD_DIM || T > INT32_MAX) return RQ_ERR_UNSUPPORTED;
-  if (!any_q && !any_k) return RQ_OK;
-  if ((any_q && (ld_qg % 8 != 0 || !aligned(qg, 16) || !aligned(q_w, 16) || !aligned(q_out, 16) ||
-                 !aligned(gate_out, 16))) ||
-      (any_k && (ld_k % 8 != 0 || !aligned(k, 16) || !aligned(k_w, 16) || !aligned(k_out, 16))))
-    return RQ_ERR_UNSUPPORTED;
-  const Span ins[4] = {any_q ? span_of(qg, T, ld_qg, 2 * Hq * D, 2) : Span{0, 0},
-                       any_k ? span_of(k, T, ld_k, Hk * D, 2) : Span{0, 0},
-                       any_q ? span_of(q_w, 1, D, D, 2) : Span{0, 0}, any_k ? span_of(k_w, 1, D, D, 2) : Span{0, 0}};
-  const Span outs[3] = {any_q ? span_of(q_out, T, Hq * D, Hq * D, 2) : Span{0, 0},
-                        any_k ? span_of(k_out, T, Hk * D, Hk * D, 2) : Span{0, 0},
-                        any_q ? span_of(gate_out, T, Hq * D, Hq * D, 2) : Span{0, 0}};
-  if (!outputs_disjoint(outs, 3, ins, 4, -1, -1)) return RQ_ERR_INVALID;
-  rq_status st = check_device();
-  if (st != RQ_OK) return st;
-
-  int log2_lanes = 0;
-  while ((8 << log2_lanes) < D) ++log2_lanes;
-  QKArgs a;
-  a.qg = qg;
-  a.k = k;
-  a.qw = q_w;
-  a.kw = k_w;
+  QKArgs a = {};
   a.q_out = q_out;
   a.k_out = k_out;
-  a.gate_out = gate_out;
-  a.ld_qg = ld_qg;
-  a.ld_k = ld_k;
-  a.units = T * (Hq + Hk);
-  a.Hq = (int)Hq;
-  a.Hk = (int)Hk;
-  a.D = (int)D;
-  a.eps = eps;
-  a.inv_d = 1.0f / (float)D;
-  const int64_t heads_per_wave = kWave >> log2_lanes;
-  const int64_t blocks = (a.units + heads_per_wave - 1) / heads_per_wave;
-  if (blocks > INT32_MAX) return RQ_ERR_UNSUPPORTED;
-  return launch(reinterpret_cast<const void*>(kQKKernels[log2_lanes]), dim3((unsigned)blocks), dim3(kQKBlock), &a,
-                stream);
+  return qk_impl<false>(qg, ld_qg, k, ld_k, q_w, k_w, T, Hq, Hk, D, eps, a, q_out, k_out, gate_out, stream);
+}
+
+rq_status qk_gemma_rmsnorm_gate_fp8(const uint16_t* qg, int64_t ld_qg, const uint16_t* k, int64_t ld_k,
+                                    const uint16_t* q_w, const uint16_t* k_w, int64_t T, int64_t Hq, int64_t Hk,
+                                    int64_t D, float eps, uint8_t* q_codes, float* q_scale, uint8_t* k_codes,
+                                    float* k_scale, uint16_t* gate_out, void* stream) {
+  QKArgs a = {};
+  a.q_codes = q_codes;
+  a.k_codes = k_codes;
+  a.q_scale = q_scale;
+  a.k_scale = k_scale;
+  return qk_impl<true>(qg, ld_qg, k, ld_k, q_w, k_w, T, Hq, Hk, D, eps, a, q_codes, k_codes, gate_out, stream);
 }
 
 const char* rq_status_string(rq_status status) {

@@ -515,6 +515,11 @@ def pin_qk_fp8(ref):
             top = (o[name].reshape(-1, D) & 0x7F).max(axis=1)
             assert (top[np.abs(np_bf16_value(heads.reshape(-1, D))).max(axis=1) > 0] == 0x7E).all()
         assert (o["gate"] == g2).all()
+    # a side with no heads
+    w = inputs.QKWorkload("qk_fp8_no_k", 2, 3, 0, 64, seed=5)
+    d = inputs.qk_inputs(w)
+    o = ref.qk_gemma_rmsnorm_gate_fp8(*(inputs.bits(d[n]) for n in ("qg", "k", "q_w", "k_w")), 3, 0, 64, w.eps)
+    assert o["k"].size == 0 and o["q"].shape == (2, 3, 64)
     # closed form: constant heads with w = 0 normalize to exactly 1 (-1 for k)
     T, Hq, Hk, D = 2, 3, 1, 128
     qg = np_bf16_round(np.full((T, 2 * Hq * D), 3.0))
