@@ -335,24 +335,29 @@ def qk_fp8_bytes(T: int, Hq: int, Hk: int, D: int) -> int:
 
 def qk_prefill(torch, rq, dev, T: int = 8192, Hq: int = 16, Hk: int = 2, D: int = 256, calls: int = 24):
     """Both QK entry points at a prefill batch (T tokens), GB/s of algorithmic
-    bytes: a graph of `calls` back-to-back calls over 3 rotating input sets
-    (400 MiB, more than the Infinity Cache), one uploaded replay timed."""
+    bytes: a graph of `calls` back-to-back calls over 3 rotating sets of inputs
+    and outputs (800 MiB, more than the Infinity Cache), one uploaded replay
+    timed."""
     nsets = 3
     gen = torch.Generator(device="cpu").manual_seed(1007)
     qg = [torch.randn((T, 2 * Hq * D), generator=gen).to(torch.bfloat16).to(dev) for _ in range(nsets)]
     kk = [torch.randn((T, Hk * D), generator=gen).to(torch.bfloat16).to(dev) for _ in range(nsets)]
     qw = (0.1 * torch.randn(D, generator=gen)).to(torch.bfloat16).to(dev)
     kw = (0.1 * torch.randn(D, generator=gen)).to(torch.bfloat16).to(dev)
-    bf = [torch.empty((T, h, D), dtype=torch.bfloat16, device=dev) for h in (Hq, Hk, Hq)]
-    f8 = (torch.empty((T, Hq, D), dtype=torch.uint8, device=dev), torch.empty((T, Hq), dtype=torch.float32, device=dev),
-          torch.empty((T, Hk, D), dtype=torch.uint8, device=dev), torch.empty((T, Hk), dtype=torch.float32, device=dev))
+    # outputs rotate with the inputs, so that no call's writes stay in the cache
+    bf = [[torch.empty((T, h, D), dtype=torch.bfloat16, device=dev) for h in (Hq, Hk, Hq)] for _ in range(nsets)]
+    f8 = [(torch.empty((T, Hq, D), dtype=torch.uint8, device=dev), torch.empty((T, Hq), dtype=torch.float32, device=dev),
+           torch.empty((T, Hk, D), dtype=torch.uint8, device=dev), torch.empty((T, Hk), dtype=torch.float32, device=dev))
+          for _ in range(nsets)]
     fns = {
         "qk_bf16": (lambda i: rq.qk_gemma_rmsnorm_gate(qg[i % nsets], kk[i % nsets], qw, kw, Hq, Hk, D, 1e-6,
-                                                       q_out=bf[0], k_out=bf[1], gate_out=bf[2]),
+                                                       q_out=bf[i % nsets][0], k_out=bf[i % nsets][1],
+                                                       gate_out=bf[i % nsets][2]),
                     qk_bytes(T, Hq, Hk, D)),
         "qk_fp8": (lambda i: rq.qk_gemma_rmsnorm_gate_fp8(qg[i % nsets], kk[i % nsets], qw, kw, Hq, Hk, D, 1e-6,
-                                                          q_out=f8[0], q_scale_out=f8[1], k_out=f8[2],
-                                                          k_scale_out=f8[3], gate_out=bf[2]),
+                                                          q_out=f8[i % nsets][0], q_scale_out=f8[i % nsets][1],
+                                                          k_out=f8[i % nsets][2], k_scale_out=f8[i % nsets][3],
+                                                          gate_out=bf[i % nsets][2]),
                    qk_fp8_bytes(T, Hq, Hk, D)),
     }
     res = {"T": T, "Hq": Hq, "Hk": Hk, "D": D}
