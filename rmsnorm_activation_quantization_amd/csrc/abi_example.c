@@ -5,7 +5,8 @@
  *   code is 0x7E (448 * 1/448 = 1 -> 448); the MXFP4 block maximum 1 gives the
  *   E8M0 byte 125 and every E2M1 code 6 (1 * 2^2 = 4), packed as 0x66;
  *   a QK head of constant 1024 with eps = 0 has rstd = 2^-10 exactly, so with
- *   w = 0 the normalized head is 1.0 and the gate is copied unchanged.
+ *   w = 0 the normalized head is 1.0 and the gate is copied unchanged; its FP8
+ *   variant gives codes 0x7E and scale 1/448 for every head.
  * Prints "abi example ok" and returns 0 on success. */
 #include <hip/hip_runtime_api.h>
 #include <stdint.h>
@@ -117,6 +118,32 @@ int main(void) {
     EXPECT(all_u16(h16, nk, 0x3F80), "normalized k == 1");
     CHECK_HIP(hipMemcpy(h16, go, nq * 2, hipMemcpyDeviceToHost));
     EXPECT(all_u16(h16, nq, 0x4480), "gate copied");
+    /* the FP8 variant: every normalized head is 1, so codes 0x7E and scale 1/448 a head */
+    {
+      uint8_t *qc, *kc;
+      float *qs, *ks;
+      float hq[T * HQ], hk[T * HK];
+      CHECK_HIP(hipMalloc((void**)&qc, nq));
+      CHECK_HIP(hipMalloc((void**)&kc, nk));
+      CHECK_HIP(hipMalloc((void**)&qs, sizeof hq));
+      CHECK_HIP(hipMalloc((void**)&ks, sizeof hk));
+      EXPECT(qk_gemma_rmsnorm_gate_fp8(qg, 2 * HQ * D, k, HK * D, qw, qw, T, HQ, HK, D, 0.0f, qc, qs, kc, ks, go,
+                                       stream) == RQ_OK,
+             "qk fp8 call");
+      EXPECT(qk_gemma_rmsnorm_gate_fp8(qg, 2 * HQ * D, k, HK * D, qw, qw, T, HQ, HK, D, 0.0f, qc, NULL, kc, ks, go,
+                                       stream) == RQ_ERR_INVALID,
+             "qk fp8 without q scales is invalid");
+      CHECK_HIP(hipStreamSynchronize(stream));
+      CHECK_HIP(hipMemcpy(h8, qc, nq, hipMemcpyDeviceToHost));
+      EXPECT(all_u8(h8, nq, 0x7E), "q FP8 codes == 0x7E");
+      CHECK_HIP(hipMemcpy(h8, kc, nk, hipMemcpyDeviceToHost));
+      EXPECT(all_u8(h8, nk, 0x7E), "k FP8 codes == 0x7E");
+      CHECK_HIP(hipMemcpy(hq, qs, sizeof hq, hipMemcpyDeviceToHost));
+      CHECK_HIP(hipMemcpy(hk, ks, sizeof hk, hipMemcpyDeviceToHost));
+      for (int i = 0; i < T * HQ; ++i) EXPECT(hq[i] == 1.0f / 448.0f, "q scale == 1/448");
+      for (int i = 0; i < T * HK; ++i) EXPECT(hk[i] == 1.0f / 448.0f, "k scale == 1/448");
+      hipFree(qc); hipFree(kc); hipFree(qs); hipFree(ks);
+    }
     hipFree(qg); hipFree(k); hipFree(qw); hipFree(qo); hipFree(ko); hipFree(go);
   }
 
