@@ -324,7 +324,11 @@ def decode_latency(torch, rq, inputs, dev, calls: int = 200, replays: int = 7):
         lambda i: rq.qk_gemma_rmsnorm_gate_fp8(qg[i % nq], kk[i % nq], qd["q_w"], qd["k_w"], qw.Hq, qw.Hk, qw.D,
                                                qw.eps, q_out=o8[0], q_scale_out=o8[1], k_out=o8[2],
                                                k_scale_out=o8[3], gate_out=outs[2])), 3)
-    res["pages_context_us"] = {"qk_gemma_rmsnorm_gate_kernel_mi355x_tp2": 4.6, "launch_floor_gfx950": 4.2}
+    # The pages' own MI355X figures, as context (other kernels, other machines' runs): the fused QK
+    # norm + gate kernel per attention layer, the gfx950 launch floor, and the related FlyDSL hc_mix
+    # gate at M = 1, 2, 4, 8, 16 (its Speed Tests table).
+    res["pages_context_us"] = {"qk_gemma_rmsnorm_gate_kernel_mi355x_tp2": 4.6, "launch_floor_gfx950": 4.2,
+                               "hc_mix_gate_mi355x_M1_2_4_8_16": [18.1, 18.8, 20.3, 22.1, 26.3]}
     return res
 
 
