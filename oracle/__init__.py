@@ -94,6 +94,13 @@ class Oracle:
             getattr(lib, "rq_ref_rmsnorm_quant_mxfp4" + sfx).argtypes = row_args + [_u16p, _u8p, _u8p, _u16p]
             getattr(lib, "rq_ref_quantize_fp8" + sfx).argtypes = [_u16p, _i64, _i64, _i64, _u8p, _f32p]
             getattr(lib, "rq_ref_quantize_mxfp4" + sfx).argtypes = [_u16p, _i64, _i64, _u8p, _u8p]
+        for sfx in ("", "_f16"):
+            fn = getattr(lib, "rq_ref_rmsnorm_quant_fp8_per_group_tscale" + sfx)
+            fn.argtypes = row_args + [_i64, _u16p, _u8p, _f32p, _i64, _u16p]
+            fn.restype = ctypes.c_int
+            fn = getattr(lib, "rq_ref_rmsnorm_quant_mxfp4_tscale" + sfx)
+            fn.argtypes = row_args + [_u16p, _u8p, _u8p, _i64, _u16p]
+            fn.restype = ctypes.c_int
         lib.rq_ref_qk_gemma_rmsnorm_gate.argtypes = [
             _u16p, _i64, _u16p, _i64, _u16p, _u16p, _i64, _i64, _i64, _i64, ctypes.c_float,
             _u16p, _u16p, _u16p]
@@ -200,6 +207,37 @@ class Oracle:
         rc = self._fn("rq_ref_rmsnorm_quant_mxfp4", dtype)(
             _ptr(x, _u16p), ldx, _ptr(residual, _u16p), ldr, _ptr(weight, _u16p), M, H, eps,
             _ptr(out["residual_out"], _u16p), _ptr(out["q"], _u8p), _ptr(out["scale"], _u8p),
+            _ptr(out["y"], _u16p))
+        if rc != 0:
+            raise ValueError("oracle rejected the arguments")
+        return out
+
+    # ---- transposed scales: scale (m, g) at [g, m] of a [G, ld_scale] array ----
+    def fp8_per_group_tscale(self, x, residual, weight, eps, group, ld_scale=None, emit_y=False,
+                             dtype="bf16") -> dict:
+        x, ldx, residual, ldr, weight, M, H = self._row_inputs(x, residual, weight)
+        G = H // group if group > 0 else 0
+        ld = M if ld_scale is None else ld_scale
+        out = dict(residual_out=np.zeros((M, H), np.uint16), q=np.zeros((M, H), np.uint8),
+                   scale=np.full((max(G, 1), max(ld, 1)), -1.0, np.float32),
+                   y=np.zeros((M, H), np.uint16) if emit_y else None)
+        rc = self._fn("rq_ref_rmsnorm_quant_fp8_per_group_tscale", dtype)(
+            _ptr(x, _u16p), ldx, _ptr(residual, _u16p), ldr, _ptr(weight, _u16p), M, H, eps,
+            group, _ptr(out["residual_out"], _u16p), _ptr(out["q"], _u8p),
+            _ptr(out["scale"], _f32p), ld, _ptr(out["y"], _u16p))
+        if rc != 0:
+            raise ValueError("oracle rejected the arguments")
+        return out
+
+    def mxfp4_tscale(self, x, residual, weight, eps, ld_scale=None, emit_y=False, dtype="bf16") -> dict:
+        x, ldx, residual, ldr, weight, M, H = self._row_inputs(x, residual, weight)
+        ld = M if ld_scale is None else ld_scale
+        out = dict(residual_out=np.zeros((M, H), np.uint16), q=np.zeros((M, H // 2), np.uint8),
+                   scale=np.full((max(H // 32, 1), max(ld, 1)), 0xAB, np.uint8),
+                   y=np.zeros((M, H), np.uint16) if emit_y else None)
+        rc = self._fn("rq_ref_rmsnorm_quant_mxfp4_tscale", dtype)(
+            _ptr(x, _u16p), ldx, _ptr(residual, _u16p), ldr, _ptr(weight, _u16p), M, H, eps,
+            _ptr(out["residual_out"], _u16p), _ptr(out["q"], _u8p), _ptr(out["scale"], _u8p), ld,
             _ptr(out["y"], _u16p))
         if rc != 0:
             raise ValueError("oracle rejected the arguments")

@@ -304,6 +304,45 @@ int quantize_mxfp4_rows(const Elem& e, const uint16_t* y, int64_t M, int64_t H, 
   return 0;
 }
 
+// The same steps with the scales written column-major: scale (m, g) at
+// scale_out[g * ld_scale + m], ld_scale >= M.  A layout only: the values are
+// those of the row-major functions above, stored transposed.
+template <typename S>
+bool bad_transposed_scales(const S* scale_out, int64_t M, int64_t ld_scale) {
+  return M < 0 || ld_scale < M || ld_scale < 1 || (M > 0 && !scale_out);
+}
+
+template <typename S>
+void store_transposed(const std::vector<S>& row_major, int64_t M, int64_t G, S* scale_out, int64_t ld_scale) {
+  for (int64_t m = 0; m < M; ++m)
+    for (int64_t g = 0; g < G; ++g) scale_out[g * ld_scale + m] = row_major[m * G + g];
+}
+
+int fused_fp8_tscale(const Elem& e, const uint16_t* x, int64_t ldx, const uint16_t* residual, int64_t ldr,
+                     const uint16_t* weight, int64_t M, int64_t H, float eps, int64_t group,
+                     uint16_t* residual_out, uint8_t* q_out, float* scale_out, int64_t ld_scale,
+                     uint16_t* y_out) {
+  if (bad_transposed_scales(scale_out, M, ld_scale) || group <= 0 || H <= 0 || H % group != 0) return 1;
+  const int64_t G = H / group;
+  std::vector<float> rm((size_t)(M > 0 ? M : 0) * G + 1);
+  int rc = fused_fp8(e, x, ldx, residual, ldr, weight, M, H, eps, group, residual_out, q_out, rm.data(), y_out);
+  if (rc != 0) return rc;
+  store_transposed(rm, M, G, scale_out, ld_scale);
+  return 0;
+}
+
+int fused_mxfp4_tscale(const Elem& e, const uint16_t* x, int64_t ldx, const uint16_t* residual, int64_t ldr,
+                       const uint16_t* weight, int64_t M, int64_t H, float eps, uint16_t* residual_out,
+                       uint8_t* q_out, uint8_t* scale_out, int64_t ld_scale, uint16_t* y_out) {
+  if (bad_transposed_scales(scale_out, M, ld_scale) || H <= 0 || H % 32 != 0) return 1;
+  const int64_t B = H / 32;
+  std::vector<uint8_t> rm((size_t)(M > 0 ? M : 0) * B + 1);
+  int rc = fused_mxfp4(e, x, ldx, residual, ldr, weight, M, H, eps, residual_out, q_out, rm.data(), y_out);
+  if (rc != 0) return rc;
+  store_transposed(rm, M, B, scale_out, ld_scale);
+  return 0;
+}
+
 }  // namespace
 
 extern "C" {
@@ -352,6 +391,20 @@ uint16_t rq_ref_f16_from_f64(double v) { return f16_round(v); }
   int rq_ref_quantize_mxfp4##SUFFIX(const uint16_t* y, int64_t M, int64_t H, uint8_t* q_out,        \
                                     uint8_t* scale_out) {                                          \
     return quantize_mxfp4_rows(ELEM, y, M, H, q_out, scale_out);                                   \
+  }                                                                                                \
+  int rq_ref_rmsnorm_quant_fp8_per_group_tscale##SUFFIX(                                            \
+      const uint16_t* x, int64_t ldx, const uint16_t* residual, int64_t ldr, const uint16_t* weight, \
+      int64_t M, int64_t H, float eps, int64_t group, uint16_t* residual_out, uint8_t* q_out,       \
+      float* scale_out, int64_t ld_scale, uint16_t* y_out) {                                       \
+    return fused_fp8_tscale(ELEM, x, ldx, residual, ldr, weight, M, H, eps, group, residual_out,    \
+                            q_out, scale_out, ld_scale, y_out);                                    \
+  }                                                                                                \
+  int rq_ref_rmsnorm_quant_mxfp4_tscale##SUFFIX(                                                    \
+      const uint16_t* x, int64_t ldx, const uint16_t* residual, int64_t ldr, const uint16_t* weight, \
+      int64_t M, int64_t H, float eps, uint16_t* residual_out, uint8_t* q_out, uint8_t* scale_out,  \
+      int64_t ld_scale, uint16_t* y_out) {                                                         \
+    return fused_mxfp4_tscale(ELEM, x, ldx, residual, ldr, weight, M, H, eps, residual_out, q_out,  \
+                              scale_out, ld_scale, y_out);                                         \
   }
 
 RQ_REF_ROW_EXPORTS(, kBf16)

@@ -126,6 +126,30 @@ int rq_ref_quantize_fp8_f16(const uint16_t* y, int64_t M, int64_t H, int64_t gro
 int rq_ref_quantize_mxfp4_f16(const uint16_t* y, int64_t M, int64_t H,
                               uint8_t* q_out, uint8_t* scale_out);
 
+/* ---- transposed scales ----
+ * The fused per-group FP8 and MXFP4 steps with the scales stored
+ * column-major for consumers that read them per group (the scale transpose
+ * for the preshuffled-weight GEMM named in the review of sglang PR #29723):
+ * scale (m, g) at scale_out[g * ld_scale + m], ld_scale >= M; scale_out holds
+ * (H / granule - 1) * ld_scale + M values.  Everything else as above; the
+ * _f16 names take fp16 rows. */
+int rq_ref_rmsnorm_quant_fp8_per_group_tscale(
+    const uint16_t* x, int64_t ldx, const uint16_t* residual, int64_t ldr,
+    const uint16_t* weight, int64_t M, int64_t H, float eps, int64_t group,
+    uint16_t* residual_out, uint8_t* q_out, float* scale_out, int64_t ld_scale, uint16_t* y_out);
+int rq_ref_rmsnorm_quant_mxfp4_tscale(
+    const uint16_t* x, int64_t ldx, const uint16_t* residual, int64_t ldr,
+    const uint16_t* weight, int64_t M, int64_t H, float eps,
+    uint16_t* residual_out, uint8_t* q_out, uint8_t* scale_out, int64_t ld_scale, uint16_t* y_out);
+int rq_ref_rmsnorm_quant_fp8_per_group_tscale_f16(
+    const uint16_t* x, int64_t ldx, const uint16_t* residual, int64_t ldr,
+    const uint16_t* weight, int64_t M, int64_t H, float eps, int64_t group,
+    uint16_t* residual_out, uint8_t* q_out, float* scale_out, int64_t ld_scale, uint16_t* y_out);
+int rq_ref_rmsnorm_quant_mxfp4_tscale_f16(
+    const uint16_t* x, int64_t ldx, const uint16_t* residual, int64_t ldr,
+    const uint16_t* weight, int64_t M, int64_t H, float eps,
+    uint16_t* residual_out, uint8_t* q_out, uint8_t* scale_out, int64_t ld_scale, uint16_t* y_out);
+
 /* ---- the QK variant ---- */
 
 /* qg: [T, ld_qg] with per-token layout [q_0 | gate_0 | q_1 | gate_1 | ...],

@@ -536,6 +536,37 @@ def pin_qk_fp8(ref):
     assert ((o["q"] & 0x7F) == 0).all() and ((o["k"] & 0x7F) == 0).all()
 
 
+def pin_transposed_scales(ref):
+    """Transposed scales: numpy's per-group FP8 and MXFP4 scales, transposed into
+    a [G, ld] array; the padding columns past M are left alone; codes and
+    residual_out as the row-major step."""
+    for dtype, seed in (("bf16", 21), ("fp16", 22)):
+        rnd, _ = NP_CODEC[dtype]
+        rng = np.random.default_rng(seed)
+        M, H, ld = 5, 256, 8
+        xb, rb = rnd(rng.normal(0, 1, (M, H))), rnd(rng.normal(0, 1, (M, H)))
+        wb = rnd(rng.normal(1, 0.1, H))
+        res, y = np_norm(xb, rb, wb, 1e-6, dtype)
+        for group in (32, 128):
+            codes, scale = np_fp8(y, group, dtype)
+            o = ref.fp8_per_group_tscale(xb, rb, wb, 1e-6, group, ld_scale=ld, dtype=dtype)
+            assert (o["q"] == codes).all() and (o["residual_out"] == res).all()
+            assert np.array_equal(o["scale"][:, :M].view(np.uint32), scale.T.view(np.uint32)), \
+                f"{dtype} group {group}: transposed scales differ"
+            assert (o["scale"][:, M:] == -1.0).all(), "the padding past M must not be written"
+        packed, byte = np_mxfp4(y, dtype)
+        o = ref.mxfp4_tscale(xb, rb, wb, 1e-6, ld_scale=ld, dtype=dtype)
+        assert (o["q"] == packed).all() and (o["scale"][:, :M] == byte.T).all()
+        assert (o["scale"][:, M:] == 0xAB).all()
+    # a leading dimension below M is refused
+    try:
+        ref.fp8_per_group_tscale(xb, rb, wb, 1e-6, 32, ld_scale=M - 1)
+    except ValueError:
+        pass
+    else:
+        raise AssertionError("ld_scale < M must be refused")
+
+
 def pin_invariants_on_workloads(ref):
     """On the C1..C3 workloads: the max-|y| element of each granule encodes at
     the top of the format, dequantized codes stay within half a step of y, and
@@ -677,6 +708,7 @@ ALL_PINS = [
     pin_e2m1_table, pin_e2m1_bruteforce, pin_e8m0,
     pin_fp8_weight_probe, pin_mxfp4_weight_probe, pin_group_weight_probe,
     pin_constant_row, pin_zero_and_sign, pin_independent_rows,
-    pin_strided_inputs, pin_qk, pin_qk_fp8, pin_invariants_on_workloads, pin_quantize_step,
+    pin_strided_inputs, pin_qk, pin_qk_fp8, pin_transposed_scales, pin_invariants_on_workloads,
+    pin_quantize_step,
     pin_f16_decode, pin_f16_round, pin_f16_rows, pin_f16_weight_probe,
 ]
