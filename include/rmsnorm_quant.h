@@ -191,6 +191,41 @@ rq_status quantize_mxfp4_f16(
     const uint16_t* y, int64_t ldy, int64_t M, int64_t H,
     uint8_t* q_out, uint8_t* scale_out, void* stream);
 
+/* ---- column-major scales ----
+ * The review of sglang PR #29723 names a transpose of the activation scales
+ * for the GEMM that takes preshuffled weights (_maybe_transpose_aiter_
+ * bpreshuffle_scale) without stating the layout.  Read here as: the scales
+ * stored column-major, one contiguous run of M values per group or block,
+ * with a leading dimension the caller may pad.  The values are exactly those
+ * of the row-major calls; only where they are stored differs:
+ *  scale_out  per-group FP8: fp32 [H / group, ld_scale], scale of row m and
+ *             group g at scale_out[g * ld_scale + m];
+ *             MXFP4: uint8 E8M0 [H / 32, ld_scale], same indexing
+ *  ld_scale   >= max(M, 1); entries past M in each run are not written
+ * Everything else (arguments, layouts of the other outputs, aliasing, errors)
+ * as rmsnorm_quant_fp8_per_group / rmsnorm_quant_mxfp4; ld_scale < 1 or
+ * < M is RQ_ERR_INVALID.  The _f16 names take fp16 rows. */
+rq_status rmsnorm_quant_fp8_per_group_tscale(
+    const uint16_t* x, int64_t ldx, const uint16_t* residual, int64_t ldr,
+    const uint16_t* weight, int64_t M, int64_t H, float eps, int64_t group,
+    uint16_t* residual_out, uint8_t* q_out, float* scale_out, int64_t ld_scale,
+    uint16_t* y_out, void* stream);
+rq_status rmsnorm_quant_mxfp4_tscale(
+    const uint16_t* x, int64_t ldx, const uint16_t* residual, int64_t ldr,
+    const uint16_t* weight, int64_t M, int64_t H, float eps,
+    uint16_t* residual_out, uint8_t* q_out, uint8_t* scale_out, int64_t ld_scale,
+    uint16_t* y_out, void* stream);
+rq_status rmsnorm_quant_fp8_per_group_tscale_f16(
+    const uint16_t* x, int64_t ldx, const uint16_t* residual, int64_t ldr,
+    const uint16_t* weight, int64_t M, int64_t H, float eps, int64_t group,
+    uint16_t* residual_out, uint8_t* q_out, float* scale_out, int64_t ld_scale,
+    uint16_t* y_out, void* stream);
+rq_status rmsnorm_quant_mxfp4_tscale_f16(
+    const uint16_t* x, int64_t ldx, const uint16_t* residual, int64_t ldr,
+    const uint16_t* weight, int64_t M, int64_t H, float eps,
+    uint16_t* residual_out, uint8_t* q_out, uint8_t* scale_out, int64_t ld_scale,
+    uint16_t* y_out, void* stream);
+
 /* QK GemmaRMSNorm + gate de-interleave.  sglang PR #27656 ("Fuse QK RMSNorm +
  * gate extraction Triton kernel for Qwen3.5 on HIP"), Motivation and
  * Modifications: reads q and gate from the interleaved per-token layout

@@ -42,6 +42,8 @@ _SIGNATURES = {
     "rmsnorm_quant_fp8_per_token": [_p, _i64, _p, _i64, _p, _i64, _i64, _f32, _p, _p, _p, _p, _p],
     "rmsnorm_quant_fp8_per_group": [_p, _i64, _p, _i64, _p, _i64, _i64, _f32, _i64, _p, _p, _p, _p, _p],
     "rmsnorm_quant_mxfp4": [_p, _i64, _p, _i64, _p, _i64, _i64, _f32, _p, _p, _p, _p, _p],
+    "rmsnorm_quant_fp8_per_group_tscale": [_p, _i64, _p, _i64, _p, _i64, _i64, _f32, _i64, _p, _p, _p, _i64, _p, _p],
+    "rmsnorm_quant_mxfp4_tscale": [_p, _i64, _p, _i64, _p, _i64, _i64, _f32, _p, _p, _p, _i64, _p, _p],
     "qk_gemma_rmsnorm_gate": [_p, _i64, _p, _i64, _p, _p, _i64, _i64, _i64, _i64, _f32, _p, _p, _p, _p],
     "qk_gemma_rmsnorm_gate_fp8": [_p, _i64, _p, _i64, _p, _p, _i64, _i64, _i64, _i64, _f32, _p, _p, _p, _p, _p,
                                   _p],
@@ -52,6 +54,7 @@ _SIGNATURES = {
 }
 # fp16 variants of the row entry points (same arguments)
 for _name in ("rmsnorm_quant_fp8_per_token", "rmsnorm_quant_fp8_per_group", "rmsnorm_quant_mxfp4",
+              "rmsnorm_quant_fp8_per_group_tscale", "rmsnorm_quant_mxfp4_tscale",
               "quantize_fp8_per_token", "quantize_fp8_per_group", "quantize_mxfp4"):
     _SIGNATURES[_name + "_f16"] = _SIGNATURES[_name]
 _SIGNATURES["rmsnorm_residual_f16"] = _SIGNATURES["rmsnorm_residual_bf16"]
@@ -165,15 +168,31 @@ def _row_outputs(x, residual, weight, residual_out, y_out, emit_y):
     return M, H, residual_out, y_out
 
 
+def _out(t, shape, dtypes, name, like):
+    """A caller-supplied output: the exact shape, one of the dtypes, contiguous,
+    on the device of `like`.  The library cannot see buffer sizes, so a wrong
+    output tensor is refused here rather than written past its end."""
+    if tuple(t.shape) != tuple(shape) or t.dtype not in dtypes or not t.is_contiguous() or t.device != like.device:
+        raise ValueError(f"{name} must be a contiguous {list(shape)} {dtypes[0]} tensor on {like.device}")
+    return t
+
+
+_CODES8 = (torch.uint8, torch.float8_e4m3fn)
+
+
 def rmsnorm_quant_fp8_per_token(x, residual, weight, eps: float = 1e-6, *, residual_out=None, q_out=None,
                                 scale_out=None, emit_y: bool = False, y_out=None, stream=None):
     """-> (q [M, H] float8_e4m3fn, residual_out [M, H] bf16, scale [M, 1] fp32, y or None), or None."""
     ldx, ldr = _rows(x, "x"), _rows(residual, "residual", x.dtype)
     M, H, residual_out, y_out = _row_outputs(x, residual, weight, residual_out, y_out, emit_y)
-    if q_out is None:
-        q_out = torch.empty((M, H), dtype=torch.uint8, device=x.device)
+    q_out = torch.empty((M, H), dtype=torch.uint8, device=x.device) if q_out is None else \
+        _out(q_out, (M, H), _CODES8, "q_out", x)
     if scale_out is None:
         scale_out = torch.empty((M,), dtype=torch.float32, device=x.device)
+    elif tuple(scale_out.shape) not in ((M,), (M, 1)):
+        raise ValueError(f"scale_out must be a contiguous [{M}] or [{M}, 1] float32 tensor")
+    else:
+        _out(scale_out, scale_out.shape, (torch.float32,), "scale_out", x)
     st = _fn("rmsnorm_quant_fp8_per_token", x.dtype)(
         _ptr(x), ldx, _ptr(residual), ldr, _ptr(weight), M, H, eps, _ptr(residual_out), _ptr(q_out),
         _ptr(scale_out), _ptr(y_out), _stream(stream, x))
@@ -187,10 +206,11 @@ def rmsnorm_quant_fp8_per_group(x, residual, weight, eps: float = 1e-6, group: i
     """-> (q [M, H] float8_e4m3fn, residual_out, scale [M, H/group] fp32, y or None), or None."""
     ldx, ldr = _rows(x, "x"), _rows(residual, "residual", x.dtype)
     M, H, residual_out, y_out = _row_outputs(x, residual, weight, residual_out, y_out, emit_y)
-    if q_out is None:
-        q_out = torch.empty((M, H), dtype=torch.uint8, device=x.device)
-    if scale_out is None:
-        scale_out = torch.empty((M, max(H // group, 1) if group > 0 else 1), dtype=torch.float32, device=x.device)
+    G = max(H // group, 1) if group > 0 else 1
+    q_out = torch.empty((M, H), dtype=torch.uint8, device=x.device) if q_out is None else \
+        _out(q_out, (M, H), _CODES8, "q_out", x)
+    scale_out = torch.empty((M, G), dtype=torch.float32, device=x.device) if scale_out is None else \
+        _out(scale_out, (M, G), (torch.float32,), "scale_out", x)
     st = _fn("rmsnorm_quant_fp8_per_group", x.dtype)(
         _ptr(x), ldx, _ptr(residual), ldr, _ptr(weight), M, H, eps, group, _ptr(residual_out), _ptr(q_out),
         _ptr(scale_out), _ptr(y_out), _stream(stream, x))
@@ -204,14 +224,62 @@ def rmsnorm_quant_mxfp4(x, residual, weight, eps: float = 1e-6, *, residual_out=
     """-> (q [M, H/2] uint8 packed E2M1, residual_out, scale [M, H/32] uint8 E8M0, y or None), or None."""
     ldx, ldr = _rows(x, "x"), _rows(residual, "residual", x.dtype)
     M, H, residual_out, y_out = _row_outputs(x, residual, weight, residual_out, y_out, emit_y)
-    if q_out is None:
-        q_out = torch.empty((M, H // 2), dtype=torch.uint8, device=x.device)
-    if scale_out is None:
-        scale_out = torch.empty((M, max(H // 32, 1)), dtype=torch.uint8, device=x.device)
+    q_out = torch.empty((M, H // 2), dtype=torch.uint8, device=x.device) if q_out is None else \
+        _out(q_out, (M, H // 2), (torch.uint8,), "q_out", x)
+    scale_out = torch.empty((M, max(H // 32, 1)), dtype=torch.uint8, device=x.device) if scale_out is None else \
+        _out(scale_out, (M, max(H // 32, 1)), (torch.uint8,), "scale_out", x)
     st = _fn("rmsnorm_quant_mxfp4", x.dtype)(
         _ptr(x), ldx, _ptr(residual), ldr, _ptr(weight), M, H, eps, _ptr(residual_out), _ptr(q_out),
         _ptr(scale_out), _ptr(y_out), _stream(stream, x))
     if not _check(st, "rmsnorm_quant_mxfp4"):
+        return None
+    return q_out, residual_out, scale_out, y_out
+
+
+def _tscale_out(scale_out, rows, M, dtype, x):
+    """Column-major scales: a [rows, n >= M] tensor with unit column stride
+    (a view of a wider buffer is fine); its row stride is ld_scale."""
+    if scale_out is None:
+        scale_out = torch.empty((rows, max(M, 1)), dtype=dtype, device=x.device)
+    if (scale_out.dim() != 2 or scale_out.shape[0] != rows or scale_out.shape[1] < M or scale_out.dtype != dtype
+            or (scale_out.shape[1] > 1 and scale_out.stride(1) != 1) or scale_out.device != x.device):
+        raise ValueError(f"scale_out must be a [{rows}, >= {M}] {dtype} tensor with unit column stride")
+    ld = scale_out.stride(0) if rows > 1 else max(scale_out.shape[1], 1)
+    return scale_out, ld
+
+
+def rmsnorm_quant_fp8_per_group_tscale(x, residual, weight, eps: float = 1e-6, group: int = 128, *,
+                                       residual_out=None, q_out=None, scale_out=None, emit_y: bool = False,
+                                       y_out=None, stream=None):
+    """Per-group FP8 with column-major scales: scale of row m, group g at scale[g, m].
+    -> (q [M, H] float8_e4m3fn, residual_out, scale [H/group, >= M] fp32, y or None), or None."""
+    ldx, ldr = _rows(x, "x"), _rows(residual, "residual", x.dtype)
+    M, H, residual_out, y_out = _row_outputs(x, residual, weight, residual_out, y_out, emit_y)
+    G = max(H // group, 1) if group > 0 else 1
+    q_out = torch.empty((M, H), dtype=torch.uint8, device=x.device) if q_out is None else \
+        _out(q_out, (M, H), _CODES8, "q_out", x)
+    scale_out, ld = _tscale_out(scale_out, G, M, torch.float32, x)
+    st = _fn("rmsnorm_quant_fp8_per_group_tscale", x.dtype)(
+        _ptr(x), ldx, _ptr(residual), ldr, _ptr(weight), M, H, eps, group, _ptr(residual_out), _ptr(q_out),
+        _ptr(scale_out), ld, _ptr(y_out), _stream(stream, x))
+    if not _check(st, "rmsnorm_quant_fp8_per_group_tscale"):
+        return None
+    return q_out.view(torch.float8_e4m3fn), residual_out, scale_out, y_out
+
+
+def rmsnorm_quant_mxfp4_tscale(x, residual, weight, eps: float = 1e-6, *, residual_out=None, q_out=None,
+                               scale_out=None, emit_y: bool = False, y_out=None, stream=None):
+    """MXFP4 with column-major E8M0 scales: block b of row m at scale[b, m].
+    -> (q [M, H/2] uint8 packed E2M1, residual_out, scale [H/32, >= M] uint8, y or None), or None."""
+    ldx, ldr = _rows(x, "x"), _rows(residual, "residual", x.dtype)
+    M, H, residual_out, y_out = _row_outputs(x, residual, weight, residual_out, y_out, emit_y)
+    q_out = torch.empty((M, H // 2), dtype=torch.uint8, device=x.device) if q_out is None else \
+        _out(q_out, (M, H // 2), (torch.uint8,), "q_out", x)
+    scale_out, ld = _tscale_out(scale_out, max(H // 32, 1), M, torch.uint8, x)
+    st = _fn("rmsnorm_quant_mxfp4_tscale", x.dtype)(
+        _ptr(x), ldx, _ptr(residual), ldr, _ptr(weight), M, H, eps, _ptr(residual_out), _ptr(q_out),
+        _ptr(scale_out), ld, _ptr(y_out), _stream(stream, x))
+    if not _check(st, "rmsnorm_quant_mxfp4_tscale"):
         return None
     return q_out, residual_out, scale_out, y_out
 
@@ -300,8 +368,14 @@ def _quant_input(y):
 def quantize_fp8_per_token(y, *, q_out=None, scale_out=None, stream=None):
     """-> (q [M, H] float8_e4m3fn, scale [M, 1] fp32), or None."""
     ldy, M, H = _quant_input(y)
-    q_out = torch.empty((M, H), dtype=torch.uint8, device=y.device) if q_out is None else q_out
-    scale_out = torch.empty((M,), dtype=torch.float32, device=y.device) if scale_out is None else scale_out
+    q_out = torch.empty((M, H), dtype=torch.uint8, device=y.device) if q_out is None else \
+        _out(q_out, (M, H), _CODES8, "q_out", y)
+    if scale_out is None:
+        scale_out = torch.empty((M,), dtype=torch.float32, device=y.device)
+    elif tuple(scale_out.shape) not in ((M,), (M, 1)):
+        raise ValueError(f"scale_out must be a contiguous [{M}] or [{M}, 1] float32 tensor")
+    else:
+        _out(scale_out, scale_out.shape, (torch.float32,), "scale_out", y)
     st = _fn("quantize_fp8_per_token", y.dtype)(_ptr(y), ldy, M, H, _ptr(q_out), _ptr(scale_out), _stream(stream, y))
     if not _check(st, "quantize_fp8_per_token"):
         return None
@@ -311,9 +385,11 @@ def quantize_fp8_per_token(y, *, q_out=None, scale_out=None, stream=None):
 def quantize_fp8_per_group(y, group: int = 128, *, q_out=None, scale_out=None, stream=None):
     """-> (q [M, H] float8_e4m3fn, scale [M, H/group] fp32), or None."""
     ldy, M, H = _quant_input(y)
-    q_out = torch.empty((M, H), dtype=torch.uint8, device=y.device) if q_out is None else q_out
-    if scale_out is None:
-        scale_out = torch.empty((M, max(H // group, 1) if group > 0 else 1), dtype=torch.float32, device=y.device)
+    G = max(H // group, 1) if group > 0 else 1
+    q_out = torch.empty((M, H), dtype=torch.uint8, device=y.device) if q_out is None else \
+        _out(q_out, (M, H), _CODES8, "q_out", y)
+    scale_out = torch.empty((M, G), dtype=torch.float32, device=y.device) if scale_out is None else \
+        _out(scale_out, (M, G), (torch.float32,), "scale_out", y)
     st = _fn("quantize_fp8_per_group", y.dtype)(_ptr(y), ldy, M, H, group, _ptr(q_out), _ptr(scale_out), _stream(stream, y))
     if not _check(st, "quantize_fp8_per_group"):
         return None
@@ -323,9 +399,10 @@ def quantize_fp8_per_group(y, group: int = 128, *, q_out=None, scale_out=None, s
 def quantize_mxfp4(y, *, q_out=None, scale_out=None, stream=None):
     """-> (q [M, H/2] uint8 packed E2M1, scale [M, H/32] uint8 E8M0), or None."""
     ldy, M, H = _quant_input(y)
-    q_out = torch.empty((M, H // 2), dtype=torch.uint8, device=y.device) if q_out is None else q_out
-    if scale_out is None:
-        scale_out = torch.empty((M, max(H // 32, 1)), dtype=torch.uint8, device=y.device)
+    q_out = torch.empty((M, H // 2), dtype=torch.uint8, device=y.device) if q_out is None else \
+        _out(q_out, (M, H // 2), (torch.uint8,), "q_out", y)
+    scale_out = torch.empty((M, max(H // 32, 1)), dtype=torch.uint8, device=y.device) if scale_out is None else \
+        _out(scale_out, (M, max(H // 32, 1)), (torch.uint8,), "scale_out", y)
     st = _fn("quantize_mxfp4", y.dtype)(_ptr(y), ldy, M, H, _ptr(q_out), _ptr(scale_out), _stream(stream, y))
     if not _check(st, "quantize_mxfp4"):
         return None
@@ -342,3 +419,5 @@ rmsnorm_residual_f16 = rmsnorm_residual_bf16
 quantize_fp8_per_token_f16 = quantize_fp8_per_token
 quantize_fp8_per_group_f16 = quantize_fp8_per_group
 quantize_mxfp4_f16 = quantize_mxfp4
+rmsnorm_quant_fp8_per_group_tscale_f16 = rmsnorm_quant_fp8_per_group_tscale
+rmsnorm_quant_mxfp4_tscale_f16 = rmsnorm_quant_mxfp4_tscale

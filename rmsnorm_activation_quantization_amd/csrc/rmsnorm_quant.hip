@@ -335,6 +335,7 @@ struct RowArgs {
   float inv_h;           // 1 / H, rounded on the host
   int group_log2_lanes;  // per-group FP8: log2(group / 8)
   int groups_per_row;    // per-group FP8: H / group
+  int64_t scale_ld;      // per-group FP8 and MXFP4: 0 for row-major scales, else scale (m, g) at g * scale_ld + m
 };
 
 // Sum of a row from per-lane piece sums (one per chunk): each 64-lane block
@@ -540,8 +541,11 @@ __global__ __launch_bounds__(block_threads<kWPR>()) void fused_rows(const RowArg
       const uint2 codes = fp8_codes<E>(yp[c], g);
       if (live && (c < kNC - 1 || col < H)) {
         store8<kNT>(a.q + row * H + col, codes);
-        if ((t & ((1 << gl) - 1)) == 0)
-          reinterpret_cast<float*>(a.scale)[row * a.groups_per_row + (col >> (gl + 3))] = g.scale;
+        if ((t & ((1 << gl) - 1)) == 0) {
+          const int64_t gi = col >> (gl + 3);
+          reinterpret_cast<float*>(a.scale)[a.scale_ld ? gi * a.scale_ld + row : row * a.groups_per_row + gi] =
+              g.scale;
+        }
       }
     }
   } else {
@@ -553,7 +557,11 @@ __global__ __launch_bounds__(block_threads<kWPR>()) void fused_rows(const RowArg
       const uint32_t codes = mxfp4_codes<E>(yp[c], byte);
       if (live && (c < kNC - 1 || col < H)) {
         store4<kNT>(a.q + row * (H / 2) + col / 2, codes);
-        if ((t & 3) == 0) reinterpret_cast<uint8_t*>(a.scale)[row * (H / 32) + col / 32] = (uint8_t)byte;
+        if ((t & 3) == 0) {
+          const int64_t bi = col / 32;
+          reinterpret_cast<uint8_t*>(a.scale)[a.scale_ld ? bi * a.scale_ld + row : row * (H / 32) + bi] =
+              (uint8_t)byte;
+        }
       }
     }
   }
@@ -743,8 +751,9 @@ rq_status row_preflight(const uint16_t* x, int64_t ldx, const uint16_t* residual
                         const uint16_t* weight, int64_t M, int64_t H, float eps,
                         const uint16_t* residual_out, const uint8_t* q_out, const void* scale_out,
                         int64_t scale_count, int64_t scale_bytes, const uint16_t* y_out,
-                        int64_t granule, int code_bits) {
+                        int64_t granule, int code_bits, int64_t scale_ld = 0) {
   if (M < 0 || H <= 0 || !(eps >= 0.0f) || ldx < H || ldr < H) return RQ_ERR_INVALID;
+  if (scale_ld < 0 || (scale_ld > 0 && scale_ld < M)) return RQ_ERR_INVALID;
   if (M > 0 && (!x || !residual || !weight || !residual_out || !q_out || !scale_out)) return RQ_ERR_INVALID;
   if (H % 8 != 0 || H > RQ_MAX_HIDDEN || M > INT32_MAX) return RQ_ERR_UNSUPPORTED;
   if (granule <= 0 || H % granule != 0) return RQ_ERR_UNSUPPORTED;
@@ -754,8 +763,10 @@ rq_status row_preflight(const uint16_t* x, int64_t ldx, const uint16_t* residual
       !aligned(scale_out, scale_bytes))
     return RQ_ERR_UNSUPPORTED;
   const Span ins[3] = {span_of(x, M, ldx, H, 2), span_of(residual, M, ldr, H, 2), span_of(weight, 1, H, H, 2)};
+  const Span scales = scale_ld > 0 ? span_of(scale_out, scale_count, scale_ld, M, scale_bytes)  // [G, scale_ld]
+                                   : span_of(scale_out, M, scale_count, scale_count, scale_bytes);
   const Span outs[4] = {span_of(residual_out, M, H, H, 2), span_of(q_out, M, H * code_bits / 8, H * code_bits / 8, 1),
-                        span_of(scale_out, M, scale_count, scale_count, scale_bytes), span_of(y_out, M, H, H, 2)};
+                        scales, span_of(y_out, M, H, H, 2)};
   if (!outputs_disjoint(outs, 4, ins, 3, /*inplace_out=*/0, /*inplace_in=*/1)) return RQ_ERR_INVALID;
   return check_device();
 }
@@ -861,6 +872,7 @@ RowArgs make_row_args(const uint16_t* x, int64_t ldx, const uint16_t* residual, 
   a.inv_h = 1.0f / (float)H;
   a.group_log2_lanes = 0;
   a.groups_per_row = 0;
+  a.scale_ld = 0;
   return a;
 }
 
@@ -876,31 +888,35 @@ rq_status fp8_per_token_impl(const uint16_t* x, int64_t ldx, const uint16_t* res
   return launch_rows<E, kFp8Token>(a, stream);
 }
 
+// scale_ld: 0 for row-major scales [M, H / granule]; otherwise the leading
+// dimension (>= M) of column-major scales [H / granule, scale_ld].
 template <typename E>
 rq_status fp8_per_group_impl(const uint16_t* x, int64_t ldx, const uint16_t* residual, int64_t ldr,
                              const uint16_t* weight, int64_t M, int64_t H, float eps, int64_t group,
                              uint16_t* residual_out, uint8_t* q_out, float* scale_out, uint16_t* y_out,
-                             void* stream) {
+                             void* stream, int64_t scale_ld = 0) {
   if (group <= 0) return RQ_ERR_INVALID;
   const int log2_lanes = group_log2_lanes(group);
   const int64_t granule = log2_lanes < 0 ? -1 : group;
   rq_status st = row_preflight(x, ldx, residual, ldr, weight, M, H, eps, residual_out, q_out, scale_out,
-                               log2_lanes < 0 ? 1 : H / group, 4, y_out, granule, 8);
+                               log2_lanes < 0 ? 1 : H / group, 4, y_out, granule, 8, scale_ld);
   if (st != RQ_OK || M == 0) return st;
   RowArgs a = make_row_args(x, ldx, residual, ldr, weight, M, H, eps, residual_out, q_out, scale_out, y_out);
   a.group_log2_lanes = log2_lanes;
   a.groups_per_row = (int)(H / group);
+  a.scale_ld = scale_ld;
   return launch_rows<E, kFp8Group>(a, stream);
 }
 
 template <typename E>
 rq_status mxfp4_impl(const uint16_t* x, int64_t ldx, const uint16_t* residual, int64_t ldr, const uint16_t* weight,
                      int64_t M, int64_t H, float eps, uint16_t* residual_out, uint8_t* q_out, uint8_t* scale_out,
-                     uint16_t* y_out, void* stream) {
+                     uint16_t* y_out, void* stream, int64_t scale_ld = 0) {
   rq_status st = row_preflight(x, ldx, residual, ldr, weight, M, H, eps, residual_out, q_out, scale_out, H / 32, 1,
-                               y_out, 32, 4);
+                               y_out, 32, 4, scale_ld);
   if (st != RQ_OK || M == 0) return st;
   RowArgs a = make_row_args(x, ldx, residual, ldr, weight, M, H, eps, residual_out, q_out, scale_out, y_out);
+  a.scale_ld = scale_ld;
   return launch_rows<E, kMxfp4>(a, stream);
 }
 
@@ -1033,6 +1049,22 @@ extern "C" {
   rq_status quantize_mxfp4##SUFFIX(const uint16_t* y, int64_t ldy, int64_t M, int64_t H, uint8_t* q_out,          \
                                    uint8_t* scale_out, void* stream) {                                            \
     return quant_mxfp4_impl<E>(y, ldy, M, H, q_out, scale_out, stream);                                            \
+  }                                                                                                                \
+  rq_status rmsnorm_quant_fp8_per_group_tscale##SUFFIX(                                                            \
+      const uint16_t* x, int64_t ldx, const uint16_t* residual, int64_t ldr, const uint16_t* weight, int64_t M,    \
+      int64_t H, float eps, int64_t group, uint16_t* residual_out, uint8_t* q_out, float* scale_out,               \
+      int64_t ld_scale, uint16_t* y_out, void* stream) {                                                           \
+    if (ld_scale < 1) return RQ_ERR_INVALID;                                                                       \
+    return fp8_per_group_impl<E>(x, ldx, residual, ldr, weight, M, H, eps, group, residual_out, q_out, scale_out,  \
+                                 y_out, stream, ld_scale);                                                         \
+  }                                                                                                                \
+  rq_status rmsnorm_quant_mxfp4_tscale##SUFFIX(                                                                    \
+      const uint16_t* x, int64_t ldx, const uint16_t* residual, int64_t ldr, const uint16_t* weight, int64_t M,    \
+      int64_t H, float eps, uint16_t* residual_out, uint8_t* q_out, uint8_t* scale_out, int64_t ld_scale,          \
+      uint16_t* y_out, void* stream) {                                                                             \
+    if (ld_scale < 1) return RQ_ERR_INVALID;                                                                       \
+    return mxfp4_impl<E>(x, ldx, residual, ldr, weight, M, H, eps, residual_out, q_out, scale_out, y_out, stream,   \
+                         ld_scale);                                                                                \
   }
 
 RQ_ROW_EXPORTS(, Bf16)

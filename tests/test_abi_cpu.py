@@ -175,3 +175,45 @@ def test_quant_preflight(lib, fn):
     if fn == "quantize_fp8_per_group":
         assert call(group=96) == rq.RQ_ERR_UNSUPPORTED
         assert call(group=0) == rq.RQ_ERR_INVALID
+
+
+@pytest.mark.parametrize("fn", ["rmsnorm_quant_fp8_per_group_tscale", "rmsnorm_quant_mxfp4_tscale"])
+def test_tscale_preflight(lib, fn):
+    x, r, w, ro, q, s, y = BUF[:7]
+    M, H = 4, 256
+
+    def call(ld, M=M, s=s):
+        if fn == "rmsnorm_quant_fp8_per_group_tscale":
+            return lib.rmsnorm_quant_fp8_per_group_tscale(x, H, r, H, w, M, H, 1e-6, 128, ro, q, s, ld, y, None)
+        return lib.rmsnorm_quant_mxfp4_tscale(x, H, r, H, w, M, H, 1e-6, ro, q, s, ld, None, None)
+
+    assert call(0) == rq.RQ_ERR_INVALID               # no leading dimension
+    assert call(M - 1) == rq.RQ_ERR_INVALID           # below the row count
+    assert call(8, s=None) == rq.RQ_ERR_INVALID
+    # the column-major span [(G - 1) * ld + M] is what must stay clear of the other buffers:
+    # scales starting 4 KiB below the codes with ld = 4096 run into them, with ld = M they do not
+    assert call(4096, s=q - 4096) == rq.RQ_ERR_INVALID
+    assert call(8, s=ro + 64) == rq.RQ_ERR_INVALID    # inside residual_out
+    assert call(1, M=0, s=None) == rq.RQ_OK
+
+
+def test_qk_fp8_preflight(lib):
+    f = lib.qk_gemma_rmsnorm_gate_fp8
+    qg, k, qw, kw, qc, qs, kc, ks, go = BUF[:8] + [A * 9]
+    T, Hq, Hk, D = 64, 16, 2, 256
+    ok = (qg, 2 * Hq * D, k, Hk * D, qw, kw, T, Hq, Hk, D, 1e-6, qc, qs, kc, ks, go, None)
+
+    def call(**kw_):
+        args = list(ok)
+        names = ["qg", "ld_qg", "k", "ld_k", "qw", "kw", "T", "Hq", "Hk", "D", "eps", "qc", "qs", "kc", "ks", "go"]
+        for n, v in kw_.items():
+            args[names.index(n)] = v
+        return f(*args)
+
+    assert call(qs=None) == rq.RQ_ERR_INVALID
+    assert call(ks=None) == rq.RQ_ERR_INVALID
+    assert call(qs=qc + 16) == rq.RQ_ERR_INVALID        # scales inside the codes
+    assert call(qs=qs + 2) == rq.RQ_ERR_UNSUPPORTED     # misaligned fp32 scales
+    assert call(qc=qc + 4) == rq.RQ_ERR_UNSUPPORTED     # codes not 8-byte aligned
+    assert call(T=-1) == rq.RQ_ERR_INVALID
+    assert call(T=0, qg=None, k=None, qw=None, kw=None, qc=None, qs=None, kc=None, ks=None, go=None) == rq.RQ_OK

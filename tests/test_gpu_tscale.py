@@ -1,0 +1,87 @@
+"""GPU parity of the column-major-scale entry points (rmsnorm_quant_fp8_per_group_tscale,
+rmsnorm_quant_mxfp4_tscale and their fp16 names): against the oracle's transposed-scale
+functions, and bit for bit against the row-major calls on the same rows (the same kernel
+computes both; only where the scales are stored differs).  Padding columns of the scale
+array past M must stay untouched."""
+
+from __future__ import annotations
+
+import numpy as np
+import pytest
+import torch
+
+import rmsnorm_activation_quantization_amd as rq
+from rmsnorm_activation_quantization_amd import inputs
+from parity import check_fp8, check_mxfp4, to_np
+
+pytestmark = pytest.mark.gpu
+DEV = "cuda:0"
+CASES = [("bf16", 16, 4096, 128), ("bf16", 16, 7168, 32), ("bf16", 3, 544, 32), ("bf16", 130, 1024, 512),
+         ("bf16", 65, 4096, 64), ("fp16", 17, 2048, 128), ("fp16", 9, 16384, 256), ("bf16", 8192, 4096, 128)]
+
+
+def padded(M):
+    return ((M + 3) // 4) * 4 + 4  # a padded leading dimension, as blockwise GEMMs ask for
+
+
+@pytest.mark.parametrize("dtype,M,H,group", CASES, ids=[f"{d}-{m}x{h}-g{g}" for d, m, h, g in CASES])
+def test_tscale_fp8_group(ref, dtype, M, H, group):
+    tdt = torch.float16 if dtype == "fp16" else torch.bfloat16
+    d = inputs.random_rows(M, H, seed=M * 31 + H + group, dtype=tdt)
+    x, r, w = (d[k].to(DEV) for k in ("x", "residual", "weight"))
+    G, ld = H // group, padded(M)
+    buf = torch.full((G, ld), -7.0, dtype=torch.float32, device=DEV)
+    out = rq.rmsnorm_quant_fp8_per_group_tscale(x, r, w, 1e-6, group, scale_out=buf, emit_y=True)
+    row = rq.rmsnorm_quant_fp8_per_group(x, r, w, 1e-6, group, emit_y=True)
+    assert out is not None and row is not None
+    torch.cuda.synchronize()
+    q, ro, sc, y = out
+    assert sc.data_ptr() == buf.data_ptr()
+    assert torch.equal(q.view(torch.uint8), row[0].view(torch.uint8)) and torch.equal(ro, row[1]) and torch.equal(y, row[3])
+    assert torch.equal(sc[:, :M], row[2].t()), "transposed scales differ from the row-major call's"
+    assert (sc[:, M:] == -7.0).all(), "the padding past M was written"
+    if M * H <= 1 << 22:
+        xb, rb, wb = (inputs.bits(d[k]) for k in ("x", "residual", "weight"))
+        o = ref.fp8_per_group_tscale(xb, rb, wb, 1e-6, group, ld_scale=ld, emit_y=True, dtype=dtype)
+        gpu = to_np(dict(q=q, residual_out=ro, y=y))
+        gpu["scale"] = sc[:, :M].t().contiguous().cpu().numpy()
+        want = dict(o, scale=np.ascontiguousarray(o["scale"][:, :M].T))
+        check_fp8(gpu, want, ref.quantize_fp8(gpu["y"], group, dtype=dtype), group, f"tscale {dtype} {M}x{H}")
+
+
+@pytest.mark.parametrize("dtype,M,H,group", CASES, ids=[f"{d}-{m}x{h}" for d, m, h, g in CASES])
+def test_tscale_mxfp4(ref, dtype, M, H, group):
+    tdt = torch.float16 if dtype == "fp16" else torch.bfloat16
+    d = inputs.random_rows(M, H, seed=M * 37 + H, dtype=tdt)
+    x, r, w = (d[k].to(DEV) for k in ("x", "residual", "weight"))
+    B, ld = H // 32, padded(M)
+    buf = torch.full((B, ld), 0xAB, dtype=torch.uint8, device=DEV)
+    out = rq.rmsnorm_quant_mxfp4_tscale(x, r, w, 1e-6, scale_out=buf, emit_y=True)
+    row = rq.rmsnorm_quant_mxfp4(x, r, w, 1e-6, emit_y=True)
+    assert out is not None and row is not None
+    torch.cuda.synchronize()
+    q, ro, sc, y = out
+    assert torch.equal(q, row[0]) and torch.equal(ro, row[1]) and torch.equal(y, row[3])
+    assert torch.equal(sc[:, :M], row[2].t()), "transposed E8M0 bytes differ from the row-major call's"
+    assert (sc[:, M:] == 0xAB).all(), "the padding past M was written"
+    if M * H <= 1 << 22:
+        xb, rb, wb = (inputs.bits(d[k]) for k in ("x", "residual", "weight"))
+        o = ref.mxfp4_tscale(xb, rb, wb, 1e-6, ld_scale=ld, emit_y=True, dtype=dtype)
+        gpu = to_np(dict(q=q, residual_out=ro, y=y))
+        gpu["scale"] = sc[:, :M].t().contiguous().cpu().numpy()
+        want = dict(o, scale=np.ascontiguousarray(o["scale"][:, :M].T))
+        check_mxfp4(gpu, want, ref.quantize_mxfp4(gpu["y"], dtype=dtype), f"tscale mx {dtype} {M}x{H}")
+
+
+def test_tscale_default_and_errors():
+    d = inputs.random_rows(4, 256, seed=5)
+    x, r, w = (d[k].to(DEV) for k in ("x", "residual", "weight"))
+    q, _, sc, _ = rq.rmsnorm_quant_fp8_per_group_tscale(x, r, w, 1e-6, 64)
+    assert sc.shape == (4, 4)  # [H / group, M] by default
+    with pytest.raises(ValueError):  # fewer columns than rows
+        rq.rmsnorm_quant_mxfp4_tscale(x, r, w, 1e-6, scale_out=torch.empty((8, 3), dtype=torch.uint8, device=DEV))
+    with pytest.raises(ValueError):  # a wrong-sized row-major output is refused before the launch
+        rq.rmsnorm_quant_fp8_per_group(x, r, w, 1e-6, 64, scale_out=torch.empty((4, 3), device=DEV))
+    empty = torch.empty((0, 256), dtype=torch.bfloat16, device=DEV)
+    out = rq.rmsnorm_quant_mxfp4_tscale(empty, empty, w, 1e-6)
+    assert out is not None and out[2].shape == (8, 1)
