@@ -595,6 +595,9 @@ struct QKArgs {
 constexpr int kQKBlock = 64;  // one wave a workgroup: spreads a small decode batch over many CUs
 
 // kLog2Lanes: lanes per head = 2^kLog2Lanes >= D / 8; 64 >> kLog2Lanes heads a wave.
+// q, k and the gate stream through non-temporal loads and stores (8 % faster
+// than cached ones at 8192 tokens on MI355X, the same at decode sizes); the
+// head weights use cached loads.
 // kFp8: write each normalized q and k head as E4M3FN codes with one fp32 scale
 // (amax / 448) per head instead of bf16; the bf16 head it quantizes is the
 // one the bf16 variant writes, bit for bit.
@@ -619,9 +622,9 @@ __global__ __launch_bounds__(kQKBlock) void qk_gemma_gate(const QKArgs a) {
     src = a.k + tok * a.ld_k + (int64_t)a.D * (h - a.Hq) + col;
   }
   if (active) {
-    v = *reinterpret_cast<const uint4*>(src);
+    v = load16<true>(src);  // streaming: non-temporal
     w = *reinterpret_cast<const uint4*>((is_q ? a.qw : a.kw) + col);
-    if (is_q) gate = *reinterpret_cast<const uint4*>(src + a.D);
+    if (is_q) gate = load16<true>(src + a.D);
   }
   const uint32_t vs[4] = {v.x, v.y, v.z, v.w};
   const uint32_t ws[4] = {w.x, w.y, w.z, w.w};
@@ -657,8 +660,8 @@ __global__ __launch_bounds__(kQKBlock) void qk_gemma_gate(const QKArgs a) {
   const int64_t o = head * a.D + col;
   if constexpr (!kFp8) {
     if (active) {
-      *reinterpret_cast<uint4*>((is_q ? a.q_out : a.k_out) + o) = out;
-      if (is_q) *reinterpret_cast<uint4*>(a.gate_out + o) = gate;
+      store16<true>((is_q ? a.q_out : a.k_out) + o, out);
+      if (is_q) store16<true>(a.gate_out + o, gate);
     }
   } else {
     // The head's lanes form an aligned group; lanes past D (and heads past
@@ -667,8 +670,8 @@ __global__ __launch_bounds__(kQKBlock) void qk_gemma_gate(const QKArgs a) {
     const Fp8Granule g = fp8_granule<Bf16>(m);
     const uint2 codes = fp8_codes<Bf16>(out, g);
     if (active) {
-      *reinterpret_cast<uint2*>((is_q ? a.q_codes : a.k_codes) + o) = codes;
-      if (is_q) *reinterpret_cast<uint4*>(a.gate_out + o) = gate;
+      store8<true>((is_q ? a.q_codes : a.k_codes) + o, codes);
+      if (is_q) store16<true>(a.gate_out + o, gate);
       if (col == 0) (is_q ? a.q_scale : a.k_scale)[head] = g.scale;
     }
   }
