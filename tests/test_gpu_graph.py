@@ -4,6 +4,9 @@ reproduce the eager results bit for bit."""
 
 from __future__ import annotations
 
+import hashlib
+
+import numpy as np
 import pytest
 import torch
 
@@ -109,3 +112,59 @@ def test_graph_replay_unfused_and_fp16():
         torch.cuda.synchronize()
         for a, b in zip(bufs, eager):
             assert torch.equal(a.view(torch.uint8), b.view(torch.uint8)), f"replay {i} differs from eager"
+
+
+def test_graph_replay_stress_bitwise():
+    """3000 replays of a captured decode graph (per-group FP8, MXFP4 with
+    column-major scales, QK-FP8), the outputs hashed (SHA-256) every 100
+    replays and compared with the eager result's hash; a one-bit change of a
+    copy must change the hash (positive control of the comparison itself)."""
+    d = inputs.row_inputs(inputs.FP8_GROUP_DECODE)
+    x, r, w = (d[k].to(DEV) for k in ("x", "residual", "weight"))
+    qd = inputs.qk_inputs(inputs.QK_DECODE)
+    qg, k, qw, kw = (qd[n].to(DEV) for n in ("qg", "k", "q_w", "k_w"))
+    M, H = x.shape
+    q8, ro8, s8 = (torch.empty((M, H), dtype=torch.uint8, device=DEV), torch.empty_like(x),
+                   torch.empty((M, H // 128), dtype=torch.float32, device=DEV))
+    q4, ro4, s4 = (torch.empty((M, H // 2), dtype=torch.uint8, device=DEV), torch.empty_like(x),
+                   torch.empty((H // 32, M), dtype=torch.uint8, device=DEV))
+    qc = (torch.empty((64, 16, 256), dtype=torch.uint8, device=DEV), torch.empty((64, 16), device=DEV),
+          torch.empty((64, 2, 256), dtype=torch.uint8, device=DEV), torch.empty((64, 2), device=DEV),
+          torch.empty((64, 16, 256), dtype=torch.bfloat16, device=DEV))
+    outs = [q8, ro8, s8, q4, ro4, s4, *qc]
+
+    def step():
+        assert rq.rmsnorm_quant_fp8_per_group(x, r, w, 1e-6, 128, q_out=q8, residual_out=ro8, scale_out=s8) is not None
+        assert rq.rmsnorm_quant_mxfp4_tscale(x, r, w, 1e-6, q_out=q4, residual_out=ro4, scale_out=s4) is not None
+        assert rq.qk_gemma_rmsnorm_gate_fp8(qg, k, qw, kw, 16, 2, 256, 1e-6, q_out=qc[0], q_scale_out=qc[1],
+                                            k_out=qc[2], k_scale_out=qc[3], gate_out=qc[4]) is not None
+
+    def digest(tensors):
+        h = hashlib.sha256()
+        for t in tensors:
+            h.update(t.contiguous().view(torch.uint8).cpu().numpy().tobytes())
+        return h.hexdigest()
+
+    step()
+    torch.cuda.synchronize()
+    want = digest(outs)
+    flipped = [t.clone() for t in outs]
+    flipped[3].view(torch.uint8).view(-1)[7] ^= 1
+    assert digest(flipped) != want, "the hash comparison must see a one-bit change"
+
+    st = torch.cuda.Stream()
+    st.wait_stream(torch.cuda.current_stream())
+    with torch.cuda.stream(st):
+        step()
+    torch.cuda.current_stream().wait_stream(st)
+    torch.cuda.synchronize()
+    g = torch.cuda.CUDAGraph()
+    with torch.cuda.graph(g):
+        step()
+    for i in range(30):
+        for t in outs:
+            t.zero_()
+        for _ in range(100):
+            g.replay()
+        torch.cuda.synchronize()
+        assert digest(outs) == want, f"outputs differ from the eager result after {100 * (i + 1)} replays"

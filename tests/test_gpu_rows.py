@@ -78,8 +78,11 @@ def test_workload_parity(ref, fmt, wl):
     run_case(ref, fmt, inputs.row_inputs(wl), wl.eps, what=f"{fmt}-{wl.name}")
 
 
+# ragged lengths, and each side of the few-rows tiling switch (one chunk a lane while
+# rows x waves fit one wave per SIMD: M <= 64 at H = 4096, M <= 32 at H = 7168 and 8192)
 SHAPES = [(1, 32), (1, 2048), (3, 520), (15, 4096), (16, 7168), (17, 1056), (63, 4096), (64, 4096), (65, 4096),
-          (65, 7168), (257, 2080), (33, 8192), (70, 8192), (5, 8224), (9, 16384), (100, 16384), (130, 64)]
+          (32, 7168), (33, 7168), (65, 7168), (257, 2080), (32, 8192), (33, 8192), (70, 8192), (5, 8224), (9, 16384),
+          (100, 16384), (130, 64)]
 
 
 @pytest.mark.parametrize("fmt", ["fp8_token", "fp8_group", "mxfp4"])
