@@ -29,7 +29,9 @@
  *    kernels on `stream` (a hipStream_t; NULL = the null stream), so calls may
  *    be captured into a hipGraph.
  *  - Inputs x and residual may be strided views (row stride ldx / ldr in
- *    elements); every output is contiguous.  residual_out may alias residual
+ *    elements); every output is contiguous, except the column-major scale
+ *    arrays of the _tscale calls, which take a leading dimension.
+ *    residual_out may alias residual
  *    exactly (in place) when ldr == H; any other overlap between an output and
  *    any other buffer is rejected.
  *  - Errors are decided by deterministic checks before anything is enqueued,
