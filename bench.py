@@ -69,7 +69,8 @@ def main():
     world = int(os.environ.get("WORLD_SIZE", "1"))
     if args.gpus != 1 or world != 1:
         print(f"bench.py runs on one GPU only (asked for {max(args.gpus, world)}): this path has no multi-GPU "
-              "part; rows shard across GPUs without communication, see DESIGN.md.", file=sys.stderr)
+              "part; its rows shard across GPUs with no communication of their own, and the all-reduce in "
+              "front of it is not built here.", file=sys.stderr)
         sys.exit(2)
 
     import torch
