@@ -38,7 +38,8 @@
  *    so on any error return nothing has been written:
  *      RQ_ERR_INVALID      a null pointer with M > 0, a negative size,
  *                          ld < row length, eps negative or NaN, overlapping
- *                          buffers;
+ *                          buffers, a stride or size whose extent could not
+ *                          be a real buffer (2^48 bytes or more);
  *      RQ_ERR_UNSUPPORTED  the device is not gfx950, a row start is not
  *                          16-byte aligned, H % 8 != 0, H above
  *                          RQ_MAX_HIDDEN, a granule that does not divide H,
@@ -240,6 +241,7 @@ rq_status rmsnorm_quant_mxfp4_tscale_f16(
  *  k         [T, ld_k] bf16, ld_k >= Hk * D; head h at columns [Dh, D(h + 1))
  *  q_w, k_w  [D] bf16 weights, applied as (1 + w)
  *  D         head dimension: a multiple of 8, at most RQ_MAX_HEAD_DIM
+ *  Hq, Hk    heads per token, each at most 65536
  *  q_out     [T, Hq, D] bf16 out; k_out [T, Hk, D]; gate_out [T, Hq, D]
  *            (gate is copied bit for bit)
  */

@@ -592,6 +592,7 @@ struct QKArgs {
   float inv_d;  // 1 / D, rounded on the host
 };
 
+constexpr int64_t kMaxHeads = int64_t(1) << 16;  // q or k heads per token accepted by the QK entry points
 constexpr int kQKBlock = 64;  // one wave a workgroup: spreads a small decode batch over many CUs
 
 // kLog2Lanes: lanes per head = 2^kLog2Lanes >= D / 8; 64 >> kLog2Lanes heads a wave.
@@ -726,17 +727,29 @@ bool aligned(const void* p, uintptr_t n) { return (reinterpret_cast<uintptr_t>(p
 
 struct Span {
   uintptr_t lo, hi;  // [lo, hi) in bytes; empty when lo == hi
+  bool ok;           // false when the extent cannot be a real buffer (it would overflow)
 };
+// No buffer spans 2^48 bytes or more; larger extents (absurd strides or
+// counts) are refused rather than computed with overflow.
+constexpr int64_t kMaxExtentBytes = int64_t(1) << 48;
 Span span_of(const void* p, int64_t rows, int64_t ld, int64_t width, int64_t elem_bytes) {
-  if (!p || rows <= 0 || width <= 0) return {0, 0};
-  uintptr_t lo = reinterpret_cast<uintptr_t>(p);
-  return {lo, lo + (uintptr_t)(((rows - 1) * ld + width) * elem_bytes)};
+  if (!p || rows <= 0 || width <= 0) return {0, 0, true};
+  const int64_t limit = kMaxExtentBytes / elem_bytes;  // in elements
+  if (width > limit || ld < 0 || (rows > 1 && ld > (limit - width) / (rows - 1))) return {0, 0, false};
+  const uintptr_t lo = reinterpret_cast<uintptr_t>(p);
+  const uintptr_t bytes = (uintptr_t)(((rows - 1) * ld + width) * elem_bytes);
+  if (lo + bytes < lo) return {0, 0, false};
+  return {lo, lo + bytes, true};
 }
 bool overlap(const Span& a, const Span& b) { return a.lo < a.hi && b.lo < b.hi && a.lo < b.hi && b.lo < a.hi; }
 
 // Every output must be disjoint from every other buffer, except residual_out
-// aliasing residual exactly (ldr == H).
+// aliasing residual exactly (ldr == H); every extent must be representable.
 bool outputs_disjoint(const Span* outs, int n_out, const Span* ins, int n_in, int inplace_out, int inplace_in) {
+  for (int i = 0; i < n_out; ++i)
+    if (!outs[i].ok) return false;
+  for (int j = 0; j < n_in; ++j)
+    if (!ins[j].ok) return false;
   for (int i = 0; i < n_out; ++i) {
     for (int j = i + 1; j < n_out; ++j)
       if (overlap(outs[i], outs[j])) return false;
@@ -971,25 +984,27 @@ rq_status qk_impl(const uint16_t* qg, int64_t ld_qg, const uint16_t* k, int64_t 
                   const void* q_dst, const void* k_dst, uint16_t* gate_out, void* stream) {
   constexpr int kOutBytes = kFp8 ? 1 : 2;  // bytes per q or k output element
   if (T < 0 || Hq < 0 || Hk < 0 || D <= 0 || !(eps >= 0.0f)) return RQ_ERR_INVALID;
+  // bounded first, so that the products below cannot overflow
+  if (D > RQ_MAX_HEAD_DIM || Hq > kMaxHeads || Hk > kMaxHeads) return RQ_ERR_UNSUPPORTED;
   if (ld_qg < 2 * Hq * D || ld_k < Hk * D) return RQ_ERR_INVALID;
   const bool any_q = T > 0 && Hq > 0, any_k = T > 0 && Hk > 0;
   if (any_q && (!qg || !q_w || !q_dst || !gate_out || (kFp8 && !a.q_scale))) return RQ_ERR_INVALID;
   if (any_k && (!k || !k_w || !k_dst || (kFp8 && !a.k_scale))) return RQ_ERR_INVALID;
-  if (D % 8 != 0 || D > RQ_MAX_HEAD_DIM || T > INT32_MAX) return RQ_ERR_UNSUPPORTED;
+  if (D % 8 != 0 || D > RQ_MAX_HEAD_DIM || T > INT32_MAX || Hq > kMaxHeads || Hk > kMaxHeads) return RQ_ERR_UNSUPPORTED;
   if (!any_q && !any_k) return RQ_OK;
   if ((any_q && (ld_qg % 8 != 0 || !aligned(qg, 16) || !aligned(q_w, 16) || !aligned(q_dst, 8 * kOutBytes) ||
                  !aligned(gate_out, 16) || (kFp8 && !aligned(a.q_scale, 4)))) ||
       (any_k && (ld_k % 8 != 0 || !aligned(k, 16) || !aligned(k_w, 16) || !aligned(k_dst, 8 * kOutBytes) ||
                  (kFp8 && !aligned(a.k_scale, 4)))))
     return RQ_ERR_UNSUPPORTED;
-  const Span ins[4] = {any_q ? span_of(qg, T, ld_qg, 2 * Hq * D, 2) : Span{0, 0},
-                       any_k ? span_of(k, T, ld_k, Hk * D, 2) : Span{0, 0},
-                       any_q ? span_of(q_w, 1, D, D, 2) : Span{0, 0}, any_k ? span_of(k_w, 1, D, D, 2) : Span{0, 0}};
-  const Span outs[5] = {any_q ? span_of(q_dst, T, Hq * D, Hq * D, kOutBytes) : Span{0, 0},
-                        any_k ? span_of(k_dst, T, Hk * D, Hk * D, kOutBytes) : Span{0, 0},
-                        any_q ? span_of(gate_out, T, Hq * D, Hq * D, 2) : Span{0, 0},
-                        kFp8 && any_q ? span_of(a.q_scale, T, Hq, Hq, 4) : Span{0, 0},
-                        kFp8 && any_k ? span_of(a.k_scale, T, Hk, Hk, 4) : Span{0, 0}};
+  const Span ins[4] = {any_q ? span_of(qg, T, ld_qg, 2 * Hq * D, 2) : Span{0, 0, true},
+                       any_k ? span_of(k, T, ld_k, Hk * D, 2) : Span{0, 0, true},
+                       any_q ? span_of(q_w, 1, D, D, 2) : Span{0, 0, true}, any_k ? span_of(k_w, 1, D, D, 2) : Span{0, 0, true}};
+  const Span outs[5] = {any_q ? span_of(q_dst, T, Hq * D, Hq * D, kOutBytes) : Span{0, 0, true},
+                        any_k ? span_of(k_dst, T, Hk * D, Hk * D, kOutBytes) : Span{0, 0, true},
+                        any_q ? span_of(gate_out, T, Hq * D, Hq * D, 2) : Span{0, 0, true},
+                        kFp8 && any_q ? span_of(a.q_scale, T, Hq, Hq, 4) : Span{0, 0, true},
+                        kFp8 && any_k ? span_of(a.k_scale, T, Hk, Hk, 4) : Span{0, 0, true}};
   if (!outputs_disjoint(outs, 5, ins, 4, -1, -1)) return RQ_ERR_INVALID;
   rq_status st = check_device();
   if (st != RQ_OK) return st;

@@ -217,3 +217,20 @@ def test_qk_fp8_preflight(lib):
     assert call(qc=qc + 4) == rq.RQ_ERR_UNSUPPORTED     # codes not 8-byte aligned
     assert call(T=-1) == rq.RQ_ERR_INVALID
     assert call(T=0, qg=None, k=None, qw=None, kw=None, qc=None, qs=None, kc=None, ks=None, go=None) == rq.RQ_OK
+
+
+def test_absurd_extents_are_invalid(lib):
+    """Strides or counts whose extent could not be a real buffer are refused
+    before any arithmetic on them can overflow."""
+    x, r, w, ro, q, s, y = BUF[:7]
+    huge = 1 << 62
+    assert lib.rmsnorm_quant_fp8_per_token(x, huge, r, 256, w, 4, 256, 1e-6, ro, q, s, None, None) == \
+        rq.RQ_ERR_INVALID
+    assert lib.rmsnorm_quant_mxfp4(x, 256, r, 1 << 40, w, 1 << 20, 256, 1e-6, ro, q, s, None, None) == \
+        rq.RQ_ERR_INVALID
+    assert lib.quantize_fp8_per_token(y, huge, 4, 256, q, s, None) == rq.RQ_ERR_INVALID
+    assert lib.rmsnorm_quant_fp8_per_group_tscale(x, 256, r, 256, w, 4, 256, 1e-6, 128, ro, q, s, huge, None,
+                                                  None) == rq.RQ_ERR_INVALID
+    f = lib.qk_gemma_rmsnorm_gate
+    assert f(x, huge, r, 512, w, w, 4, 1, 1, 256, 1e-6, ro, q, y, None) == rq.RQ_ERR_INVALID
+    assert f(x, 1 << 40, r, 1 << 40, w, w, 4, 1 << 40, 1, 256, 1e-6, ro, q, y, None) == rq.RQ_ERR_UNSUPPORTED
