@@ -61,7 +61,65 @@ def parse():
     p.add_argument("--no-decode", action="store_true")
     p.add_argument("--profile-pass", action="store_true",
                    help="short run for rocprofv3: warmup + steps only, plus a 256 MiB device copy for calibration")
+    p.add_argument("--sweep", action="store_true",
+                   help="instead of the step: µs per call and GB/s of the three fused formats over a range of "
+                        "row counts at H = 4096 and 7168 (one JSON line per shape)")
     return p.parse_args()
+
+
+def sweep(torch, rq, dev, calls: int = 50, replays: int = 5):
+    """Row-count sweep of the fused formats: for each [M, H], a graph of `calls`
+    back-to-back calls over rotating input and output sets (at least 512 MiB of
+    inputs, or 1024 sets), median replay / calls.  Inputs ~ N(0, 1), weight
+    ~ N(1, 0.1), drawn on the device from a seeded generator."""
+    import statistics
+    gen = torch.Generator(device=dev).manual_seed(1008)
+    for H in (4096, 7168):
+        w = (1.0 + 0.1 * torch.randn(H, generator=gen, device=dev)).to(torch.bfloat16)
+        for M in (1, 4, 16, 64, 128, 256, 512, 1024, 4096, 8192):
+            n = max(2, min(1024, (512 << 20) // (4 * M * H)))
+            xs = torch.randn((n, M, H), generator=gen, device=dev).to(torch.bfloat16)
+            rs = torch.randn((n, M, H), generator=gen, device=dev).to(torch.bfloat16)
+            no = min(n, 4)
+            ro = torch.empty((no, M, H), dtype=torch.bfloat16, device=dev)
+            q8 = torch.empty((no, M, H), dtype=torch.uint8, device=dev)
+            q4 = torch.empty((no, M, H // 2), dtype=torch.uint8, device=dev)
+            st = torch.empty((no, M), dtype=torch.float32, device=dev)
+            sg = torch.empty((no, M, H // 128), dtype=torch.float32, device=dev)
+            sm = torch.empty((no, M, H // 32), dtype=torch.uint8, device=dev)
+            fns = {
+                "fp8_token": lambda i: rq.rmsnorm_quant_fp8_per_token(
+                    xs[i % n], rs[i % n], w, 1e-6, q_out=q8[i % no], residual_out=ro[i % no], scale_out=st[i % no]),
+                "fp8_group": lambda i: rq.rmsnorm_quant_fp8_per_group(
+                    xs[i % n], rs[i % n], w, 1e-6, 128, q_out=q8[i % no], residual_out=ro[i % no],
+                    scale_out=sg[i % no]),
+                "mxfp4": lambda i: rq.rmsnorm_quant_mxfp4(
+                    xs[i % n], rs[i % n], w, 1e-6, q_out=q4[i % no], residual_out=ro[i % no], scale_out=sm[i % no]),
+            }
+            line = {"M": M, "H": H, "rotating_sets": n}
+            for fmt, fn in fns.items():
+                for i in range(3):
+                    fn(i)
+                torch.cuda.synchronize()
+                g = torch.cuda.CUDAGraph()
+                with torch.cuda.graph(g):
+                    for i in range(calls):
+                        fn(i)
+                upload_graphs(torch, [g], torch.cuda.current_stream())
+                times = []
+                for _ in range(replays):
+                    a, b = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+                    a.record()
+                    g.replay()
+                    b.record()
+                    torch.cuda.synchronize()
+                    times.append(1000.0 * a.elapsed_time(b) / calls)
+                us = statistics.median(times)
+                gbs = row_bytes(fmt, M, H) / (us * 1e-6) / 1e9
+                line[fmt] = {"us": round(us, 3), "GBps": round(gbs, 1), "frac_of_peak": round(gbs / HBM_PEAK_GBS, 4)}
+                del g
+            print(json.dumps(line), flush=True)
+            del xs, rs, ro, q8, q4, st, sg, sm
 
 
 def main():
@@ -81,6 +139,9 @@ def main():
     dev = torch.device("cuda:0")
     rq.lib()
     stream = torch.cuda.current_stream()
+    if args.sweep:
+        sweep(torch, rq, dev)
+        return
 
     # ---- inputs resident in HBM ----
     wl = inputs.PREFILL
