@@ -85,3 +85,25 @@ def test_tscale_default_and_errors():
     empty = torch.empty((0, 256), dtype=torch.bfloat16, device=DEV)
     out = rq.rmsnorm_quant_mxfp4_tscale(empty, empty, w, 1e-6)
     assert out is not None and out[2].shape == (8, 1)
+
+
+@pytest.mark.parametrize("M,H", [(8, 4096), (12, 1024), (6, 8192), (64, 2048)])
+def test_tscale_tiny_and_normal_rows_share_a_workgroup(M, H):
+    """Rows whose squares underflow (eps = 0, |r| ~ 2^-70, the rescaled sum) next
+    to ordinary rows in the same multi-row workgroup: the column-major calls
+    take both sums in one exchange and must give the row-major calls' bits."""
+    d = inputs.random_rows(M, H, seed=M + H, dtype=torch.bfloat16)
+    x, r, w = (d[k].to(DEV) for k in ("x", "residual", "weight"))
+    tiny = torch.zeros(M, 1, device=DEV)
+    tiny[0::2] = 1.0
+    scale = torch.where(tiny > 0, torch.tensor(2.0 ** -70, device=DEV), torch.tensor(1.0, device=DEV))
+    x = (x.float() * scale).to(torch.bfloat16)
+    r = (r.float() * scale).to(torch.bfloat16)
+    for tfn, rfn, kw in ((rq.rmsnorm_quant_fp8_per_group_tscale, rq.rmsnorm_quant_fp8_per_group, dict(group=64)),
+                         (rq.rmsnorm_quant_mxfp4_tscale, rq.rmsnorm_quant_mxfp4, {})):
+        a = tfn(x, r, w, 0.0, emit_y=True, **kw)
+        b = rfn(x, r, w, 0.0, emit_y=True, **kw)
+        torch.cuda.synchronize()
+        assert torch.equal(a[3], b[3]) and torch.equal(a[1], b[1]), "y or residual_out differs"
+        assert torch.equal(a[0].view(torch.uint8), b[0].view(torch.uint8)), "codes differ"
+        assert torch.equal(a[2][:, :M], b[2].t()), "scales differ"
