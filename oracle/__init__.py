@@ -114,6 +114,10 @@ class Oracle:
             _u16p, _i64, _u16p, _i64, _u16p, _u16p, _i64, _i64, _i64, _i64, ctypes.c_float,
             _u8p, _f32p, _u8p, _f32p, _u16p]
         lib.rq_ref_qk_gemma_rmsnorm_gate_fp8.restype = ctypes.c_int
+        lib.rq_ref_qk_gemma_rmsnorm_gate_mxfp4.argtypes = [
+            _u16p, _i64, _u16p, _i64, _u16p, _u16p, _i64, _i64, _i64, _i64, ctypes.c_float,
+            _u8p, _u8p, _u8p, _u8p, _u16p]
+        lib.rq_ref_qk_gemma_rmsnorm_gate_mxfp4.restype = ctypes.c_int
 
     def _fn(self, name, dtype):
         if dtype not in ("bf16", "fp16"):
@@ -299,6 +303,26 @@ class Oracle:
             _ptr(qg, _u16p), ld_qg, _ptr(k, _u16p), ld_k, _ptr(q_w, _u16p), _ptr(k_w, _u16p),
             T, Hq, Hk, D, eps, _ptr(out["q"], _u8p), _ptr(out["q_scale"], _f32p), _ptr(out["k"], _u8p),
             _ptr(out["k_scale"], _f32p), _ptr(out["gate"], _u16p))
+        if rc != 0:
+            raise ValueError("oracle rejected the arguments")
+        return out
+
+    def qk_gemma_rmsnorm_gate_mxfp4(self, qg, k, q_w, k_w, Hq, Hk, D, eps) -> dict:
+        """The QK step with per-head MXFP4 outputs: q [T, Hq, D/2] and k [T, Hk, D/2]
+        packed E2M1, q_scale [T, Hq, D/32] and k_scale [T, Hk, D/32] E8M0, gate bf16."""
+        qg, ld_qg = _rows(qg)
+        k, ld_k = _rows(k)
+        T = qg.shape[0]
+        assert k.shape[0] == T
+        q_w = np.ascontiguousarray(q_w, dtype=np.uint16)
+        k_w = np.ascontiguousarray(k_w, dtype=np.uint16)
+        out = dict(q=np.zeros((T, Hq, D // 2), np.uint8), q_scale=np.zeros((T, Hq, D // 32), np.uint8),
+                   k=np.zeros((T, Hk, D // 2), np.uint8), k_scale=np.zeros((T, Hk, D // 32), np.uint8),
+                   gate=np.zeros((T, Hq, D), np.uint16))
+        rc = self.lib.rq_ref_qk_gemma_rmsnorm_gate_mxfp4(
+            _ptr(qg, _u16p), ld_qg, _ptr(k, _u16p), ld_k, _ptr(q_w, _u16p), _ptr(k_w, _u16p),
+            T, Hq, Hk, D, eps, _ptr(out["q"], _u8p), _ptr(out["q_scale"], _u8p), _ptr(out["k"], _u8p),
+            _ptr(out["k_scale"], _u8p), _ptr(out["gate"], _u16p))
         if rc != 0:
             raise ValueError("oracle rejected the arguments")
         return out

@@ -463,4 +463,25 @@ int rq_ref_qk_gemma_rmsnorm_gate_fp8(
   return quantize_fp8_rows(kBf16, k_bf16.data(), T * Hk, D, D, k_codes, k_scale);
 }
 
+// The QK step followed by MXFP4 quantization of the normalized q and k: each
+// bf16 head is a row of D values quantized with one E8M0 scale per 32
+// elements, exactly as the rows of the fused step (D a multiple of 32).
+int rq_ref_qk_gemma_rmsnorm_gate_mxfp4(
+    const uint16_t* qg, int64_t ld_qg, const uint16_t* k, int64_t ld_k,
+    const uint16_t* q_w, const uint16_t* k_w, int64_t T, int64_t Hq, int64_t Hk,
+    int64_t D, float eps, uint8_t* q_codes, uint8_t* q_scale, uint8_t* k_codes, uint8_t* k_scale,
+    uint16_t* gate_out) {
+  if (D <= 0 || D % 32 != 0) return 1;
+  if (T > 0 && (!q_codes || !q_scale || !k_codes || !k_scale)) return 1;
+  const size_t nq = (size_t)(T > 0 ? T : 0) * (size_t)(Hq > 0 ? Hq : 0) * (size_t)D;
+  const size_t nk = (size_t)(T > 0 ? T : 0) * (size_t)(Hk > 0 ? Hk : 0) * (size_t)D;
+  std::vector<uint16_t> q_bf16(nq > 0 ? nq : 1), k_bf16(nk > 0 ? nk : 1);
+  int rc = rq_ref_qk_gemma_rmsnorm_gate(qg, ld_qg, k, ld_k, q_w, k_w, T, Hq, Hk, D, eps, q_bf16.data(),
+                                        k_bf16.data(), gate_out);
+  if (rc != 0) return rc;
+  rc = quantize_mxfp4_rows(kBf16, q_bf16.data(), T * Hq, D, q_codes, q_scale);
+  if (rc != 0) return rc;
+  return quantize_mxfp4_rows(kBf16, k_bf16.data(), T * Hk, D, k_codes, k_scale);
+}
+
 }  // extern "C"

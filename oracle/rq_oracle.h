@@ -173,6 +173,18 @@ int rq_ref_qk_gemma_rmsnorm_gate_fp8(
     int64_t D, float eps, uint8_t* q_codes, float* q_scale, uint8_t* k_codes, float* k_scale,
     uint16_t* gate_out);
 
+/* The QK step, then MXFP4 quantization of each normalized head: each bf16
+ * head is a row of D values (D a multiple of 32) quantized with one E8M0
+ * byte per 32 elements, as in rq_ref_rmsnorm_quant_mxfp4.
+ * q_codes [T, Hq, D / 2] and k_codes [T, Hk, D / 2] packed E2M1 (element 2j
+ * in the low nibble of byte j); q_scale [T, Hq, D / 32] and
+ * k_scale [T, Hk, D / 32] E8M0 bytes; gate_out as above. */
+int rq_ref_qk_gemma_rmsnorm_gate_mxfp4(
+    const uint16_t* qg, int64_t ld_qg, const uint16_t* k, int64_t ld_k,
+    const uint16_t* q_w, const uint16_t* k_w, int64_t T, int64_t Hq, int64_t Hk,
+    int64_t D, float eps, uint8_t* q_codes, uint8_t* q_scale, uint8_t* k_codes, uint8_t* k_scale,
+    uint16_t* gate_out);
+
 #ifdef __cplusplus
 }
 #endif

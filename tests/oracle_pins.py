@@ -536,6 +536,41 @@ def pin_qk_fp8(ref):
     assert ((o["q"] & 0x7F) == 0).all() and ((o["k"] & 0x7F) == 0).all()
 
 
+def pin_qk_mxfp4(ref):
+    """QK with per-head MXFP4 outputs against numpy (the QK formulation, then the
+    MXFP4 rule on each head's D values), a closed form and a zero head."""
+    for D, ld_pad in ((64, 24), (256, 8)):
+        w = inputs.QKWorkload(f"qk_mx_{D}", 4, 3, 2, D, seed=31 + D)
+        d = inputs.qk_inputs(w, ld_k=2 * D + ld_pad)
+        qg, k, qw, kw = (inputs.bits(d[n]) for n in ("qg", "k", "q_w", "k_w"))
+        o = ref.qk_gemma_rmsnorm_gate_mxfp4(qg, k, qw, kw, w.Hq, w.Hk, w.D, w.eps)
+        q2, k2, g2 = np_qk(qg, k, qw, kw, w.Hq, w.Hk, w.D, w.eps)
+        for name, heads in (("q", q2), ("k", k2)):
+            packed, byte = np_mxfp4(heads.reshape(-1, D))
+            assert (o[name].reshape(-1, D // 2) == packed).all(), f"{name} codes differ from numpy at D={D}"
+            assert (o[name + "_scale"].reshape(-1, D // 32) == byte).all(), f"{name} E8M0 differ at D={D}"
+        assert (o["gate"] == g2).all()
+    # constant heads with w = 0 normalize to 1 (q) and -1 (k): byte 125, codes 6 / 0xE packed 0x66 / 0xEE
+    T, Hq, Hk, D = 2, 2, 1, 128
+    qg = np_bf16_round(np.full((T, 2 * Hq * D), 3.0))
+    k = np_bf16_round(np.full((T, Hk * D), -0.25))
+    z = np.zeros(D, np.uint16)
+    o = ref.qk_gemma_rmsnorm_gate_mxfp4(qg, k, z, z, Hq, Hk, D, 1e-6)
+    assert (o["q"] == 0x66).all() and (o["k"] == 0xEE).all()
+    assert (o["q_scale"] == 125).all() and (o["k_scale"] == 125).all()
+    o = ref.qk_gemma_rmsnorm_gate_mxfp4(np.zeros((1, 2 * D), np.uint16), np.zeros((1, D), np.uint16),
+                                        z, z, 1, 1, D, 1e-6)
+    assert (o["q_scale"] == 0).all() and ((o["q"] & 0x77) == 0).all()
+    # D not a multiple of 32 is refused
+    try:
+        ref.qk_gemma_rmsnorm_gate_mxfp4(np.zeros((1, 2 * 40), np.uint16), np.zeros((1, 40), np.uint16),
+                                        np.zeros(40, np.uint16), np.zeros(40, np.uint16), 1, 1, 40, 1e-6)
+    except ValueError:
+        pass
+    else:
+        raise AssertionError("D % 32 != 0 must be refused")
+
+
 def pin_transposed_scales(ref):
     """Transposed scales: numpy's per-group FP8 and MXFP4 scales, transposed into
     a [G, ld] array; the padding columns past M are left alone; codes and
@@ -708,7 +743,7 @@ ALL_PINS = [
     pin_e2m1_table, pin_e2m1_bruteforce, pin_e8m0,
     pin_fp8_weight_probe, pin_mxfp4_weight_probe, pin_group_weight_probe,
     pin_constant_row, pin_zero_and_sign, pin_independent_rows,
-    pin_strided_inputs, pin_qk, pin_qk_fp8, pin_transposed_scales, pin_invariants_on_workloads,
+    pin_strided_inputs, pin_qk, pin_qk_fp8, pin_qk_mxfp4, pin_transposed_scales, pin_invariants_on_workloads,
     pin_quantize_step,
     pin_f16_decode, pin_f16_round, pin_f16_rows, pin_f16_weight_probe,
 ]

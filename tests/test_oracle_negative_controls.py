@@ -46,6 +46,8 @@ MUTATIONS = {
                                  "quantize_fp8_rows(kBf16, q_bf16.data(), T, Hq * D, Hq * D, q_codes, q_scale)"),
     "tscale_row_major_index": ("scale_out[g * ld_scale + m] = row_major[m * G + g]",
                                "scale_out[m * G + g] = row_major[m * G + g]"),
+    "qk_mxfp4_k_from_q": ("quantize_mxfp4_rows(kBf16, k_bf16.data(), T * Hk, D, k_codes, k_scale)",
+                          "quantize_mxfp4_rows(kBf16, q_bf16.data(), T * Hk, D, k_codes, k_scale)"),
     "qk_fp8_k_from_q": ("quantize_fp8_rows(kBf16, k_bf16.data(), T * Hk, D, D, k_codes, k_scale)",
                         "quantize_fp8_rows(kBf16, q_bf16.data(), T * Hk, D, D, k_codes, k_scale)"),
 }
