@@ -383,6 +383,14 @@ def decode_latency(torch, rq, inputs, dev, calls: int = 200, replays: int = 7):
           torch.empty((qw.T, qw.Hq), dtype=torch.float32, device=dev),
           torch.empty((qw.T, qw.Hk, qw.D), dtype=torch.uint8, device=dev),
           torch.empty((qw.T, qw.Hk), dtype=torch.float32, device=dev))
+    o4 = (torch.empty((qw.T, qw.Hq, qw.D // 2), dtype=torch.uint8, device=dev),
+          torch.empty((qw.T, qw.Hq, qw.D // 32), dtype=torch.uint8, device=dev),
+          torch.empty((qw.T, qw.Hk, qw.D // 2), dtype=torch.uint8, device=dev),
+          torch.empty((qw.T, qw.Hk, qw.D // 32), dtype=torch.uint8, device=dev))
+    res[f"qk_mxfp4_{qw.T}x{qw.Hq}x{qw.Hk}x{qw.D}_us"] = round(graph_us(
+        lambda i: rq.qk_gemma_rmsnorm_gate_mxfp4(qg[i % nq], kk[i % nq], qd["q_w"], qd["k_w"], qw.Hq, qw.Hk, qw.D,
+                                                 qw.eps, q_out=o4[0], q_scale_out=o4[1], k_out=o4[2],
+                                                 k_scale_out=o4[3], gate_out=outs[2])), 3)
     res[f"qk_fp8_{qw.T}x{qw.Hq}x{qw.Hk}x{qw.D}_us"] = round(graph_us(
         lambda i: rq.qk_gemma_rmsnorm_gate_fp8(qg[i % nq], kk[i % nq], qd["q_w"], qd["k_w"], qw.Hq, qw.Hk, qw.D,
                                                qw.eps, q_out=o8[0], q_scale_out=o8[1], k_out=o8[2],
@@ -401,6 +409,12 @@ def qk_fp8_bytes(T: int, Hq: int, Hk: int, D: int) -> int:
     return 2 * (T * 2 * Hq * D + T * Hk * D + 2 * D) + T * (Hq + Hk) * D + 4 * T * (Hq + Hk) + 2 * T * Hq * D
 
 
+def qk_mxfp4_bytes(T: int, Hq: int, Hk: int, D: int) -> int:
+    """qg, k and both weights read; packed E2M1 q and k, their E8M0 bytes and the
+    bf16 gate written."""
+    return 2 * (T * 2 * Hq * D + T * Hk * D + 2 * D) + T * (Hq + Hk) * (D // 2 + D // 32) + 2 * T * Hq * D
+
+
 def qk_prefill(torch, rq, dev, T: int = 8192, Hq: int = 16, Hk: int = 2, D: int = 256, calls: int = 24):
     """Both QK entry points at a prefill batch (T tokens), GB/s of algorithmic
     bytes: a graph of `calls` back-to-back calls over 3 rotating sets of inputs
@@ -417,6 +431,10 @@ def qk_prefill(torch, rq, dev, T: int = 8192, Hq: int = 16, Hk: int = 2, D: int 
     f8 = [(torch.empty((T, Hq, D), dtype=torch.uint8, device=dev), torch.empty((T, Hq), dtype=torch.float32, device=dev),
            torch.empty((T, Hk, D), dtype=torch.uint8, device=dev), torch.empty((T, Hk), dtype=torch.float32, device=dev))
           for _ in range(nsets)]
+    f4 = [(torch.empty((T, Hq, D // 2), dtype=torch.uint8, device=dev),
+           torch.empty((T, Hq, D // 32), dtype=torch.uint8, device=dev),
+           torch.empty((T, Hk, D // 2), dtype=torch.uint8, device=dev),
+           torch.empty((T, Hk, D // 32), dtype=torch.uint8, device=dev)) for _ in range(nsets)]
     fns = {
         "qk_bf16": (lambda i: rq.qk_gemma_rmsnorm_gate(qg[i % nsets], kk[i % nsets], qw, kw, Hq, Hk, D, 1e-6,
                                                        q_out=bf[i % nsets][0], k_out=bf[i % nsets][1],
@@ -427,6 +445,11 @@ def qk_prefill(torch, rq, dev, T: int = 8192, Hq: int = 16, Hk: int = 2, D: int 
                                                           k_out=f8[i % nsets][2], k_scale_out=f8[i % nsets][3],
                                                           gate_out=bf[i % nsets][2]),
                    qk_fp8_bytes(T, Hq, Hk, D)),
+        "qk_mxfp4": (lambda i: rq.qk_gemma_rmsnorm_gate_mxfp4(qg[i % nsets], kk[i % nsets], qw, kw, Hq, Hk, D, 1e-6,
+                                                              q_out=f4[i % nsets][0], q_scale_out=f4[i % nsets][1],
+                                                              k_out=f4[i % nsets][2], k_scale_out=f4[i % nsets][3],
+                                                              gate_out=bf[i % nsets][2]),
+                     qk_mxfp4_bytes(T, Hq, Hk, D)),
     }
     res = {"T": T, "Hq": Hq, "Hk": Hk, "D": D}
     for name, (fn, nbytes) in fns.items():

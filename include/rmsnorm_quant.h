@@ -275,6 +275,25 @@ rq_status qk_gemma_rmsnorm_gate_fp8(
     int64_t D, float eps, uint8_t* q_codes, float* q_scale, uint8_t* k_codes,
     float* k_scale, uint16_t* gate_out, void* stream);
 
+/* QK GemmaRMSNorm + gate de-interleave with MXFP4 q and k: each normalized
+ * bf16 head (bit-identical to what qk_gemma_rmsnorm_gate writes) is
+ * quantized as an MXFP4 row of D values, exactly as rmsnorm_quant_mxfp4
+ * quantizes y (one E8M0 byte per 32 elements, E2M1 codes two per byte).
+ *
+ *  qg, k, q_w, k_w, T, Hq, Hk, eps   as for qk_gemma_rmsnorm_gate
+ *  D         a multiple of 32, at most RQ_MAX_HEAD_DIM (else RQ_ERR_UNSUPPORTED)
+ *  q_codes   [T, Hq, D / 2] uint8 out (4-byte aligned): element 2j of a head
+ *            in the low nibble of byte j
+ *  q_scale   [T, Hq, D / 32] uint8 out: E8M0 bytes
+ *  k_codes   [T, Hk, D / 2] uint8 out; k_scale [T, Hk, D / 32] uint8 out
+ *  gate_out  [T, Hq, D] bf16 out (copied bit for bit)
+ * Errors as for qk_gemma_rmsnorm_gate_fp8. */
+rq_status qk_gemma_rmsnorm_gate_mxfp4(
+    const uint16_t* qg, int64_t ld_qg, const uint16_t* k, int64_t ld_k,
+    const uint16_t* q_w, const uint16_t* k_w, int64_t T, int64_t Hq, int64_t Hk,
+    int64_t D, float eps, uint8_t* q_codes, uint8_t* q_scale, uint8_t* k_codes,
+    uint8_t* k_scale, uint16_t* gate_out, void* stream);
+
 /* Static, human-readable name of a status code. */
 const char* rq_status_string(rq_status status);
 

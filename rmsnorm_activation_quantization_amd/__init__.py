@@ -11,6 +11,7 @@ that ABI.  Entry points keep the C names:
                                 the same with column-major scales [groups, >= M]
   qk_gemma_rmsnorm_gate         QK GemmaRMSNorm + gate de-interleave
   qk_gemma_rmsnorm_gate_fp8     ... with q and k as FP8 E4M3FN, one scale per head
+  qk_gemma_rmsnorm_gate_mxfp4   ... with q and k as MXFP4, one E8M0 scale per 32 elements
 
 and the unfused sequence, one launch per step (bit-identical results):
 
@@ -22,7 +23,8 @@ dtype (the _f16 names are the same functions, named after the C entry points).
 """
 
 from .binding import (RQ_ERR_HIP, RQ_ERR_INVALID, RQ_ERR_UNSUPPORTED, RQ_MAX_HEAD_DIM, RQ_MAX_HIDDEN, RQ_OK,
-                      lib, library_path, qk_gemma_rmsnorm_gate, qk_gemma_rmsnorm_gate_fp8, quantize_fp8_per_group,
+                      lib, library_path, qk_gemma_rmsnorm_gate, qk_gemma_rmsnorm_gate_fp8, qk_gemma_rmsnorm_gate_mxfp4,
+                      quantize_fp8_per_group,
                       rmsnorm_quant_fp8_per_group_tscale, rmsnorm_quant_fp8_per_group_tscale_f16,
                       rmsnorm_quant_mxfp4_tscale, rmsnorm_quant_mxfp4_tscale_f16, quantize_fp8_per_group_f16,
                       quantize_fp8_per_token, quantize_fp8_per_token_f16, quantize_mxfp4, quantize_mxfp4_f16,
@@ -32,7 +34,7 @@ from .binding import (RQ_ERR_HIP, RQ_ERR_INVALID, RQ_ERR_UNSUPPORTED, RQ_MAX_HEA
 
 __all__ = [
     "rmsnorm_quant_fp8_per_token", "rmsnorm_quant_fp8_per_group", "rmsnorm_quant_mxfp4", "qk_gemma_rmsnorm_gate",
-    "qk_gemma_rmsnorm_gate_fp8", "rmsnorm_quant_fp8_per_group_tscale", "rmsnorm_quant_mxfp4_tscale",
+    "qk_gemma_rmsnorm_gate_fp8", "qk_gemma_rmsnorm_gate_mxfp4", "rmsnorm_quant_fp8_per_group_tscale", "rmsnorm_quant_mxfp4_tscale",
     "rmsnorm_quant_fp8_per_group_tscale_f16", "rmsnorm_quant_mxfp4_tscale_f16",
     "rmsnorm_residual_bf16", "quantize_fp8_per_token", "quantize_fp8_per_group", "quantize_mxfp4",
     "rmsnorm_quant_fp8_per_token_f16", "rmsnorm_quant_fp8_per_group_f16", "rmsnorm_quant_mxfp4_f16",

@@ -47,6 +47,8 @@ _SIGNATURES = {
     "qk_gemma_rmsnorm_gate": [_p, _i64, _p, _i64, _p, _p, _i64, _i64, _i64, _i64, _f32, _p, _p, _p, _p],
     "qk_gemma_rmsnorm_gate_fp8": [_p, _i64, _p, _i64, _p, _p, _i64, _i64, _i64, _i64, _f32, _p, _p, _p, _p, _p,
                                   _p],
+    "qk_gemma_rmsnorm_gate_mxfp4": [_p, _i64, _p, _i64, _p, _p, _i64, _i64, _i64, _i64, _f32, _p, _p, _p, _p, _p,
+                                    _p],
     "rmsnorm_residual_bf16": [_p, _i64, _p, _i64, _p, _i64, _i64, _f32, _p, _p, _p],
     "quantize_fp8_per_token": [_p, _i64, _i64, _i64, _p, _p, _p],
     "quantize_fp8_per_group": [_p, _i64, _i64, _i64, _i64, _p, _p, _p],
@@ -345,6 +347,40 @@ def qk_gemma_rmsnorm_gate_fp8(qg, k, q_w, k_w, num_q_heads: int, num_k_heads: in
     if not _check(st, "qk_gemma_rmsnorm_gate_fp8"):
         return None
     return q_out, q_scale_out, k_out, k_scale_out, gate_out
+
+
+def qk_gemma_rmsnorm_gate_mxfp4(qg, k, q_w, k_w, num_q_heads: int, num_k_heads: int, head_dim: int,
+                                eps: float = 1e-6, *, q_out=None, q_scale_out=None, k_out=None, k_scale_out=None,
+                                gate_out=None, stream=None):
+    """As qk_gemma_rmsnorm_gate, with q and k quantized to MXFP4 (head_dim a multiple of 32).
+    -> (q [T, Hq, D/2] uint8 packed E2M1, q_scale [T, Hq, D/32] uint8 E8M0, k [T, Hk, D/2], k_scale [T, Hk, D/32],
+        gate [T, Hq, D] bf16), or None."""
+    ld_qg, ld_k = _rows(qg, "qg", torch.bfloat16), _rows(k, "k", torch.bfloat16)
+    T = qg.shape[0]
+    Hq, Hk, D = num_q_heads, num_k_heads, head_dim
+    if k.shape[0] != T:
+        raise ValueError("qg and k must have the same number of tokens")
+    for name, w in (("q_w", q_w), ("k_w", k_w)):
+        if w.shape != (D,) or w.dtype != torch.bfloat16 or not w.is_contiguous():
+            raise ValueError(f"{name} must be a contiguous [head_dim] bfloat16 tensor")
+    dev = qg.device
+    u8 = torch.uint8
+    shapes = {"q_out": (T, Hq, D // 2), "q_scale_out": (T, Hq, max(D // 32, 1)), "k_out": (T, Hk, D // 2),
+              "k_scale_out": (T, Hk, max(D // 32, 1)), "gate_out": (T, Hq, D)}
+    given = {"q_out": q_out, "q_scale_out": q_scale_out, "k_out": k_out, "k_scale_out": k_scale_out,
+             "gate_out": gate_out}
+    outs = {}
+    for name, shape in shapes.items():
+        dt = torch.bfloat16 if name == "gate_out" else u8
+        t = given[name]
+        outs[name] = torch.empty(shape, dtype=dt, device=dev) if t is None else _out(t, shape, (dt,), name, qg)
+    st = lib().qk_gemma_rmsnorm_gate_mxfp4(
+        _ptr(qg), ld_qg, _ptr(k), ld_k, _ptr(q_w), _ptr(k_w), T, Hq, Hk, D, eps, _ptr(outs["q_out"]),
+        _ptr(outs["q_scale_out"]), _ptr(outs["k_out"]), _ptr(outs["k_scale_out"]), _ptr(outs["gate_out"]),
+        _stream(stream, qg))
+    if not _check(st, "qk_gemma_rmsnorm_gate_mxfp4"):
+        return None
+    return outs["q_out"], outs["q_scale_out"], outs["k_out"], outs["k_scale_out"], outs["gate_out"]
 
 
 # ---- the unfused sequence, one launch per step ----

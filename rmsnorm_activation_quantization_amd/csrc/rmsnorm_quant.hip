@@ -575,13 +575,13 @@ struct QKArgs {
   const uint16_t* k;
   const uint16_t* qw;
   const uint16_t* kw;
-  uint16_t* q_out;     // bf16 outputs (kFp8 false)
+  uint16_t* q_out;     // bf16 outputs (kQKBf16)
   uint16_t* k_out;
   uint16_t* gate_out;
-  uint8_t* q_codes;    // per-head FP8 outputs (kFp8 true)
+  uint8_t* q_codes;    // quantized outputs: FP8 codes (kQKFp8) or packed E2M1 (kQKMxfp4)
   uint8_t* k_codes;
-  float* q_scale;
-  float* k_scale;
+  void* q_scale;       // fp32 per head (kQKFp8) or E8M0 bytes per 32 elements (kQKMxfp4)
+  void* k_scale;
   int64_t ld_qg;
   int64_t ld_k;
   int64_t units;  // T * (Hq + Hk) heads to normalize
@@ -593,16 +593,18 @@ struct QKArgs {
 };
 
 constexpr int64_t kMaxHeads = int64_t(1) << 16;  // q or k heads per token accepted by the QK entry points
+enum QKOut { kQKBf16 = 0, kQKFp8 = 1, kQKMxfp4 = 2 };
 constexpr int kQKBlock = 64;  // one wave a workgroup: spreads a small decode batch over many CUs
 
 // kLog2Lanes: lanes per head = 2^kLog2Lanes >= D / 8; 64 >> kLog2Lanes heads a wave.
 // q, k and the gate stream through non-temporal loads and stores (8 % faster
 // than cached ones at 8192 tokens on MI355X, the same at decode sizes); the
 // head weights use cached loads.
-// kFp8: write each normalized q and k head as E4M3FN codes with one fp32 scale
-// (amax / 448) per head instead of bf16; the bf16 head it quantizes is the
-// one the bf16 variant writes, bit for bit.
-template <int kLog2Lanes, bool kFp8>
+// kOut: bf16 heads; or each normalized head quantized, as E4M3FN codes with
+// one fp32 scale (amax / 448) per head (kQKFp8), or as MXFP4 with one E8M0
+// byte per 32 elements (kQKMxfp4).  The bf16 head a quantized variant
+// quantizes is the one the bf16 variant writes, bit for bit.
+template <int kLog2Lanes, int kOut>
 __global__ __launch_bounds__(kQKBlock) void qk_gemma_gate(const QKArgs a) {
   constexpr int kLanesPerHead = 1 << kLog2Lanes;
   constexpr int kHeadsPerWave = kWave / kLanesPerHead;
@@ -659,12 +661,12 @@ __global__ __launch_bounds__(kQKBlock) void qk_gemma_gate(const QKArgs a) {
   const uint4 out = make_uint4(p[0], p[1], p[2], p[3]);
   const int64_t head = is_q ? tok * a.Hq + h : tok * a.Hk + (h - a.Hq);  // in the contiguous q or k output
   const int64_t o = head * a.D + col;
-  if constexpr (!kFp8) {
+  if constexpr (kOut == kQKBf16) {
     if (active) {
       store16<true>((is_q ? a.q_out : a.k_out) + o, out);
       if (is_q) store16<true>(a.gate_out + o, gate);
     }
-  } else {
+  } else if constexpr (kOut == kQKFp8) {
     // The head's lanes form an aligned group; lanes past D (and heads past
     // the end) hold zeros, which leave the maximum unchanged.
     const uint32_t m = group_max(chunk_abs_max(out), kLog2Lanes);
@@ -673,7 +675,17 @@ __global__ __launch_bounds__(kQKBlock) void qk_gemma_gate(const QKArgs a) {
     if (active) {
       store8<true>((is_q ? a.q_codes : a.k_codes) + o, codes);
       if (is_q) store16<true>(a.gate_out + o, gate);
-      if (col == 0) (is_q ? a.q_scale : a.k_scale)[head] = g.scale;
+      if (col == 0) reinterpret_cast<float*>(is_q ? a.q_scale : a.k_scale)[head] = g.scale;
+    }
+  } else {
+    // A 32-element block is four aligned lanes (D is a multiple of 32).
+    const uint32_t m = group_max_c<2>(chunk_abs_max(out));
+    const uint32_t byte = e8m0_byte(Bf16::value(m));
+    const uint32_t codes = mxfp4_codes<Bf16>(out, byte);
+    if (active) {
+      store4<true>((is_q ? a.q_codes : a.k_codes) + o / 2, codes);
+      if (is_q) store16<true>(a.gate_out + o, gate);
+      if ((col & 31) == 0) reinterpret_cast<uint8_t*>(is_q ? a.q_scale : a.k_scale)[o / 32] = (uint8_t)byte;
     }
   }
 }
@@ -696,11 +708,11 @@ struct RowKernels {
       RowKernelsW<E, kMode, kStage, 1>::k, RowKernelsW<E, kMode, kStage, 2>::k, RowKernelsW<E, kMode, kStage, 4>::k,
       RowKernelsW<E, kMode, kStage, 8>::k, RowKernelsW<E, kMode, kStage, 16>::k};
 };
-template <bool kFp8>
+template <int kOut>
 struct QKKernels {
-  static constexpr QKKernel k[7] = {&qk_gemma_gate<0, kFp8>, &qk_gemma_gate<1, kFp8>, &qk_gemma_gate<2, kFp8>,
-                                    &qk_gemma_gate<3, kFp8>, &qk_gemma_gate<4, kFp8>, &qk_gemma_gate<5, kFp8>,
-                                    &qk_gemma_gate<6, kFp8>};
+  static constexpr QKKernel k[7] = {&qk_gemma_gate<0, kOut>, &qk_gemma_gate<1, kOut>, &qk_gemma_gate<2, kOut>,
+                                    &qk_gemma_gate<3, kOut>, &qk_gemma_gate<4, kOut>, &qk_gemma_gate<5, kOut>,
+                                    &qk_gemma_gate<6, kOut>};
 };
 
 // ---------------------------------------------------------------------------
@@ -976,35 +988,41 @@ rq_status quant_mxfp4_impl(const uint16_t* y, int64_t ldy, int64_t M, int64_t H,
   return launch_rows<E, kMxfp4, kStageQuantize>(a, stream);
 }
 
-// Checks and launch of both QK variants.  q_dst / k_dst are the q and k
-// outputs (bf16 rows, or FP8 codes with the scales already in `a`).
-template <bool kFp8>
+// Checks and launch of the QK variants.  q_dst / k_dst are the q and k
+// outputs (bf16 rows, or codes with the scales already in `a`).
+template <int kOut>
 rq_status qk_impl(const uint16_t* qg, int64_t ld_qg, const uint16_t* k, int64_t ld_k, const uint16_t* q_w,
                   const uint16_t* k_w, int64_t T, int64_t Hq, int64_t Hk, int64_t D, float eps, QKArgs& a,
                   const void* q_dst, const void* k_dst, uint16_t* gate_out, void* stream) {
-  constexpr int kOutBytes = kFp8 ? 1 : 2;  // bytes per q or k output element
+  constexpr bool kQuant = kOut != kQKBf16;
   if (T < 0 || Hq < 0 || Hk < 0 || D <= 0 || !(eps >= 0.0f)) return RQ_ERR_INVALID;
   // bounded first, so that the products below cannot overflow
   if (D > RQ_MAX_HEAD_DIM || Hq > kMaxHeads || Hk > kMaxHeads) return RQ_ERR_UNSUPPORTED;
   if (ld_qg < 2 * Hq * D || ld_k < Hk * D) return RQ_ERR_INVALID;
   const bool any_q = T > 0 && Hq > 0, any_k = T > 0 && Hk > 0;
-  if (any_q && (!qg || !q_w || !q_dst || !gate_out || (kFp8 && !a.q_scale))) return RQ_ERR_INVALID;
-  if (any_k && (!k || !k_w || !k_dst || (kFp8 && !a.k_scale))) return RQ_ERR_INVALID;
-  if (D % 8 != 0 || D > RQ_MAX_HEAD_DIM || T > INT32_MAX || Hq > kMaxHeads || Hk > kMaxHeads) return RQ_ERR_UNSUPPORTED;
+  if (any_q && (!qg || !q_w || !q_dst || !gate_out || (kQuant && !a.q_scale))) return RQ_ERR_INVALID;
+  if (any_k && (!k || !k_w || !k_dst || (kQuant && !a.k_scale))) return RQ_ERR_INVALID;
+  if (D % (kOut == kQKMxfp4 ? 32 : 8) != 0 || T > INT32_MAX) return RQ_ERR_UNSUPPORTED;
   if (!any_q && !any_k) return RQ_OK;
-  if ((any_q && (ld_qg % 8 != 0 || !aligned(qg, 16) || !aligned(q_w, 16) || !aligned(q_dst, 8 * kOutBytes) ||
-                 !aligned(gate_out, 16) || (kFp8 && !aligned(a.q_scale, 4)))) ||
-      (any_k && (ld_k % 8 != 0 || !aligned(k, 16) || !aligned(k_w, 16) || !aligned(k_dst, 8 * kOutBytes) ||
-                 (kFp8 && !aligned(a.k_scale, 4)))))
+  // Per head: output bytes, their store alignment, scale bytes and alignment.
+  const int64_t out_b = kOut == kQKBf16 ? 2 * D : (kOut == kQKFp8 ? D : D / 2);
+  const uintptr_t out_align = kOut == kQKBf16 ? 16 : (kOut == kQKFp8 ? 8 : 4);
+  const int64_t sc_b = kOut == kQKFp8 ? 4 : (kOut == kQKMxfp4 ? D / 32 : 0);
+  const uintptr_t sc_align = kOut == kQKFp8 ? 4 : 1;
+  if ((any_q && (ld_qg % 8 != 0 || !aligned(qg, 16) || !aligned(q_w, 16) || !aligned(q_dst, out_align) ||
+                 !aligned(gate_out, 16) || (kQuant && !aligned(a.q_scale, sc_align)))) ||
+      (any_k && (ld_k % 8 != 0 || !aligned(k, 16) || !aligned(k_w, 16) || !aligned(k_dst, out_align) ||
+                 (kQuant && !aligned(a.k_scale, sc_align)))))
     return RQ_ERR_UNSUPPORTED;
-  const Span ins[4] = {any_q ? span_of(qg, T, ld_qg, 2 * Hq * D, 2) : Span{0, 0, true},
-                       any_k ? span_of(k, T, ld_k, Hk * D, 2) : Span{0, 0, true},
-                       any_q ? span_of(q_w, 1, D, D, 2) : Span{0, 0, true}, any_k ? span_of(k_w, 1, D, D, 2) : Span{0, 0, true}};
-  const Span outs[5] = {any_q ? span_of(q_dst, T, Hq * D, Hq * D, kOutBytes) : Span{0, 0, true},
-                        any_k ? span_of(k_dst, T, Hk * D, Hk * D, kOutBytes) : Span{0, 0, true},
-                        any_q ? span_of(gate_out, T, Hq * D, Hq * D, 2) : Span{0, 0, true},
-                        kFp8 && any_q ? span_of(a.q_scale, T, Hq, Hq, 4) : Span{0, 0, true},
-                        kFp8 && any_k ? span_of(a.k_scale, T, Hk, Hk, 4) : Span{0, 0, true}};
+  const Span none{0, 0, true};
+  const Span ins[4] = {any_q ? span_of(qg, T, ld_qg, 2 * Hq * D, 2) : none,
+                       any_k ? span_of(k, T, ld_k, Hk * D, 2) : none,
+                       any_q ? span_of(q_w, 1, D, D, 2) : none, any_k ? span_of(k_w, 1, D, D, 2) : none};
+  const Span outs[5] = {any_q ? span_of(q_dst, T, Hq * out_b, Hq * out_b, 1) : none,
+                        any_k ? span_of(k_dst, T, Hk * out_b, Hk * out_b, 1) : none,
+                        any_q ? span_of(gate_out, T, Hq * D, Hq * D, 2) : none,
+                        kQuant && any_q ? span_of(a.q_scale, T, Hq * sc_b, Hq * sc_b, 1) : none,
+                        kQuant && any_k ? span_of(a.k_scale, T, Hk * sc_b, Hk * sc_b, 1) : none};
   if (!outputs_disjoint(outs, 5, ins, 4, -1, -1)) return RQ_ERR_INVALID;
   rq_status st = check_device();
   if (st != RQ_OK) return st;
@@ -1027,7 +1045,7 @@ rq_status qk_impl(const uint16_t* qg, int64_t ld_qg, const uint16_t* k, int64_t 
   const int64_t heads_per_wave = kWave >> log2_lanes;
   const int64_t blocks = (a.units + heads_per_wave - 1) / heads_per_wave;
   if (blocks > INT32_MAX) return RQ_ERR_UNSUPPORTED;
-  return launch(reinterpret_cast<const void*>(QKKernels<kFp8>::k[log2_lanes]), dim3((unsigned)blocks),
+  return launch(reinterpret_cast<const void*>(QKKernels<kOut>::k[log2_lanes]), dim3((unsigned)blocks),
                 dim3(kQKBlock), &a, stream);
 }
 
@@ -1107,7 +1125,7 @@ rq_status qk_gemma_rmsnorm_gate(const uint16_t* qg, int64_t ld_qg, const uint16_
   QKArgs a = {};
   a.q_out = q_out;
   a.k_out = k_out;
-  return qk_impl<false>(qg, ld_qg, k, ld_k, q_w, k_w, T, Hq, Hk, D, eps, a, q_out, k_out, gate_out, stream);
+  return qk_impl<kQKBf16>(qg, ld_qg, k, ld_k, q_w, k_w, T, Hq, Hk, D, eps, a, q_out, k_out, gate_out, stream);
 }
 
 rq_status qk_gemma_rmsnorm_gate_fp8(const uint16_t* qg, int64_t ld_qg, const uint16_t* k, int64_t ld_k,
@@ -1119,7 +1137,19 @@ rq_status qk_gemma_rmsnorm_gate_fp8(const uint16_t* qg, int64_t ld_qg, const uin
   a.k_codes = k_codes;
   a.q_scale = q_scale;
   a.k_scale = k_scale;
-  return qk_impl<true>(qg, ld_qg, k, ld_k, q_w, k_w, T, Hq, Hk, D, eps, a, q_codes, k_codes, gate_out, stream);
+  return qk_impl<kQKFp8>(qg, ld_qg, k, ld_k, q_w, k_w, T, Hq, Hk, D, eps, a, q_codes, k_codes, gate_out, stream);
+}
+
+rq_status qk_gemma_rmsnorm_gate_mxfp4(const uint16_t* qg, int64_t ld_qg, const uint16_t* k, int64_t ld_k,
+                                      const uint16_t* q_w, const uint16_t* k_w, int64_t T, int64_t Hq, int64_t Hk,
+                                      int64_t D, float eps, uint8_t* q_codes, uint8_t* q_scale, uint8_t* k_codes,
+                                      uint8_t* k_scale, uint16_t* gate_out, void* stream) {
+  QKArgs a = {};
+  a.q_codes = q_codes;
+  a.k_codes = k_codes;
+  a.q_scale = q_scale;
+  a.k_scale = k_scale;
+  return qk_impl<kQKMxfp4>(qg, ld_qg, k, ld_k, q_w, k_w, T, Hq, Hk, D, eps, a, q_codes, k_codes, gate_out, stream);
 }
 
 const char* rq_status_string(rq_status status) {

@@ -234,3 +234,18 @@ def test_absurd_extents_are_invalid(lib):
     f = lib.qk_gemma_rmsnorm_gate
     assert f(x, huge, r, 512, w, w, 4, 1, 1, 256, 1e-6, ro, q, y, None) == rq.RQ_ERR_INVALID
     assert f(x, 1 << 40, r, 1 << 40, w, w, 4, 1 << 40, 1, 256, 1e-6, ro, q, y, None) == rq.RQ_ERR_UNSUPPORTED
+
+
+def test_qk_mxfp4_preflight(lib):
+    f = lib.qk_gemma_rmsnorm_gate_mxfp4
+    qg, k, qw, kw, qc, qs, kc, ks, go = BUF[:8] + [A * 9]
+    T, Hq, Hk, D = 64, 16, 2, 256
+    ok = [qg, 2 * Hq * D, k, Hk * D, qw, kw, T, Hq, Hk, D, 1e-6, qc, qs, kc, ks, go, None]
+    assert f(*ok[:11], qc, None, kc, ks, go, None) == rq.RQ_ERR_INVALID              # q scales missing
+    assert f(*ok[:11], qc, qc + 64, kc, ks, go, None) == rq.RQ_ERR_INVALID           # scales inside the codes
+    assert f(*ok[:11], qc + 2, qs, kc, ks, go, None) == rq.RQ_ERR_UNSUPPORTED        # codes not 4-byte aligned
+    assert f(qg, 2 * Hq * 40, k, Hk * 40, qw, kw, T, Hq, Hk, 40, 1e-6, qc, qs, kc, ks, go, None) == \
+        rq.RQ_ERR_UNSUPPORTED                                                        # D % 32
+    assert f(None, 0, None, 0, None, None, 0, Hq, Hk, D, 1e-6, None, None, None, None, None, None) == rq.RQ_ERR_INVALID
+    assert f(None, 2 * Hq * D, None, Hk * D, None, None, 0, Hq, Hk, D, 1e-6, None, None, None, None, None, None) == \
+        rq.RQ_OK
