@@ -642,11 +642,20 @@ def cpu_baseline(inputs, wl, qw, nbytes):
             elapsed += time.perf_counter() - t0
             reps += 1
     cpu_s = time.process_time() - cpu0
+    # the same oracle on one thread, over one slice of the rows
+    one_rows = max(1, rows // 16)
+    t0 = time.perf_counter()
+    part(0, one_rows)
+    one_s = time.perf_counter() - t0
+    one_bytes = sum(row_bytes(f, one_rows, wl.H) for f in ("fp8_token", "fp8_group", "mxfp4"))
     return {"value": round(reps * step_bytes / elapsed / 1e9, 3), "unit": "GB/s", "cores": threads,
             "kind": "oracle",
             "sample": f"{reps} whole step(s): all {rows} rows of [{rows}, {wl.H}] in the three formats plus the "
                       f"QK case, threaded over row slices",
-            "wall_s": round(elapsed, 3), "cpu_s": round(cpu_s, 2)}
+            "wall_s": round(elapsed, 3), "cpu_s": round(cpu_s, 2),
+            "single_thread": {"value": round(one_bytes / one_s / 1e9, 3), "unit": "GB/s", "cores": 1,
+                              "sample": f"the first {one_rows} rows of [{rows}, {wl.H}] in the three formats",
+                              "wall_s": round(one_s, 3)}}
 
 
 if __name__ == "__main__":
