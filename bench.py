@@ -76,7 +76,7 @@ def sweep(torch, rq, dev, calls: int = 50, replays: int = 5):
     gen = torch.Generator(device=dev).manual_seed(1008)
     for H in (4096, 7168):
         w = (1.0 + 0.1 * torch.randn(H, generator=gen, device=dev)).to(torch.bfloat16)
-        for M in (1, 4, 16, 64, 128, 256, 512, 1024, 4096, 8192):
+        for M in (1, 4, 16, 64, 128, 256, 512, 1024, 2048, 4096, 8192):
             n = max(2, min(1024, (512 << 20) // (4 * M * H)))
             xs = torch.randn((n, M, H), generator=gen, device=dev).to(torch.bfloat16)
             rs = torch.randn((n, M, H), generator=gen, device=dev).to(torch.bfloat16)

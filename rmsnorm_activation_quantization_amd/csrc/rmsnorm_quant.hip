@@ -848,8 +848,8 @@ rq_status launch(const void* kernel, dim3 grid, dim3 block, void* args, void* st
   return err == hipSuccess ? RQ_OK : RQ_ERR_HIP;
 }
 
-// One wave per SIMD over the whole chip (256 CUs x 4 SIMDs).
-constexpr int64_t kChipSimds = 1024;
+// Waves the chip holds at once: 256 CUs x 4 SIMDs x 8 wave slots per SIMD.
+constexpr int64_t kResidentWaves = 256 * 4 * 8;
 
 int chunks_per_lane(int H, int l) {
   const int lanes = kWave << l;
@@ -857,15 +857,17 @@ int chunks_per_lane(int H, int l) {
 }
 
 // Waves per row (a power of two, 1..16).  Many rows: the fewest for which a
-// lane holds at most kMaxChunks chunks of 8 elements (few registers, many waves
-// in flight to cover HBM latency).  Few rows, where the launch cannot fill the
-// chip anyway: more waves, so that a lane holds one chunk, while the launch
-// stays within one wave per SIMD; a lane's dependent chain from load to store
-// is then as short as it gets.  The row's sum is the same for every tiling.
+// lane holds at most kMaxChunks chunks of 8 elements (few registers, and the
+// waves of later rows take the slots that finished ones free).  Fewer rows,
+// where the whole launch fits in the chip's wave slots at once: more waves, so
+// that a lane holds one chunk, as long as the launch still fits; a lane's
+// dependent chain from load to store is then as short as it gets, and there is
+// no second generation of waves to wait for.  The row's sum is the same for
+// every tiling.
 int waves_per_row_log2(int64_t M, int H) {
   int l = 0;
   while (l < 4 && chunks_per_lane(H, l) > kMaxChunks) ++l;
-  while (l < 4 && chunks_per_lane(H, l) > 1 && M * (int64_t)(2 << l) <= kChipSimds) ++l;
+  while (l < 4 && chunks_per_lane(H, l) > 1 && M * (int64_t)(2 << l) <= kResidentWaves) ++l;
   return l;
 }
 

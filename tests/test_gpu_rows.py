@@ -78,11 +78,12 @@ def test_workload_parity(ref, fmt, wl):
     run_case(ref, fmt, inputs.row_inputs(wl), wl.eps, what=f"{fmt}-{wl.name}")
 
 
-# ragged lengths, and each side of the few-rows tiling switch (one chunk a lane while
-# rows x waves fit one wave per SIMD: M <= 64 at H = 4096, M <= 32 at H = 7168 and 8192)
-SHAPES = [(1, 32), (1, 2048), (3, 520), (15, 4096), (16, 7168), (17, 1056), (63, 4096), (64, 4096), (65, 4096),
-          (32, 7168), (33, 7168), (65, 7168), (257, 2080), (32, 8192), (33, 8192), (70, 8192), (5, 8224), (9, 16384),
-          (100, 16384), (130, 64)]
+# ragged lengths, and each side of the tiling switch (one chunk a lane while rows x waves
+# fit the chip's 8192 wave slots at once: M <= 4096 at H = 1024, M <= 1024 at H = 4096,
+# M <= 512 at H = 7168 and 8192)
+SHAPES = [(1, 32), (1, 2048), (3, 520), (15, 4096), (16, 7168), (17, 1056), (64, 4096), (1024, 4096), (1025, 4096),
+          (512, 7168), (513, 7168), (65, 7168), (257, 2080), (512, 8192), (513, 8192), (70, 8192), (4096, 1024),
+          (4097, 1024), (5, 8224), (9, 16384), (100, 16384), (130, 64)]
 
 
 @pytest.mark.parametrize("fmt", ["fp8_token", "fp8_group", "mxfp4"])
@@ -264,8 +265,9 @@ def test_batch_invariance(H):
     one chunk a lane) and inside a prefill batch (fewer waves, two chunks a
     lane): the row's sum of squares is added in one order for every tiling.
     Also rows small enough for the rescaled re-sum (eps 0, |r| ~ 2^-60)."""
+    rows = 8192 if H < 4096 else 2048  # enough rows for the two-chunk tiling at every H
     for mag, eps in ((1.0, 1e-6), (2.0 ** -60, 0.0)):
-        big = inputs.random_rows(2048, H, seed=H + 11, dtype=torch.bfloat16)
+        big = inputs.random_rows(rows, H, seed=H + 11, dtype=torch.bfloat16)
         x, r, w = (big[k].to(DEV) for k in ("x", "residual", "weight"))
         x, r = (x.float() * mag).to(torch.bfloat16), (r.float() * mag).to(torch.bfloat16)
         for fmt in ("fp8_token", "fp8_group", "mxfp4"):
