@@ -43,11 +43,17 @@
  *      RQ_ERR_UNSUPPORTED  the device is not gfx950, a row start is not
  *                          16-byte aligned, H % 8 != 0, H above
  *                          RQ_MAX_HIDDEN, a granule that does not divide H,
- *                          or an unsupported group size.  This is the "cannot
- *                          fuse, use the unfused path" answer of PR #29723.
+ *                          an unsupported group size, or M (or T) above
+ *                          2^31 - 1.  This is the "cannot fuse, use the
+ *                          unfused path" answer of PR #29723.
  *      RQ_ERR_HIP          the kernel launch itself failed.
  *    Faults inside a kernel surface at the caller's next synchronization.
  *  - M == 0 (or T == 0) returns RQ_OK and launches nothing.
+ *  - A call is one launch per step unless its grid would exceed 2^31
+ *    work-items (for instance more than 2^25 rows at H <= 1024, or 2^21 rows
+ *    at H = 16384); then the rows (or heads) are split over several launches
+ *    of the same kernel, with the same results.  RQ_ERR_HIP from a later
+ *    launch leaves the earlier ones enqueued.
  */
 #ifndef RMSNORM_QUANT_H
 #define RMSNORM_QUANT_H

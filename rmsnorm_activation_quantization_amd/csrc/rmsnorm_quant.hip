@@ -53,6 +53,7 @@
 //        saturating at 6).
 #include <hip/hip_runtime.h>
 
+#include <algorithm>
 #include <atomic>
 #include <cstdint>
 #include <cstring>
@@ -329,6 +330,7 @@ struct RowArgs {
   uint16_t* y_out;
   int64_t ldx;
   int64_t ldr;
+  int64_t row0;          // first row of this launch (a batch too large for one grid takes several)
   int M;
   int H;
   float eps;
@@ -384,7 +386,7 @@ __global__ __launch_bounds__(block_threads<kWPR>()) void fused_rows(const RowArg
   const int wave = threadIdx.x / kWave;            // wave in the workgroup
   const int rloc = wave / kWPR;                     // row in the workgroup
   const int wrow = wave % kWPR;                     // wave in the row
-  const int64_t row = (int64_t)blockIdx.x * kRPB + rloc;
+  const int64_t row = a.row0 + (int64_t)blockIdx.x * kRPB + rloc;
   const int t = (int)threadIdx.x % kLanes;          // lane in the row
   // A row past the end only happens in the last workgroup of the few-waves
   // tilings; its waves still reach every barrier (loads and stores are masked).
@@ -585,6 +587,7 @@ struct QKArgs {
   int64_t ld_qg;
   int64_t ld_k;
   int64_t units;  // T * (Hq + Hk) heads to normalize
+  int64_t unit0;  // first head of this launch (a batch too large for one grid takes several)
   int Hq;
   int Hk;
   int D;
@@ -609,7 +612,7 @@ __global__ __launch_bounds__(kQKBlock) void qk_gemma_gate(const QKArgs a) {
   constexpr int kLanesPerHead = 1 << kLog2Lanes;
   constexpr int kHeadsPerWave = kWave / kLanesPerHead;
   const int lane = threadIdx.x;
-  const int64_t unit = (int64_t)blockIdx.x * kHeadsPerWave + lane / kLanesPerHead;
+  const int64_t unit = a.unit0 + (int64_t)blockIdx.x * kHeadsPerWave + lane / kLanesPerHead;
   const int col = (lane % kLanesPerHead) * 8;
   const int heads = a.Hq + a.Hk;
   const bool active = unit < a.units && col < a.D;
@@ -848,6 +851,11 @@ rq_status launch(const void* kernel, dim3 grid, dim3 block, void* args, void* st
   return err == hipSuccess ? RQ_OK : RQ_ERR_HIP;
 }
 
+// Work-items one launch may hold.  A dispatch packet carries the grid size in
+// work-items as a 32-bit count; a larger batch is split into launches of at
+// most this many work-items each, every launch told its first row or head.
+constexpr int64_t kMaxGridItems = int64_t(1) << 31;
+
 // Waves the chip holds at once: 256 CUs x 4 SIMDs x 8 wave slots per SIMD.
 constexpr int64_t kResidentWaves = 256 * 4 * 8;
 
@@ -878,15 +886,22 @@ rq_status launch_rows(RowArgs& a, void* stream) {
   const int lanes = kWave * wpr;
   const int nc = chunks_per_lane(a.H, l);
   const int rpb = wpr == 1 ? 4 : 1;
-  const unsigned blocks = (unsigned)((a.M + rpb - 1) / rpb);
-  return launch(reinterpret_cast<const void*>(RowKernels<E, kMode, kStage>::k[l][nc - 1]), dim3(blocks),
-                dim3((unsigned)(lanes * rpb)), &a, stream);
+  const int64_t rows_per_launch = kMaxGridItems / lanes;  // a multiple of rpb
+  const void* kernel = reinterpret_cast<const void*>(RowKernels<E, kMode, kStage>::k[l][nc - 1]);
+  for (int64_t row0 = 0; row0 < a.M; row0 += rows_per_launch) {
+    const int64_t rows = std::min<int64_t>(a.M - row0, rows_per_launch);
+    a.row0 = row0;
+    const rq_status st = launch(kernel, dim3((unsigned)((rows + rpb - 1) / rpb)), dim3((unsigned)(lanes * rpb)), &a,
+                                stream);
+    if (st != RQ_OK) return st;
+  }
+  return RQ_OK;
 }
 
 RowArgs make_row_args(const uint16_t* x, int64_t ldx, const uint16_t* residual, int64_t ldr, const uint16_t* weight,
                       int64_t M, int64_t H, float eps, uint16_t* residual_out, uint8_t* q_out, void* scale_out,
                       uint16_t* y_out) {
-  RowArgs a;
+  RowArgs a = {};
   a.x = x;
   a.res = residual;
   a.w = weight;
@@ -1045,10 +1060,16 @@ rq_status qk_impl(const uint16_t* qg, int64_t ld_qg, const uint16_t* k, int64_t 
   a.eps = eps;
   a.inv_d = 1.0f / (float)D;
   const int64_t heads_per_wave = kWave >> log2_lanes;
-  const int64_t blocks = (a.units + heads_per_wave - 1) / heads_per_wave;
-  if (blocks > INT32_MAX) return RQ_ERR_UNSUPPORTED;
-  return launch(reinterpret_cast<const void*>(QKKernels<kOut>::k[log2_lanes]), dim3((unsigned)blocks),
-                dim3(kQKBlock), &a, stream);
+  const int64_t units_per_launch = kMaxGridItems / kQKBlock * heads_per_wave;
+  const void* kernel = reinterpret_cast<const void*>(QKKernels<kOut>::k[log2_lanes]);
+  for (int64_t unit0 = 0; unit0 < a.units; unit0 += units_per_launch) {
+    const int64_t units = std::min<int64_t>(a.units - unit0, units_per_launch);
+    a.unit0 = unit0;
+    const rq_status st = launch(kernel, dim3((unsigned)((units + heads_per_wave - 1) / heads_per_wave)),
+                                dim3(kQKBlock), &a, stream);
+    if (st != RQ_OK) return st;
+  }
+  return RQ_OK;
 }
 
 }  // namespace

@@ -359,3 +359,51 @@ def test_tiny_rows_without_eps(ref, fmt, M, H):
     gpu = gpu_call(fmt, *_probe_tensors(xb, rb, wb), 0.0)
     o = oracle_call(ref, fmt, xb, rb, wb, 0.0)
     check(ref, fmt, gpu, o, 128, f"tiny-{fmt}-{M}x{H}")
+
+
+@pytest.mark.parametrize("fmt", ["fp8_token", "fp8_group", "mxfp4"])
+def test_batch_split_over_launches(ref, fmt):
+    """A batch whose grid would pass 2^31 work-items goes out as several
+    launches: at H = 32 (one wave a row) a launch holds 2^25 rows, so 2^25 + 5
+    rows take two.  Every row is written (sentinels in every output are gone
+    and residual_out is x + residual everywhere), and rows on each side of the
+    split and at both ends match the oracle."""
+    H, M, split = 32, (1 << 25) + 5, 1 << 25
+    gen = torch.Generator(device=DEV).manual_seed(4242)
+    x = torch.randn((M, H), generator=gen, device=DEV).to(torch.bfloat16)
+    r = torch.randn((M, H), generator=gen, device=DEV).to(torch.bfloat16)
+    w = (1.0 + 0.1 * torch.randn(H, generator=gen, device=DEV)).to(torch.bfloat16)
+    ro = torch.full((M, H), float("nan"), dtype=torch.bfloat16, device=DEV)
+    y = torch.full((M, H), float("nan"), dtype=torch.bfloat16, device=DEV)
+    if fmt == "mxfp4":
+        q = torch.full((M, H // 2), 0x77, dtype=torch.uint8, device=DEV)
+        s = torch.full((M, H // 32), 255, dtype=torch.uint8, device=DEV)
+        out = rq.rmsnorm_quant_mxfp4(x, r, w, 1e-6, q_out=q, residual_out=ro, scale_out=s, y_out=y)
+    elif fmt == "fp8_group":
+        q = torch.full((M, H), 0x7F, dtype=torch.uint8, device=DEV)
+        s = torch.full((M, 1), float("nan"), dtype=torch.float32, device=DEV)
+        out = rq.rmsnorm_quant_fp8_per_group(x, r, w, 1e-6, 32, q_out=q, residual_out=ro, scale_out=s, y_out=y)
+    else:
+        q = torch.full((M, H), 0x7F, dtype=torch.uint8, device=DEV)
+        s = torch.full((M,), float("nan"), dtype=torch.float32, device=DEV)
+        out = rq.rmsnorm_quant_fp8_per_token(x, r, w, 1e-6, q_out=q, residual_out=ro, scale_out=s, y_out=y)
+    assert out is not None
+    torch.cuda.synchronize()
+    step = 1 << 22
+    for a in range(0, M, step):
+        b = min(M, a + step)
+        assert torch.equal(ro[a:b], (x[a:b].float() + r[a:b].float()).to(torch.bfloat16)), f"rows {a}..{b}"
+        assert not torch.isnan(y[a:b]).any(), f"y not written in rows {a}..{b}"
+    if fmt == "mxfp4":
+        assert (s != 255).all(), "an E8M0 byte was not written"
+    else:
+        assert torch.isfinite(s).all() and (s > 0).all(), "a scale was not written"
+        assert (q != 0x7F).all(), "an FP8 code was not written"
+    picks = np.r_[0:16, split - 16:split + 5]
+    idx = torch.as_tensor(picks, device=DEV)
+    gpu = to_np(dict(q=q[idx], residual_out=ro[idx], scale=s.view(M, -1)[idx], y=y[idx]))
+    xb, rb, wb = (inputs.bits(t.cpu()) for t in (x[idx], r[idx], w))
+    o = oracle_call(ref, fmt, xb, rb, wb, 1e-6, 32)
+    print(check(ref, fmt, gpu, o, 32, f"{fmt} split {M}x{H}"), flush=True)
+    del x, r, ro, y, q, s
+    torch.cuda.empty_cache()
