@@ -124,7 +124,7 @@ rq_status rmsnorm_quant_fp8_per_group(
  *  scale_out  [M, H / 32] uint8 out: E8M0 byte s per 32-element block,
  *             s = clamp(floor(log2 max|y|) - 2 + 127, 0, 254); an all-zero
  *             block has s = 0 and codes 0x0 / 0x8 (sign of zero); a block
- *             holding NaN has s = 255 and unspecified codes
+ *             holding NaN or Inf has s = 255 and unspecified codes
  */
 rq_status rmsnorm_quant_mxfp4(
     const uint16_t* x, int64_t ldx, const uint16_t* residual, int64_t ldr,
