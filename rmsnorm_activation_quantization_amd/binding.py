@@ -151,15 +151,25 @@ def _rows(t: torch.Tensor, name: str, dtype=None) -> int:
     return t.stride(0) if t.shape[0] > 1 else t.shape[1]
 
 
+def _same_device(like: torch.Tensor, **tensors) -> None:
+    """Every given tensor (None skipped) on the device of `like`: the kernels
+    dereference every pointer on that device, so a host tensor or one on
+    another GPU is refused here."""
+    for name, t in tensors.items():
+        if t is not None and t.device != like.device:
+            raise ValueError(f"{name} is on {t.device}; every tensor must be on {like.device}")
+
+
 def _row_outputs(x, residual, weight, residual_out, y_out, emit_y):
-    """Checks the row inputs (one element type for all) and allocates the
-    missing row outputs in that type."""
+    """Checks the row inputs (one element type for all, one device) and
+    allocates the missing row outputs in that type."""
     M, H = x.shape
     dt = x.dtype
     if residual.shape != (M, H) or weight.shape != (H,) or residual.dtype != dt or weight.dtype != dt:
         raise ValueError(f"residual must be [M, H] and weight [H], both {dt} like x")
     if not weight.is_contiguous():
         raise ValueError("weight must be contiguous")
+    _same_device(x, residual=residual, weight=weight, residual_out=residual_out, y_out=y_out)
     if residual_out is None:
         residual_out = torch.empty((M, H), dtype=dt, device=x.device)
     if y_out is None and emit_y:
@@ -286,18 +296,25 @@ def rmsnorm_quant_mxfp4_tscale(x, residual, weight, eps: float = 1e-6, *, residu
     return q_out, residual_out, scale_out, y_out
 
 
+def _qk_inputs(qg, k, q_w, k_w, head_dim: int):
+    """Checks of the QK inputs (bf16 only, one device) -> (ld_qg, ld_k, T)."""
+    ld_qg, ld_k = _rows(qg, "qg", torch.bfloat16), _rows(k, "k", torch.bfloat16)
+    T = qg.shape[0]
+    if k.shape[0] != T:
+        raise ValueError("qg and k must have the same number of tokens")
+    for name, w in (("q_w", q_w), ("k_w", k_w)):
+        if w.shape != (head_dim,) or w.dtype != torch.bfloat16 or not w.is_contiguous():
+            raise ValueError(f"{name} must be a contiguous [head_dim] bfloat16 tensor")
+    _same_device(qg, k=k, q_w=q_w, k_w=k_w)
+    return ld_qg, ld_k, T
+
+
 def qk_gemma_rmsnorm_gate(qg, k, q_w, k_w, num_q_heads: int, num_k_heads: int, head_dim: int,
                           eps: float = 1e-6, *, q_out=None, k_out=None, gate_out=None, stream=None):
     """qg [T, >= 2*Hq*D] interleaved per head as [q | gate]; k [T, >= Hk*D] (row stride allowed).
     -> (q [T, Hq, D], k [T, Hk, D], gate [T, Hq, D]) contiguous bf16, or None."""
-    ld_qg, ld_k = _rows(qg, "qg", torch.bfloat16), _rows(k, "k", torch.bfloat16)
-    T = qg.shape[0]
+    ld_qg, ld_k, T = _qk_inputs(qg, k, q_w, k_w, head_dim)
     Hq, Hk, D = num_q_heads, num_k_heads, head_dim
-    if k.shape[0] != T:
-        raise ValueError("qg and k must have the same number of tokens")
-    for name, w in (("q_w", q_w), ("k_w", k_w)):  # this variant is bf16 only
-        if w.shape != (D,) or w.dtype != torch.bfloat16 or not w.is_contiguous():
-            raise ValueError(f"{name} must be a contiguous [head_dim] bfloat16 tensor")
     dev = qg.device
     q_out = torch.empty((T, Hq, D), dtype=torch.bfloat16, device=dev) if q_out is None else q_out
     k_out = torch.empty((T, Hk, D), dtype=torch.bfloat16, device=dev) if k_out is None else k_out
@@ -305,6 +322,7 @@ def qk_gemma_rmsnorm_gate(qg, k, q_w, k_w, num_q_heads: int, num_k_heads: int, h
     for name, t, h in (("q_out", q_out, Hq), ("k_out", k_out, Hk), ("gate_out", gate_out, Hq)):
         if t.shape != (T, h, D) or t.dtype != torch.bfloat16 or not t.is_contiguous():
             raise ValueError(f"{name} must be a contiguous [T, heads, head_dim] bfloat16 tensor")
+    _same_device(qg, q_out=q_out, k_out=k_out, gate_out=gate_out)
     st = lib().qk_gemma_rmsnorm_gate(
         _ptr(qg), ld_qg, _ptr(k), ld_k, _ptr(q_w), _ptr(k_w), T, Hq, Hk, D, eps, _ptr(q_out), _ptr(k_out),
         _ptr(gate_out), _stream(stream, qg))
@@ -319,14 +337,8 @@ def qk_gemma_rmsnorm_gate_fp8(qg, k, q_w, k_w, num_q_heads: int, num_k_heads: in
     """As qk_gemma_rmsnorm_gate, with q and k quantized per head to FP8 E4M3FN.
     -> (q [T, Hq, D] float8_e4m3fn, q_scale [T, Hq] fp32, k [T, Hk, D] float8_e4m3fn, k_scale [T, Hk] fp32,
         gate [T, Hq, D] bf16), or None."""
-    ld_qg, ld_k = _rows(qg, "qg", torch.bfloat16), _rows(k, "k", torch.bfloat16)
-    T = qg.shape[0]
+    ld_qg, ld_k, T = _qk_inputs(qg, k, q_w, k_w, head_dim)
     Hq, Hk, D = num_q_heads, num_k_heads, head_dim
-    if k.shape[0] != T:
-        raise ValueError("qg and k must have the same number of tokens")
-    for name, w in (("q_w", q_w), ("k_w", k_w)):
-        if w.shape != (D,) or w.dtype != torch.bfloat16 or not w.is_contiguous():
-            raise ValueError(f"{name} must be a contiguous [head_dim] bfloat16 tensor")
     dev = qg.device
     fp8 = torch.float8_e4m3fn
     q_out = torch.empty((T, Hq, D), dtype=fp8, device=dev) if q_out is None else q_out
@@ -341,6 +353,7 @@ def qk_gemma_rmsnorm_gate_fp8(qg, k, q_w, k_w, num_q_heads: int, num_k_heads: in
                                 ("gate_out", gate_out, (T, Hq, D), (torch.bfloat16,))):
         if tuple(t.shape) != shape or t.dtype not in dts or not t.is_contiguous():
             raise ValueError(f"{name} must be a contiguous {list(shape)} tensor of {dts[0]}")
+    _same_device(qg, q_out=q_out, k_out=k_out, q_scale_out=q_scale_out, k_scale_out=k_scale_out, gate_out=gate_out)
     st = lib().qk_gemma_rmsnorm_gate_fp8(
         _ptr(qg), ld_qg, _ptr(k), ld_k, _ptr(q_w), _ptr(k_w), T, Hq, Hk, D, eps, _ptr(q_out), _ptr(q_scale_out),
         _ptr(k_out), _ptr(k_scale_out), _ptr(gate_out), _stream(stream, qg))
@@ -355,14 +368,8 @@ def qk_gemma_rmsnorm_gate_mxfp4(qg, k, q_w, k_w, num_q_heads: int, num_k_heads: 
     """As qk_gemma_rmsnorm_gate, with q and k quantized to MXFP4 (head_dim a multiple of 32).
     -> (q [T, Hq, D/2] uint8 packed E2M1, q_scale [T, Hq, D/32] uint8 E8M0, k [T, Hk, D/2], k_scale [T, Hk, D/32],
         gate [T, Hq, D] bf16), or None."""
-    ld_qg, ld_k = _rows(qg, "qg", torch.bfloat16), _rows(k, "k", torch.bfloat16)
-    T = qg.shape[0]
+    ld_qg, ld_k, T = _qk_inputs(qg, k, q_w, k_w, head_dim)
     Hq, Hk, D = num_q_heads, num_k_heads, head_dim
-    if k.shape[0] != T:
-        raise ValueError("qg and k must have the same number of tokens")
-    for name, w in (("q_w", q_w), ("k_w", k_w)):
-        if w.shape != (D,) or w.dtype != torch.bfloat16 or not w.is_contiguous():
-            raise ValueError(f"{name} must be a contiguous [head_dim] bfloat16 tensor")
     dev = qg.device
     u8 = torch.uint8
     shapes = {"q_out": (T, Hq, D // 2), "q_scale_out": (T, Hq, max(D // 32, 1)), "k_out": (T, Hk, D // 2),

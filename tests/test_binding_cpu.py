@@ -47,3 +47,11 @@ def test_fp16_names_are_the_dispatching_functions():
     assert rq.rmsnorm_quant_fp8_per_token_f16 is rq.rmsnorm_quant_fp8_per_token
     assert rq.rmsnorm_residual_f16 is rq.rmsnorm_residual_bf16
     assert rq.quantize_mxfp4_f16 is rq.quantize_mxfp4
+
+
+def test_tensors_on_another_device_are_refused():
+    from rmsnorm_activation_quantization_amd import binding
+    like = torch.zeros(4, 256, dtype=torch.bfloat16)
+    binding._same_device(like, a=torch.zeros(3), b=None)
+    with pytest.raises(ValueError, match="weight is on meta"):
+        binding._same_device(like, weight=torch.empty(256, dtype=torch.bfloat16, device="meta"))

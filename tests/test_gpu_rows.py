@@ -407,3 +407,29 @@ def test_batch_split_over_launches(ref, fmt):
     print(check(ref, fmt, gpu, o, 32, f"{fmt} split {M}x{H}"), flush=True)
     del x, r, ro, y, q, s
     torch.cuda.empty_cache()
+
+
+def test_tensors_on_another_device_are_refused():
+    """A host tensor among device tensors is refused before any launch (the
+    kernels would dereference its address on the GPU)."""
+    d = inputs.random_rows(4, 256, seed=3)
+    x, r, w = (d[k].to(DEV) for k in ("x", "residual", "weight"))
+    for fn in (rq.rmsnorm_quant_fp8_per_token, rq.rmsnorm_quant_mxfp4, rq.rmsnorm_residual_bf16):
+        with pytest.raises(ValueError, match="weight is on cpu"):
+            fn(x, r, w.cpu())
+        with pytest.raises(ValueError, match="residual_out is on cpu"):
+            fn(x, r, w, residual_out=torch.empty(4, 256, dtype=torch.bfloat16))
+    with pytest.raises(ValueError, match="y_out is on cpu"):
+        rq.rmsnorm_quant_fp8_per_group(x, r, w, 1e-6, 128, y_out=torch.empty(4, 256, dtype=torch.bfloat16))
+    qg = torch.zeros(2, 2 * 2 * 64, dtype=torch.bfloat16, device=DEV)
+    k = torch.zeros(2, 64, dtype=torch.bfloat16, device=DEV)
+    qw = torch.zeros(64, dtype=torch.bfloat16, device=DEV)
+    for fn in (rq.qk_gemma_rmsnorm_gate, rq.qk_gemma_rmsnorm_gate_fp8, rq.qk_gemma_rmsnorm_gate_mxfp4):
+        with pytest.raises(ValueError, match="k_w is on cpu"):
+            fn(qg, k, qw, qw.cpu(), 2, 1, 64)
+        assert fn(qg, k, qw, qw, 2, 1, 64) is not None
+    with pytest.raises(ValueError, match="gate_out is on cpu"):
+        rq.qk_gemma_rmsnorm_gate(qg, k, qw, qw, 2, 1, 64, gate_out=torch.empty(2, 2, 64, dtype=torch.bfloat16))
+    with pytest.raises(ValueError, match="q_scale_out is on cpu"):
+        rq.qk_gemma_rmsnorm_gate_fp8(qg, k, qw, qw, 2, 1, 64, q_scale_out=torch.empty(2, 2))
+    torch.cuda.synchronize()
