@@ -16,8 +16,11 @@ from parity import check_fp8, check_mxfp4, to_np
 
 pytestmark = pytest.mark.gpu
 DEV = "cuda:0"
+# Row counts beyond a few hundred with four rows a workgroup (3000 x 256) and one
+# row a workgroup (1100 x 4096, 700 x 2048, 8192 x 4096).
 CASES = [("bf16", 16, 4096, 128), ("bf16", 16, 7168, 32), ("bf16", 3, 544, 32), ("bf16", 130, 1024, 512),
-         ("bf16", 65, 4096, 64), ("fp16", 17, 2048, 128), ("fp16", 9, 16384, 256), ("bf16", 8192, 4096, 128)]
+         ("bf16", 65, 4096, 64), ("fp16", 17, 2048, 128), ("fp16", 9, 16384, 256), ("bf16", 8192, 4096, 128),
+         ("bf16", 3000, 256, 32), ("bf16", 1100, 4096, 128), ("fp16", 700, 2048, 64)]
 
 
 def padded(M):
