@@ -28,6 +28,15 @@
  * fixes scale = amax / 448 (FP8) and E8M0 exponent floor(log2 amax) - 2
  * (MXFP4, one scale per 32 elements).
  *
+ * Pins: every function here is checked by the CPU tests against closed forms,
+ * format tables, exhaustive searches, hand-derived goldens and an independent
+ * numpy formulation (with planted mistakes as negative controls).  Parity
+ * unpinned against the pages themselves, which print no outputs: the rounding
+ * order inside RMSNorm (one rounding of r * rstd * w, fp64 here), the FP8
+ * flavour (OCP E4M3FN, read from the /448), the E8M0 rule without a mantissa
+ * round-up, the scale layouts, and the granule of the quantized QK variants
+ * (one FP8 scale per head of a token; MXFP4 heads as rows of D values).
+ *
  * Return value of the row functions: 0 on success, 1 on an invalid argument
  * (null pointer with M > 0, negative size, leading dimension below the row
  * length, H not divisible by the granule).  Nothing is written on failure.
