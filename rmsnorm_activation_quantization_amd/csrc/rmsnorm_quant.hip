@@ -63,6 +63,8 @@
 
 #define RQ_QUOTIENT_QUALIFIERS __device__ __forceinline__
 #include "fp8_quotient.h"
+#define RQ_HEAD_INDEX_QUALIFIERS __device__ __forceinline__
+#include "head_index.h"
 
 namespace {
 
@@ -586,8 +588,10 @@ struct QKArgs {
   void* k_scale;
   int64_t ld_qg;
   int64_t ld_k;
-  int64_t units;  // T * (Hq + Hk) heads to normalize
-  int64_t unit0;  // first head of this launch (a batch too large for one grid takes several)
+  int64_t tok0;          // first token of this launch (a batch too large for one grid takes several)
+  uint32_t units;         // heads this launch normalizes: its tokens * (Hq + Hk), below 2^31
+  uint32_t heads_magic;   // division by Hq + Hk (head_index.h)
+  uint32_t heads_shift;
   int Hq;
   int Hk;
   int D;
@@ -612,12 +616,14 @@ __global__ __launch_bounds__(kQKBlock) void qk_gemma_gate(const QKArgs a) {
   constexpr int kLanesPerHead = 1 << kLog2Lanes;
   constexpr int kHeadsPerWave = kWave / kLanesPerHead;
   const int lane = threadIdx.x;
-  const int64_t unit = a.unit0 + (int64_t)blockIdx.x * kHeadsPerWave + lane / kLanesPerHead;
+  // flat head index within the launch (token-major), below 2^31
+  const uint32_t unit = blockIdx.x * (uint32_t)kHeadsPerWave + (uint32_t)(lane / kLanesPerHead);
   const int col = (lane % kLanesPerHead) * 8;
-  const int heads = a.Hq + a.Hk;
+  const uint32_t heads = (uint32_t)(a.Hq + a.Hk);
   const bool active = unit < a.units && col < a.D;
-  const int64_t tok = active ? unit / heads : 0;
-  const int h = active ? (int)(unit % heads) : 0;
+  const uint32_t tl = rq_head_quotient(unit, a.heads_magic, a.heads_shift);
+  const int64_t tok = active ? a.tok0 + tl : 0;
+  const int h = active ? (int)(unit - tl * heads) : 0;
   const bool is_q = h < a.Hq;
 
   uint4 v = make_uint4(0, 0, 0, 0), w = make_uint4(0, 0, 0, 0), gate = make_uint4(0, 0, 0, 0);
@@ -1053,18 +1059,24 @@ rq_status qk_impl(const uint16_t* qg, int64_t ld_qg, const uint16_t* k, int64_t 
   a.gate_out = gate_out;
   a.ld_qg = ld_qg;
   a.ld_k = ld_k;
-  a.units = T * (Hq + Hk);
+  const int64_t heads = Hq + Hk;
+  const rq_head_divisor div = rq_head_divisor_of((uint32_t)heads);
+  a.heads_magic = div.magic;
+  a.heads_shift = div.shift;
   a.Hq = (int)Hq;
   a.Hk = (int)Hk;
   a.D = (int)D;
   a.eps = eps;
   a.inv_d = 1.0f / (float)D;
   const int64_t heads_per_wave = kWave >> log2_lanes;
-  const int64_t units_per_launch = kMaxGridItems / kQKBlock * heads_per_wave;
+  // Whole tokens a launch, at most 2^31 work-items: the flat head index of a
+  // launch stays below 2^31 (heads <= 2^17, so a launch holds >= 2^8 tokens).
+  const int64_t tokens_per_launch = kMaxGridItems / kQKBlock * heads_per_wave / heads;
   const void* kernel = reinterpret_cast<const void*>(QKKernels<kOut>::k[log2_lanes]);
-  for (int64_t unit0 = 0; unit0 < a.units; unit0 += units_per_launch) {
-    const int64_t units = std::min<int64_t>(a.units - unit0, units_per_launch);
-    a.unit0 = unit0;
+  for (int64_t tok0 = 0; tok0 < T; tok0 += tokens_per_launch) {
+    const int64_t units = std::min<int64_t>(T - tok0, tokens_per_launch) * heads;
+    a.tok0 = tok0;
+    a.units = (uint32_t)units;
     const rq_status st = launch(kernel, dim3((unsigned)((units + heads_per_wave - 1) / heads_per_wave)),
                                 dim3(kQKBlock), &a, stream);
     if (st != RQ_OK) return st;
