@@ -55,3 +55,15 @@ def test_tensors_on_another_device_are_refused():
     binding._same_device(like, a=torch.zeros(3), b=None)
     with pytest.raises(ValueError, match="weight is on meta"):
         binding._same_device(like, weight=torch.empty(256, dtype=torch.bfloat16, device="meta"))
+
+
+def test_missing_library_fails_loudly(monkeypatch):
+    """No other code path: without the built library every call raises."""
+    from rmsnorm_activation_quantization_amd import binding
+    monkeypatch.setattr(binding, "_lib", None)
+    monkeypatch.setattr(binding._build, "LIBRARY", "/nonexistent/librmsnorm_quant.so")
+    monkeypatch.setattr(binding, "_FN_CACHE", {})
+    with pytest.raises(RuntimeError, match="missing"):
+        binding.lib()
+    with pytest.raises(RuntimeError, match="missing"):
+        binding._fn("rmsnorm_quant_mxfp4", torch.bfloat16)
