@@ -4,7 +4,6 @@ rejects bad arguments before touching the HIP runtime.  Pointers here are
 fake, aligned integers: the preflight never dereferences them and every case
 returns before any HIP call."""
 
-import ctypes
 import os
 import re
 import subprocess
