@@ -269,6 +269,7 @@ def main():
         result["unfused_vs_fused"] = unfused_comparison(torch, rq, inputs, dev, sets, outs, per_kernel_us, args)
         result["qk_prefill"] = qk_prefill(torch, rq, dev)
         result["column_major_scales_8192x4096"] = transposed_scales(torch, rq, dev, sets, outs, args)
+        result["fp16_rows_8192x4096"] = fp16_rows(torch, rq, dev, sets, outs, args)
     if not args.no_cpu_baseline and not args.profile_pass:
         result["cpu_baseline"] = cpu_baseline(inputs, wl, qw, nbytes)
     print(json.dumps(result), flush=True)
@@ -473,12 +474,38 @@ def qk_prefill(torch, rq, dev, T: int = 8192, Hq: int = 16, Hk: int = 2, D: int 
     return res
 
 
-def transposed_scales(torch, rq, dev, sets, outs, args, replays: int = 5):
-    """The column-major-scale entry points at [8192, 4096] (leading dimension
-    M) next to the row-major calls: for each, an uploaded graph of K calls over
-    the rotating sets (codes and residual_out reuse the rotating output sets),
-    the two graphs replayed alternately, median replay / K."""
+def paired_us(torch, pair, n, steps, replays: int = 5):
+    """Median µs per call of two call sequences timed alternately: each is an
+    uploaded graph of `steps` calls over `n` rotating sets, the two graphs
+    replayed in turn `replays` times."""
     import statistics
+    graphs = []
+    for fn in pair:
+        for j in range(n):
+            fn(j)
+        torch.cuda.synchronize()
+        g = torch.cuda.CUDAGraph()
+        with torch.cuda.graph(g):
+            for j in range(steps):
+                fn(j)
+        graphs.append(g)
+    upload_graphs(torch, graphs, torch.cuda.current_stream())
+    times = ([], [])
+    for _ in range(replays):
+        for g, t in zip(graphs, times):
+            a, b = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+            a.record()
+            g.replay()
+            b.record()
+            torch.cuda.synchronize()
+            t.append(1000.0 * a.elapsed_time(b) / steps)
+    return statistics.median(times[0]), statistics.median(times[1])
+
+
+def transposed_scales(torch, rq, dev, sets, outs, args):
+    """The column-major-scale entry points at [8192, 4096] (leading dimension
+    M) next to the row-major calls, timed alternately (paired_us); codes and
+    residual_out reuse the rotating output sets."""
     M, H = sets[0]["x"].shape
     n = len(sets)
     g_scales = [torch.empty((H // 128, M), dtype=torch.float32, device=dev) for _ in range(n)]
@@ -500,31 +527,44 @@ def transposed_scales(torch, rq, dev, sets, outs, args, replays: int = 5):
     }
     res = {}
     for fmt, pair in fns.items():
-        graphs = []
-        for fn in pair:
-            for j in range(n):
-                fn(j)
-            torch.cuda.synchronize()
-            g = torch.cuda.CUDAGraph()
-            with torch.cuda.graph(g):
-                for j in range(args.steps):
-                    fn(j)
-            graphs.append(g)
-        upload_graphs(torch, graphs, torch.cuda.current_stream())
-        times = ([], [])
-        for _ in range(replays):
-            for g, t in zip(graphs, times):
-                a, b = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
-                a.record()
-                g.replay()
-                b.record()
-                torch.cuda.synchronize()
-                t.append(1000.0 * a.elapsed_time(b) / args.steps)
-        us, row_us = statistics.median(times[0]), statistics.median(times[1])
+        us, row_us = paired_us(torch, pair, n, args.steps)
         nbytes = row_bytes(fmt, M, H)
         res[fmt] = {"us": round(us, 3), "GBps": round(nbytes / (us * 1e-6) / 1e9, 1),
                     "frac_of_peak": round(nbytes / (us * 1e-6) / 1e9 / HBM_PEAK_GBS, 4),
                     "row_major_us": round(row_us, 3)}
+    return res
+
+
+def fp16_rows(torch, rq, dev, sets, outs, args):
+    """The fused formats on fp16 rows (the same values as the bf16 sets, cast)
+    at [8192, 4096], timed alternately with the bf16 calls (paired_us); codes
+    and scales reuse the rotating output sets, residual_out has fp16 buffers of
+    its own."""
+    M, H = sets[0]["x"].shape
+    n = len(sets)
+    h16 = [{k: v.to(torch.float16) for k, v in st.items()} for st in sets]
+    ro16 = [torch.empty((M, H), dtype=torch.float16, device=dev) for _ in range(n)]
+    calls = {"fp8_token": (rq.rmsnorm_quant_fp8_per_token, "t", ()),
+             "fp8_group": (rq.rmsnorm_quant_fp8_per_group, "g", (128,)),
+             "mxfp4": (rq.rmsnorm_quant_mxfp4, "m", ())}
+    res = {}
+    for fmt, (fn, key, extra) in calls.items():
+        def f16(j, fn=fn, key=key, extra=extra):
+            d = h16[j % n]
+            q, _, sc = outs[j % n][key]
+            return fn(d["x"], d["residual"], d["weight"], 1e-6, *extra, q_out=q, residual_out=ro16[j % n],
+                      scale_out=sc)
+
+        def bf16(j, fn=fn, key=key, extra=extra):
+            d = sets[j % n]
+            q, ro, sc = outs[j % n][key]
+            return fn(d["x"], d["residual"], d["weight"], 1e-6, *extra, q_out=q, residual_out=ro, scale_out=sc)
+
+        us, bf_us = paired_us(torch, (f16, bf16), n, args.steps)
+        nbytes = row_bytes(fmt, M, H)
+        res[fmt] = {"us": round(us, 3), "GBps": round(nbytes / (us * 1e-6) / 1e9, 1),
+                    "frac_of_peak": round(nbytes / (us * 1e-6) / 1e9 / HBM_PEAK_GBS, 4), "bf16_us": round(bf_us, 3)}
+    del h16, ro16
     return res
 
 
