@@ -1,0 +1,105 @@
+"""Non-finite values in QK heads (reading c16: a NaN or Inf stays inside its
+head, or its 32-element block for MXFP4), through the bf16, FP8 and MXFP4 QK
+entry points, against the CPU oracle.
+
+One q head holds a NaN: the whole normalized head is NaN, its FP8 scale is
+NaN and its codes are NaN codes, every E8M0 byte of it is 255.  One k head
+holds +Inf: rstd is 0, so that element becomes NaN and the others signed
+zeros; FP8 scale NaN; the Inf's block has E8M0 255 and the other blocks byte 0
+with signed-zero codes.  A gate element of +Inf is copied bit for bit.  Every
+other head is unaffected."""
+
+from __future__ import annotations
+
+import numpy as np
+import pytest
+import torch
+
+import rmsnorm_activation_quantization_amd as rq
+from rmsnorm_activation_quantization_amd import inputs
+from parity import check_bf16_close
+
+pytestmark = pytest.mark.gpu
+DEV = "cuda:0"
+T, HQ, HK, D = 4, 3, 2, 128
+NAN_Q = (1, 1)   # token, q head
+INF_K = (3, 1)   # token, k head
+INF_GATE = (2, 0)
+
+
+def host_inputs():
+    d = inputs.qk_inputs(inputs.QKWorkload("qk_nonfinite", T, HQ, HK, D, seed=77))
+    qg, k = inputs.bits(d["qg"]).copy(), inputs.bits(d["k"]).copy()
+    qg[NAN_Q[0], 2 * D * NAN_Q[1] + 5] = 0x7FC0
+    k[INF_K[0], D * INF_K[1] + 7] = 0x7F80
+    qg[INF_GATE[0], 2 * D * INF_GATE[1] + D + 3] = 0x7F80
+    return qg, k, inputs.bits(d["q_w"]), inputs.bits(d["k_w"])
+
+
+def device(a):
+    return inputs.from_bits(a).to(DEV)
+
+
+def is_nan16(b):
+    return ((b & 0x7FFF) > 0x7F80)
+
+
+def test_qk_nonfinite_heads(ref):
+    qg, k, qw, kw = host_inputs()
+    q, kk, gate = rq.qk_gemma_rmsnorm_gate(device(qg), device(k), device(qw), device(kw), HQ, HK, D, 1e-6)
+    torch.cuda.synchronize()
+    qb, kb, gb = inputs.bits(q), inputs.bits(kk), inputs.bits(gate)
+    o = ref.qk_gemma_rmsnorm_gate(qg, k, qw, kw, HQ, HK, D, 1e-6)
+    assert (gb == o["gate"]).all() and gb[INF_GATE[0], INF_GATE[1], 3] == 0x7F80, "gate copy"
+    assert is_nan16(qb[NAN_Q]).all() and is_nan16(o["q"][NAN_Q]).all(), "a NaN head normalizes to NaN"
+    # the Inf head: NaN where the Inf was, signed zeros elsewhere, as in the oracle
+    assert is_nan16(kb[INF_K][7]) and is_nan16(o["k"][INF_K][7])
+    rest = np.delete(np.arange(D), 7)
+    assert (kb[INF_K][rest] & 0x7FFF == 0).all() and (kb[INF_K][rest] == o["k"][INF_K][rest]).all()
+    # every other head as usual
+    mq = np.ones((T, HQ), bool); mq[NAN_Q] = False
+    mk = np.ones((T, HK), bool); mk[INF_K] = False
+    check_bf16_close(qb[mq], o["q"][mq], "finite q heads")
+    check_bf16_close(kb[mk], o["k"][mk], "finite k heads")
+
+
+def test_qk_fp8_nonfinite_heads(ref):
+    qg, k, qw, kw = host_inputs()
+    args = (device(qg), device(k), device(qw), device(kw), HQ, HK, D, 1e-6)
+    q8, qs, k8, ks, gate = rq.qk_gemma_rmsnorm_gate_fp8(*args)
+    q, kk, _ = rq.qk_gemma_rmsnorm_gate(*args)
+    torch.cuda.synchronize()
+    qc, kc = q8.view(torch.uint8).cpu().numpy(), k8.view(torch.uint8).cpu().numpy()
+    qs, ks = qs.cpu().numpy(), ks.cpu().numpy()
+    assert np.isnan(qs[NAN_Q]) and ((qc[NAN_Q] & 0x7F) == 0x7F).all(), "a NaN head: NaN scale, NaN codes"
+    assert np.isnan(ks[INF_K]) and ((kc[INF_K] & 0x7F) == 0x7F).all(), "the Inf head holds a NaN: NaN scale"
+    o = ref.qk_gemma_rmsnorm_gate_fp8(qg, k, qw, kw, HQ, HK, D, 1e-6)
+    assert np.isnan(o["q_scale"][NAN_Q]) and np.isnan(o["k_scale"][INF_K])
+    assert (inputs.bits(gate) == o["gate"]).all()
+    # finite heads: exactly the per-head quantization of the GPU's bf16 heads
+    for codes, scale, heads, bad, H in ((qc, qs, inputs.bits(q), NAN_Q, HQ), (kc, ks, inputs.bits(kk), INF_K, HK)):
+        m = np.ones((T, H), bool); m[bad] = False
+        want = ref.quantize_fp8(heads[m].reshape(-1, D), D)
+        assert (codes[m].reshape(-1, D) == want["q"]).all()
+        assert np.array_equal(scale[m].reshape(-1).view(np.uint32), want["scale"].reshape(-1).view(np.uint32))
+
+
+def test_qk_mxfp4_nonfinite_heads(ref):
+    qg, k, qw, kw = host_inputs()
+    args = (device(qg), device(k), device(qw), device(kw), HQ, HK, D, 1e-6)
+    q4, qs, k4, ks, gate = rq.qk_gemma_rmsnorm_gate_mxfp4(*args)
+    q, kk, _ = rq.qk_gemma_rmsnorm_gate(*args)
+    torch.cuda.synchronize()
+    qc, kc, qs, ks = (t.cpu().numpy() for t in (q4, k4, qs, ks))
+    assert (qs[NAN_Q] == 255).all(), "every block of a NaN head has E8M0 255"
+    assert ks[INF_K][0] == 255 and (ks[INF_K][1:] == 0).all(), "only the Inf's block is non-finite"
+    kzero = kc[INF_K][16:]  # packed codes of blocks 1..3 (16 bytes a block): signed zeros only
+    assert ((kzero & 0x77) == 0).all()
+    o = ref.qk_gemma_rmsnorm_gate_mxfp4(qg, k, qw, kw, HQ, HK, D, 1e-6)
+    assert (o["q_scale"][NAN_Q] == 255).all() and (o["k_scale"][INF_K] == ks[INF_K]).all()
+    assert (o["k"][INF_K][16:] == kzero).all()
+    assert (inputs.bits(gate) == o["gate"]).all()
+    for codes, scale, heads, bad, H in ((qc, qs, inputs.bits(q), NAN_Q, HQ), (kc, ks, inputs.bits(kk), INF_K, HK)):
+        m = np.ones((T, H), bool); m[bad] = False
+        want = ref.quantize_mxfp4(heads[m].reshape(-1, D))
+        assert (codes[m].reshape(-1, D // 2) == want["q"]).all() and (scale[m].reshape(-1, D // 32) == want["scale"]).all()
