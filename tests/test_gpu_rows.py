@@ -433,3 +433,49 @@ def test_tensors_on_another_device_are_refused():
     with pytest.raises(ValueError, match="q_scale_out is on cpu"):
         rq.qk_gemma_rmsnorm_gate_fp8(qg, k, qw, qw, 2, 1, 64, q_scale_out=torch.empty(2, 2))
     torch.cuda.synchronize()
+
+
+@pytest.mark.parametrize("dtype", ["bf16", "fp16"])
+@pytest.mark.parametrize("fmt", ["fp8_token", "fp8_group", "mxfp4"])
+def test_inf_rows(ref, fmt, dtype):
+    """Inf in a row (reading c16): row 1 holds +Inf in x; in row 2 x + residual
+    overflows to -Inf.  rstd is 0 there, so the Inf element's y is NaN and the
+    others signed zeros: the granule holding it gets a NaN scale (E8M0 255),
+    every other granule of the row scale 0 (byte 0) and signed-zero codes.
+    Everything is compared with the oracle; rows 0 and 3 are ordinary."""
+    tdt = torch.float16 if dtype == "fp16" else torch.bfloat16
+    M, H = 4, 512
+    d = inputs.random_rows(M, H, seed=91, dtype=tdt)
+    xb, rb, wb = (inputs.bits(d[k]).copy() for k in ("x", "residual", "weight"))
+    inf = 0x7C00 if dtype == "fp16" else 0x7F80
+    big = 0x7BFF if dtype == "fp16" else 0x7F7F   # largest finite value
+    xb[1, 100] = inf
+    xb[2, 300], rb[2, 300] = big | 0x8000, big | 0x8000
+    dev = [inputs.from_bits(a, tdt).to(DEV) for a in (xb, rb, wb)]
+    gpu = gpu_call(fmt, *dev, 1e-6)
+    o = oracle_call(ref, fmt, xb, rb, wb, 1e-6) if dtype == "bf16" else \
+        getattr(ref, {"fp8_token": "fp8_per_token", "fp8_group": "fp8_per_group", "mxfp4": "mxfp4"}[fmt])(
+            xb, rb, wb, 1e-6, *((128,) if fmt == "fp8_group" else ()), emit_y=True, dtype="fp16")
+    assert (gpu["residual_out"] == o["residual_out"]).all()
+    assert gpu["residual_out"][1, 100] == inf and gpu["residual_out"][2, 300] == inf | 0x8000
+    ynan = lambda y: (y & 0x7FFF) > inf
+    for row, col in ((1, 100), (2, 300)):
+        assert ynan(gpu["y"][row, col]) and ynan(o["y"][row, col])
+        rest = np.delete(np.arange(H), col)
+        assert (gpu["y"][row, rest] & 0x7FFF == 0).all() and (gpu["y"][row, rest] == o["y"][row, rest]).all()
+        g = {"fp8_token": H, "fp8_group": 128, "mxfp4": 32}[fmt]
+        sc, osc = gpu["scale"].reshape(M, -1)[row], o["scale"].reshape(M, -1)[row]
+        if fmt == "mxfp4":
+            assert sc[col // g] == 255 and osc[col // g] == 255
+            assert (np.delete(sc, col // g) == 0).all() and (np.delete(osc, col // g) == 0).all()
+            q, oq = gpu["q"][row].reshape(-1, g // 2), o["q"][row].reshape(-1, g // 2)
+        else:
+            assert np.isnan(sc[col // g]) and np.isnan(osc[col // g])
+            others = np.delete(np.arange(sc.size), col // g)
+            assert (sc[others] == 0).all() and (osc[others] == 0).all()
+            q, oq = gpu["q"][row].reshape(-1, g), o["q"][row].reshape(-1, g)
+            assert ((q[col // g] & 0x7F) == 0x7F).all()
+        keep = np.delete(np.arange(q.shape[0]), col // g)
+        assert (q[keep] == oq[keep]).all(), "signed-zero codes of the finite granules"
+    for row in (0, 3):
+        assert (gpu["y"][row] == o["y"][row]).sum() >= H - 2
