@@ -471,13 +471,18 @@ __global__ __launch_bounds__(block_threads<kWPR>()) void fused_rows(const RowArg
     // the hardware reciprocal square root keeps it off the critical path.
     const float t_ms = __builtin_fmaf(ss, a.inv_h, a.eps);
     float rstd;
-    if (!(t_ms < 0x1p-100f)) {
-      rstd = __builtin_amdgcn_rsqf(t_ms);  // NaN and Inf propagate through here
+    if (!(t_ms < 0x1p-100f) && t_ms != __builtin_huge_valf()) {
+      rstd = __builtin_amdgcn_rsqf(t_ms);  // NaN propagates through here
     } else {
-      // Only with eps < 2^-100: the squares of a row this small underflow fp32,
-      // so sum them again with r scaled by 2^100 (exact; |r| < 2^-43 here, so the
-      // scaled squares lie in [2^-66, 2^114]).  Uniform over the row, and a
-      // multi-wave row has its workgroup to itself.
+      // The fp32 squares left their range; sum them again with r scaled by an
+      // exact power of two k, in the same order.  A row this small (only with
+      // eps < 2^-100; |r| < 2^-43) takes k = 2^100, so the scaled squares lie in
+      // [2^-66, 2^114].  A row whose sum of squares overflowed (bf16 allows |r|
+      // up to 2^128) takes k = 2^-80: scaled squares at most 2^96, their sum at
+      // most 2^110; a row holding Inf still sums to Inf and gets rstd 0, as an
+      // exact computation does.  Uniform over the row, and a multi-wave row has
+      // its workgroup to itself.
+      const float k = t_ms < 0x1p-100f ? 0x1p100f : 0x1p-80f;
       float s2c[kNC];
   #pragma unroll
       for (int c = 0; c < kNC; ++c) {
@@ -485,13 +490,13 @@ __global__ __launch_bounds__(block_threads<kWPR>()) void fused_rows(const RowArg
         s2c[c] = 0.0f;
   #pragma unroll
         for (int j = 0; j < 4; ++j) {
-          const float r0 = E::lo(rs[j]) * 0x1p100f, r1 = E::hi(rs[j]) * 0x1p100f;
+          const float r0 = E::lo(rs[j]) * k, r1 = E::hi(rs[j]) * k;
           s2c[c] = __builtin_fmaf(r0, r0, s2c[c]);
           s2c[c] = __builtin_fmaf(r1, r1, s2c[c]);
         }
       }
       const float s2 = row_sum<kNC, kWPR>(s2c, lds_sum_tiny[rloc], lane, wrow);
-      rstd = __builtin_amdgcn_rsqf(__builtin_fmaf(s2, a.inv_h, a.eps * 0x1p100f * 0x1p100f)) * 0x1p100f;
+      rstd = __builtin_amdgcn_rsqf(__builtin_fmaf(s2, a.inv_h, a.eps * k * k)) * k;
     }
 
     // 4. y = bf16((r * rstd) * w), optional bf16 side output.
@@ -649,18 +654,22 @@ __global__ __launch_bounds__(kQKBlock) void qk_gemma_gate(const QKArgs a) {
   ss = group_sum(ss, kLog2Lanes);
   const float t_ms = __builtin_fmaf(ss, a.inv_d, a.eps);
   float rstd;
-  if (!(t_ms < 0x1p-100f)) {
+  if (!(t_ms < 0x1p-100f) && t_ms != __builtin_huge_valf()) {
     rstd = __builtin_amdgcn_rsqf(t_ms);
-  } else {  // a head this small with eps < 2^-100: sum the squares of v * 2^100 (exact)
+  } else {
+    // Squares out of fp32 range: sum again with v scaled by k (exact), as in
+    // the row kernel: k = 2^100 for a head this small (eps < 2^-100), 2^-80 for
+    // a head whose sum of squares overflowed (an Inf in it still gives rstd 0).
+    const float k = t_ms < 0x1p-100f ? 0x1p100f : 0x1p-80f;
     float s2 = 0.0f;
 #pragma unroll
     for (int j = 0; j < 4; ++j) {
-      const float v0 = bf_lo(vs[j]) * 0x1p100f, v1 = bf_hi(vs[j]) * 0x1p100f;
+      const float v0 = bf_lo(vs[j]) * k, v1 = bf_hi(vs[j]) * k;
       s2 = __builtin_fmaf(v0, v0, s2);
       s2 = __builtin_fmaf(v1, v1, s2);
     }
     s2 = group_sum(s2, kLog2Lanes);
-    rstd = __builtin_amdgcn_rsqf(__builtin_fmaf(s2, a.inv_d, a.eps * 0x1p100f * 0x1p100f)) * 0x1p100f;
+    rstd = __builtin_amdgcn_rsqf(__builtin_fmaf(s2, a.inv_d, a.eps * k * k)) * k;
   }
   uint32_t p[4];
 #pragma unroll

@@ -103,3 +103,31 @@ def test_qk_mxfp4_nonfinite_heads(ref):
         m = np.ones((T, H), bool); m[bad] = False
         want = ref.quantize_mxfp4(heads[m].reshape(-1, D))
         assert (codes[m].reshape(-1, D // 2) == want["q"]).all() and (scale[m].reshape(-1, D // 32) == want["scale"]).all()
+
+
+@pytest.mark.parametrize("mag", [100, 120])
+def test_qk_huge_heads(ref, mag):
+    """Heads whose fp32 sum of squares overflows (|v| around 2^mag): rescaled
+    sum, the same results as the oracle (bf16 heads within the usual bar, FP8
+    and MXFP4 codes and scales exactly the quantization of the GPU's heads)."""
+    d = inputs.qk_inputs(inputs.QKWorkload("qk_huge", 6, 3, 2, 256, seed=mag))
+    qg = (d["qg"].float() * 2.0 ** mag).to(torch.bfloat16)
+    k = (d["k"].float() * 2.0 ** mag).to(torch.bfloat16)
+    host = (inputs.bits(qg), inputs.bits(k), inputs.bits(d["q_w"]), inputs.bits(d["k_w"]))
+    args = (qg.to(DEV), k.to(DEV), d["q_w"].to(DEV), d["k_w"].to(DEV), 3, 2, 256, 1e-6)
+    q, kk, gate = rq.qk_gemma_rmsnorm_gate(*args)
+    q8, qs8, k8, ks8, _ = rq.qk_gemma_rmsnorm_gate_fp8(*args)
+    q4, qs4, k4, ks4, _ = rq.qk_gemma_rmsnorm_gate_mxfp4(*args)
+    torch.cuda.synchronize()
+    o = ref.qk_gemma_rmsnorm_gate(*host, 3, 2, 256, 1e-6)
+    qb, kb = inputs.bits(q), inputs.bits(kk)
+    assert (inputs.bits(gate) == o["gate"]).all()
+    check_bf16_close(qb, o["q"], f"q heads at 2^{mag}")
+    check_bf16_close(kb, o["k"], f"k heads at 2^{mag}")
+    for heads, c8, s8, c4, s4 in ((qb, q8, qs8, q4, qs4), (kb, k8, ks8, k4, ks4)):
+        h = heads.reshape(-1, 256)
+        w8, w4 = ref.quantize_fp8(h, 256), ref.quantize_mxfp4(h)
+        assert (c8.view(torch.uint8).cpu().numpy().reshape(-1, 256) == w8["q"]).all()
+        assert (s8.cpu().numpy().reshape(-1) == w8["scale"].reshape(-1)).all()
+        assert (c4.cpu().numpy().reshape(-1, 128) == w4["q"]).all()
+        assert (s4.cpu().numpy().reshape(-1, 8) == w4["scale"]).all()

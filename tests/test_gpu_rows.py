@@ -479,3 +479,16 @@ def test_inf_rows(ref, fmt, dtype):
         assert (q[keep] == oq[keep]).all(), "signed-zero codes of the finite granules"
     for row in (0, 3):
         assert (gpu["y"][row] == o["y"][row]).sum() >= H - 2
+
+
+@pytest.mark.parametrize("fmt", ["fp8_token", "fp8_group", "mxfp4"])
+@pytest.mark.parametrize("M,H,mag", [(5, 16384, 60), (3, 4096, 100), (4, 7168, 120), (70, 2048, 64), (9, 544, 70)])
+def test_huge_rows(ref, fmt, M, H, mag):
+    """Rows whose fp32 sum of squares overflows (|r| around 2^mag; bf16 reaches
+    2^128): the kernel sums again with r scaled by 2^-80 and must match the
+    oracle (fp64) to the usual bar, instead of collapsing to rstd 0."""
+    d = inputs.random_rows(M, H, seed=mag + H)
+    for key in ("x", "residual"):
+        d[key] = (d[key].float() * 2.0 ** mag).to(torch.bfloat16)  # exact: a power of two, no overflow
+    group = 32 if H % 128 else 128
+    run_case(ref, fmt, d, 1e-6, group, what=f"{fmt}-huge-{M}x{H}-2^{mag}")
