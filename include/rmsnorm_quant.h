@@ -92,6 +92,8 @@ typedef enum rq_status {
  *             (nearest-even; y / scale is an IEEE fp32 quotient)
  *  scale_out  [M] fp32 out: scale = fp32(max |y| over the row) / 448;
  *             an all-zero row has scale 0 and codes 0x00 / 0x80 (sign of zero)
+ *             when eps > 0; with eps = 0 its y is 0 * (1/0), NaN, and so are
+ *             its scale and codes
  *  y_out      [M, H] bf16 out or NULL: the normalized row y
  *  stream     hipStream_t
  */

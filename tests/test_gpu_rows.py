@@ -492,3 +492,26 @@ def test_huge_rows(ref, fmt, M, H, mag):
         d[key] = (d[key].float() * 2.0 ** mag).to(torch.bfloat16)  # exact: a power of two, no overflow
     group = 32 if H % 128 else 128
     run_case(ref, fmt, d, 1e-6, group, what=f"{fmt}-huge-{M}x{H}-2^{mag}")
+
+
+@pytest.mark.parametrize("fmt", ["fp8_token", "fp8_group", "mxfp4"])
+def test_zero_row_without_eps(ref, fmt):
+    """An all-zero row with eps = 0 has rstd = 1/0 and y = 0 * Inf: NaN, on the
+    GPU as in the oracle (the NaN's sign bit may differ).  FP8: NaN scale and
+    NaN codes; MXFP4: E8M0 255.  A normal row beside it is unaffected."""
+    H = 256
+    d = inputs.random_rows(3, H, seed=5)
+    xb, rb, wb = (inputs.bits(d[k]).copy() for k in ("x", "residual", "weight"))
+    xb[0], rb[0] = 0, 0
+    xb[1], rb[1] = 0x8000, 0x8000          # -0 + -0 = -0
+    gpu = gpu_call(fmt, *(inputs.from_bits(a).to(DEV) for a in (xb, rb, wb)), 0.0)
+    o = oracle_call(ref, fmt, xb, rb, wb, 0.0)
+    assert (gpu["residual_out"] == o["residual_out"]).all()
+    for row in (0, 1):
+        assert ((gpu["y"][row] & 0x7FFF) > 0x7F80).all() and ((o["y"][row] & 0x7FFF) > 0x7F80).all()
+        if fmt == "mxfp4":
+            assert (gpu["scale"][row] == 255).all() and (o["scale"][row] == 255).all()
+        else:
+            assert np.isnan(gpu["scale"][row]).all() and np.isnan(o["scale"][row]).all()
+            assert ((gpu["q"][row] & 0x7F) == 0x7F).all() and ((o["q"][row] & 0x7F) == 0x7F).all()
+    check(ref, fmt, {k: v[2:] for k, v in gpu.items()}, {k: v[2:] for k, v in o.items()}, 128, "normal row")
