@@ -131,3 +131,26 @@ def test_qk_huge_heads(ref, mag):
         assert (s8.cpu().numpy().reshape(-1) == w8["scale"].reshape(-1)).all()
         assert (c4.cpu().numpy().reshape(-1, 128) == w4["q"]).all()
         assert (s4.cpu().numpy().reshape(-1, 8) == w4["scale"]).all()
+
+
+def test_qk_zero_head_without_eps(ref):
+    """An all-zero head with eps = 0 normalizes to 0 * (1/0), NaN, as in the
+    oracle: NaN bf16 head, NaN FP8 scale and codes, E8M0 255; the other heads
+    are unaffected."""
+    d = inputs.qk_inputs(inputs.QKWorkload("qk_zero", 3, 2, 1, 64, seed=12))
+    qg, k = inputs.bits(d["qg"]).copy(), inputs.bits(d["k"]).copy()
+    qg[1, 2 * 64 * 1: 2 * 64 * 1 + 64] = 0          # q head 1 of token 1
+    host = (qg, k, inputs.bits(d["q_w"]), inputs.bits(d["k_w"]))
+    args = (device(qg), device(k), d["q_w"].to(DEV), d["k_w"].to(DEV), 2, 1, 64, 0.0)
+    q, kk, _ = rq.qk_gemma_rmsnorm_gate(*args)
+    q8, qs8, _, _, _ = rq.qk_gemma_rmsnorm_gate_fp8(*args)
+    q4, qs4, _, _, _ = rq.qk_gemma_rmsnorm_gate_mxfp4(*args)
+    torch.cuda.synchronize()
+    o = ref.qk_gemma_rmsnorm_gate(*host, 2, 1, 64, 0.0)
+    qb = inputs.bits(q)
+    assert is_nan16(qb[1, 1]).all() and is_nan16(o["q"][1, 1]).all()
+    assert np.isnan(qs8.cpu().numpy()[1, 1]) and ((q8.view(torch.uint8).cpu().numpy()[1, 1] & 0x7F) == 0x7F).all()
+    assert (qs4.cpu().numpy()[1, 1] == 255).all()
+    m = np.ones((3, 2), bool); m[1, 1] = False
+    check_bf16_close(qb[m], o["q"][m], "other q heads")
+    check_bf16_close(inputs.bits(kk), o["k"], "k heads")
