@@ -167,3 +167,64 @@ def test_graph_replay_stress_bitwise():
             g.replay()
         torch.cuda.synchronize()
         assert digest(outs) == want, f"outputs differ from the eager result after {100 * (i + 1)} replays"
+
+
+def test_graph_replay_quantized_qk_and_column_major_scales():
+    """The QK entry points with FP8 and MXFP4 q and k, and the column-major-scale
+    row calls, inside one captured graph; each replay reproduces the eager
+    results bit for bit (outputs cleared by fill kernels between replays)."""
+    d = inputs.row_inputs(inputs.DECODE_4096)
+    x, r, w = (d[k].to(DEV) for k in ("x", "residual", "weight"))
+    qd = inputs.qk_inputs(inputs.QK_DECODE)
+    qg, k, qw, kw = (qd[n].to(DEV) for n in ("qg", "k", "q_w", "k_w"))
+    M, H = x.shape
+    u8, f32, bf = torch.uint8, torch.float32, torch.bfloat16
+    outs = dict(
+        q8=torch.empty((64, 16, 256), dtype=u8, device=DEV), qs8=torch.empty((64, 16), dtype=f32, device=DEV),
+        k8=torch.empty((64, 2, 256), dtype=u8, device=DEV), ks8=torch.empty((64, 2), dtype=f32, device=DEV),
+        g8=torch.empty((64, 16, 256), dtype=bf, device=DEV),
+        q4=torch.empty((64, 16, 128), dtype=u8, device=DEV), qs4=torch.empty((64, 16, 8), dtype=u8, device=DEV),
+        k4=torch.empty((64, 2, 128), dtype=u8, device=DEV), ks4=torch.empty((64, 2, 8), dtype=u8, device=DEV),
+        g4=torch.empty((64, 16, 256), dtype=bf, device=DEV),
+        tq=torch.empty((M, H), dtype=u8, device=DEV), tro=torch.empty((M, H), dtype=bf, device=DEV),
+        ts=torch.empty((H // 128, M + 8), dtype=f32, device=DEV),
+        mq=torch.empty((M, H // 2), dtype=u8, device=DEV), mro=torch.empty((M, H), dtype=bf, device=DEV),
+        ms=torch.empty((H // 32, M + 8), dtype=u8, device=DEV),
+    )
+
+    def step():
+        o = outs
+        assert rq.qk_gemma_rmsnorm_gate_fp8(qg, k, qw, kw, 16, 2, 256, 1e-6, q_out=o["q8"], q_scale_out=o["qs8"],
+                                            k_out=o["k8"], k_scale_out=o["ks8"], gate_out=o["g8"]) is not None
+        assert rq.qk_gemma_rmsnorm_gate_mxfp4(qg, k, qw, kw, 16, 2, 256, 1e-6, q_out=o["q4"], q_scale_out=o["qs4"],
+                                              k_out=o["k4"], k_scale_out=o["ks4"], gate_out=o["g4"]) is not None
+        assert rq.rmsnorm_quant_fp8_per_group_tscale(x, r, w, 1e-6, 128, q_out=o["tq"], residual_out=o["tro"],
+                                                     scale_out=o["ts"][:, :M]) is not None
+        assert rq.rmsnorm_quant_mxfp4_tscale(x, r, w, 1e-6, q_out=o["mq"], residual_out=o["mro"],
+                                             scale_out=o["ms"][:, :M]) is not None
+
+    def snapshot():
+        return [t.clone() for t in outs.values()]
+
+    for t in outs.values():
+        t.zero_()
+    step()
+    torch.cuda.synchronize()
+    eager = snapshot()
+    s = torch.cuda.Stream()
+    s.wait_stream(torch.cuda.current_stream())
+    with torch.cuda.stream(s):
+        step()
+    torch.cuda.current_stream().wait_stream(s)
+    torch.cuda.synchronize()
+    g = torch.cuda.CUDAGraph()
+    with torch.cuda.graph(g):
+        step()
+    for i in range(4):
+        for t in outs.values():
+            t.zero_()
+        _ = (x.float() * 3).sum().item()
+        g.replay()
+        torch.cuda.synchronize()
+        for name, a, b in zip(outs, snapshot(), eager):
+            assert torch.equal(a.view(torch.uint8), b.view(torch.uint8)), f"replay {i}: {name} differs from eager"
