@@ -669,8 +669,10 @@ def cpu_baseline(inputs, wl, qw, nbytes):
     """The oracle as it stands (untuned, one row at a time in fp64), threaded
     over row slices (ctypes releases the GIL) on the host cores next to the GPU.
     Sample: whole steps of the benchmark's work (all rows, the three formats and
-    the QK case), repeated until about 10 s of CPU time have been spent."""
+    the QK case), at least three and until about 10 s of CPU time have been
+    spent; the median step.  On one thread: a slice of the rows, median of three."""
     import concurrent.futures as cf
+    import statistics
 
     import oracle
     ref = oracle.get()
@@ -688,29 +690,32 @@ def cpu_baseline(inputs, wl, qw, nbytes):
         ref.mxfp4(xb[lo:hi], rb[lo:hi], wb, wl.eps)
 
     step_bytes = sum(nbytes.values())
-    reps, elapsed = 0, 0.0
+    steps = []
     cpu0 = time.process_time()
     with cf.ThreadPoolExecutor(threads) as ex:
-        while reps < 8 and (reps == 0 or time.process_time() - cpu0 < 10.0):
+        while len(steps) < 3 or (len(steps) < 8 and time.process_time() - cpu0 < 10.0):
             t0 = time.perf_counter()
             list(ex.map(lambda b: part(*b), bounds))
             ref.qk_gemma_rmsnorm_gate(*qargs, qw.Hq, qw.Hk, qw.D, qw.eps)
-            elapsed += time.perf_counter() - t0
-            reps += 1
+            steps.append(time.perf_counter() - t0)
     cpu_s = time.process_time() - cpu0
     # the same oracle on one thread, over one slice of the rows
     one_rows = max(1, rows // 16)
-    t0 = time.perf_counter()
-    part(0, one_rows)
-    one_s = time.perf_counter() - t0
+    ones = []
+    for _ in range(3):
+        t0 = time.perf_counter()
+        part(0, one_rows)
+        ones.append(time.perf_counter() - t0)
     one_bytes = sum(row_bytes(f, one_rows, wl.H) for f in ("fp8_token", "fp8_group", "mxfp4"))
-    return {"value": round(reps * step_bytes / elapsed / 1e9, 3), "unit": "GB/s", "cores": threads,
+    step_s, one_s = statistics.median(steps), statistics.median(ones)
+    return {"value": round(step_bytes / step_s / 1e9, 3), "unit": "GB/s", "cores": threads,
             "kind": "oracle",
-            "sample": f"{reps} whole step(s): all {rows} rows of [{rows}, {wl.H}] in the three formats plus the "
-                      f"QK case, threaded over row slices",
-            "wall_s": round(elapsed, 3), "cpu_s": round(cpu_s, 2),
+            "sample": f"{len(steps)} whole steps (the median taken): all {rows} rows of [{rows}, {wl.H}] in the "
+                      f"three formats plus the QK case, threaded over row slices",
+            "step_s": round(step_s, 3), "wall_s": round(sum(steps), 3), "cpu_s": round(cpu_s, 2),
             "single_thread": {"value": round(one_bytes / one_s / 1e9, 3), "unit": "GB/s", "cores": 1,
-                              "sample": f"the first {one_rows} rows of [{rows}, {wl.H}] in the three formats",
+                              "sample": f"the first {one_rows} rows of [{rows}, {wl.H}] in the three formats, "
+                                        f"median of 3",
                               "wall_s": round(one_s, 3)}}
 
 
