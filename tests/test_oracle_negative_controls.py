@@ -48,6 +48,9 @@ MUTATIONS = {
                                "scale_out[m * G + g] = row_major[m * G + g]"),
     "qk_mxfp4_k_from_q": ("quantize_mxfp4_rows(kBf16, k_bf16.data(), T * Hk, D, k_codes, k_scale)",
                           "quantize_mxfp4_rows(kBf16, q_bf16.data(), T * Hk, D, k_codes, k_scale)"),
+    "qk_drop_eps": ("std::sqrt(ss / (double)D + (double)eps)", "std::sqrt(ss / (double)D)"),
+    "qk_mean_over_D_minus_1": ("std::sqrt(ss / (double)D + (double)eps)", "std::sqrt(ss / (double)(D - 1) + (double)eps)"),
+    "qk_k_uses_q_weight": ("gemma_norm(k + t * ld_k + D * h, k_w,", "gemma_norm(k + t * ld_k + D * h, q_w,"),
     "qk_fp8_k_from_q": ("quantize_fp8_rows(kBf16, k_bf16.data(), T * Hk, D, D, k_codes, k_scale)",
                         "quantize_fp8_rows(kBf16, q_bf16.data(), T * Hk, D, D, k_codes, k_scale)"),
 }
