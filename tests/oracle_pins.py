@@ -737,6 +737,70 @@ def pin_f16_weight_probe(ref):
     assert (m["scale"] == bytes_).all() and (m["q"] == packed).all()
 
 
+def pin_nonfinite_granules(ref):
+    """Reading c16: a NaN reaches every value that depends on it and no other.
+    In the quantize step a NaN element makes its own granule's FP8 scale NaN
+    (E8M0 byte 255) and leaves the others as they were.  In the whole step a NaN
+    in x makes the row's rstd NaN, so every granule of that row is NaN; an Inf
+    makes rstd 0 (1/sqrt(Inf)), so its element is NaN (Inf * 0) and the rest of
+    the row signed zeros: only its own granule is non-finite."""
+    d = inputs.random_rows(3, 256, seed=8)
+    xb, rb, wb = (inputs.bits(d[k]).copy() for k in ("x", "residual", "weight"))
+    o = ref.fp8_per_token(xb, rb, wb, 1e-6, emit_y=True)
+    y = o["y"].copy()
+    y[1, 70] = 0x7FC0                                   # NaN in group 0 (of 128), block 2 (of 32)
+    q0, qn = ref.quantize_fp8(o["y"], 128), ref.quantize_fp8(y, 128)
+    assert np.isnan(qn["scale"][1, 0]) and (qn["scale"][1, 1] == q0["scale"][1, 1])
+    assert (qn["q"][1, 128:] == q0["q"][1, 128:]).all() and qn["q"][1, 70] & 0x7F == 0x7F
+    assert (qn["scale"][[0, 2]] == q0["scale"][[0, 2]]).all()
+    m0, mn = ref.quantize_mxfp4(o["y"]), ref.quantize_mxfp4(y)
+    assert mn["scale"][1, 2] == 255
+    assert (np.delete(mn["scale"][1], 2) == np.delete(m0["scale"][1], 2)).all()
+    xb[1, 70] = 0x7FC0                                  # NaN in x: the whole row
+    xb[2, 200] = 0x7F80                                 # +Inf in x: group 1, block 6
+    t = ref.fp8_per_token(xb, rb, wb, 1e-6, emit_y=True)
+    assert np.isnan(t["scale"][1]).all() and np.isnan(t["scale"][2]).all() and np.isfinite(t["scale"][0]).all()
+    assert ((t["y"][1] & 0x7FFF) > 0x7F80).all()
+    assert (t["y"][2, 200] & 0x7FFF) > 0x7F80 and (np.delete(t["y"][2], 200) & 0x7FFF == 0).all()
+    g = ref.fp8_per_group(xb, rb, wb, 1e-6, 128)
+    assert np.isnan(g["scale"][1]).all() and np.isnan(g["scale"][2, 1]) and g["scale"][2, 0] == 0.0
+    mx = ref.mxfp4(xb, rb, wb, 1e-6)
+    assert (mx["scale"][1] == 255).all() and mx["scale"][2, 6] == 255 and (np.delete(mx["scale"][2], 6) == 0).all()
+
+
+def pin_scale_invariance(ref):
+    """With eps = 0 the step is invariant under scaling x and residual by 2^k
+    (exactly: the residual add, the squares, their sum, the square root and
+    the reciprocal all commute with power-of-two scaling when nothing
+    overflows or underflows in the arithmetic used), so y, the codes and the
+    scales are bit-identical for k = -60, 60 and 100; residual_out scales by
+    2^k.  The same holds for QK heads.  Pins the oracle's behaviour for rows
+    whose squares leave the fp32 range."""
+    d = inputs.random_rows(3, 512, seed=9)
+    xb, rb, wb = (inputs.bits(d[k]) for k in ("x", "residual", "weight"))
+    scaled = lambda a, k: np_bf16_round(np_bf16_value(a) * 2.0 ** k)
+    base = dict(t=ref.fp8_per_token(xb, rb, wb, 0.0, emit_y=True), g=ref.fp8_per_group(xb, rb, wb, 0.0, 128),
+                m=ref.mxfp4(xb, rb, wb, 0.0, emit_y=True))
+    for k in (-60, 60, 100):
+        xs, rs = scaled(xb, k), scaled(rb, k)
+        assert (np_bf16_value(xs) == np_bf16_value(xb) * 2.0 ** k).all()
+        t = ref.fp8_per_token(xs, rs, wb, 0.0, emit_y=True)
+        assert (np_bf16_value(t["residual_out"]) == np_bf16_value(base["t"]["residual_out"]) * 2.0 ** k).all()
+        assert (t["y"] == base["t"]["y"]).all(), f"y changed under scaling by 2^{k}"
+        assert (t["q"] == base["t"]["q"]).all() and (t["scale"] == base["t"]["scale"]).all()
+        g = ref.fp8_per_group(xs, rs, wb, 0.0, 128)
+        assert (g["q"] == base["g"]["q"]).all() and (g["scale"] == base["g"]["scale"]).all()
+        m = ref.mxfp4(xs, rs, wb, 0.0, emit_y=True)
+        assert (m["q"] == base["m"]["q"]).all() and (m["scale"] == base["m"]["scale"]).all()
+    w = inputs.QKWorkload("qk_scale", 2, 2, 1, 64, seed=10)
+    qd = inputs.qk_inputs(w)
+    qg, kk, qw, kw = (inputs.bits(qd[n]) for n in ("qg", "k", "q_w", "k_w"))
+    o0 = ref.qk_gemma_rmsnorm_gate(qg, kk, qw, kw, 2, 1, 64, 0.0)
+    for k in (-60, 100):
+        o = ref.qk_gemma_rmsnorm_gate(scaled(qg, k), scaled(kk, k), qw, kw, 2, 1, 64, 0.0)
+        assert (o["q"] == o0["q"]).all() and (o["k"] == o0["k"]).all(), f"QK changed under scaling by 2^{k}"
+
+
 ALL_PINS = [
     pin_bf16_decode, pin_bf16_round_vs_torch, pin_bf16_round_vs_search,
     pin_e4m3_table, pin_e4m3_bruteforce, pin_e4m3_fp32_quotients,
@@ -746,4 +810,5 @@ ALL_PINS = [
     pin_strided_inputs, pin_qk, pin_qk_fp8, pin_qk_mxfp4, pin_transposed_scales, pin_invariants_on_workloads,
     pin_quantize_step,
     pin_f16_decode, pin_f16_round, pin_f16_rows, pin_f16_weight_probe,
+    pin_nonfinite_granules, pin_scale_invariance,
 ]

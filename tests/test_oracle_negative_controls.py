@@ -48,6 +48,10 @@ MUTATIONS = {
                                "scale_out[m * G + g] = row_major[m * G + g]"),
     "qk_mxfp4_k_from_q": ("quantize_mxfp4_rows(kBf16, k_bf16.data(), T * Hk, D, k_codes, k_scale)",
                           "quantize_mxfp4_rows(kBf16, q_bf16.data(), T * Hk, D, k_codes, k_scale)"),
+    "mxfp4_scale_direction": ("std::ldexp(e.value(y[i]), -((int)b - 127))", "std::ldexp(e.value(y[i]), ((int)b - 127))"),
+    "group_scale_index": ("scale_out + m * G + g);", "scale_out + m * G);"),
+    "amax_ignores_nan": ("    if (std::isnan(a)) return a;\n", ""),
+    "sum_of_squares_in_float": ("double ss = 0.0;", "float ss = 0.0f;"),
     "qk_drop_eps": ("std::sqrt(ss / (double)D + (double)eps)", "std::sqrt(ss / (double)D)"),
     "qk_mean_over_D_minus_1": ("std::sqrt(ss / (double)D + (double)eps)", "std::sqrt(ss / (double)(D - 1) + (double)eps)"),
     "qk_k_uses_q_weight": ("gemma_norm(k + t * ld_k + D * h, k_w,", "gemma_norm(k + t * ld_k + D * h, q_w,"),
