@@ -51,6 +51,8 @@ MUTATIONS = {
     "mxfp4_scale_direction": ("std::ldexp(e.value(y[i]), -((int)b - 127))", "std::ldexp(e.value(y[i]), ((int)b - 127))"),
     "group_scale_index": ("scale_out + m * G + g);", "scale_out + m * G);"),
     "amax_ignores_nan": ("    if (std::isnan(a)) return a;\n", ""),
+    "quotient_in_double": ("float quotient = (float)v / s;  // IEEE fp32 division\n      q[i] = e4m3fn_round((double)quotient);",
+                           "double quotient = v / (double)s;\n      q[i] = e4m3fn_round(quotient);"),
     "sum_of_squares_in_float": ("double ss = 0.0;", "float ss = 0.0f;"),
     "qk_drop_eps": ("std::sqrt(ss / (double)D + (double)eps)", "std::sqrt(ss / (double)D)"),
     "qk_mean_over_D_minus_1": ("std::sqrt(ss / (double)D + (double)eps)", "std::sqrt(ss / (double)(D - 1) + (double)eps)"),
