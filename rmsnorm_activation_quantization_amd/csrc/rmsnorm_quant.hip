@@ -79,7 +79,9 @@ constexpr int kWave = 64;
 constexpr int kMaxChunks = 2;  // chunks per lane; rows need at most 16 waves * 64 lanes * 8 * 2 = 16384
 
 enum QuantMode { kFp8Token = 0, kFp8Group = 1, kMxfp4 = 2 };
-enum Stage { kStageFused = 0, kStageNorm = 1, kStageQuantize = 2 };
+// kStageFusedColScales: the fused step with column-major scales (the layout is a
+// compile-time choice, so the row-major kernels never read the scale stride).
+enum Stage { kStageFused = 0, kStageNorm = 1, kStageQuantize = 2, kStageFusedColScales = 3 };
 
 // ---------------------------------------------------------------------------
 // bf16 <-> fp32
@@ -339,7 +341,7 @@ struct RowArgs {
   float inv_h;           // 1 / H, rounded on the host
   int group_log2_lanes;  // per-group FP8: log2(group / 8)
   int groups_per_row;    // per-group FP8: H / group
-  int64_t scale_ld;      // per-group FP8 and MXFP4: 0 for row-major scales, else scale (m, g) at g * scale_ld + m
+  int64_t scale_ld;      // column-major scales (kStageFusedColScales): scale (m, g) at g * scale_ld + m
 };
 
 // Sum of a row from per-lane piece sums (one per chunk): each 64-lane block
@@ -375,15 +377,16 @@ constexpr int rows_per_block() { return kWPR == 1 ? 4 : 1; }
 template <int kWPR>
 constexpr int block_threads() { return kWave * kWPR * rows_per_block<kWPR>(); }
 
-// kStage selects what one launch does: the fused step (norm + quantize), or
-// one launch of the unfused sequence (norm alone writing y, or quantize alone
-// reading y from a.x with stride a.ldx).
+// kStage selects what one launch does: the fused step (norm + quantize; with
+// row-major or column-major scales), or one launch of the unfused sequence (norm
+// alone writing y, or quantize alone reading y from a.x with stride a.ldx).
 template <typename E, int kMode, int kNC, int kWPR, int kStage>
 __global__ __launch_bounds__(block_threads<kWPR>()) void fused_rows(const RowArgs a) {
   constexpr int kLanes = kWave * kWPR;
   constexpr int kChunk = kLanes * 8;
   constexpr int kRPB = rows_per_block<kWPR>();
   constexpr bool kNT = true;
+  constexpr bool kColScales = kStage == kStageFusedColScales;
   const int lane = threadIdx.x & (kWave - 1);
   const int wave = threadIdx.x / kWave;            // wave in the workgroup
   const int rloc = wave / kWPR;                     // row in the workgroup
@@ -552,7 +555,7 @@ __global__ __launch_bounds__(block_threads<kWPR>()) void fused_rows(const RowArg
         store8<kNT>(a.q + row * H + col, codes);
         if ((t & ((1 << gl) - 1)) == 0) {
           const int64_t gi = col >> (gl + 3);
-          reinterpret_cast<float*>(a.scale)[a.scale_ld ? gi * a.scale_ld + row : row * a.groups_per_row + gi] =
+          reinterpret_cast<float*>(a.scale)[kColScales ? gi * a.scale_ld + row : row * a.groups_per_row + gi] =
               g.scale;
         }
       }
@@ -568,7 +571,7 @@ __global__ __launch_bounds__(block_threads<kWPR>()) void fused_rows(const RowArg
         store4<kNT>(a.q + row * (H / 2) + col / 2, codes);
         if ((t & 3) == 0) {
           const int64_t bi = col / 32;
-          reinterpret_cast<uint8_t*>(a.scale)[a.scale_ld ? bi * a.scale_ld + row : row * (H / 32) + bi] =
+          reinterpret_cast<uint8_t*>(a.scale)[kColScales ? bi * a.scale_ld + row : row * (H / 32) + bi] =
               (uint8_t)byte;
         }
       }
@@ -965,7 +968,7 @@ rq_status fp8_per_group_impl(const uint16_t* x, int64_t ldx, const uint16_t* res
   a.group_log2_lanes = log2_lanes;
   a.groups_per_row = (int)(H / group);
   a.scale_ld = scale_ld;
-  return launch_rows<E, kFp8Group>(a, stream);
+  return scale_ld ? launch_rows<E, kFp8Group, kStageFusedColScales>(a, stream) : launch_rows<E, kFp8Group>(a, stream);
 }
 
 template <typename E>
@@ -977,7 +980,7 @@ rq_status mxfp4_impl(const uint16_t* x, int64_t ldx, const uint16_t* residual, i
   if (st != RQ_OK || M == 0) return st;
   RowArgs a = make_row_args(x, ldx, residual, ldr, weight, M, H, eps, residual_out, q_out, scale_out, y_out);
   a.scale_ld = scale_ld;
-  return launch_rows<E, kMxfp4>(a, stream);
+  return scale_ld ? launch_rows<E, kMxfp4, kStageFusedColScales>(a, stream) : launch_rows<E, kMxfp4>(a, stream);
 }
 
 template <typename E>
