@@ -397,6 +397,16 @@ __global__ __launch_bounds__(block_threads<kWPR>()) void fused_rows(const RowArg
   // tilings; its waves still reach every barrier (loads and stores are masked).
   const bool live = row < a.M;
   const int H = a.H;
+  if constexpr (kWPR <= 8) {
+    // Left to itself the compiler loads the row pointers in three rounds (the
+    // weight's, then x's and the residual's, each behind its own wait) and the
+    // output pointers later still.  An empty use of each puts them all in the
+    // first batch of argument loads: 1-5 % faster from 1 to 256 rows on MI355X.
+    // Rows of 16 waves (1024-thread workgroups) measured 2-3 % slower with it,
+    // so they keep the compiler's order.  No instruction is emitted.
+    asm volatile("" ::"s"(a.x), "s"(a.res), "s"(a.w), "s"(a.res_out));
+    asm volatile("" ::"s"(a.q), "s"(a.scale), "s"(a.y_out));
+  }
 
   __shared__ float lds_sum[kRPB][kWPR * kNC];
   __shared__ float lds_sum_tiny[kRPB][kWPR * kNC];
