@@ -17,7 +17,7 @@ import torch
 import rmsnorm_activation_quantization_amd as rq
 from rmsnorm_activation_quantization_amd import inputs
 from oracle_pins import np_bf16_round
-from parity import CODE_MATCH_MIN, check_bf16_close, signed_key
+from parity import CODE_MATCH_MIN, check_bf16_close, code_steps, signed_key
 
 pytestmark = pytest.mark.gpu
 DEV = "cuda:0"
@@ -45,13 +45,13 @@ def check_heads(codes, scale, heads_gpu, o_codes, o_scale, o_heads, what):
     match = float((codes == o_codes).mean()) if codes.size else 1.0
     assert match >= CODE_MATCH_MIN, f"{what}: only {match:.5f} of codes identical"
     nan = ((codes & 0x7F) == 0x7F) | ((o_codes & 0x7F) == 0x7F)
-    steps = np.abs(signed_key(codes, 0x80) - signed_key(o_codes, 0x80))[~nan]
+    steps = code_steps(codes, o_codes, 0x80)[~nan]
     assert steps.max(initial=0) <= 1, f"{what}: a code is {int(steps.max())} steps from the oracle's"
     diff = scale.view(np.uint32) != o_scale.view(np.uint32)
     if diff.any():
         ga = np.abs(signed_key(heads_gpu.reshape(-1, D), 0x8000)).max(axis=1)
         oa = np.abs(signed_key(o_heads.reshape(-1, D), 0x8000)).max(axis=1)
-        assert (np.abs(ga - oa)[diff] <= 1).all(), f"{what}: a scale differs without a one-ulp amax change"
+        assert (np.abs(ga - oa)[diff] == 1).all(), f"{what}: a scale differs without a one-ulp amax change"
     return match
 
 
