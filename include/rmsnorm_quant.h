@@ -40,13 +40,16 @@
  *                          ld < row length, eps negative or NaN, overlapping
  *                          buffers, a stride or size whose extent could not
  *                          be a real buffer (2^48 bytes or more);
- *      RQ_ERR_UNSUPPORTED  the device is not gfx950, a row start is not
- *                          16-byte aligned, H % 8 != 0, H above
- *                          RQ_MAX_HIDDEN, a granule that does not divide H,
- *                          an unsupported group size, or M (or T) above
- *                          2^31 - 1.  This is the "cannot fuse, use the
- *                          unfused path" answer of PR #29723.
- *      RQ_ERR_HIP          the kernel launch itself failed.
+ *      RQ_ERR_UNSUPPORTED  a row start is not 16-byte aligned, H % 8 != 0,
+ *                          H above RQ_MAX_HIDDEN, a granule that does not
+ *                          divide H, an unsupported group size, or M (or T)
+ *                          above 2^31 - 1.  This is the "cannot fuse, use
+ *                          the unfused path" answer of PR #29723.
+ *      RQ_ERR_DEVICE       the current HIP device is not an MI355X (gfx950).
+ *                          Every entry point, fused or unfused, returns it
+ *                          there, so it is an error, not a fallback signal.
+ *      RQ_ERR_HIP          the kernel launch itself failed, or the HIP
+ *                          runtime could not name the current device.
  *    Faults inside a kernel surface at the caller's next synchronization.
  *  - M == 0 (or T == 0) returns RQ_OK and launches nothing.
  *  - A call is one launch per step unless its grid would exceed 2^31
@@ -68,7 +71,8 @@ typedef enum rq_status {
   RQ_OK = 0,
   RQ_ERR_INVALID = 1,
   RQ_ERR_UNSUPPORTED = 2,
-  RQ_ERR_HIP = 3
+  RQ_ERR_HIP = 3,
+  RQ_ERR_DEVICE = 4
 } rq_status;
 
 /* Largest row length the fused row kernels accept (the row is held in

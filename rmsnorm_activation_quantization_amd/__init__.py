@@ -22,7 +22,7 @@ Row functions take bf16 or fp16 tensors and return their rows in the same
 dtype (the _f16 names are the same functions, named after the C entry points).
 """
 
-from .binding import (RQ_ERR_HIP, RQ_ERR_INVALID, RQ_ERR_UNSUPPORTED, RQ_MAX_HEAD_DIM, RQ_MAX_HIDDEN, RQ_OK,
+from .binding import (RQ_ERR_DEVICE, RQ_ERR_HIP, RQ_ERR_INVALID, RQ_ERR_UNSUPPORTED, RQ_MAX_HEAD_DIM, RQ_MAX_HIDDEN, RQ_OK,
                       lib, library_path, qk_gemma_rmsnorm_gate, qk_gemma_rmsnorm_gate_fp8, qk_gemma_rmsnorm_gate_mxfp4,
                       quantize_fp8_per_group,
                       rmsnorm_quant_fp8_per_group_tscale, rmsnorm_quant_fp8_per_group_tscale_f16,
@@ -40,5 +40,6 @@ __all__ = [
     "rmsnorm_quant_fp8_per_token_f16", "rmsnorm_quant_fp8_per_group_f16", "rmsnorm_quant_mxfp4_f16",
     "rmsnorm_residual_f16", "quantize_fp8_per_token_f16", "quantize_fp8_per_group_f16", "quantize_mxfp4_f16",
     "lib", "library_path", "status_string", "RQ_OK", "RQ_ERR_INVALID", "RQ_ERR_UNSUPPORTED", "RQ_ERR_HIP",
+    "RQ_ERR_DEVICE",
     "RQ_MAX_HIDDEN", "RQ_MAX_HEAD_DIM",
 ]

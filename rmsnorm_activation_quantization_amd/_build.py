@@ -10,6 +10,11 @@ ROOT = os.path.dirname(PKG)
 SOURCE = os.path.join(PKG, "csrc", "rmsnorm_quant.hip")
 INCLUDE = os.path.join(ROOT, "include")
 LIBRARY = os.path.join(PKG, "librmsnorm_quant.so")
+# The same source with the per-launch grid limit lowered to 2^14 work-items, so
+# that tests reach the multi-launch split of rows and QK heads with small
+# batches (a test build only; nothing else loads it).
+GRID_SPLIT_LIBRARY = os.path.join(PKG, "librmsnorm_quant_gridsplit.so")
+GRID_SPLIT_FLAGS = ("-DRQ_MAX_GRID_ITEMS=16384",)
 EXAMPLE_SOURCE = os.path.join(PKG, "csrc", "abi_example.c")
 EXAMPLE = os.path.join(PKG, "rq_abi_example")
 ROCM = os.environ.get("ROCM_PATH", "/opt/rocm")

@@ -3,7 +3,8 @@
 Every entry point has the name of the C function it calls (include/rmsnorm_quant.h).
 torch supplies device memory and the current stream; every step of the
 computation runs in the library's HIP kernels.  There is no other code path:
-if the library is missing or the device is not an MI355X, calls fail loudly.
+if the library is missing (RuntimeError at the first call) or the device is
+not an MI355X (RQ_ERR_DEVICE, RuntimeError), calls fail loudly.
 
 bf16 and fp16 rows: every row function dispatches on the dtype of x (or y):
 bf16 tensors run the bf16 kernels, fp16 tensors the _f16 ones, and the row
@@ -12,9 +13,10 @@ through the step).  Mixing dtypes raises ValueError.
 
 Return convention, following sglang PR #29723 (Key changes: the fused call
 returns its tuple, or None when the backend cannot fuse so that the caller runs
-the unfused sequence): a tuple on success; None for RQ_ERR_UNSUPPORTED, which
-the library decides before enqueuing anything; ValueError for RQ_ERR_INVALID;
-RuntimeError for RQ_ERR_HIP.
+the unfused sequence): a tuple on success; None for RQ_ERR_UNSUPPORTED (a shape
+or alignment the kernels do not take), which the library decides before
+enqueuing anything; ValueError for RQ_ERR_INVALID; RuntimeError for
+RQ_ERR_DEVICE and RQ_ERR_HIP.
 """
 
 from __future__ import annotations
@@ -27,7 +29,7 @@ import torch
 
 from . import _build
 
-RQ_OK, RQ_ERR_INVALID, RQ_ERR_UNSUPPORTED, RQ_ERR_HIP = 0, 1, 2, 3
+RQ_OK, RQ_ERR_INVALID, RQ_ERR_UNSUPPORTED, RQ_ERR_HIP, RQ_ERR_DEVICE = 0, 1, 2, 3, 4
 RQ_MAX_HIDDEN = 16384
 RQ_MAX_HEAD_DIM = 512
 
@@ -85,24 +87,29 @@ def library_path() -> str:
     return _build.LIBRARY
 
 
+def load(path: str) -> ctypes.CDLL:
+    """A build of the library at `path`, with every entry point's C signature
+    set.  Raises if the file does not exist."""
+    if not os.path.exists(path):
+        raise RuntimeError(
+            f"{path} is missing: build it first (python -c 'import __graft_entry__ as g; g.build()')")
+    handle = ctypes.CDLL(path)
+    for name, argtypes in _SIGNATURES.items():
+        fn = getattr(handle, name)
+        fn.argtypes = argtypes
+        fn.restype = ctypes.c_int
+    handle.rq_status_string.argtypes = [ctypes.c_int]
+    handle.rq_status_string.restype = ctypes.c_char_p
+    return handle
+
+
 def lib() -> ctypes.CDLL:
     """The loaded C library.  Raises if it has not been built."""
     global _lib
     if _lib is None:
         with _lock:
             if _lib is None:
-                path = library_path()
-                if not os.path.exists(path):
-                    raise RuntimeError(
-                        f"{path} is missing: build it first (python -c 'import __graft_entry__ as g; g.build()')")
-                handle = ctypes.CDLL(path)
-                for name, argtypes in _SIGNATURES.items():
-                    fn = getattr(handle, name)
-                    fn.argtypes = argtypes
-                    fn.restype = ctypes.c_int
-                handle.rq_status_string.argtypes = [ctypes.c_int]
-                handle.rq_status_string.restype = ctypes.c_char_p
-                _lib = handle
+                _lib = load(library_path())
     return _lib
 
 
@@ -111,7 +118,9 @@ def status_string(status: int) -> str:
 
 
 def _check(status: int, name: str):
-    """Map a status code: True on success, False for 'cannot fuse', raise otherwise."""
+    """Map a status code: True on success, False for 'cannot fuse'
+    (RQ_ERR_UNSUPPORTED), raise otherwise (ValueError for RQ_ERR_INVALID,
+    RuntimeError for RQ_ERR_DEVICE, RQ_ERR_HIP and unknown codes)."""
     if status == RQ_OK:
         return True
     if status == RQ_ERR_UNSUPPORTED:

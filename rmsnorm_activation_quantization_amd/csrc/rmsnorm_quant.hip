@@ -759,10 +759,14 @@ struct QKKernels {
 constexpr int kMaxDevices = 64;
 std::atomic<int> g_arch_state[kMaxDevices];  // 0 unknown, 1 gfx950, 2 other
 
+// A device other than gfx950 is RQ_ERR_DEVICE, not RQ_ERR_UNSUPPORTED: no entry
+// point of this library (fused or unfused) can run there, so "cannot fuse,
+// run the unfused sequence" would send the caller to calls that fail the same
+// way.
 rq_status check_device() {
   int dev = 0;
   if (hipGetDevice(&dev) != hipSuccess) return RQ_ERR_HIP;
-  if (dev < 0 || dev >= kMaxDevices) return RQ_ERR_UNSUPPORTED;
+  if (dev < 0 || dev >= kMaxDevices) return RQ_ERR_DEVICE;
   int state = g_arch_state[dev].load(std::memory_order_relaxed);
   if (state == 0) {
     hipDeviceProp_t prop;
@@ -770,7 +774,7 @@ rq_status check_device() {
     state = std::strncmp(prop.gcnArchName, "gfx950", 6) == 0 ? 1 : 2;
     g_arch_state[dev].store(state, std::memory_order_relaxed);
   }
-  return state == 1 ? RQ_OK : RQ_ERR_UNSUPPORTED;
+  return state == 1 ? RQ_OK : RQ_ERR_DEVICE;
 }
 
 bool aligned(const void* p, uintptr_t n) { return (reinterpret_cast<uintptr_t>(p) & (n - 1)) == 0; }
@@ -889,7 +893,13 @@ rq_status launch(const void* kernel, dim3 grid, dim3 block, void* args, void* st
 // Work-items one launch may hold.  A dispatch packet carries the grid size in
 // work-items as a 32-bit count; a larger batch is split into launches of at
 // most this many work-items each, every launch told its first row or head.
-constexpr int64_t kMaxGridItems = int64_t(1) << 31;
+// A build may lower the limit (RQ_MAX_GRID_ITEMS, a multiple of 256) so that
+// tests reach the split with small batches; the results do not change.
+#ifndef RQ_MAX_GRID_ITEMS
+#define RQ_MAX_GRID_ITEMS (int64_t(1) << 31)
+#endif
+constexpr int64_t kMaxGridItems = RQ_MAX_GRID_ITEMS;
+static_assert(kMaxGridItems % 256 == 0 && kMaxGridItems <= (int64_t(1) << 31), "grid limit");
 
 // Waves the chip holds at once: 256 CUs x 4 SIMDs x 8 wave slots per SIMD.
 constexpr int64_t kResidentWaves = 256 * 4 * 8;
@@ -1101,6 +1111,7 @@ rq_status qk_impl(const uint16_t* qg, int64_t ld_qg, const uint16_t* k, int64_t 
   // Whole tokens a launch, at most 2^31 work-items: the flat head index of a
   // launch stays below 2^31 (heads <= 2^17, so a launch holds >= 2^8 tokens).
   const int64_t tokens_per_launch = kMaxGridItems / kQKBlock * heads_per_wave / heads;
+  if (tokens_per_launch < 1) return RQ_ERR_UNSUPPORTED;  // only under a lowered grid limit
   const void* kernel = reinterpret_cast<const void*>(QKKernels<kOut>::k[log2_lanes]);
   for (int64_t tok0 = 0; tok0 < T; tok0 += tokens_per_launch) {
     const int64_t units = std::min<int64_t>(T - tok0, tokens_per_launch) * heads;
@@ -1221,8 +1232,9 @@ const char* rq_status_string(rq_status status) {
     case RQ_OK: return "RQ_OK";
     case RQ_ERR_INVALID: return "RQ_ERR_INVALID: invalid argument (null pointer, size, stride, eps or overlap)";
     case RQ_ERR_UNSUPPORTED:
-      return "RQ_ERR_UNSUPPORTED: not gfx950, misaligned rows, or a shape this library does not fuse";
+      return "RQ_ERR_UNSUPPORTED: misaligned rows, or a shape this library does not fuse";
     case RQ_ERR_HIP: return "RQ_ERR_HIP: the HIP runtime rejected the launch";
+    case RQ_ERR_DEVICE: return "RQ_ERR_DEVICE: the current device is not an MI355X (gfx950)";
   }
   return "unknown rq_status";
 }

@@ -54,8 +54,9 @@ def test_library_does_not_link_the_oracle():
 
 
 def test_status_strings(lib):
-    for code in (rq.RQ_OK, rq.RQ_ERR_INVALID, rq.RQ_ERR_UNSUPPORTED, rq.RQ_ERR_HIP):
+    for code in (rq.RQ_OK, rq.RQ_ERR_INVALID, rq.RQ_ERR_UNSUPPORTED, rq.RQ_ERR_HIP, rq.RQ_ERR_DEVICE):
         assert rq.status_string(code).startswith(("RQ_OK", "RQ_ERR"))
+    assert "gfx950" in rq.status_string(rq.RQ_ERR_DEVICE)
     assert rq.status_string(99) == "unknown rq_status"
 
 

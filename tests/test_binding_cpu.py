@@ -67,3 +67,20 @@ def test_missing_library_fails_loudly(monkeypatch):
         binding.lib()
     with pytest.raises(RuntimeError, match="missing"):
         binding._fn("rmsnorm_quant_mxfp4", torch.bfloat16)
+
+
+def test_status_mapping():
+    """'Cannot fuse' (a shape or alignment the kernels do not take) is the
+    binding's None; a device that is not an MI355X, a failed launch and an
+    unknown code raise, and so does an invalid argument."""
+    from rmsnorm_activation_quantization_amd import binding
+    assert binding._check(rq.RQ_OK, "f") is True
+    assert binding._check(rq.RQ_ERR_UNSUPPORTED, "f") is False
+    with pytest.raises(ValueError):
+        binding._check(rq.RQ_ERR_INVALID, "f")
+    with pytest.raises(RuntimeError, match="gfx950"):
+        binding._check(rq.RQ_ERR_DEVICE, "f")
+    with pytest.raises(RuntimeError):
+        binding._check(rq.RQ_ERR_HIP, "f")
+    with pytest.raises(RuntimeError):
+        binding._check(99, "f")
