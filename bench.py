@@ -163,6 +163,9 @@ def main():
         ))
     qw = inputs.QK_DECODE
     qd = {k: v.to(dev) for k, v in inputs.qk_inputs(qw).items()}
+    # The QK call reads a different copy of its inputs on every call (256 sets of
+    # 2.2 MB, 570 MB in all), so that it reads cold rows like the row kernels.
+    qk_sets = {n: qd[n].unsqueeze(0).repeat(QK_SETS, 1, 1) for n in ("qg", "k")}
     qk_out = (torch.empty((qw.T, qw.Hq, qw.D), dtype=torch.bfloat16, device=dev),
               torch.empty((qw.T, qw.Hk, qw.D), dtype=torch.bfloat16, device=dev),
               torch.empty((qw.T, qw.Hq, qw.D), dtype=torch.bfloat16, device=dev))
@@ -171,7 +174,9 @@ def main():
     nbytes = {"fp8_token": row_bytes("fp8_token", M, H), "fp8_group": row_bytes("fp8_group", M, H),
               "mxfp4": row_bytes("mxfp4", M, H), "qk": qk_bytes(qw.T, qw.Hq, qw.Hk, qw.D)}
 
-    def call(name, s):
+    def call(name, n):
+        """The n-th call of a kernel: rows rotate over the input sets, QK over its own pool."""
+        s = n % args.sets
         i, o = sets[s], outs[s]
         if name == "fp8_token":
             q, ro, sc = o["t"]
@@ -186,8 +191,9 @@ def main():
             r = rq.rmsnorm_quant_mxfp4(i["x"], i["residual"], i["weight"], wl.eps, q_out=q, residual_out=ro,
                                        scale_out=sc)
         else:
-            r = rq.qk_gemma_rmsnorm_gate(qd["qg"], qd["k"], qd["q_w"], qd["k_w"], qw.Hq, qw.Hk, qw.D, qw.eps,
-                                         q_out=qk_out[0], k_out=qk_out[1], gate_out=qk_out[2])
+            r = rq.qk_gemma_rmsnorm_gate(qk_sets["qg"][n % QK_SETS], qk_sets["k"][n % QK_SETS], qd["q_w"], qd["k_w"],
+                                         qw.Hq, qw.Hk, qw.D, qw.eps, q_out=qk_out[0], k_out=qk_out[1],
+                                         gate_out=qk_out[2])
         if r is None:
             raise RuntimeError(f"{name}: the library refused a supported shape")
 
@@ -195,7 +201,7 @@ def main():
     j = 0
     for w in range(args.warmup):
         for name in kernels:
-            call(name, j % args.sets)
+            call(name, j)
             j += 1
     torch.cuda.synchronize()
 
@@ -212,7 +218,7 @@ def main():
         g = torch.cuda.CUDAGraph()
         with torch.cuda.graph(g):
             for k in range(args.steps):
-                call(name, (j + k) % args.sets)
+                call(name, j + k)
         graphs[name] = g
     j += args.steps
     upload_graphs(torch, graphs.values(), stream)
@@ -247,10 +253,22 @@ def main():
         kernels_out[name] = {"us": round(us, 3), "bytes": nbytes[name], "GBps": round(gbs, 1),
                              "frac_of_peak": round(gbs / HBM_PEAK_GBS, 4)}
 
-    dom = max(("fp8_token", "fp8_group", "mxfp4"), key=lambda n: per_kernel_us[n])  # largest share of the step
+    # Each prefill kernel alone: its own K-call graph replayed after an untimed
+    # replay, the kernels taken in turn, median over the replays.  Inside the
+    # step a kernel's time depends on which phase ran before it; alone it does
+    # not, so the roofline kernel and its figure come from these times.
+    prefill = ("fp8_token", "fp8_group", "mxfp4")
+    alone = alone_us(torch, {n: graphs[n] for n in prefill}, args.steps, stream)
+    alone_out = {}
+    for name in prefill:
+        gbs = nbytes[name] / (alone[name] * 1e-6) / 1e9
+        alone_out[name] = {"us": round(alone[name], 3), "GBps": round(gbs, 1), "frac_of_peak": round(gbs / HBM_PEAK_GBS, 4)}
+    dom = max(prefill, key=lambda n: alone[n])  # the largest share of the step
     roofline = {"bound": "hbm", "kernel": f"rmsnorm_quant_{dom} [{M}, {H}]",
-                "achieved": kernels_out[dom]["GBps"], "peak": HBM_PEAK_GBS, "unit": "GB/s",
-                "frac": kernels_out[dom]["frac_of_peak"], "traffic": measured_traffic(dom)}
+                "achieved": alone_out[dom]["GBps"], "peak": HBM_PEAK_GBS, "unit": "GB/s",
+                "frac": alone_out[dom]["frac_of_peak"], "traffic": measured_traffic(dom),
+                "timing": f"median of {ALONE_REPLAYS} replays of a {args.steps}-call graph of this kernel alone "
+                          f"(HIP events on its stream)", "in_step_us": round(per_kernel_us[dom], 3)}
 
     result = {
         "metric": METRIC, "value": round(value, 1), "unit": "GB/s", "n_gpus": 1, "steps": args.steps,
@@ -261,10 +279,12 @@ def main():
                    "M": M, "H": H, "eps": wl.eps, "rotating_input_sets": args.sets, "step_bytes": step_bytes},
         "frac_of_peak": round(value / HBM_PEAK_GBS, 4),
         "kernels": kernels_out,
+        "kernels_alone": alone_out,
         "roofline": roofline,
         "wall_s_timed": round(wall, 4),
     }
     if not args.no_decode and not args.profile_pass:
+        result["prefill_4096x4096"] = half_batch(torch, rq, dev, sets, outs, args, stream)
         result["decode"] = decode_latency(torch, rq, inputs, dev)
         result["unfused_vs_fused"] = unfused_comparison(torch, rq, inputs, dev, sets, outs, per_kernel_us, args)
         result["qk_prefill"] = qk_prefill(torch, rq, dev)
@@ -273,6 +293,75 @@ def main():
     if not args.no_cpu_baseline and not args.profile_pass:
         result["cpu_baseline"] = cpu_baseline(inputs, wl, qw, nbytes)
     print(json.dumps(result), flush=True)
+
+
+ALONE_REPLAYS = 7
+QK_SETS = 256
+
+
+def alone_us(torch, graphs, calls, stream, replays=ALONE_REPLAYS):
+    """Median µs per call of each graph of `calls` back-to-back calls: one
+    untimed replay each, then `replays` rounds replaying the graphs in turn,
+    HIP events on the launch stream around each replay."""
+    import statistics
+    for g in graphs.values():
+        g.replay()
+    torch.cuda.synchronize()
+    times = {n: [] for n in graphs}
+    for _ in range(replays):
+        for n, g in graphs.items():
+            a, b = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+            a.record(stream)
+            g.replay()
+            b.record(stream)
+            torch.cuda.synchronize()
+            times[n].append(1000.0 * a.elapsed_time(b) / calls)
+    return {n: statistics.median(t) for n, t in times.items()}
+
+
+def half_batch(torch, rq, dev, sets, outs, args, stream):
+    """The three fused formats at [M/2, H] (4096 rows at the benchmark's shape),
+    the low end of the prefill range: 2 x sets rotating input sets (each half of
+    each [M, H] set, 512 MiB of inputs in all) and outputs, timed like
+    alone_us."""
+    M, H = sets[0]["x"].shape
+    h = M // 2
+    halves = [(st, o, lo) for st, o in zip(sets, outs) for lo in (0, h)]
+    n = len(halves)
+    key = {"fp8_token": "t", "fp8_group": "g", "mxfp4": "m"}
+
+    def fn(fmt, k):
+        st, o, lo = halves[k % n]
+        q, ro, sc = o[key[fmt]]
+        x, r, w = st["x"][lo:lo + h], st["residual"][lo:lo + h], st["weight"]
+        if fmt == "fp8_token":
+            return rq.rmsnorm_quant_fp8_per_token(x, r, w, 1e-6, q_out=q[lo:lo + h], residual_out=ro[lo:lo + h],
+                                                  scale_out=sc[lo:lo + h])
+        if fmt == "fp8_group":
+            return rq.rmsnorm_quant_fp8_per_group(x, r, w, 1e-6, 128, q_out=q[lo:lo + h], residual_out=ro[lo:lo + h],
+                                                  scale_out=sc[lo:lo + h])
+        return rq.rmsnorm_quant_mxfp4(x, r, w, 1e-6, q_out=q[lo:lo + h], residual_out=ro[lo:lo + h],
+                                      scale_out=sc[lo:lo + h])
+
+    calls = 2 * args.steps
+    graphs = {}
+    for fmt in key:
+        for k in range(n):
+            fn(fmt, k)
+        torch.cuda.synchronize()
+        g = torch.cuda.CUDAGraph()
+        with torch.cuda.graph(g):
+            for k in range(calls):
+                fn(fmt, k)
+        graphs[fmt] = g
+    upload_graphs(torch, graphs.values(), stream)
+    us = alone_us(torch, graphs, calls, stream)
+    res = {"M": h, "H": H, "rotating_input_sets": n}
+    for fmt in key:
+        nb = row_bytes(fmt, h, H)
+        gbs = nb / (us[fmt] * 1e-6) / 1e9
+        res[fmt] = {"us": round(us[fmt], 3), "bytes": nb, "GBps": round(gbs, 1), "frac_of_peak": round(gbs / HBM_PEAK_GBS, 4)}
+    return res
 
 
 def upload_graphs(torch, graphs, stream) -> None:
@@ -680,7 +769,11 @@ def cpu_baseline(inputs, wl, qw, nbytes):
     xb, rb, wb = (inputs.bits(d[k]) for k in ("x", "residual", "weight"))
     qd = inputs.qk_inputs(qw)
     qargs = [inputs.bits(qd[n]) for n in ("qg", "k", "q_w", "k_w")]
-    threads = max(1, min(16, len(os.sched_getaffinity(0))))
+    # Every core of the affinity set, unless the host states a smaller thread
+    # share for this process (OMP_NUM_THREADS, as a shared GPU host does).
+    affinity = len(os.sched_getaffinity(0))
+    share = int(os.environ.get("OMP_NUM_THREADS", "0") or 0)
+    threads = max(1, min(affinity, share) if share > 0 else affinity)
     rows = wl.M
     bounds = [(i * rows // threads, (i + 1) * rows // threads) for i in range(threads)]
 
@@ -709,7 +802,7 @@ def cpu_baseline(inputs, wl, qw, nbytes):
     one_bytes = sum(row_bytes(f, one_rows, wl.H) for f in ("fp8_token", "fp8_group", "mxfp4"))
     step_s, one_s = statistics.median(steps), statistics.median(ones)
     return {"value": round(step_bytes / step_s / 1e9, 3), "unit": "GB/s", "cores": threads,
-            "kind": "oracle",
+            "affinity_cores": affinity, "thread_share": share or None, "kind": "oracle",
             "sample": f"{len(steps)} whole steps (the median taken): all {rows} rows of [{rows}, {wl.H}] in the "
                       f"three formats plus the QK case, threaded over row slices",
             "step_s": round(step_s, 3), "wall_s": round(sum(steps), 3), "cpu_s": round(cpu_s, 2),
