@@ -370,28 +370,58 @@ __device__ __forceinline__ float row_sum(float (&part)[kNC], float* lds, int lan
   return s;
 }
 
-// Rows a workgroup holds: four one-wave rows, or one row of several waves (so
-// every barrier of a multi-wave row is uniform over its workgroup).
-template <int kWPR>
-constexpr int rows_per_block() { return kWPR == 1 ? 4 : 1; }
-template <int kWPR>
-constexpr int block_threads() { return kWave * kWPR * rows_per_block<kWPR>(); }
+// Rows a workgroup holds: four one-wave rows; one row of several waves; or, for
+// MXFP4 with column-major scales, as many rows of two or four waves as fill 512
+// threads, so that the workgroup can store each scale column's bytes for
+// consecutive rows together (kStagedColScales).
+constexpr int rows_per_block_of(int wpr, int mode, int stage) {
+  return wpr == 1 ? 4 : (stage == kStageFusedColScales && mode == kMxfp4 && wpr <= 4 ? 512 / (kWave * wpr) : 1);
+}
+template <int kWPR, int kMode, int kStage>
+constexpr int rows_per_block() { return rows_per_block_of(kWPR, kMode, kStage); }
+template <int kWPR, int kMode, int kStage>
+constexpr int block_threads() { return kWave * kWPR * rows_per_block<kWPR, kMode, kStage>(); }
+
+// Column-major scales: the order in which workgroups take rows.  Workgroups are
+// dealt to the 8 XCDs in turn (workgroup b runs on XCD b % 8), so in dispatch
+// order consecutive rows land on different XCDs, and every line of a scale
+// column (32 fp32 or 128 E8M0 values of consecutive rows) collects its values
+// in eight L2s, each writing back its part of the line.  This order hands each
+// XCD runs of 128 consecutive rows instead, so that one L2 fills each line.
+// Measured on MI355X at [8192, 4096]: per-group FP8 goes from 41.3 to 39.5 us
+// (row-major scales: 39.5 us) and the extra 64-byte write requests of the
+// partial lines disappear.  The tail of the grid past the last whole span of
+// 8 runs keeps dispatch order.  A bijection on [0, n).
+template <int kRPB>
+__device__ __forceinline__ uint32_t xcd_run_order(uint32_t b, uint32_t n) {
+  constexpr uint32_t kXcds = 8, kRun = 128 / kRPB;  // workgroups per run of 128 rows
+  constexpr uint32_t kSpan = kXcds * kRun;
+  if (b >= n / kSpan * kSpan) return b;
+  const uint32_t x = b % kXcds, k = b / kXcds;
+  return ((k / kRun) * kXcds + x) * kRun + k % kRun;
+}
 
 // kStage selects what one launch does: the fused step (norm + quantize; with
 // row-major or column-major scales), or one launch of the unfused sequence (norm
 // alone writing y, or quantize alone reading y from a.x with stride a.ldx).
 template <typename E, int kMode, int kNC, int kWPR, int kStage>
-__global__ __launch_bounds__(block_threads<kWPR>()) void fused_rows(const RowArgs a) {
+__global__ __launch_bounds__((block_threads<kWPR, kMode, kStage>())) void fused_rows(const RowArgs a) {
   constexpr int kLanes = kWave * kWPR;
   constexpr int kChunk = kLanes * 8;
-  constexpr int kRPB = rows_per_block<kWPR>();
+  constexpr int kRPB = rows_per_block<kWPR, kMode, kStage>();
   constexpr bool kNT = true;
   constexpr bool kColScales = kStage == kStageFusedColScales;
+  // MXFP4 with column-major scales and several rows a workgroup: the E8M0 bytes
+  // go through LDS and leave as runs of kRPB consecutive rows per scale column
+  // (one store per run instead of one per byte; measured 2-3 us faster at
+  // [8192, 4096] than one row a workgroup).
+  constexpr bool kStagedColScales = kColScales && kMode == kMxfp4 && kRPB > 1;
   const int lane = threadIdx.x & (kWave - 1);
   const int wave = threadIdx.x / kWave;            // wave in the workgroup
   const int rloc = wave / kWPR;                     // row in the workgroup
   const int wrow = wave % kWPR;                     // wave in the row
-  const int64_t row = a.row0 + (int64_t)blockIdx.x * kRPB + rloc;
+  const uint32_t blk = kColScales ? xcd_run_order<kRPB>(blockIdx.x, gridDim.x) : blockIdx.x;
+  const int64_t row = a.row0 + (int64_t)blk * kRPB + rloc;
   const int t = (int)threadIdx.x % kLanes;          // lane in the row
   // A row past the end only happens in the last workgroup of the few-waves
   // tilings; its waves still reach every barrier (loads and stores are masked).
@@ -411,6 +441,7 @@ __global__ __launch_bounds__(block_threads<kWPR>()) void fused_rows(const RowArg
   __shared__ float lds_sum[kRPB][kWPR * kNC];
   __shared__ float lds_sum_tiny[kRPB][kWPR * kNC];
   __shared__ uint32_t lds_max[kRPB][kWPR];
+  __shared__ uint8_t lds_e8m0[kStagedColScales ? kRPB : 1][kStagedColScales ? RQ_MAX_HIDDEN / 32 : 1];
 
   uint4 yp[kNC];
   if constexpr (kStage == kStageQuantize) {
@@ -483,8 +514,25 @@ __global__ __launch_bounds__(block_threads<kWPR>()) void fused_rows(const RowArg
     // rstd need not be correctly rounded (the tolerance on y is one bf16 ulp):
     // the hardware reciprocal square root keeps it off the critical path.
     const float t_ms = __builtin_fmaf(ss, a.inv_h, a.eps);
+    const bool in_range = !(t_ms < 0x1p-100f) && t_ms != __builtin_huge_valf();
+    // The second sum below has a barrier.  A multi-wave row alone in its
+    // workgroup takes it uniformly; with several multi-wave rows a workgroup,
+    // every wave reads every row's block sums (already in LDS, added in the same
+    // order as row_sum) and the whole workgroup takes the second sum when any
+    // of its rows needs it.
+    bool all_in_range = in_range;
+    if constexpr (kRPB > 1 && kWPR > 1) {
+#pragma unroll
+      for (int r = 0; r < kRPB; ++r) {
+        float sr = lds_sum[r][0];
+#pragma unroll
+        for (int b = 1; b < kNC * kWPR; ++b) sr += lds_sum[r][b];
+        const float tr = __builtin_fmaf(sr, a.inv_h, a.eps);
+        all_in_range = all_in_range && !(tr < 0x1p-100f) && tr != __builtin_huge_valf();
+      }
+    }
     float rstd;
-    if (!(t_ms < 0x1p-100f) && t_ms != __builtin_huge_valf()) {
+    if (__builtin_expect(all_in_range, true)) {
       rstd = __builtin_amdgcn_rsqf(t_ms);  // NaN propagates through here
     } else {
       // The fp32 squares left their range; sum them again with r scaled by an
@@ -509,7 +557,8 @@ __global__ __launch_bounds__(block_threads<kWPR>()) void fused_rows(const RowArg
         }
       }
       const float s2 = row_sum<kNC, kWPR>(s2c, lds_sum_tiny[rloc], lane, wrow);
-      rstd = __builtin_amdgcn_rsqf(__builtin_fmaf(s2, a.inv_h, a.eps * k * k)) * k;
+      rstd = in_range ? __builtin_amdgcn_rsqf(t_ms)
+                      : __builtin_amdgcn_rsqf(__builtin_fmaf(s2, a.inv_h, a.eps * k * k)) * k;
     }
 
     // 4. y = bf16((r * rstd) * w), optional bf16 side output.
@@ -581,9 +630,22 @@ __global__ __launch_bounds__(block_threads<kWPR>()) void fused_rows(const RowArg
         store4<kNT>(a.q + row * (H / 2) + col / 2, codes);
         if ((t & 3) == 0) {
           const int64_t bi = col / 32;
-          reinterpret_cast<uint8_t*>(a.scale)[kColScales ? bi * a.scale_ld + row : row * (H / 32) + bi] =
-              (uint8_t)byte;
+          if constexpr (kStagedColScales)
+            lds_e8m0[rloc][bi] = (uint8_t)byte;
+          else
+            reinterpret_cast<uint8_t*>(a.scale)[kColScales ? bi * a.scale_ld + row : row * (H / 32) + bi] =
+                (uint8_t)byte;
         }
+      }
+    }
+    if constexpr (kStagedColScales) {
+      // Every row of the workgroup has staged its bytes; each thread stores one
+      // byte, consecutive threads taking consecutive rows of a scale column.
+      __syncthreads();
+      const int64_t row_first = row - rloc;
+      for (int i = threadIdx.x; i < (H / 32) * kRPB; i += kRPB * kLanes) {
+        const int bi = i / kRPB, r = i % kRPB;
+        if (row_first + r < a.M) reinterpret_cast<uint8_t*>(a.scale)[bi * a.scale_ld + row_first + r] = lds_e8m0[r][bi];
       }
     }
   }
@@ -911,26 +973,32 @@ int chunks_per_lane(int H, int l) {
 
 // Waves per row (a power of two, 1..16).  Many rows: the fewest for which a
 // lane holds at most kMaxChunks chunks of 8 elements (few registers, and the
-// waves of later rows take the slots that finished ones free).  Fewer rows,
-// where the whole launch fits in the chip's wave slots at once: more waves, so
-// that a lane holds one chunk, as long as the launch still fits; a lane's
-// dependent chain from load to store is then as short as it gets, and there is
-// no second generation of waves to wait for.  The row's sum is the same for
-// every tiling.
-int waves_per_row_log2(int64_t M, int H) {
+// waves of later rows take the slots that finished ones free), except that a
+// row which one chunk of at most 8 waves covers exactly (H = 1024, 2048, 4096)
+// takes those waves with one chunk a lane: measured on MI355X 0-2.5 % faster
+// than two chunks from 2048 to 16384 rows at those widths, and not at widths
+// that would leave lanes idle (3072) or need 16-wave rows (5120-8192).  Fewer
+// rows, where the whole launch fits in the chip's wave slots at once: more
+// waves, so that a lane holds one chunk, as long as the launch still fits; a
+// lane's dependent chain from load to store is then as short as it gets, and
+// there is no second generation of waves to wait for.  The column-major scale
+// kernels keep the two-chunk shape they were measured in.  The row's sum is
+// the same for every tiling.
+int waves_per_row_log2(int64_t M, int H, bool one_chunk_rows) {
   int l = 0;
   while (l < 4 && chunks_per_lane(H, l) > kMaxChunks) ++l;
+  if (one_chunk_rows && l < 3 && chunks_per_lane(H, l) == 2 && H == 8 * (kWave << (l + 1))) ++l;
   while (l < 4 && chunks_per_lane(H, l) > 1 && M * (int64_t)(2 << l) <= kResidentWaves) ++l;
   return l;
 }
 
 template <typename E, int kMode, int kStage = kStageFused>
 rq_status launch_rows(RowArgs& a, void* stream) {
-  const int l = waves_per_row_log2(a.M, a.H);
+  const int l = waves_per_row_log2(a.M, a.H, kStage != kStageFusedColScales);
   const int wpr = 1 << l;
   const int lanes = kWave * wpr;
   const int nc = chunks_per_lane(a.H, l);
-  const int rpb = wpr == 1 ? 4 : 1;
+  const int rpb = rows_per_block_of(wpr, kMode, kStage);
   const int64_t rows_per_launch = kMaxGridItems / lanes;  // a multiple of rpb
   const void* kernel = reinterpret_cast<const void*>(RowKernels<E, kMode, kStage>::k[l][nc - 1]);
   for (int64_t row0 = 0; row0 < a.M; row0 += rows_per_launch) {

@@ -43,7 +43,7 @@ def using(handle):
 
 
 def launches_rows(M, H):
-    lanes = 64 * (4 if H == 4096 and M > 1024 else {256: 1, 4096: 8, 7168: 16}[H])
+    lanes = 64 * {256: 1, 4096: 8, 7168: 16}[H]
     return -(-M // (LIMIT // lanes))
 
 

@@ -110,3 +110,40 @@ def test_tscale_tiny_and_normal_rows_share_a_workgroup(M, H):
         assert torch.equal(a[3], b[3]) and torch.equal(a[1], b[1]), "y or residual_out differs"
         assert torch.equal(a[0].view(torch.uint8), b[0].view(torch.uint8)), "codes differ"
         assert torch.equal(a[2][:, :M], b[2].t()), "scales differ"
+
+
+MIXED = [(2049, 4096), (2049, 1024), (5001, 2048)]
+
+
+@pytest.mark.parametrize("M,H", MIXED, ids=[f"{m}x{h}" for m, h in MIXED])
+def test_tscale_mxfp4_mixed_rows_in_a_workgroup(ref, M, H):
+    """MXFP4 with column-major scales holds 2 or 4 multi-wave rows a workgroup
+    at these shapes.  Rows whose fp32 sum of squares overflows (|r| ~ 2^70) or
+    underflows (|r| ~ 2^-60 with eps = 0) take a second, rescaled sum with a
+    barrier of its own; here they sit beside ordinary rows in the same
+    workgroups (and a dead row pads the last one), so the workgroup must take
+    that barrier together.  Everything must equal the row-major call bit for
+    bit and meet the oracle bar."""
+    d = inputs.random_rows(M, H, seed=M + H)
+    idx = torch.arange(M)
+    scale = torch.ones(M)
+    scale[idx % 5 == 0] = 2.0 ** 70
+    scale[idx % 7 == 2] = 2.0 ** -60
+    for key in ("x", "residual"):
+        d[key] = (d[key].float() * scale[:, None]).to(torch.bfloat16)  # exact: powers of two
+    x, r, w = (d[k].to(DEV) for k in ("x", "residual", "weight"))
+    ld = padded(M)
+    buf = torch.full((H // 32, ld), 0xAB, dtype=torch.uint8, device=DEV)
+    out = rq.rmsnorm_quant_mxfp4_tscale(x, r, w, 0.0, scale_out=buf, emit_y=True)
+    row = rq.rmsnorm_quant_mxfp4(x, r, w, 0.0, emit_y=True)
+    assert out is not None and row is not None
+    torch.cuda.synchronize()
+    q, ro, sc, y = out
+    assert torch.equal(q, row[0]) and torch.equal(ro, row[1]) and torch.equal(y, row[3])
+    assert torch.equal(sc[:, :M], row[2].t()), "transposed E8M0 bytes differ from the row-major call's"
+    assert (sc[:, M:] == 0xAB).all(), "the padding past M was written"
+    xb, rb, wb = (inputs.bits(d[k]) for k in ("x", "residual", "weight"))
+    o = ref.mxfp4(xb, rb, wb, 0.0, emit_y=True)
+    gpu = to_np(dict(q=q, residual_out=ro, y=y))
+    gpu["scale"] = sc[:, :M].t().contiguous().cpu().numpy()
+    check_mxfp4(gpu, o, ref.quantize_mxfp4(gpu["y"]), f"tscale mixed {M}x{H}")
