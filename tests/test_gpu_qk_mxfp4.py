@@ -14,7 +14,7 @@ import torch
 
 import rmsnorm_activation_quantization_amd as rq
 from rmsnorm_activation_quantization_amd import inputs
-from parity import CODE_MATCH_MIN, check_bf16_close, code_steps
+from parity import CODE_MATCH_MIN, check_bf16_close, code_steps, mxfp4_value_steps
 from test_gpu_qk_fp8 import gpu_inputs
 
 pytestmark = pytest.mark.gpu
@@ -47,10 +47,16 @@ def run(ref, w: inputs.QKWorkload, ld_k=None, ld_qg_pad=0):
         g, r = nibbles(codes, D), nibbles(o[name], D)
         match = float((g == r).mean())
         assert match >= CODE_MATCH_MIN, f"{w.name} {name}: only {match:.5f} of codes identical"
-        steps = code_steps(g, r, 0x8)
-        assert steps.max(initial=0) <= 1, f"{w.name} {name}: a code is {int(steps.max())} steps off"
         bd = np.abs(scale.reshape(-1).astype(int) - o[name + "_scale"].reshape(-1).astype(int))
         assert bd.max(initial=0) <= 1, f"{w.name} {name}: an E8M0 byte differs by {int(bd.max())}"
+        same = np.repeat(bd.reshape(-1, D // 32) == 0, 32, axis=1)
+        steps = code_steps(g, r, 0x8)[same]
+        assert steps.max(initial=0) <= 1, f"{w.name} {name}: a code is {int(steps.max())} steps off"
+        if (~same).any():
+            gb = np.repeat(scale.reshape(-1, D // 32).astype(np.int64), 32, axis=1)
+            rb = np.repeat(o[name + "_scale"].reshape(-1, D // 32).astype(np.int64), 32, axis=1)
+            vs = mxfp4_value_steps(g[~same], gb[~same], r[~same], rb[~same])
+            assert vs.max(initial=0) <= 1, f"{w.name} {name}: a code is {vs.max():.2f} coarse steps off"
         if bd.any():
             ga = (heads.reshape(-1, 32).astype(np.int64) & 0x7FFF).max(axis=1)
             oa = (ob[name].reshape(-1, 32).astype(np.int64) & 0x7FFF).max(axis=1)

@@ -277,3 +277,55 @@ def test_mxfp4_e8m0_off_by_one_without_amax_change_rejected(ref):
     rq["scale"][4, 1] += 1
     with pytest.raises(AssertionError, match="without a one-ulp amax change"):
         check_mxfp4(gpu, o, rq, "planted")
+
+
+# ---- MXFP4 blocks whose E8M0 byte legitimately moved ----
+
+def _probe_block(ref):
+    """20 equal rows, H = 2048, through the oracle with x = residual = 512 and eps = 0, so
+    that y equals the weight bit for bit.  Block 0 holds amax 4.0 (E8M0 127)
+    and 2.875 (code 3.0 at scale 1, index 5).  The stand-in GPU row has the
+    4.0 one ulp lower (3.984375): its block byte is 126, and 2.875 encodes as
+    6.0 at scale 1/2 (index 7), the same value two indices away."""
+    from parity import mxfp4_value_steps  # noqa: F401  (imported where it is used below)
+    H = 2048
+    w = np.full(H, 0x3F80, np.uint16)          # 1.0
+    w[0], w[1] = 0x4080, 0x4038                # 4.0, 2.875
+    xb = np.full((20, H), 0x4400, np.uint16)  # 512
+    o = ref.mxfp4(xb, xb, w, 0.0, emit_y=True)
+    assert (o["y"] == w).all() and o["scale"][0, 0] == 127
+    gy = o["y"].copy()
+    gy[0, 0] = 0x407F                          # 3.984375, one ulp below 4.0
+    rq = ref.quantize_mxfp4(gy)
+    gpu = dict(residual_out=o["residual_out"].copy(), y=gy, q=rq["q"].copy(), scale=rq["scale"].copy())
+    assert gpu["scale"][0, 0] == 126
+    return gpu, o, rq
+
+
+def test_mxfp4_moved_byte_same_value_accepted(ref):
+    gpu, o, rq = _probe_block(ref)
+    # element 1: oracle index 5 (3.0 under 2^0), stand-in index 7 (6.0 under 2^-1)
+    assert (o["q"][0, 0] >> 4) == 5 and (gpu["q"][0, 0] >> 4) == 7
+    stats = check_mxfp4(gpu, o, rq, "moved byte")
+    assert stats["scale_diffs"] == 1
+
+
+def test_mxfp4_moved_byte_value_two_coarse_steps_rejected(ref):
+    gpu, o, rq = _probe_block(ref)
+    for d in (gpu, rq):
+        d["q"][0, 0] = (d["q"][0, 0] & 0x0F) | (5 << 4)   # 3.0 under 2^-1 = 1.5 against the oracle's 3.0
+    with pytest.raises(AssertionError, match="coarser grid"):
+        check_mxfp4(gpu, o, rq, "planted")
+
+
+def test_mxfp4_value_steps():
+    from parity import mxfp4_value_steps
+    one = np.array([1])
+    # equal bytes: adjacent codes one step, 1.5 -> 3 two steps (spacing 1 above 2)
+    assert mxfp4_value_steps(np.array([3]), 127 * one, np.array([4]), 127 * one)[0] == 1.0
+    assert mxfp4_value_steps(np.array([3]), 127 * one, np.array([5]), 127 * one)[0] == 1.5
+    assert mxfp4_value_steps(np.array([6]), 127 * one, np.array([7]), 127 * one)[0] == 1.0
+    # bytes one apart: 6.0 under 2^-1 equals 3.0 under 2^0
+    assert mxfp4_value_steps(np.array([7]), 126 * one, np.array([5]), 127 * one)[0] == 0.0
+    # signs: -0.5 and +0.5 are two steps apart
+    assert mxfp4_value_steps(np.array([0x9]), 127 * one, np.array([0x1]), 127 * one)[0] == 2.0
