@@ -15,8 +15,9 @@ count every tensor once: x, residual, weight read; residual_out, codes, scales
 written (the optional bf16 side output is not requested here).
 
 The K steps run as one captured HIP graph per kernel (back-to-back launches);
-after the W eager warmup steps the graphs are replayed once untimed (K more
-warmup steps, reported as config.graph_warmup_steps) before the timed replay.
+after the W eager warmup steps the graphs are replayed four times untimed (4K
+more warmup steps, reported as config.graph_warmup_steps) before the timed
+replay.
 Also reported: per-kernel time and GB/s (HIP events on the launch stream),
 decode-size microseconds per call (M = 16, H = 4096, all formats; graph replay
 of back-to-back calls over rotating inputs, as the pages time kernels) next to
@@ -225,13 +226,14 @@ def main():
         graphs[name] = g
     j += args.steps
     upload_graphs(torch, graphs.values(), stream)
-    # One untimed replay of the step's graphs, in step order, before the timed
-    # one: the first replay of freshly uploaded graphs varies from run to run
-    # by about 3 % of the step (measured on MI355X: 5506-5667 GB/s over three
-    # runs without it, 5665-5719 with it).  The timed replay then runs with
-    # the previous step's QK phase ahead of it, as every step but the first does.
-    for name in kernels:
-        graphs[name].replay()
+    # Untimed replays of the step's graphs, in step order, before the timed one.
+    # After the host has spent its time capturing and uploading, the first
+    # replays run slower: on MI355X the timed step measured 5639-5736 GB/s
+    # after one untimed replay, 5841-5862 after two, 5926-5946 after four or
+    # eight, and with four its kernels run as fast as each alone.
+    for _ in range(GRAPH_WARMUP_REPLAYS):
+        for name in kernels:
+            graphs[name].replay()
     torch.cuda.synchronize()
     marks = [torch.cuda.Event(enable_timing=True) for _ in range(len(kernels) + 1)]
     torch.cuda.synchronize()
@@ -302,7 +304,7 @@ def main():
         "config": {"workload": f"prefill rows [{M}, {H}] bf16 (per-token FP8, per-group-128 FP8, MXFP4) + "
                                f"QK GemmaRMSNorm+gate T={qw.T} Hq={qw.Hq} Hk={qw.Hk} D={qw.D}",
                    "M": M, "H": H, "eps": wl.eps, "rotating_input_sets": args.sets, "step_bytes": step_bytes,
-                   "graph_warmup_steps": args.steps},
+                   "graph_warmup_steps": GRAPH_WARMUP_REPLAYS * args.steps},
         "frac_of_peak": round(value / HBM_PEAK_GBS, 4),
         "kernels": kernels_out,
         "kernels_alone": alone_out,
@@ -323,6 +325,7 @@ def main():
 
 ALONE_REPLAYS = 7
 QK_SETS = 256
+GRAPH_WARMUP_REPLAYS = 4
 
 
 def alone_us(torch, graphs, calls, stream, replays=ALONE_REPLAYS):
