@@ -87,9 +87,13 @@ def test_rows_split(ref, split_lib, M, H, dt, fmt):
         check_fp8(gpu, o, ref.quantize_fp8(gpu["y"], g, dtype=kind), g, f"split {fmt} [{M}, {H}]")
 
 
-def test_tscale_and_unfused_split(split_lib):
-    M, H = 300, 4096
-    d = inputs.random_rows(M, H, 9100)
+@pytest.mark.parametrize("M", [300, 1501])
+def test_tscale_and_unfused_split(split_lib, M):
+    """[300, 4096] takes one row of 8 waves a workgroup; [1501, 4096] takes the
+    column-major MXFP4 shape of two rows of 4 waves a workgroup (64 rows a
+    launch under the lowered limit, so 24 launches, the last with a dead row)."""
+    H = 4096
+    d = inputs.random_rows(M, H, 9100 + M)
     x, r, w = (d[k].to(DEV) for k in ("x", "residual", "weight"))
     calls = [lambda: rq.rmsnorm_quant_mxfp4_tscale(x, r, w, 1e-6),
              lambda: rq.rmsnorm_quant_fp8_per_group_tscale(x, r, w, 1e-6, 128),
