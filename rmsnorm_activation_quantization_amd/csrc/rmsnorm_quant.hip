@@ -370,17 +370,21 @@ __device__ __forceinline__ float row_sum(float (&part)[kNC], float* lds, int lan
   return s;
 }
 
-// Rows a workgroup holds: four one-wave rows; one row of several waves; or, for
-// MXFP4 with column-major scales, as many rows of two or four waves as fill 512
-// threads, so that the workgroup can store each scale column's bytes for
-// consecutive rows together (kStagedColScales).
-constexpr int rows_per_block_of(int wpr, int mode, int stage) {
-  return wpr == 1 ? 4 : (stage == kStageFusedColScales && mode == kMxfp4 && wpr <= 4 ? 512 / (kWave * wpr) : 1);
+// Rows a workgroup holds at once: four one-wave rows, or one row of several
+// waves (so every barrier of a multi-wave row is uniform over its workgroup).
+constexpr int rows_per_block_of(int wpr) { return wpr == 1 ? 4 : 1; }
+// Rows a workgroup takes in turn.  MXFP4 with column-major scales: two rows of
+// several waves one after the other, so that each scale column receives its
+// two bytes in one store (the scattered one-byte stores of a column-major
+// scale are what such a launch spends its extra time on; measured on MI355X
+// 3-11 % faster than one row a workgroup from H = 2048 to 8192, except at
+// [8192, 2048], and ahead of four rows in turn or two rows at once).
+// Otherwise one.
+constexpr int rows_in_turn_of(int wpr, int mode, int stage) {
+  return stage == kStageFusedColScales && mode == kMxfp4 && wpr > 1 ? 2 : 1;
 }
-template <int kWPR, int kMode, int kStage>
-constexpr int rows_per_block() { return rows_per_block_of(kWPR, kMode, kStage); }
-template <int kWPR, int kMode, int kStage>
-constexpr int block_threads() { return kWave * kWPR * rows_per_block<kWPR, kMode, kStage>(); }
+template <int kWPR>
+constexpr int block_threads() { return kWave * kWPR * rows_per_block_of(kWPR); }
 
 // Column-major scales: the order in which workgroups take rows.  Workgroups are
 // dealt to the 8 XCDs in turn (workgroup b runs on XCD b % 8), so in dispatch
@@ -392,9 +396,9 @@ constexpr int block_threads() { return kWave * kWPR * rows_per_block<kWPR, kMode
 // (row-major scales: 39.5 us) and the extra 64-byte write requests of the
 // partial lines disappear.  The tail of the grid past the last whole span of
 // 8 runs keeps dispatch order.  A bijection on [0, n).
-template <int kRPB>
+template <int kRows>
 __device__ __forceinline__ uint32_t xcd_run_order(uint32_t b, uint32_t n) {
-  constexpr uint32_t kXcds = 8, kRun = 128 / kRPB;  // workgroups per run of 128 rows
+  constexpr uint32_t kXcds = 8, kRun = 128 / kRows;  // workgroups per run of 128 rows
   constexpr uint32_t kSpan = kXcds * kRun;
   if (b >= n / kSpan * kSpan) return b;
   const uint32_t x = b % kXcds, k = b / kXcds;
@@ -405,27 +409,30 @@ __device__ __forceinline__ uint32_t xcd_run_order(uint32_t b, uint32_t n) {
 // row-major or column-major scales), or one launch of the unfused sequence (norm
 // alone writing y, or quantize alone reading y from a.x with stride a.ldx).
 template <typename E, int kMode, int kNC, int kWPR, int kStage>
-__global__ __launch_bounds__((block_threads<kWPR, kMode, kStage>())) void fused_rows(const RowArgs a) {
+__global__ __launch_bounds__((block_threads<kWPR>())) void fused_rows(const RowArgs a) {
   constexpr int kLanes = kWave * kWPR;
   constexpr int kChunk = kLanes * 8;
-  constexpr int kRPB = rows_per_block<kWPR, kMode, kStage>();
+  constexpr int kRPB = rows_per_block_of(kWPR);                  // rows at once
+  constexpr int kTurns = rows_in_turn_of(kWPR, kMode, kStage);   // rows in turn
+  constexpr int kRows = kRPB * kTurns;                           // rows a workgroup covers
   constexpr bool kNT = true;
   constexpr bool kColScales = kStage == kStageFusedColScales;
-  // MXFP4 with column-major scales and several rows a workgroup: the E8M0 bytes
-  // go through LDS and leave as runs of kRPB consecutive rows per scale column
-  // (one store per run instead of one per byte; measured 2-3 us faster at
-  // [8192, 4096] than one row a workgroup).
-  constexpr bool kStagedColScales = kColScales && kMode == kMxfp4 && kRPB > 1;
+  // Only multi-wave MXFP4 rows take turns; every other barrier below is
+  // written for one row's turn.
+  static_assert(kTurns == 1 || (kMode == kMxfp4 && kRPB == 1), "rows in turn");
   const int lane = threadIdx.x & (kWave - 1);
   const int wave = threadIdx.x / kWave;            // wave in the workgroup
-  const int rloc = wave / kWPR;                     // row in the workgroup
+  const int rloc = wave / kWPR;                     // row of the current turn
   const int wrow = wave % kWPR;                     // wave in the row
-  const uint32_t blk = kColScales ? xcd_run_order<kRPB>(blockIdx.x, gridDim.x) : blockIdx.x;
-  const int64_t row = a.row0 + (int64_t)blk * kRPB + rloc;
+  const uint32_t blk = kColScales ? xcd_run_order<kRows>(blockIdx.x, gridDim.x) : blockIdx.x;
+  const int64_t row_first = a.row0 + (int64_t)blk * kRows;
   const int t = (int)threadIdx.x % kLanes;          // lane in the row
-  // A row past the end only happens in the last workgroup of the few-waves
-  // tilings; its waves still reach every barrier (loads and stores are masked).
-  const bool live = row < a.M;
+  // A row past the end only happens in the last workgroup of a launch; its
+  // waves still reach every barrier (loads and stores are masked).  A
+  // workgroup's rows increase with its turns, so its first turn is live
+  // whenever any is.
+  const int64_t row_of_first_turn = row_first + rloc;
+  const bool live_first = row_of_first_turn < a.M;
   const int H = a.H;
   if constexpr (kWPR <= 8) {
     // Left to itself the compiler loads the row pointers in three rounds (the
@@ -438,214 +445,234 @@ __global__ __launch_bounds__((block_threads<kWPR, kMode, kStage>())) void fused_
     asm volatile("" ::"s"(a.q), "s"(a.scale), "s"(a.y_out));
   }
 
-  __shared__ float lds_sum[kRPB][kWPR * kNC];
-  __shared__ float lds_sum_tiny[kRPB][kWPR * kNC];
+  // One buffer of block sums per turn, so that a wave's next turn never writes
+  // the sums another wave of the row may still be reading.
+  __shared__ float lds_sum[kTurns][kRPB][kWPR * kNC];
+  __shared__ float lds_sum_tiny[kTurns][kRPB][kWPR * kNC];
   __shared__ uint32_t lds_max[kRPB][kWPR];
-  __shared__ uint8_t lds_e8m0[kStagedColScales ? kRPB : 1][kStagedColScales ? RQ_MAX_HIDDEN / 32 : 1];
+  // Column-major scales of multi-wave rows (and of MXFP4's four one-wave rows)
+  // wait here until the workgroup's last row has its own, then leave as one
+  // run of kRows consecutive rows per scale column (one store per column
+  // instead of one per row).  At most H / 32 scales a row (E8M0 bytes, or fp32
+  // for groups of 32 or more).  Per-group FP8 in one-wave rows stores its
+  // scales directly: those workgroups have no barrier of their own, and the
+  // one the stage needs measured 3 % slower on MI355X at [8192, 256].
+  constexpr bool kStaged = kColScales && (kMode == kMxfp4 || kWPR > 1);
+  constexpr int kScaleWords = !kStaged ? 1 : kMode == kMxfp4 ? kLanes * kNC / 16 : kLanes * kNC / 4;
+  __shared__ uint32_t lds_scales[kStaged ? kRows : 1][kScaleWords];
 
-  uint4 yp[kNC];
-  if constexpr (kStage == kStageQuantize) {
-    // The quantize launch of the unfused sequence: y comes from memory.
-    const uint16_t* yr = a.x + (live ? row : 0) * a.ldx;
+  // 1. Issue every load of a row before using any of it, the weight first.
+  //    Loads return in order, so by the time x and the residual have arrived
+  //    the weight has too, and within a turn no wait for data can be made to
+  //    include the completion of a store (the one counter of vector memory
+  //    operations counts both, and a wait behind a store waits for all); a
+  //    second turn's loads do wait behind the first turn's stores.  Rows that
+  //    take turns load the weight once, before the first.
+  uint4 wv[kNC];
+  if constexpr (kTurns > 1) {
 #pragma unroll
     for (int c = 0; c < kNC; ++c) {
       const int col = c * kChunk + t * 8;
-      yp[c] = (live && (c < kNC - 1 || col < H)) ? load16<kNT>(yr + col) : make_uint4(0, 0, 0, 0);
-    }
-  } else {
-    const uint16_t* xr = a.x + (live ? row : 0) * a.ldx;
-    const uint16_t* rr = a.res + (live ? row : 0) * a.ldr;
-
-    // 1. Issue every load of the row before using any of it, the weight
-    //    first.  Loads return in order, so by the time x and the residual have
-    //    arrived the weight has too, and no later wait for data can be made to
-    //    include the completion of a store (the one counter of vector memory
-    //    operations counts both, and a wait behind a store waits for all).
-    uint4 xv[kNC], rv[kNC], wv[kNC];
-  #pragma unroll
-    for (int c = 0; c < kNC; ++c) {
-      const int col = c * kChunk + t * 8;
-      // the weight is re-read by every row: keep it cached
-      wv[c] = (live && (c < kNC - 1 || col < H)) ? load16<false>(a.w + col) : make_uint4(0, 0, 0, 0);
-    }
-  #pragma unroll
-    for (int c = 0; c < kNC; ++c) {
-      const int col = c * kChunk + t * 8;
-      if (live && (c < kNC - 1 || col < H)) {
-        xv[c] = load16<kNT>(xr + col);
-        rv[c] = load16<kNT>(rr + col);
-      } else {
-        xv[c] = make_uint4(0, 0, 0, 0);
-        rv[c] = make_uint4(0, 0, 0, 0);
-      }
-    }
-
-    // 2. Residual add (one bf16 rounding) and the sum of squares of each
-    //    8-element piece; then the residual_out stores, after the last load.
-    uint4 rp[kNC];
-    float ssc[kNC];
-  #pragma unroll
-    for (int c = 0; c < kNC; ++c) {
-      const uint32_t xs[4] = {xv[c].x, xv[c].y, xv[c].z, xv[c].w};
-      const uint32_t rs[4] = {rv[c].x, rv[c].y, rv[c].z, rv[c].w};
-      uint32_t p[4];
-      ssc[c] = 0.0f;
-  #pragma unroll
-      for (int j = 0; j < 4; ++j) {
-        p[j] = E::pack(E::lo(xs[j]) + E::lo(rs[j]), E::hi(xs[j]) + E::hi(rs[j]));
-        const float r0 = E::lo(p[j]), r1 = E::hi(p[j]);
-        ssc[c] = __builtin_fmaf(r0, r0, ssc[c]);
-        ssc[c] = __builtin_fmaf(r1, r1, ssc[c]);
-      }
-      rp[c] = make_uint4(p[0], p[1], p[2], p[3]);
-    }
-  #pragma unroll
-    for (int c = 0; c < kNC; ++c) {
-      const int col = c * kChunk + t * 8;
-      if (live && (c < kNC - 1 || col < H)) store16<kNT>(a.res_out + row * H + col, rp[c]);
-    }
-
-    // 3. rstd over the whole row, summed in an order that does not depend on
-    //    the tiling: the 64 pieces of each 512-column block by the wave
-    //    butterfly, then the blocks' sums left to right.  Block b is chunk
-    //    b / kWPR of wave b % kWPR, so every (kWPR, kNC) launch of a row gives
-    //    the same bits, and the host may pick the tiling from the batch size.
-    const float ss = row_sum<kNC, kWPR>(ssc, lds_sum[rloc], lane, wrow);
-    // rstd need not be correctly rounded (the tolerance on y is one bf16 ulp):
-    // the hardware reciprocal square root keeps it off the critical path.
-    const float t_ms = __builtin_fmaf(ss, a.inv_h, a.eps);
-    const bool in_range = !(t_ms < 0x1p-100f) && t_ms != __builtin_huge_valf();
-    // The second sum below has a barrier.  A multi-wave row alone in its
-    // workgroup takes it uniformly; with several multi-wave rows a workgroup,
-    // every wave reads every row's block sums (already in LDS, added in the same
-    // order as row_sum) and the whole workgroup takes the second sum when any
-    // of its rows needs it.
-    bool all_in_range = in_range;
-    if constexpr (kRPB > 1 && kWPR > 1) {
-#pragma unroll
-      for (int r = 0; r < kRPB; ++r) {
-        float sr = lds_sum[r][0];
-#pragma unroll
-        for (int b = 1; b < kNC * kWPR; ++b) sr += lds_sum[r][b];
-        const float tr = __builtin_fmaf(sr, a.inv_h, a.eps);
-        all_in_range = all_in_range && !(tr < 0x1p-100f) && tr != __builtin_huge_valf();
-      }
-    }
-    float rstd;
-    if (__builtin_expect(all_in_range, true)) {
-      rstd = __builtin_amdgcn_rsqf(t_ms);  // NaN propagates through here
-    } else {
-      // The fp32 squares left their range; sum them again with r scaled by an
-      // exact power of two k, in the same order.  A row this small (only with
-      // eps < 2^-100; |r| < 2^-43) takes k = 2^100, so the scaled squares lie in
-      // [2^-66, 2^114].  A row whose sum of squares overflowed (bf16 allows |r|
-      // up to 2^128) takes k = 2^-80: scaled squares at most 2^96, their sum at
-      // most 2^110; a row holding Inf still sums to Inf and gets rstd 0, as an
-      // exact computation does.  Uniform over the row, and a multi-wave row has
-      // its workgroup to itself.
-      const float k = t_ms < 0x1p-100f ? 0x1p100f : 0x1p-80f;
-      float s2c[kNC];
-  #pragma unroll
-      for (int c = 0; c < kNC; ++c) {
-        const uint32_t rs[4] = {rp[c].x, rp[c].y, rp[c].z, rp[c].w};
-        s2c[c] = 0.0f;
-  #pragma unroll
-        for (int j = 0; j < 4; ++j) {
-          const float r0 = E::lo(rs[j]) * k, r1 = E::hi(rs[j]) * k;
-          s2c[c] = __builtin_fmaf(r0, r0, s2c[c]);
-          s2c[c] = __builtin_fmaf(r1, r1, s2c[c]);
-        }
-      }
-      const float s2 = row_sum<kNC, kWPR>(s2c, lds_sum_tiny[rloc], lane, wrow);
-      rstd = in_range ? __builtin_amdgcn_rsqf(t_ms)
-                      : __builtin_amdgcn_rsqf(__builtin_fmaf(s2, a.inv_h, a.eps * k * k)) * k;
-    }
-
-    // 4. y = bf16((r * rstd) * w), optional bf16 side output.
-  #pragma unroll
-    for (int c = 0; c < kNC; ++c) {
-      const uint32_t rs[4] = {rp[c].x, rp[c].y, rp[c].z, rp[c].w};
-      const uint32_t ws[4] = {wv[c].x, wv[c].y, wv[c].z, wv[c].w};
-      uint32_t p[4];
-  #pragma unroll
-      for (int j = 0; j < 4; ++j)
-        p[j] = E::pack((E::lo(rs[j]) * rstd) * E::lo(ws[j]), (E::hi(rs[j]) * rstd) * E::hi(ws[j]));
-      yp[c] = make_uint4(p[0], p[1], p[2], p[3]);
-    }
-    if (a.y_out) {
-  #pragma unroll
-      for (int c = 0; c < kNC; ++c) {
-        const int col = c * kChunk + t * 8;
-        if (live && (c < kNC - 1 || col < H)) store16<kNT>(a.y_out + row * H + col, yp[c]);
-      }
+      wv[c] = (live_first && (c < kNC - 1 || col < H)) ? load16<false>(a.w + col) : make_uint4(0, 0, 0, 0);
     }
   }
-  if constexpr (kStage == kStageNorm) return;
 
-  // 5. Absmax per granule, scale, quantize, pack, store.
-  if (kMode == kFp8Token) {
-    uint32_t m = 0;
+#pragma unroll 1
+  for (int turn = 0; turn < kTurns; ++turn) {
+    const int rw = turn * kRPB + rloc;                // row of the workgroup
+    const int64_t row = kTurns == 1 ? row_of_first_turn : row_first + rw;
+    const bool live = kTurns == 1 ? live_first : row < a.M;
+    uint4 yp[kNC];
+    if constexpr (kStage == kStageQuantize) {
+      // The quantize launch of the unfused sequence: y comes from memory.
+      const uint16_t* yr = a.x + (live ? row : 0) * a.ldx;
 #pragma unroll
-    for (int c = 0; c < kNC; ++c) m = umax(m, chunk_abs_max(yp[c]));
-    m = group_max(m, 6);
-    if (kWPR > 1) {
-      if (lane == 0) lds_max[rloc][wrow] = m;
-      __syncthreads();
-#pragma unroll
-      for (int w = 0; w < kWPR; ++w) m = umax(m, lds_max[rloc][w]);
+      for (int c = 0; c < kNC; ++c) {
+        const int col = c * kChunk + t * 8;
+        yp[c] = (live && (c < kNC - 1 || col < H)) ? load16<kNT>(yr + col) : make_uint4(0, 0, 0, 0);
+      }
+    } else {
+      const uint16_t* xr = a.x + (live ? row : 0) * a.ldx;
+      const uint16_t* rr = a.res + (live ? row : 0) * a.ldr;
+      uint4 xv[kNC], rv[kNC];
+      if constexpr (kTurns == 1) {
+    #pragma unroll
+        for (int c = 0; c < kNC; ++c) {
+          const int col = c * kChunk + t * 8;
+          // the weight is re-read by every row: keep it cached
+          wv[c] = (live && (c < kNC - 1 || col < H)) ? load16<false>(a.w + col) : make_uint4(0, 0, 0, 0);
+        }
+      }
+    #pragma unroll
+      for (int c = 0; c < kNC; ++c) {
+        const int col = c * kChunk + t * 8;
+        if (live && (c < kNC - 1 || col < H)) {
+          xv[c] = load16<kNT>(xr + col);
+          rv[c] = load16<kNT>(rr + col);
+        } else {
+          xv[c] = make_uint4(0, 0, 0, 0);
+          rv[c] = make_uint4(0, 0, 0, 0);
+        }
+      }
+
+      // 2. Residual add (one bf16 rounding) and the sum of squares of each
+      //    8-element piece; then the residual_out stores, after the last load.
+      uint4 rp[kNC];
+      float ssc[kNC];
+    #pragma unroll
+      for (int c = 0; c < kNC; ++c) {
+        const uint32_t xs[4] = {xv[c].x, xv[c].y, xv[c].z, xv[c].w};
+        const uint32_t rs[4] = {rv[c].x, rv[c].y, rv[c].z, rv[c].w};
+        uint32_t p[4];
+        ssc[c] = 0.0f;
+    #pragma unroll
+        for (int j = 0; j < 4; ++j) {
+          p[j] = E::pack(E::lo(xs[j]) + E::lo(rs[j]), E::hi(xs[j]) + E::hi(rs[j]));
+          const float r0 = E::lo(p[j]), r1 = E::hi(p[j]);
+          ssc[c] = __builtin_fmaf(r0, r0, ssc[c]);
+          ssc[c] = __builtin_fmaf(r1, r1, ssc[c]);
+        }
+        rp[c] = make_uint4(p[0], p[1], p[2], p[3]);
+      }
+    #pragma unroll
+      for (int c = 0; c < kNC; ++c) {
+        const int col = c * kChunk + t * 8;
+        if (live && (c < kNC - 1 || col < H)) store16<kNT>(a.res_out + row * H + col, rp[c]);
+      }
+
+      // 3. rstd over the whole row, summed in an order that does not depend on
+      //    the tiling: the 64 pieces of each 512-column block by the wave
+      //    butterfly, then the blocks' sums left to right.  Block b is chunk
+      //    b / kWPR of wave b % kWPR, so every (kWPR, kNC) launch of a row gives
+      //    the same bits, and the host may pick the tiling from the batch size.
+      const float ss = row_sum<kNC, kWPR>(ssc, lds_sum[turn][rloc], lane, wrow);
+      // rstd need not be correctly rounded (the tolerance on y is one bf16 ulp):
+      // the hardware reciprocal square root keeps it off the critical path.
+      const float t_ms = __builtin_fmaf(ss, a.inv_h, a.eps);
+      float rstd;
+      if (__builtin_expect(!(t_ms < 0x1p-100f) && t_ms != __builtin_huge_valf(), true)) {
+        rstd = __builtin_amdgcn_rsqf(t_ms);  // NaN propagates through here
+      } else {
+        // The fp32 squares left their range; sum them again with r scaled by an
+        // exact power of two k, in the same order.  A row this small (only with
+        // eps < 2^-100; |r| < 2^-43) takes k = 2^100, so the scaled squares lie in
+        // [2^-66, 2^114].  A row whose sum of squares overflowed (bf16 allows |r|
+        // up to 2^128) takes k = 2^-80: scaled squares at most 2^96, their sum at
+        // most 2^110; a row holding Inf still sums to Inf and gets rstd 0, as an
+        // exact computation does.  Uniform over the row, and a multi-wave row has
+        // its workgroup to itself.
+        const float k = t_ms < 0x1p-100f ? 0x1p100f : 0x1p-80f;
+        float s2c[kNC];
+    #pragma unroll
+        for (int c = 0; c < kNC; ++c) {
+          const uint32_t rs[4] = {rp[c].x, rp[c].y, rp[c].z, rp[c].w};
+          s2c[c] = 0.0f;
+    #pragma unroll
+          for (int j = 0; j < 4; ++j) {
+            const float r0 = E::lo(rs[j]) * k, r1 = E::hi(rs[j]) * k;
+            s2c[c] = __builtin_fmaf(r0, r0, s2c[c]);
+            s2c[c] = __builtin_fmaf(r1, r1, s2c[c]);
+          }
+        }
+        const float s2 = row_sum<kNC, kWPR>(s2c, lds_sum_tiny[turn][rloc], lane, wrow);
+        rstd = __builtin_amdgcn_rsqf(__builtin_fmaf(s2, a.inv_h, a.eps * k * k)) * k;
+      }
+
+      // 4. y = bf16((r * rstd) * w), optional bf16 side output.
+    #pragma unroll
+      for (int c = 0; c < kNC; ++c) {
+        const uint32_t rs[4] = {rp[c].x, rp[c].y, rp[c].z, rp[c].w};
+        const uint32_t ws[4] = {wv[c].x, wv[c].y, wv[c].z, wv[c].w};
+        uint32_t p[4];
+    #pragma unroll
+        for (int j = 0; j < 4; ++j)
+          p[j] = E::pack((E::lo(rs[j]) * rstd) * E::lo(ws[j]), (E::hi(rs[j]) * rstd) * E::hi(ws[j]));
+        yp[c] = make_uint4(p[0], p[1], p[2], p[3]);
+      }
+      if (a.y_out) {
+    #pragma unroll
+        for (int c = 0; c < kNC; ++c) {
+          const int col = c * kChunk + t * 8;
+          if (live && (c < kNC - 1 || col < H)) store16<kNT>(a.y_out + row * H + col, yp[c]);
+        }
+      }
     }
-    const Fp8Granule g = fp8_granule<E>(m);
-    if (live && t == 0) reinterpret_cast<float*>(a.scale)[row] = g.scale;
+    if constexpr (kStage == kStageNorm) continue;
+
+    // 5. Absmax per granule, scale, quantize, pack, store.
+    if (kMode == kFp8Token) {
+      uint32_t m = 0;
 #pragma unroll
-    for (int c = 0; c < kNC; ++c) {
-      const int col = c * kChunk + t * 8;
-      const uint2 codes = fp8_codes<E>(yp[c], g);
-      if (live && (c < kNC - 1 || col < H)) store8<kNT>(a.q + row * H + col, codes);
-    }
-  } else if (kMode == kFp8Group) {
-    const int gl = a.group_log2_lanes;
+      for (int c = 0; c < kNC; ++c) m = umax(m, chunk_abs_max(yp[c]));
+      m = group_max(m, 6);
+      if (kWPR > 1) {
+        if (lane == 0) lds_max[rloc][wrow] = m;
+        __syncthreads();
 #pragma unroll
-    for (int c = 0; c < kNC; ++c) {
-      const int col = c * kChunk + t * 8;
-      const uint32_t m = group_max(chunk_abs_max(yp[c]), gl);
+        for (int w = 0; w < kWPR; ++w) m = umax(m, lds_max[rloc][w]);
+      }
       const Fp8Granule g = fp8_granule<E>(m);
-      const uint2 codes = fp8_codes<E>(yp[c], g);
-      if (live && (c < kNC - 1 || col < H)) {
-        store8<kNT>(a.q + row * H + col, codes);
-        if ((t & ((1 << gl) - 1)) == 0) {
-          const int64_t gi = col >> (gl + 3);
-          reinterpret_cast<float*>(a.scale)[kColScales ? gi * a.scale_ld + row : row * a.groups_per_row + gi] =
-              g.scale;
-        }
-      }
-    }
-  } else {
+      if (live && t == 0) reinterpret_cast<float*>(a.scale)[row] = g.scale;
 #pragma unroll
-    for (int c = 0; c < kNC; ++c) {
-      const int col = c * kChunk + t * 8;
-      const uint32_t m = group_max_c<2>(chunk_abs_max(yp[c]));
-      const uint32_t byte = e8m0_byte(E::value(m));
-      const uint32_t codes = mxfp4_codes<E>(yp[c], byte);
-      if (live && (c < kNC - 1 || col < H)) {
-        store4<kNT>(a.q + row * (H / 2) + col / 2, codes);
-        if ((t & 3) == 0) {
-          const int64_t bi = col / 32;
-          if constexpr (kStagedColScales)
-            lds_e8m0[rloc][bi] = (uint8_t)byte;
-          else
-            reinterpret_cast<uint8_t*>(a.scale)[kColScales ? bi * a.scale_ld + row : row * (H / 32) + bi] =
-                (uint8_t)byte;
+      for (int c = 0; c < kNC; ++c) {
+        const int col = c * kChunk + t * 8;
+        const uint2 codes = fp8_codes<E>(yp[c], g);
+        if (live && (c < kNC - 1 || col < H)) store8<kNT>(a.q + row * H + col, codes);
+      }
+    } else if (kMode == kFp8Group) {
+      const int gl = a.group_log2_lanes;
+#pragma unroll
+      for (int c = 0; c < kNC; ++c) {
+        const int col = c * kChunk + t * 8;
+        const uint32_t m = group_max(chunk_abs_max(yp[c]), gl);
+        const Fp8Granule g = fp8_granule<E>(m);
+        const uint2 codes = fp8_codes<E>(yp[c], g);
+        if (live && (c < kNC - 1 || col < H)) {
+          store8<kNT>(a.q + row * H + col, codes);
+          if ((t & ((1 << gl) - 1)) == 0) {
+            const int64_t gi = col >> (gl + 3);
+            if constexpr (kStaged)
+              lds_scales[rw][gi] = __builtin_bit_cast(uint32_t, g.scale);
+            else
+              reinterpret_cast<float*>(a.scale)[kColScales ? gi * a.scale_ld + row : row * a.groups_per_row + gi] =
+                  g.scale;
+          }
+        }
+      }
+    } else {
+#pragma unroll
+      for (int c = 0; c < kNC; ++c) {
+        const int col = c * kChunk + t * 8;
+        const uint32_t m = group_max_c<2>(chunk_abs_max(yp[c]));
+        const uint32_t byte = e8m0_byte(E::value(m));
+        const uint32_t codes = mxfp4_codes<E>(yp[c], byte);
+        if (live && (c < kNC - 1 || col < H)) {
+          store4<kNT>(a.q + row * (H / 2) + col / 2, codes);
+          if ((t & 3) == 0) {
+            const int64_t bi = col / 32;
+            if constexpr (kStaged)
+              reinterpret_cast<uint8_t*>(lds_scales[rw])[bi] = (uint8_t)byte;
+            else
+              reinterpret_cast<uint8_t*>(a.scale)[row * (H / 32) + bi] = (uint8_t)byte;
+          }
         }
       }
     }
-    if constexpr (kStagedColScales) {
-      // Every row of the workgroup has staged its bytes; each thread stores one
-      // byte, consecutive threads taking consecutive rows of a scale column.
-      __syncthreads();
-      const int64_t row_first = row - rloc;
-      for (int i = threadIdx.x; i < (H / 32) * kRPB; i += kRPB * kLanes) {
-        const int bi = i / kRPB, r = i % kRPB;
-        if (row_first + r < a.M) reinterpret_cast<uint8_t*>(a.scale)[bi * a.scale_ld + row_first + r] = lds_e8m0[r][bi];
+  }  // turns
+
+  if constexpr (kStaged) {
+    // Every row of the workgroup has its scales in LDS; each thread stores one,
+    // consecutive threads taking consecutive rows of a scale column.
+    __syncthreads();
+    const int n = kMode == kMxfp4 ? H / 32 : a.groups_per_row;
+    for (int i = threadIdx.x; i < n * kRows; i += kRPB * kLanes) {
+      const int si = i / kRows, r = i % kRows;
+      if (row_first + r < a.M) {
+        const int64_t at = (int64_t)si * a.scale_ld + row_first + r;
+        if constexpr (kMode == kMxfp4)
+          reinterpret_cast<uint8_t*>(a.scale)[at] = reinterpret_cast<const uint8_t*>(lds_scales[r])[si];
+        else
+          reinterpret_cast<uint32_t*>(a.scale)[at] = lds_scales[r][si];
       }
     }
   }
@@ -982,30 +1009,35 @@ int chunks_per_lane(int H, int l) {
 // waves, so that a lane holds one chunk, as long as the launch still fits; a
 // lane's dependent chain from load to store is then as short as it gets, and
 // there is no second generation of waves to wait for.  The column-major scale
-// kernels keep the two-chunk shape they were measured in.  The row's sum is
-// the same for every tiling.
-int waves_per_row_log2(int64_t M, int H, bool one_chunk_rows) {
+// kernels take the same tiling (per-group FP8 with its scales staged in LDS:
+// measured on MI355X from 1 % slower to 4 % faster than with the fewest waves,
+// over 1024-8192 rows and H = 2048-8192).  The row's sum is the same for every
+// tiling.
+int waves_per_row_log2(int64_t M, int H) {
   int l = 0;
   while (l < 4 && chunks_per_lane(H, l) > kMaxChunks) ++l;
-  if (one_chunk_rows && l < 3 && chunks_per_lane(H, l) == 2 && H == 8 * (kWave << (l + 1))) ++l;
+  if (l < 3 && chunks_per_lane(H, l) == 2 && H == 8 * (kWave << (l + 1))) ++l;
   while (l < 4 && chunks_per_lane(H, l) > 1 && M * (int64_t)(2 << l) <= kResidentWaves) ++l;
   return l;
 }
 
 template <typename E, int kMode, int kStage = kStageFused>
 rq_status launch_rows(RowArgs& a, void* stream) {
-  const int l = waves_per_row_log2(a.M, a.H, kStage != kStageFusedColScales);
+  const int l = waves_per_row_log2(a.M, a.H);
   const int wpr = 1 << l;
   const int lanes = kWave * wpr;
   const int nc = chunks_per_lane(a.H, l);
-  const int rpb = rows_per_block_of(wpr, kMode, kStage);
-  const int64_t rows_per_launch = kMaxGridItems / lanes;  // a multiple of rpb
+  const int rpb = rows_per_block_of(wpr);
+  const int rows_per_wg = rpb * rows_in_turn_of(wpr, kMode, kStage);
+  // A power of two of at least rows_per_wg rows, so that no workgroup's rows
+  // straddle two launches.
+  const int64_t rows_per_launch = kMaxGridItems / lanes;
   const void* kernel = reinterpret_cast<const void*>(RowKernels<E, kMode, kStage>::k[l][nc - 1]);
   for (int64_t row0 = 0; row0 < a.M; row0 += rows_per_launch) {
     const int64_t rows = std::min<int64_t>(a.M - row0, rows_per_launch);
     a.row0 = row0;
-    const rq_status st = launch(kernel, dim3((unsigned)((rows + rpb - 1) / rpb)), dim3((unsigned)(lanes * rpb)), &a,
-                                stream);
+    const rq_status st = launch(kernel, dim3((unsigned)((rows + rows_per_wg - 1) / rows_per_wg)),
+                                dim3((unsigned)(lanes * rpb)), &a, stream);
     if (st != RQ_OK) return st;
   }
   return RQ_OK;

@@ -16,11 +16,14 @@ from parity import check_fp8, check_mxfp4, to_np
 
 pytestmark = pytest.mark.gpu
 DEV = "cuda:0"
-# Row counts beyond a few hundred with four rows a workgroup (3000 x 256) and one
-# row a workgroup (1100 x 4096, 700 x 2048, 8192 x 4096).
+# Row counts beyond a few hundred with four one-wave rows a workgroup (3000 x 256)
+# and multi-wave rows (1100 x 4096, 700 x 2048, 8192 x 4096: one row a workgroup
+# for per-group FP8, two in turn for MXFP4); odd counts (3, 17, 65, 9) leave the
+# last MXFP4 workgroup's second turn past the end.  H = 16384 fills the LDS stage
+# of 16-wave rows exactly (512 E8M0 bytes; 512 fp32 scales at group 32).
 CASES = [("bf16", 16, 4096, 128), ("bf16", 16, 7168, 32), ("bf16", 3, 544, 32), ("bf16", 130, 1024, 512),
          ("bf16", 65, 4096, 64), ("fp16", 17, 2048, 128), ("fp16", 9, 16384, 256), ("bf16", 8192, 4096, 128),
-         ("bf16", 3000, 256, 32), ("bf16", 1100, 4096, 128), ("fp16", 700, 2048, 64)]
+         ("bf16", 3000, 256, 32), ("bf16", 1100, 4096, 128), ("fp16", 700, 2048, 64), ("bf16", 5, 16384, 32)]
 
 
 def padded(M):
@@ -93,8 +96,9 @@ def test_tscale_default_and_errors():
 @pytest.mark.parametrize("M,H", [(8, 4096), (12, 1024), (6, 8192), (64, 2048)])
 def test_tscale_tiny_and_normal_rows_share_a_workgroup(M, H):
     """Rows whose squares underflow (eps = 0, |r| ~ 2^-70, the rescaled sum) next
-    to ordinary rows in the same multi-row workgroup: the column-major calls
-    take both sums in one exchange and must give the row-major calls' bits."""
+    to ordinary rows in the same workgroup (four one-wave rows at once, or two
+    multi-wave MXFP4 rows in turn): the column-major calls must give the
+    row-major calls' bits."""
     d = inputs.random_rows(M, H, seed=M + H, dtype=torch.bfloat16)
     x, r, w = (d[k].to(DEV) for k in ("x", "residual", "weight"))
     tiny = torch.zeros(M, 1, device=DEV)
@@ -117,13 +121,13 @@ MIXED = [(2049, 4096), (2049, 1024), (5001, 2048)]
 
 @pytest.mark.parametrize("M,H", MIXED, ids=[f"{m}x{h}" for m, h in MIXED])
 def test_tscale_mxfp4_mixed_rows_in_a_workgroup(ref, M, H):
-    """MXFP4 with column-major scales holds 2 or 4 multi-wave rows a workgroup
-    at these shapes.  Rows whose fp32 sum of squares overflows (|r| ~ 2^70) or
-    underflows (|r| ~ 2^-60 with eps = 0) take a second, rescaled sum with a
-    barrier of its own; here they sit beside ordinary rows in the same
-    workgroups (and a dead row pads the last one), so the workgroup must take
-    that barrier together.  Everything must equal the row-major call bit for
-    bit and meet the oracle bar."""
+    """MXFP4 with column-major scales takes two multi-wave rows in turn a
+    workgroup at these shapes.  Rows whose fp32 sum of squares overflows
+    (|r| ~ 2^70) or underflows (|r| ~ 2^-60 with eps = 0) take a second,
+    rescaled sum with a barrier of its own; here they sit beside ordinary rows
+    in the same workgroups (and a dead row pads the last one), one turn taking
+    that barrier and the other not.  Everything must equal the row-major call
+    bit for bit and meet the oracle bar."""
     d = inputs.random_rows(M, H, seed=M + H)
     idx = torch.arange(M)
     scale = torch.ones(M)
