@@ -376,9 +376,10 @@ constexpr int rows_per_block_of(int wpr) { return wpr == 1 ? 4 : 1; }
 // Rows a workgroup takes in turn.  MXFP4 with column-major scales: two rows of
 // several waves one after the other, so that each scale column receives its
 // two bytes in one store (the scattered one-byte stores of a column-major
-// scale are what such a launch spends its extra time on; measured on MI355X
-// 3-11 % faster than one row a workgroup from H = 2048 to 8192, except at
-// [8192, 2048], and ahead of four rows in turn or two rows at once).
+// scale are what such a launch spends its extra time on).  Measured on MI355X
+// over 1024-8192 rows at H = 2048-8192: 1.5-8 % faster than one row a
+// workgroup (1.4 % slower at [2048, 7168]); four rows in turn were slower at
+// H = 4096 and mixed at wider rows, two rows at once slower throughout.
 // Otherwise one.
 constexpr int rows_in_turn_of(int wpr, int mode, int stage) {
   return stage == kStageFusedColScales && mode == kMxfp4 && wpr > 1 ? 2 : 1;
