@@ -478,6 +478,8 @@ __global__ __launch_bounds__((block_threads<kWPR>())) void fused_rows(const RowA
     }
   }
 
+  // Not unrolled: two unrolled turns of MXFP4 rows measured 0.5-2.2 us slower
+  // at [8192, 4096], [8192, 7168] and [4096, 8192] on MI355X.
 #pragma unroll 1
   for (int turn = 0; turn < kTurns; ++turn) {
     const int rw = turn * kRPB + rloc;                // row of the workgroup
