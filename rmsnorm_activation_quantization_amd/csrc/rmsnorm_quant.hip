@@ -563,7 +563,7 @@ __global__ __launch_bounds__((block_threads<kWPR>())) void fused_rows(const RowA
         // up to 2^128) takes k = 2^-80: scaled squares at most 2^96, their sum at
         // most 2^110; a row holding Inf still sums to Inf and gets rstd 0, as an
         // exact computation does.  Uniform over the row, and a multi-wave row has
-        // its workgroup to itself.
+        // its workgroup to itself for its turn.
         const float k = t_ms < 0x1p-100f ? 0x1p100f : 0x1p-80f;
         float s2c[kNC];
     #pragma unroll
