@@ -17,13 +17,15 @@ from parity import check_fp8, check_mxfp4, to_np
 pytestmark = pytest.mark.gpu
 DEV = "cuda:0"
 # Row counts beyond a few hundred with four one-wave rows a workgroup (3000 x 256)
-# and multi-wave rows (1100 x 4096, 700 x 2048, 8192 x 4096: one row a workgroup
-# for per-group FP8, two in turn for MXFP4); odd counts (3, 17, 65, 9) leave the
-# last MXFP4 workgroup's second turn past the end.  H = 16384 fills the LDS stage
-# of 16-wave rows exactly (512 E8M0 bytes; 512 fp32 scales at group 32).
+# and multi-wave rows (1100 x 4096, 700 x 2048, 8192 x 4096, and 520 x 7168 with
+# two chunks a lane: one row a workgroup for per-group FP8, two in turn for
+# MXFP4); odd counts (3, 17, 65, 9) leave the last MXFP4 workgroup's second turn
+# past the end.  H = 16384 fills the LDS stage of 16-wave rows exactly (512 E8M0
+# bytes; 512 fp32 scales at group 32).
 CASES = [("bf16", 16, 4096, 128), ("bf16", 16, 7168, 32), ("bf16", 3, 544, 32), ("bf16", 130, 1024, 512),
          ("bf16", 65, 4096, 64), ("fp16", 17, 2048, 128), ("fp16", 9, 16384, 256), ("bf16", 8192, 4096, 128),
-         ("bf16", 3000, 256, 32), ("bf16", 1100, 4096, 128), ("fp16", 700, 2048, 64), ("bf16", 5, 16384, 32)]
+         ("bf16", 3000, 256, 32), ("bf16", 1100, 4096, 128), ("fp16", 700, 2048, 64), ("bf16", 5, 16384, 32),
+         ("bf16", 520, 7168, 64)]
 
 
 def padded(M):
@@ -116,7 +118,7 @@ def test_tscale_tiny_and_normal_rows_share_a_workgroup(M, H):
         assert torch.equal(a[2][:, :M], b[2].t()), "scales differ"
 
 
-MIXED = [(2049, 4096), (2049, 1024), (5001, 2048)]
+MIXED = [(2049, 4096), (2049, 1024), (5001, 2048), (1025, 7168)]
 
 
 @pytest.mark.parametrize("M,H", MIXED, ids=[f"{m}x{h}" for m, h in MIXED])
