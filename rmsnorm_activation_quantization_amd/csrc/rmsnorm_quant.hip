@@ -80,8 +80,12 @@ constexpr int kMaxChunks = 2;  // chunks per lane; rows need at most 16 waves * 
 
 enum QuantMode { kFp8Token = 0, kFp8Group = 1, kMxfp4 = 2 };
 // kStageFusedColScales: the fused step with column-major scales (the layout is a
-// compile-time choice, so the row-major kernels never read the scale stride).
-enum Stage { kStageFused = 0, kStageNorm = 1, kStageQuantize = 2, kStageFusedColScales = 3 };
+// compile-time choice, so the row-major kernels never read the scale stride),
+// each scale stored by the lane that computes it; kStageFusedColScalesStaged:
+// the same with the scales staged in LDS and stored as runs along M, MXFP4's
+// multi-wave rows two in turn a workgroup (the host's choice for large
+// batches, see kStagedColScaleRows).
+enum Stage { kStageFused = 0, kStageNorm = 1, kStageQuantize = 2, kStageFusedColScales = 3, kStageFusedColScalesStaged = 4 };
 
 // ---------------------------------------------------------------------------
 // bf16 <-> fp32
@@ -373,17 +377,30 @@ __device__ __forceinline__ float row_sum(float (&part)[kNC], float* lds, int lan
 // Rows a workgroup holds at once: four one-wave rows, or one row of several
 // waves (so every barrier of a multi-wave row is uniform over its workgroup).
 constexpr int rows_per_block_of(int wpr) { return wpr == 1 ? 4 : 1; }
-// Rows a workgroup takes in turn.  MXFP4 with column-major scales: two rows of
-// several waves one after the other, so that each scale column receives its
-// two bytes in one store (the scattered one-byte stores of a column-major
-// scale are what such a launch spends its extra time on).  Measured on MI355X
-// over 1024-8192 rows at H = 2048-8192: 1.5-8 % faster than one row a
-// workgroup (1.4 % slower at [2048, 7168]); four rows in turn were slower at
-// H = 4096 and mixed at wider rows, two rows at once slower throughout.
-// Otherwise one.
+// Rows a workgroup takes in turn: two multi-wave MXFP4 rows one after the
+// other in the staged column-major kernels, so that each scale column receives
+// its two bytes in one store (the scattered one-byte stores of a column-major
+// scale are what such a launch spends its extra time on); otherwise one.
+// Measured on MI355X over 1024-8192 rows at H = 2048-8192: 1.5-8 % faster than
+// one row a workgroup (1.4 % slower at [2048, 7168]).  Four rows in turn were
+// slower at H = 4096 and mixed at wider rows, two rows at once slower
+// throughout.
 constexpr int rows_in_turn_of(int wpr, int mode, int stage) {
-  return stage == kStageFusedColScales && mode == kMxfp4 && wpr > 1 ? 2 : 1;
+  return stage == kStageFusedColScalesStaged && mode == kMxfp4 && wpr > 1 ? 2 : 1;
 }
+
+// Column-major scales: batches of at least this many rows, whose launch also
+// fills the chip's wave slots (M x waves per row >= kResidentWaves), take the
+// staged kernels (scales stored as runs along M, MXFP4 rows in turn); smaller
+// ones store each scale from the lane that computes it.  Measured on MI355X at
+// H = 2048-7168: in smaller batches the staged kernels' final barrier, and the
+// second turn's latency when the pairs of rows leave fewer than two
+// workgroups or sixteen waves a CU, cost more than the scattered stores
+// (MXFP4 up to 1.69x the row-major call's time at 4-512 rows, 1.24x at
+// [1024, 2048], against 0.99-1.08x stored directly; per-group FP8 1.04-1.09x
+// against 1.00-1.05x); beyond, the runs along M win (MXFP4 [1024, 4096]
+// 7.33 against 7.57 us).
+constexpr int64_t kStagedColScaleRows = 1024;
 template <int kWPR>
 constexpr int block_threads() { return kWave * kWPR * rows_per_block_of(kWPR); }
 
@@ -417,7 +434,7 @@ __global__ __launch_bounds__((block_threads<kWPR>())) void fused_rows(const RowA
   constexpr int kTurns = rows_in_turn_of(kWPR, kMode, kStage);   // rows in turn
   constexpr int kRows = kRPB * kTurns;                           // rows a workgroup covers
   constexpr bool kNT = true;
-  constexpr bool kColScales = kStage == kStageFusedColScales;
+  constexpr bool kColScales = kStage == kStageFusedColScales || kStage == kStageFusedColScalesStaged;
   // Only multi-wave MXFP4 rows take turns; every other barrier below is
   // written for one row's turn.
   static_assert(kTurns == 1 || (kMode == kMxfp4 && kRPB == 1), "rows in turn");
@@ -451,14 +468,14 @@ __global__ __launch_bounds__((block_threads<kWPR>())) void fused_rows(const RowA
   __shared__ float lds_sum[kTurns][kRPB][kWPR * kNC];
   __shared__ float lds_sum_tiny[kTurns][kRPB][kWPR * kNC];
   __shared__ uint32_t lds_max[kRPB][kWPR];
-  // Column-major scales of multi-wave rows (and of MXFP4's four one-wave rows)
-  // wait here until the workgroup's last row has its own, then leave as one
-  // run of kRows consecutive rows per scale column (one store per column
-  // instead of one per row).  At most H / 32 scales a row (E8M0 bytes, or fp32
-  // for groups of 32 or more).  Per-group FP8 in one-wave rows stores its
-  // scales directly: those workgroups have no barrier of their own, and the
-  // one the stage needs measured 3 % slower on MI355X at [8192, 256].
-  constexpr bool kStaged = kColScales && (kMode == kMxfp4 || kWPR > 1);
+  // Staged column-major scales of multi-wave rows (and of MXFP4's four
+  // one-wave rows) wait here until the workgroup's last row has its own, then
+  // leave as one run of kRows consecutive rows per scale column (one store per
+  // column instead of one per row).  At most H / 32 scales a row (E8M0 bytes,
+  // or fp32 for groups of 32 or more).  Per-group FP8 in one-wave rows stores
+  // its scales directly: those workgroups have no barrier of their own, and
+  // the one the stage needs measured 3 % slower on MI355X at [8192, 256].
+  constexpr bool kStaged = kStage == kStageFusedColScalesStaged && (kMode == kMxfp4 || kWPR > 1);
   constexpr int kScaleWords = !kStaged ? 1 : kMode == kMxfp4 ? kLanes * kNC / 16 : kLanes * kNC / 4;
   __shared__ uint32_t lds_scales[kStaged ? kRows : 1][kScaleWords];
 
@@ -656,7 +673,8 @@ __global__ __launch_bounds__((block_threads<kWPR>())) void fused_rows(const RowA
             if constexpr (kStaged)
               reinterpret_cast<uint8_t*>(lds_scales[rw])[bi] = (uint8_t)byte;
             else
-              reinterpret_cast<uint8_t*>(a.scale)[row * (H / 32) + bi] = (uint8_t)byte;
+              reinterpret_cast<uint8_t*>(a.scale)[kColScales ? bi * a.scale_ld + row : row * (H / 32) + bi] =
+                  (uint8_t)byte;
           }
         }
       }
@@ -1031,11 +1049,18 @@ rq_status launch_rows(RowArgs& a, void* stream) {
   const int lanes = kWave * wpr;
   const int nc = chunks_per_lane(a.H, l);
   const int rpb = rows_per_block_of(wpr);
-  const int rows_per_wg = rpb * rows_in_turn_of(wpr, kMode, kStage);
+  const void* kernel = reinterpret_cast<const void*>(RowKernels<E, kMode, kStage>::k[l][nc - 1]);
+  int turns = rows_in_turn_of(wpr, kMode, kStage);
+  if constexpr (kStage == kStageFusedColScales) {
+    if (a.M >= kStagedColScaleRows && a.M * (int64_t)wpr >= kResidentWaves) {
+      kernel = reinterpret_cast<const void*>(RowKernels<E, kMode, kStageFusedColScalesStaged>::k[l][nc - 1]);
+      turns = rows_in_turn_of(wpr, kMode, kStageFusedColScalesStaged);
+    }
+  }
+  const int rows_per_wg = rpb * turns;
   // A power of two of at least rows_per_wg rows, so that no workgroup's rows
   // straddle two launches.
   const int64_t rows_per_launch = kMaxGridItems / lanes;
-  const void* kernel = reinterpret_cast<const void*>(RowKernels<E, kMode, kStage>::k[l][nc - 1]);
   for (int64_t row0 = 0; row0 < a.M; row0 += rows_per_launch) {
     const int64_t rows = std::min<int64_t>(a.M - row0, rows_per_launch);
     a.row0 = row0;

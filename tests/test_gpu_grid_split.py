@@ -89,10 +89,11 @@ def test_rows_split(ref, split_lib, M, H, dt, fmt):
 
 @pytest.mark.parametrize("M", [300, 1501])
 def test_tscale_and_unfused_split(split_lib, M):
-    """Both sizes take rows of 8 waves with one chunk a lane, and column-major
-    MXFP4 two such rows in turn a workgroup.  Under the lowered limit a launch
-    holds 32 rows: [1501, 4096] takes 47 launches, the last of 29 rows, whose
-    last workgroup's second turn is past the end."""
+    """Both sizes take rows of 8 waves with one chunk a lane.  [300, 4096]
+    stores its column-major scales directly; [1501, 4096] stages them, and
+    column-major MXFP4 takes two rows in turn a workgroup.  Under the lowered
+    limit a launch holds 32 rows: [1501, 4096] takes 47 launches, the last of
+    29 rows, whose last workgroup's second turn is past the end."""
     H = 4096
     d = inputs.random_rows(M, H, 9100 + M)
     x, r, w = (d[k].to(DEV) for k in ("x", "residual", "weight"))

@@ -16,16 +16,21 @@ from parity import check_fp8, check_mxfp4, to_np
 
 pytestmark = pytest.mark.gpu
 DEV = "cuda:0"
-# Row counts beyond a few hundred with four one-wave rows a workgroup (3000 x 256)
-# and multi-wave rows (1100 x 4096, 700 x 2048, 8192 x 4096, and 520 x 7168 with
-# two chunks a lane: one row a workgroup for per-group FP8, two in turn for
-# MXFP4); odd counts (3, 17, 65, 9) leave the last MXFP4 workgroup's second turn
-# past the end.  H = 16384 fills the LDS stage of 16-wave rows exactly (512 E8M0
-# bytes; 512 fp32 scales at group 32).
+# Small batches store each column-major scale from the lane that computes it
+# (every case below 1024 rows, and 3000 x 256); batches of at least 1024 rows
+# whose launch fills the chip's wave slots stage the scales in LDS and store
+# runs along M, MXFP4 taking two multi-wave rows in turn a workgroup
+# (1100 x 4096, 8192 x 4096; 8200 x 256 with four one-wave rows a workgroup;
+# the mixed-row test below adds odd counts, whose last MXFP4 workgroup has its
+# second turn past the end, and 1025 x 7168 with two chunks a lane).  The small
+# cases take every tiling of the direct stores, 520 x 7168 with two chunks a
+# lane.  At H = 16384 the small cases take the direct stores' 16-wave rows and
+# 1024 x 16384 fills the staged kernels' LDS stage exactly (512 E8M0 bytes;
+# 512 fp32 scales at group 32).
 CASES = [("bf16", 16, 4096, 128), ("bf16", 16, 7168, 32), ("bf16", 3, 544, 32), ("bf16", 130, 1024, 512),
          ("bf16", 65, 4096, 64), ("fp16", 17, 2048, 128), ("fp16", 9, 16384, 256), ("bf16", 8192, 4096, 128),
          ("bf16", 3000, 256, 32), ("bf16", 1100, 4096, 128), ("fp16", 700, 2048, 64), ("bf16", 5, 16384, 32),
-         ("bf16", 520, 7168, 64)]
+         ("bf16", 520, 7168, 64), ("bf16", 8200, 256, 32), ("bf16", 1024, 16384, 32)]
 
 
 def padded(M):
@@ -118,7 +123,7 @@ def test_tscale_tiny_and_normal_rows_share_a_workgroup(M, H):
         assert torch.equal(a[2][:, :M], b[2].t()), "scales differ"
 
 
-MIXED = [(2049, 4096), (2049, 1024), (5001, 2048), (1025, 7168)]
+MIXED = [(2049, 4096), (4101, 1024), (5001, 2048), (1025, 7168)]
 
 
 @pytest.mark.parametrize("M,H", MIXED, ids=[f"{m}x{h}" for m, h in MIXED])
