@@ -66,16 +66,19 @@ def parse():
                    help="short run for rocprofv3: warmup + steps, the prefill kernels alone, the column-major-scale "
                         "calls (4 each at ld = M, then ld = M + 64) and a 256 MiB device copy for calibration")
     p.add_argument("--sweep", action="store_true",
-                   help="instead of the step: µs per call and GB/s of the three fused formats over a range of "
-                        "row counts at H = 4096 and 7168 (one JSON line per shape)")
+                   help="instead of the step: µs per call and GB/s of the three fused formats and the two "
+                        "column-major-scale calls over a range of row counts at H = 4096 and 7168 (one JSON line "
+                        "per shape)")
     return p.parse_args()
 
 
 def sweep(torch, rq, dev, calls: int = 50, replays: int = 5):
-    """Row-count sweep of the fused formats: for each [M, H], a graph of `calls`
-    back-to-back calls over rotating input and output sets (at least 512 MiB of
-    inputs, or 1024 sets), median replay / calls.  Inputs ~ N(0, 1), weight
-    ~ N(1, 0.1), drawn on the device from a seeded generator."""
+    """Row-count sweep of the fused formats, row-major and column-major scales
+    (leading dimension M): for each [M, H], a graph of `calls` back-to-back
+    calls over rotating input and output sets (at least 512 MiB of inputs, or
+    1024 sets), replayed once untimed, then the median replay / calls.
+    Inputs ~ N(0, 1), weight ~ N(1, 0.1), drawn on the device from a seeded
+    generator."""
     import statistics
     gen = torch.Generator(device=dev).manual_seed(1008)
     for H in (4096, 7168):
@@ -91,6 +94,8 @@ def sweep(torch, rq, dev, calls: int = 50, replays: int = 5):
             st = torch.empty((no, M), dtype=torch.float32, device=dev)
             sg = torch.empty((no, M, H // 128), dtype=torch.float32, device=dev)
             sm = torch.empty((no, M, H // 32), dtype=torch.uint8, device=dev)
+            tg = torch.empty((no, H // 128, M), dtype=torch.float32, device=dev)
+            tm = torch.empty((no, H // 32, M), dtype=torch.uint8, device=dev)
             fns = {
                 "fp8_token": lambda i: rq.rmsnorm_quant_fp8_per_token(
                     xs[i % n], rs[i % n], w, 1e-6, q_out=q8[i % no], residual_out=ro[i % no], scale_out=st[i % no]),
@@ -99,6 +104,11 @@ def sweep(torch, rq, dev, calls: int = 50, replays: int = 5):
                     scale_out=sg[i % no]),
                 "mxfp4": lambda i: rq.rmsnorm_quant_mxfp4(
                     xs[i % n], rs[i % n], w, 1e-6, q_out=q4[i % no], residual_out=ro[i % no], scale_out=sm[i % no]),
+                "fp8_group_tscale": lambda i: rq.rmsnorm_quant_fp8_per_group_tscale(
+                    xs[i % n], rs[i % n], w, 1e-6, 128, q_out=q8[i % no], residual_out=ro[i % no],
+                    scale_out=tg[i % no]),
+                "mxfp4_tscale": lambda i: rq.rmsnorm_quant_mxfp4_tscale(
+                    xs[i % n], rs[i % n], w, 1e-6, q_out=q4[i % no], residual_out=ro[i % no], scale_out=tm[i % no]),
             }
             line = {"M": M, "H": H, "rotating_sets": n}
             for fmt, fn in fns.items():
@@ -110,6 +120,8 @@ def sweep(torch, rq, dev, calls: int = 50, replays: int = 5):
                     for i in range(calls):
                         fn(i)
                 upload_graphs(torch, [g], torch.cuda.current_stream())
+                g.replay()  # untimed: the first replay after capture runs slower
+                torch.cuda.synchronize()
                 times = []
                 for _ in range(replays):
                     a, b = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
@@ -119,11 +131,11 @@ def sweep(torch, rq, dev, calls: int = 50, replays: int = 5):
                     torch.cuda.synchronize()
                     times.append(1000.0 * a.elapsed_time(b) / calls)
                 us = statistics.median(times)
-                gbs = row_bytes(fmt, M, H) / (us * 1e-6) / 1e9
+                gbs = row_bytes(fmt.replace("_tscale", ""), M, H) / (us * 1e-6) / 1e9
                 line[fmt] = {"us": round(us, 3), "GBps": round(gbs, 1), "frac_of_peak": round(gbs / HBM_PEAK_GBS, 4)}
                 del g
             print(json.dumps(line), flush=True)
-            del xs, rs, ro, q8, q4, st, sg, sm
+            del xs, rs, ro, q8, q4, st, sg, sm, tg, tm
 
 
 def main():
