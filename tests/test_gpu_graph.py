@@ -228,3 +228,54 @@ def test_graph_replay_quantized_qk_and_column_major_scales():
         torch.cuda.synchronize()
         for name, a, b in zip(outs, snapshot(), eager):
             assert torch.equal(a.view(torch.uint8), b.view(torch.uint8)), f"replay {i}: {name} differs from eager"
+
+
+def test_graph_replay_staged_column_major_scales():
+    """Batches large enough for the staged column-major kernels (scales run
+    along M through LDS, MXFP4 rows two in turn a workgroup): [1101, 4096], an
+    odd count, so the last MXFP4 workgroup's second turn is past the end.  Each
+    replay reproduces the eager results bit for bit, padding past M untouched."""
+    M, H = 1101, 4096
+    d = inputs.random_rows(M, H, seed=1101)
+    x, r, w = (d[k].to(DEV) for k in ("x", "residual", "weight"))
+    u8, f32, bf = torch.uint8, torch.float32, torch.bfloat16
+    outs = dict(
+        tq=torch.empty((M, H), dtype=u8, device=DEV), tro=torch.empty((M, H), dtype=bf, device=DEV),
+        ts=torch.empty((H // 128, M + 3), dtype=f32, device=DEV),
+        mq=torch.empty((M, H // 2), dtype=u8, device=DEV), mro=torch.empty((M, H), dtype=bf, device=DEV),
+        ms=torch.empty((H // 32, M + 3), dtype=u8, device=DEV),
+    )
+
+    def step():
+        o = outs
+        assert rq.rmsnorm_quant_fp8_per_group_tscale(x, r, w, 1e-6, 128, q_out=o["tq"], residual_out=o["tro"],
+                                                     scale_out=o["ts"][:, :M]) is not None
+        assert rq.rmsnorm_quant_mxfp4_tscale(x, r, w, 1e-6, q_out=o["mq"], residual_out=o["mro"],
+                                             scale_out=o["ms"][:, :M]) is not None
+
+    def snapshot():
+        return [t.clone() for t in outs.values()]
+
+    for t in outs.values():
+        t.zero_()
+    step()
+    torch.cuda.synchronize()
+    eager = snapshot()
+    s = torch.cuda.Stream()
+    s.wait_stream(torch.cuda.current_stream())
+    with torch.cuda.stream(s):
+        step()
+    torch.cuda.current_stream().wait_stream(s)
+    torch.cuda.synchronize()
+    g = torch.cuda.CUDAGraph()
+    with torch.cuda.graph(g):
+        step()
+    for i in range(4):
+        for t in outs.values():
+            t.zero_()
+        _ = (x.float() * 3).sum().item()
+        g.replay()
+        torch.cuda.synchronize()
+        for name, a, b in zip(outs, snapshot(), eager):
+            assert torch.equal(a.view(torch.uint8), b.view(torch.uint8)), f"replay {i}: {name} differs from eager"
+        assert (outs["ts"][:, M:] == 0).all() and (outs["ms"][:, M:] == 0).all(), "padding past M written"
