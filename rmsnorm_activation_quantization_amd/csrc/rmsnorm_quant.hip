@@ -1032,8 +1032,9 @@ int chunks_per_lane(int H, int l) {
 // there is no second generation of waves to wait for.  The column-major scale
 // kernels take the same tiling (per-group FP8 with its scales staged in LDS:
 // measured on MI355X from 1 % slower to 4 % faster than with the fewest waves,
-// over 1024-8192 rows and H = 2048-8192).  The row's sum is the same for every
-// tiling.
+// over 1024-8192 rows and H = 2048-8192), except that the staged ones give
+// rows of 7168-8192 one chunk of 16 waves (launch_rows).  The row's sum is the
+// same for every tiling.
 int waves_per_row_log2(int64_t M, int H) {
   int l = 0;
   while (l < 4 && chunks_per_lane(H, l) > kMaxChunks) ++l;
@@ -1044,7 +1045,17 @@ int waves_per_row_log2(int64_t M, int H) {
 
 template <typename E, int kMode, int kStage = kStageFused>
 rq_status launch_rows(RowArgs& a, void* stream) {
-  const int l = waves_per_row_log2(a.M, a.H);
+  int l = waves_per_row_log2(a.M, a.H);
+  bool staged = false;
+  if constexpr (kStage == kStageFusedColScales) {
+    staged = a.M >= kStagedColScaleRows && a.M * (int64_t)(1 << l) >= kResidentWaves;
+    // Staged column-major scales of wide rows take one chunk of 16 waves where
+    // the row tiling gives two chunks of 8, when at most an eighth of the
+    // lanes would sit idle (H >= 7168): measured on MI355X 0-11 % faster at
+    // 2048-8192 rows of 7168 and 8192 (the row-major kernels measured up to 8 %
+    // slower that way), 3-4 % slower at 5120 where 37.5 % of the lanes idle.
+    if (staged && l == 3 && chunks_per_lane(a.H, 3) == 2 && 8 * a.H >= 7 * (kWave << 4) * 8) l = 4;
+  }
   const int wpr = 1 << l;
   const int lanes = kWave * wpr;
   const int nc = chunks_per_lane(a.H, l);
@@ -1052,7 +1063,7 @@ rq_status launch_rows(RowArgs& a, void* stream) {
   const void* kernel = reinterpret_cast<const void*>(RowKernels<E, kMode, kStage>::k[l][nc - 1]);
   int turns = rows_in_turn_of(wpr, kMode, kStage);
   if constexpr (kStage == kStageFusedColScales) {
-    if (a.M >= kStagedColScaleRows && a.M * (int64_t)wpr >= kResidentWaves) {
+    if (staged) {
       kernel = reinterpret_cast<const void*>(RowKernels<E, kMode, kStageFusedColScalesStaged>::k[l][nc - 1]);
       turns = rows_in_turn_of(wpr, kMode, kStageFusedColScalesStaged);
     }

@@ -22,7 +22,8 @@ DEV = "cuda:0"
 # runs along M, MXFP4 taking two multi-wave rows in turn a workgroup
 # (1100 x 4096, 8192 x 4096; 8200 x 256 with four one-wave rows a workgroup;
 # the mixed-row test below adds odd counts, whose last MXFP4 workgroup has its
-# second turn past the end, and 1025 x 7168 with two chunks a lane).  The small
+# second turn past the end; 1025 x 7168 and 1030 x 8192 take 16 waves with one
+# chunk a lane, the staged tiling of rows that wide).  The small
 # cases take every tiling of the direct stores, 520 x 7168 with two chunks a
 # lane.  At H = 16384 the small cases take the direct stores' 16-wave rows and
 # 1024 x 16384 fills the staged kernels' LDS stage exactly (512 E8M0 bytes;
@@ -30,7 +31,7 @@ DEV = "cuda:0"
 CASES = [("bf16", 16, 4096, 128), ("bf16", 16, 7168, 32), ("bf16", 3, 544, 32), ("bf16", 130, 1024, 512),
          ("bf16", 65, 4096, 64), ("fp16", 17, 2048, 128), ("fp16", 9, 16384, 256), ("bf16", 8192, 4096, 128),
          ("bf16", 3000, 256, 32), ("bf16", 1100, 4096, 128), ("fp16", 700, 2048, 64), ("bf16", 5, 16384, 32),
-         ("bf16", 520, 7168, 64), ("bf16", 8200, 256, 32), ("bf16", 1024, 16384, 32)]
+         ("bf16", 520, 7168, 64), ("bf16", 8200, 256, 32), ("bf16", 1024, 16384, 32), ("bf16", 1030, 8192, 128)]
 
 
 def padded(M):
