@@ -18,11 +18,16 @@ The K steps run as one captured HIP graph per kernel (back-to-back launches);
 after the W eager warmup steps the graphs are replayed four times untimed (4K
 more warmup steps, reported as config.graph_warmup_steps) before the timed
 replay.
-Also reported: per-kernel time and GB/s (HIP events on the launch stream),
-decode-size microseconds per call (M = 16, H = 4096, all formats; graph replay
-of back-to-back calls over rotating inputs, as the pages time kernels) next to
-the launch floor of a one-element kernel timed the same way, and the CPU oracle
-timed on the host cores as the CPU baseline.
+Also reported: per-kernel time and GB/s in the step (HIP events on the launch
+stream) and alone (each prefill kernel's graph replayed in turn, median; the
+roofline comes from these), [4096, 4096] in the three formats, decode-size
+microseconds per call (M = 16, H = 4096, all formats, C1, C3 and the QK
+variants; graph replay of back-to-back calls over rotating inputs, as the
+pages time kernels) next to the launch floor of a one-element kernel timed the
+same way, the unfused sequence, QK and its quantized variants at 8192 tokens,
+column-major scales and fp16 rows at [8192, 4096] (each timed alternately with
+its bf16 row-major counterpart), and the CPU oracle timed on the host cores as
+the CPU baseline.
 """
 
 from __future__ import annotations
