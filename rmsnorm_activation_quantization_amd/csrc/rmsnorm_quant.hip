@@ -48,9 +48,9 @@
 //        which equals the IEEE fp32 quotient for every bf16 or fp16 y and
 //        fp32 scale >= 2^-64 (checked exhaustively on the host by the test
 //        suite); the hardware converter then rounds to E4M3FN (nearest-even).
-//   MXFP4: E8M0 byte from the fp32 exponent of amax; y * 2^(127 - byte) is
-//        exact, and the hardware converter rounds to E2M1 (nearest-even,
-//        saturating at 6).
+//   MXFP4: E8M0 byte from the fp32 exponent of amax; the hardware converter
+//        divides y by the block scale 2^(byte - 127), exactly, and rounds to
+//        E2M1 (nearest-even, saturating at 6).
 #include <hip/hip_runtime.h>
 
 #include <algorithm>
@@ -106,6 +106,12 @@ struct Bf16 {
   __device__ static float hi(uint32_t w) { return bf_hi(w); }
   __device__ static uint32_t pack(float a, float b) { return pack_bf16(a, b); }
   __device__ static float value(uint32_t h) { return __uint_as_float(h << 16); }  // one element's bits
+  // v_cvt_scalef32_pk_fp4_bf16: the pair's two E2M1 codes, each element divided
+  // by s, into byte kSel of old.
+  template <int kSel>
+  __device__ static uint32_t fp4x2(uint32_t old, uint32_t w, float s) {
+    return (uint32_t)__builtin_amdgcn_cvt_scalef32_pk_fp4_bf16(old, __builtin_bit_cast(bf16x2_t, w), s, kSel);
+  }
 };
 struct F16 {
   __device__ static float lo(uint32_t w) { return (float)__builtin_bit_cast(_Float16, (uint16_t)(w & 0xFFFFu)); }
@@ -116,6 +122,11 @@ struct F16 {
     return __builtin_bit_cast(uint32_t, __builtin_convertvector(v, f16x2_t));
   }
   __device__ static float value(uint32_t h) { return (float)__builtin_bit_cast(_Float16, (uint16_t)h); }
+  // v_cvt_scalef32_pk_fp4_f16, as the bf16 one
+  template <int kSel>
+  __device__ static uint32_t fp4x2(uint32_t old, uint32_t w, float s) {
+    return (uint32_t)__builtin_amdgcn_cvt_scalef32_pk_fp4_f16(old, __builtin_bit_cast(f16x2_t, w), s, kSel);
+  }
 };
 
 // Largest |bf16| or |fp16| bit pattern of a packed pair per half (integer max of the
@@ -303,17 +314,23 @@ __device__ __forceinline__ uint32_t e8m0_byte(float amax) {
   return e >= 2u ? e - 2u : 0u;
 }
 
-// Eight values -> eight E2M1 codes (one uint32, element i in nibble i).
-// y * 2^(127 - byte) is exact (power-of-two scaling of a bf16 or fp16 value);
-// byte is at most 252 for a finite amax, so the factor is a normal fp32.
+// Eight values -> eight E2M1 codes (one uint32, element i in nibble i): each
+// value over the block scale 2^(byte - 127), rounded once to nearest even,
+// saturating.  The converter takes the packed 16-bit elements as they are and
+// divides by its fp32 scale operand, which holds that scale itself (byte 0 is
+// 2^-127, an fp32 subnormal; a finite block's byte is at most 252).  Measured
+// on MI355X over every bf16 and every fp16 pair at every such byte, the codes
+// are those of scaling in fp32 first (exact: a power of two) and converting at
+// scale 1.  A non-finite block (byte 255) passes +Inf; its codes are left
+// unspecified.
 template <typename E>
 __device__ __forceinline__ uint32_t mxfp4_codes(const uint4& y, uint32_t byte) {
-  const float f = __uint_as_float((254u - byte) << 23);
+  const float s = __uint_as_float(byte != 0u ? byte << 23 : 0x00400000u);
   uint32_t d = 0;
-  d = (uint32_t)__builtin_amdgcn_cvt_scalef32_pk_fp4_f32(d, E::lo(y.x) * f, E::hi(y.x) * f, 1.0f, 0);
-  d = (uint32_t)__builtin_amdgcn_cvt_scalef32_pk_fp4_f32(d, E::lo(y.y) * f, E::hi(y.y) * f, 1.0f, 1);
-  d = (uint32_t)__builtin_amdgcn_cvt_scalef32_pk_fp4_f32(d, E::lo(y.z) * f, E::hi(y.z) * f, 1.0f, 2);
-  d = (uint32_t)__builtin_amdgcn_cvt_scalef32_pk_fp4_f32(d, E::lo(y.w) * f, E::hi(y.w) * f, 1.0f, 3);
+  d = E::template fp4x2<0>(d, y.x, s);
+  d = E::template fp4x2<1>(d, y.y, s);
+  d = E::template fp4x2<2>(d, y.z, s);
+  d = E::template fp4x2<3>(d, y.w, s);
   return d;
 }
 

@@ -113,6 +113,35 @@ def np_e2m1(v: np.ndarray) -> np.ndarray:
     return np.where(np.signbit(v), idx | np.uint8(0x8), idx).astype(np.uint8)
 
 
+def every_e8m0_byte_blocks(dtype: str = "bf16", H: int = 4096) -> np.ndarray:
+    """Rows of H bit patterns, in 32-element blocks that reach every E8M0 byte a
+    finite block of the type can take.  For each exponent e from the smallest
+    subnormal's to the largest finite one, blocks lead with 2^e and their other
+    31 elements take every magnitude below 2^(e+1), both signs (finite
+    magnitudes ascend with their patterns).  The block maximum keeps exponent e,
+    so each value meets every block scale it can sit under (bf16 bytes 0-252,
+    clamped to 0 for e below -125; fp16 bytes 101-140).  Padding is 1.0."""
+    if dtype == "bf16":
+        exps, one = range(-133, 128), 0x3F80
+        pow2 = lambda e: (e + 127) << 7 if e >= -126 else 1 << (e + 133)
+    else:
+        exps, one = range(-24, 16), 0x3C00
+        pow2 = lambda e: (e + 15) << 10 if e >= -14 else 1 << (e + 24)
+    blocks = []
+    for e in exps:
+        v = np.arange(pow2(e + 1), dtype=np.uint16)  # 2^(e+1) past the largest finite value is Inf's pattern
+        v = np.concatenate([v, v | np.uint16(0x8000)])
+        n = -(-len(v) // 31)
+        blk = np.zeros((n, 32), np.uint16)
+        blk[:, 0] = pow2(e)
+        flat = np.zeros(n * 31, np.uint16)
+        flat[: len(v)] = v
+        blk[:, 1:] = flat.reshape(n, 31)
+        blocks.append(blk.reshape(-1))
+    bits = np.concatenate(blocks)
+    return np.concatenate([bits, np.full((-bits.size) % H, one, np.uint16)]).reshape(-1, H)
+
+
 def torch_bf16_add(x_bits: np.ndarray, r_bits: np.ndarray, dtype: str = "bf16") -> np.ndarray:
     """torch's CPU bf16 (or fp16) addition (an independent library routine)."""
     td = TORCH_DTYPE[dtype]

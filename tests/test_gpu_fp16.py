@@ -9,7 +9,7 @@ import torch
 
 import rmsnorm_activation_quantization_amd as rq
 from rmsnorm_activation_quantization_amd import inputs
-from oracle_pins import np_f16_round, np_f16_value
+from oracle_pins import every_e8m0_byte_blocks, np_f16_round, np_f16_value
 from parity import check_fp8, check_mxfp4, to_np
 
 pytestmark = pytest.mark.gpu
@@ -134,6 +134,23 @@ def test_fp16_mxfp4_conversion_exhaustive(ref, k):
         o = ref.mxfp4(xb, xb.copy(), wb, 0.0, dtype="fp16")
         assert (gpu["scale"] == o["scale"]).all()
         assert (gpu["q"] == o["q"]).all(), f"E2M1 codes differ in row {i} at k={k}"
+
+
+def test_fp16_mxfp4_conversion_every_scale_byte(ref):
+    """Every E8M0 byte a finite fp16 block can take (101-140), through the
+    quantize launch: blocks led by 2^e for e from -24 to 15, whose other
+    elements run through every fp16 magnitude below 2^(e+1), both signs.  Every
+    code and byte must be the oracle's bit for bit."""
+    bits = every_e8m0_byte_blocks("fp16")
+    out = rq.quantize_mxfp4(inputs.from_bits(bits, F16).to(DEV))
+    assert out is not None
+    torch.cuda.synchronize()
+    want = ref.quantize_mxfp4(bits, dtype="fp16")
+    got_q, got_s = out[0].cpu().numpy(), out[1].cpu().numpy()
+    assert (got_s == want["scale"]).all(), "E8M0 bytes differ"
+    assert len(np.unique(got_s)) == 40, "not every byte was reached"
+    bad = np.argwhere(got_q != want["q"])
+    assert len(bad) == 0, f"E2M1 codes differ at {bad[:5].tolist()}"
 
 
 def test_mixed_dtypes_are_rejected():

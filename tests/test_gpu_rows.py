@@ -9,7 +9,8 @@ import torch
 
 import rmsnorm_activation_quantization_amd as rq
 from rmsnorm_activation_quantization_amd import inputs
-from oracle_pins import fp8_probe_case, mxfp4_probe_case, np_bf16_round, np_bf16_value, BF16_VALUE
+from oracle_pins import (fp8_probe_case, mxfp4_probe_case, np_bf16_round, np_bf16_value, BF16_VALUE,
+                         every_e8m0_byte_blocks)
 from parity import check_fp8, check_mxfp4, to_np
 
 pytestmark = pytest.mark.gpu
@@ -209,6 +210,23 @@ def test_mxfp4_conversion_exhaustive(ref, k):
         o = ref.mxfp4(xb, xb.copy(), wb, 0.0)
         assert (gpu["scale"] == o["scale"]).all()
         assert (gpu["q"] == o["q"]).all(), f"E2M1 codes differ in row {i} at k={k}"
+
+
+def test_mxfp4_conversion_every_scale_byte(ref):
+    """Every E8M0 byte a finite bf16 block can take (0-252), through the quantize
+    launch: blocks led by 2^e for e from -133 (the smallest bf16 subnormal) to
+    127, whose other elements run through every bf16 magnitude below 2^(e+1),
+    both signs.  Every code and byte must be the oracle's bit for bit."""
+    bits = every_e8m0_byte_blocks("bf16")
+    out = rq.quantize_mxfp4(inputs.from_bits(bits).to(DEV))
+    assert out is not None
+    torch.cuda.synchronize()
+    want = ref.quantize_mxfp4(bits)
+    got_q, got_s = out[0].cpu().numpy(), out[1].cpu().numpy()
+    assert (got_s == want["scale"]).all(), "E8M0 bytes differ"
+    assert len(np.unique(got_s)) == 253, "not every byte was reached"
+    bad = np.argwhere(got_q != want["q"])
+    assert len(bad) == 0, f"E2M1 codes differ at {bad[:5].tolist()}"
 
 
 def test_zero_sign_tiny_and_nan(ref):
