@@ -64,6 +64,8 @@ for _name in ("rmsnorm_quant_fp8_per_token", "rmsnorm_quant_fp8_per_group", "rms
 _SIGNATURES["rmsnorm_residual_f16"] = _SIGNATURES["rmsnorm_residual_bf16"]
 
 _ELEMENT_TYPES = (torch.bfloat16, torch.float16)
+# dtypes are singletons: the checks below compare them by identity
+_BF16, _F16, _F32, _U8, _FP8 = torch.bfloat16, torch.float16, torch.float32, torch.uint8, torch.float8_e4m3fn
 
 
 _FN_CACHE: dict = {}
@@ -140,62 +142,87 @@ def _ptr(t: torch.Tensor | None) -> int | None:
 _raw_stream = getattr(torch._C, "_cuda_getCurrentRawStream", None)
 
 
-def _stream(stream, t: torch.Tensor) -> int:
+def _stream(stream, dev: torch.device) -> int:
     if stream is not None:
         return stream.cuda_stream
     if _raw_stream is not None:
-        return _raw_stream(t.get_device())
-    return torch.cuda.current_stream(t.device).cuda_stream
+        return _raw_stream(dev.index)
+    return torch.cuda.current_stream(dev).cuda_stream
 
+
+# The checks below read each tensor attribute once: every read is a call into
+# torch (0.1-0.4 us), and an eager decode-sized call is bound by this host time.
 
 def _rows(t: torch.Tensor, name: str, dtype=None) -> int:
     """Row stride (elements) of a 2-D bf16 or fp16 CUDA tensor with unit column
     stride (and the given dtype, when one is given)."""
-    if t.dim() != 2 or t.dtype not in _ELEMENT_TYPES or not t.is_cuda:
+    sh, dt = t.shape, t.dtype
+    if len(sh) != 2 or (dt is not _BF16 and dt is not _F16) or not t.is_cuda:
         raise ValueError(f"{name} must be a 2-D bfloat16 or float16 CUDA tensor")
-    if dtype is not None and t.dtype != dtype:
+    if dtype is not None and dt is not dtype:
         raise ValueError(f"{name} must have the dtype of x ({dtype})")
-    if t.shape[1] > 1 and t.stride(1) != 1:
+    st = t.stride()
+    if sh[1] > 1 and st[1] != 1:
         raise ValueError(f"{name} must have unit column stride")
-    return t.stride(0) if t.shape[0] > 1 else t.shape[1]
+    return st[0] if sh[0] > 1 else sh[1]
 
 
 def _same_device(like: torch.Tensor, **tensors) -> None:
     """Every given tensor (None skipped) on the device of `like`: the kernels
     dereference every pointer on that device, so a host tensor or one on
     another GPU is refused here."""
+    dev = like.device
     for name, t in tensors.items():
-        if t is not None and t.device != like.device:
-            raise ValueError(f"{name} is on {t.device}; every tensor must be on {like.device}")
+        if t is not None and t.device != dev:
+            raise ValueError(f"{name} is on {t.device}; every tensor must be on {dev}")
 
 
 def _row_outputs(x, residual, weight, residual_out, y_out, emit_y):
-    """Checks the row inputs (one element type for all, one device) and
-    allocates the missing row outputs in that type."""
-    M, H = x.shape
-    dt = x.dtype
-    if residual.shape != (M, H) or weight.shape != (H,) or residual.dtype != dt or weight.dtype != dt:
+    """Checks the row inputs (one element type for all, one device) and the
+    caller's row outputs, and allocates the missing ones in that type.
+    -> (M, H, device, residual_out, y_out)."""
+    sh, dt = x.shape, x.dtype
+    M, H = sh
+    if residual.shape != sh or weight.shape != (H,) or residual.dtype is not dt or weight.dtype is not dt:
         raise ValueError(f"residual must be [M, H] and weight [H], both {dt} like x")
     if not weight.is_contiguous():
         raise ValueError("weight must be contiguous")
-    _same_device(x, residual=residual, weight=weight, residual_out=residual_out, y_out=y_out)
-    if residual_out is None:
-        residual_out = torch.empty((M, H), dtype=dt, device=x.device)
-    if y_out is None and emit_y:
-        y_out = torch.empty((M, H), dtype=dt, device=x.device)
+    dev = x.device
+    for name, t in (("residual", residual), ("weight", weight), ("residual_out", residual_out), ("y_out", y_out)):
+        if t is not None and t.device != dev:
+            raise ValueError(f"{name} is on {t.device}; every tensor must be on {dev}")
     for name, t in (("residual_out", residual_out), ("y_out", y_out)):
-        if t is not None and (t.shape != (M, H) or t.dtype != dt or not t.is_contiguous()):
+        if t is not None and (t.shape != sh or t.dtype is not dt or not t.is_contiguous()):
             raise ValueError(f"{name} must be a contiguous [M, H] {dt} tensor")
-    return M, H, residual_out, y_out
+    if residual_out is None:
+        residual_out = torch.empty(sh, dtype=dt, device=dev)
+    if y_out is None and emit_y:
+        y_out = torch.empty(sh, dtype=dt, device=dev)
+    return M, H, dev, residual_out, y_out
 
 
-def _out(t, shape, dtypes, name, like):
+def _out(t, shape, dtypes, name, dev):
     """A caller-supplied output: the exact shape, one of the dtypes, contiguous,
-    on the device of `like`.  The library cannot see buffer sizes, so a wrong
-    output tensor is refused here rather than written past its end."""
-    if tuple(t.shape) != tuple(shape) or t.dtype not in dtypes or not t.is_contiguous() or t.device != like.device:
-        raise ValueError(f"{name} must be a contiguous {list(shape)} {dtypes[0]} tensor on {like.device}")
+    on device `dev`.  The library cannot see buffer sizes, so a wrong output
+    tensor is refused here rather than written past its end."""
+    if t.shape != shape or t.dtype not in dtypes or not t.is_contiguous() or t.device != dev:
+        raise ValueError(f"{name} must be a contiguous {list(shape)} {dtypes[0]} tensor on {dev}")
     return t
+
+
+def _fp8(q):
+    """Codes as float8_e4m3fn (a caller's uint8 buffer is viewed; a view costs
+    about 1 us, so fp8 buffers pass through)."""
+    return q if q.dtype is _FP8 else q.view(_FP8)
+
+
+def _token_scale(scale_out, M, dev):
+    """The per-token scale output: [M, 1] fp32, or the caller's [M] or [M, 1]."""
+    if scale_out is None:
+        return torch.empty((M, 1), dtype=_F32, device=dev)
+    if scale_out.shape != (M,) and scale_out.shape != (M, 1):
+        raise ValueError(f"scale_out must be a contiguous [{M}] or [{M}, 1] float32 tensor")
+    return _out(scale_out, scale_out.shape, (_F32,), "scale_out", dev)
 
 
 _CODES8 = (torch.uint8, torch.float8_e4m3fn)
@@ -205,68 +232,62 @@ def rmsnorm_quant_fp8_per_token(x, residual, weight, eps: float = 1e-6, *, resid
                                 scale_out=None, emit_y: bool = False, y_out=None, stream=None):
     """-> (q [M, H] float8_e4m3fn, residual_out [M, H] bf16, scale [M, 1] fp32, y or None), or None."""
     ldx, ldr = _rows(x, "x"), _rows(residual, "residual", x.dtype)
-    M, H, residual_out, y_out = _row_outputs(x, residual, weight, residual_out, y_out, emit_y)
-    q_out = torch.empty((M, H), dtype=torch.uint8, device=x.device) if q_out is None else \
-        _out(q_out, (M, H), _CODES8, "q_out", x)
-    if scale_out is None:
-        scale_out = torch.empty((M,), dtype=torch.float32, device=x.device)
-    elif tuple(scale_out.shape) not in ((M,), (M, 1)):
-        raise ValueError(f"scale_out must be a contiguous [{M}] or [{M}, 1] float32 tensor")
-    else:
-        _out(scale_out, scale_out.shape, (torch.float32,), "scale_out", x)
+    M, H, dev, residual_out, y_out = _row_outputs(x, residual, weight, residual_out, y_out, emit_y)
+    q_out = torch.empty((M, H), dtype=_FP8, device=dev) if q_out is None else _out(q_out, (M, H), _CODES8, "q_out", dev)
+    scale_out = _token_scale(scale_out, M, dev)
     st = _fn("rmsnorm_quant_fp8_per_token", x.dtype)(
-        _ptr(x), ldx, _ptr(residual), ldr, _ptr(weight), M, H, eps, _ptr(residual_out), _ptr(q_out),
-        _ptr(scale_out), _ptr(y_out), _stream(stream, x))
+        x.data_ptr(), ldx, residual.data_ptr(), ldr, weight.data_ptr(), M, H, eps, residual_out.data_ptr(),
+        q_out.data_ptr(), scale_out.data_ptr(), _ptr(y_out), _stream(stream, dev))
     if not _check(st, "rmsnorm_quant_fp8_per_token"):
         return None
-    return q_out.view(torch.float8_e4m3fn), residual_out, scale_out.view(M, 1), y_out
+    return _fp8(q_out), residual_out, scale_out if scale_out.dim() == 2 else scale_out.view(M, 1), y_out
 
 
 def rmsnorm_quant_fp8_per_group(x, residual, weight, eps: float = 1e-6, group: int = 128, *, residual_out=None,
                                 q_out=None, scale_out=None, emit_y: bool = False, y_out=None, stream=None):
     """-> (q [M, H] float8_e4m3fn, residual_out, scale [M, H/group] fp32, y or None), or None."""
     ldx, ldr = _rows(x, "x"), _rows(residual, "residual", x.dtype)
-    M, H, residual_out, y_out = _row_outputs(x, residual, weight, residual_out, y_out, emit_y)
+    M, H, dev, residual_out, y_out = _row_outputs(x, residual, weight, residual_out, y_out, emit_y)
     G = max(H // group, 1) if group > 0 else 1
-    q_out = torch.empty((M, H), dtype=torch.uint8, device=x.device) if q_out is None else \
-        _out(q_out, (M, H), _CODES8, "q_out", x)
-    scale_out = torch.empty((M, G), dtype=torch.float32, device=x.device) if scale_out is None else \
-        _out(scale_out, (M, G), (torch.float32,), "scale_out", x)
+    q_out = torch.empty((M, H), dtype=_FP8, device=dev) if q_out is None else _out(q_out, (M, H), _CODES8, "q_out", dev)
+    scale_out = torch.empty((M, G), dtype=_F32, device=dev) if scale_out is None else \
+        _out(scale_out, (M, G), (_F32,), "scale_out", dev)
     st = _fn("rmsnorm_quant_fp8_per_group", x.dtype)(
-        _ptr(x), ldx, _ptr(residual), ldr, _ptr(weight), M, H, eps, group, _ptr(residual_out), _ptr(q_out),
-        _ptr(scale_out), _ptr(y_out), _stream(stream, x))
+        x.data_ptr(), ldx, residual.data_ptr(), ldr, weight.data_ptr(), M, H, eps, group, residual_out.data_ptr(),
+        q_out.data_ptr(), scale_out.data_ptr(), _ptr(y_out), _stream(stream, dev))
     if not _check(st, "rmsnorm_quant_fp8_per_group"):
         return None
-    return q_out.view(torch.float8_e4m3fn), residual_out, scale_out, y_out
+    return _fp8(q_out), residual_out, scale_out, y_out
 
 
 def rmsnorm_quant_mxfp4(x, residual, weight, eps: float = 1e-6, *, residual_out=None, q_out=None,
                         scale_out=None, emit_y: bool = False, y_out=None, stream=None):
     """-> (q [M, H/2] uint8 packed E2M1, residual_out, scale [M, H/32] uint8 E8M0, y or None), or None."""
     ldx, ldr = _rows(x, "x"), _rows(residual, "residual", x.dtype)
-    M, H, residual_out, y_out = _row_outputs(x, residual, weight, residual_out, y_out, emit_y)
-    q_out = torch.empty((M, H // 2), dtype=torch.uint8, device=x.device) if q_out is None else \
-        _out(q_out, (M, H // 2), (torch.uint8,), "q_out", x)
-    scale_out = torch.empty((M, max(H // 32, 1)), dtype=torch.uint8, device=x.device) if scale_out is None else \
-        _out(scale_out, (M, max(H // 32, 1)), (torch.uint8,), "scale_out", x)
+    M, H, dev, residual_out, y_out = _row_outputs(x, residual, weight, residual_out, y_out, emit_y)
+    q_out = torch.empty((M, H // 2), dtype=_U8, device=dev) if q_out is None else \
+        _out(q_out, (M, H // 2), (_U8,), "q_out", dev)
+    scale_out = torch.empty((M, max(H // 32, 1)), dtype=_U8, device=dev) if scale_out is None else \
+        _out(scale_out, (M, max(H // 32, 1)), (_U8,), "scale_out", dev)
     st = _fn("rmsnorm_quant_mxfp4", x.dtype)(
-        _ptr(x), ldx, _ptr(residual), ldr, _ptr(weight), M, H, eps, _ptr(residual_out), _ptr(q_out),
-        _ptr(scale_out), _ptr(y_out), _stream(stream, x))
+        x.data_ptr(), ldx, residual.data_ptr(), ldr, weight.data_ptr(), M, H, eps, residual_out.data_ptr(),
+        q_out.data_ptr(), scale_out.data_ptr(), _ptr(y_out), _stream(stream, dev))
     if not _check(st, "rmsnorm_quant_mxfp4"):
         return None
     return q_out, residual_out, scale_out, y_out
 
 
-def _tscale_out(scale_out, rows, M, dtype, x):
+def _tscale_out(scale_out, rows, M, dtype, dev):
     """Column-major scales: a [rows, n >= M] tensor with unit column stride
     (a view of a wider buffer is fine); its row stride is ld_scale."""
     if scale_out is None:
-        scale_out = torch.empty((rows, max(M, 1)), dtype=dtype, device=x.device)
-    if (scale_out.dim() != 2 or scale_out.shape[0] != rows or scale_out.shape[1] < M or scale_out.dtype != dtype
-            or (scale_out.shape[1] > 1 and scale_out.stride(1) != 1) or scale_out.device != x.device):
+        return torch.empty((rows, max(M, 1)), dtype=dtype, device=dev), max(M, 1)
+    sh = scale_out.shape
+    st = scale_out.stride() if len(sh) == 2 else None
+    if (st is None or sh[0] != rows or sh[1] < M or scale_out.dtype is not dtype or (sh[1] > 1 and st[1] != 1)
+            or scale_out.device != dev):
         raise ValueError(f"scale_out must be a [{rows}, >= {M}] {dtype} tensor with unit column stride")
-    ld = scale_out.stride(0) if rows > 1 else max(scale_out.shape[1], 1)
-    return scale_out, ld
+    return scale_out, st[0] if rows > 1 else max(sh[1], 1)
 
 
 def rmsnorm_quant_fp8_per_group_tscale(x, residual, weight, eps: float = 1e-6, group: int = 128, *,
@@ -275,17 +296,16 @@ def rmsnorm_quant_fp8_per_group_tscale(x, residual, weight, eps: float = 1e-6, g
     """Per-group FP8 with column-major scales: scale of row m, group g at scale[g, m].
     -> (q [M, H] float8_e4m3fn, residual_out, scale [H/group, >= M] fp32, y or None), or None."""
     ldx, ldr = _rows(x, "x"), _rows(residual, "residual", x.dtype)
-    M, H, residual_out, y_out = _row_outputs(x, residual, weight, residual_out, y_out, emit_y)
+    M, H, dev, residual_out, y_out = _row_outputs(x, residual, weight, residual_out, y_out, emit_y)
     G = max(H // group, 1) if group > 0 else 1
-    q_out = torch.empty((M, H), dtype=torch.uint8, device=x.device) if q_out is None else \
-        _out(q_out, (M, H), _CODES8, "q_out", x)
-    scale_out, ld = _tscale_out(scale_out, G, M, torch.float32, x)
+    q_out = torch.empty((M, H), dtype=_FP8, device=dev) if q_out is None else _out(q_out, (M, H), _CODES8, "q_out", dev)
+    scale_out, ld = _tscale_out(scale_out, G, M, _F32, dev)
     st = _fn("rmsnorm_quant_fp8_per_group_tscale", x.dtype)(
-        _ptr(x), ldx, _ptr(residual), ldr, _ptr(weight), M, H, eps, group, _ptr(residual_out), _ptr(q_out),
-        _ptr(scale_out), ld, _ptr(y_out), _stream(stream, x))
+        x.data_ptr(), ldx, residual.data_ptr(), ldr, weight.data_ptr(), M, H, eps, group, residual_out.data_ptr(),
+        q_out.data_ptr(), scale_out.data_ptr(), ld, _ptr(y_out), _stream(stream, dev))
     if not _check(st, "rmsnorm_quant_fp8_per_group_tscale"):
         return None
-    return q_out.view(torch.float8_e4m3fn), residual_out, scale_out, y_out
+    return _fp8(q_out), residual_out, scale_out, y_out
 
 
 def rmsnorm_quant_mxfp4_tscale(x, residual, weight, eps: float = 1e-6, *, residual_out=None, q_out=None,
@@ -293,48 +313,47 @@ def rmsnorm_quant_mxfp4_tscale(x, residual, weight, eps: float = 1e-6, *, residu
     """MXFP4 with column-major E8M0 scales: block b of row m at scale[b, m].
     -> (q [M, H/2] uint8 packed E2M1, residual_out, scale [H/32, >= M] uint8, y or None), or None."""
     ldx, ldr = _rows(x, "x"), _rows(residual, "residual", x.dtype)
-    M, H, residual_out, y_out = _row_outputs(x, residual, weight, residual_out, y_out, emit_y)
-    q_out = torch.empty((M, H // 2), dtype=torch.uint8, device=x.device) if q_out is None else \
-        _out(q_out, (M, H // 2), (torch.uint8,), "q_out", x)
-    scale_out, ld = _tscale_out(scale_out, max(H // 32, 1), M, torch.uint8, x)
+    M, H, dev, residual_out, y_out = _row_outputs(x, residual, weight, residual_out, y_out, emit_y)
+    q_out = torch.empty((M, H // 2), dtype=_U8, device=dev) if q_out is None else \
+        _out(q_out, (M, H // 2), (_U8,), "q_out", dev)
+    scale_out, ld = _tscale_out(scale_out, max(H // 32, 1), M, _U8, dev)
     st = _fn("rmsnorm_quant_mxfp4_tscale", x.dtype)(
-        _ptr(x), ldx, _ptr(residual), ldr, _ptr(weight), M, H, eps, _ptr(residual_out), _ptr(q_out),
-        _ptr(scale_out), ld, _ptr(y_out), _stream(stream, x))
+        x.data_ptr(), ldx, residual.data_ptr(), ldr, weight.data_ptr(), M, H, eps, residual_out.data_ptr(),
+        q_out.data_ptr(), scale_out.data_ptr(), ld, _ptr(y_out), _stream(stream, dev))
     if not _check(st, "rmsnorm_quant_mxfp4_tscale"):
         return None
     return q_out, residual_out, scale_out, y_out
 
 
 def _qk_inputs(qg, k, q_w, k_w, head_dim: int):
-    """Checks of the QK inputs (bf16 only, one device) -> (ld_qg, ld_k, T)."""
-    ld_qg, ld_k = _rows(qg, "qg", torch.bfloat16), _rows(k, "k", torch.bfloat16)
+    """Checks of the QK inputs (bf16 only, one device) -> (ld_qg, ld_k, T, device)."""
+    ld_qg, ld_k = _rows(qg, "qg", _BF16), _rows(k, "k", _BF16)
     T = qg.shape[0]
     if k.shape[0] != T:
         raise ValueError("qg and k must have the same number of tokens")
     for name, w in (("q_w", q_w), ("k_w", k_w)):
-        if w.shape != (head_dim,) or w.dtype != torch.bfloat16 or not w.is_contiguous():
+        if w.shape != (head_dim,) or w.dtype is not _BF16 or not w.is_contiguous():
             raise ValueError(f"{name} must be a contiguous [head_dim] bfloat16 tensor")
     _same_device(qg, k=k, q_w=q_w, k_w=k_w)
-    return ld_qg, ld_k, T
+    return ld_qg, ld_k, T, qg.device
 
 
 def qk_gemma_rmsnorm_gate(qg, k, q_w, k_w, num_q_heads: int, num_k_heads: int, head_dim: int,
                           eps: float = 1e-6, *, q_out=None, k_out=None, gate_out=None, stream=None):
     """qg [T, >= 2*Hq*D] interleaved per head as [q | gate]; k [T, >= Hk*D] (row stride allowed).
     -> (q [T, Hq, D], k [T, Hk, D], gate [T, Hq, D]) contiguous bf16, or None."""
-    ld_qg, ld_k, T = _qk_inputs(qg, k, q_w, k_w, head_dim)
+    ld_qg, ld_k, T, dev = _qk_inputs(qg, k, q_w, k_w, head_dim)
     Hq, Hk, D = num_q_heads, num_k_heads, head_dim
-    dev = qg.device
     q_out = torch.empty((T, Hq, D), dtype=torch.bfloat16, device=dev) if q_out is None else q_out
     k_out = torch.empty((T, Hk, D), dtype=torch.bfloat16, device=dev) if k_out is None else k_out
     gate_out = torch.empty((T, Hq, D), dtype=torch.bfloat16, device=dev) if gate_out is None else gate_out
     for name, t, h in (("q_out", q_out, Hq), ("k_out", k_out, Hk), ("gate_out", gate_out, Hq)):
-        if t.shape != (T, h, D) or t.dtype != torch.bfloat16 or not t.is_contiguous():
+        if t.shape != (T, h, D) or t.dtype is not _BF16 or not t.is_contiguous():
             raise ValueError(f"{name} must be a contiguous [T, heads, head_dim] bfloat16 tensor")
     _same_device(qg, q_out=q_out, k_out=k_out, gate_out=gate_out)
     st = lib().qk_gemma_rmsnorm_gate(
-        _ptr(qg), ld_qg, _ptr(k), ld_k, _ptr(q_w), _ptr(k_w), T, Hq, Hk, D, eps, _ptr(q_out), _ptr(k_out),
-        _ptr(gate_out), _stream(stream, qg))
+        qg.data_ptr(), ld_qg, k.data_ptr(), ld_k, q_w.data_ptr(), k_w.data_ptr(), T, Hq, Hk, D, eps, q_out.data_ptr(),
+        k_out.data_ptr(), gate_out.data_ptr(), _stream(stream, dev))
     if not _check(st, "qk_gemma_rmsnorm_gate"):
         return None
     return q_out, k_out, gate_out
@@ -346,9 +365,8 @@ def qk_gemma_rmsnorm_gate_fp8(qg, k, q_w, k_w, num_q_heads: int, num_k_heads: in
     """As qk_gemma_rmsnorm_gate, with q and k quantized per head to FP8 E4M3FN.
     -> (q [T, Hq, D] float8_e4m3fn, q_scale [T, Hq] fp32, k [T, Hk, D] float8_e4m3fn, k_scale [T, Hk] fp32,
         gate [T, Hq, D] bf16), or None."""
-    ld_qg, ld_k, T = _qk_inputs(qg, k, q_w, k_w, head_dim)
+    ld_qg, ld_k, T, dev = _qk_inputs(qg, k, q_w, k_w, head_dim)
     Hq, Hk, D = num_q_heads, num_k_heads, head_dim
-    dev = qg.device
     fp8 = torch.float8_e4m3fn
     q_out = torch.empty((T, Hq, D), dtype=fp8, device=dev) if q_out is None else q_out
     k_out = torch.empty((T, Hk, D), dtype=fp8, device=dev) if k_out is None else k_out
@@ -360,12 +378,12 @@ def qk_gemma_rmsnorm_gate_fp8(qg, k, q_w, k_w, num_q_heads: int, num_k_heads: in
                                 ("q_scale_out", q_scale_out, (T, Hq), (torch.float32,)),
                                 ("k_scale_out", k_scale_out, (T, Hk), (torch.float32,)),
                                 ("gate_out", gate_out, (T, Hq, D), (torch.bfloat16,))):
-        if tuple(t.shape) != shape or t.dtype not in dts or not t.is_contiguous():
+        if t.shape != shape or t.dtype not in dts or not t.is_contiguous():
             raise ValueError(f"{name} must be a contiguous {list(shape)} tensor of {dts[0]}")
     _same_device(qg, q_out=q_out, k_out=k_out, q_scale_out=q_scale_out, k_scale_out=k_scale_out, gate_out=gate_out)
     st = lib().qk_gemma_rmsnorm_gate_fp8(
-        _ptr(qg), ld_qg, _ptr(k), ld_k, _ptr(q_w), _ptr(k_w), T, Hq, Hk, D, eps, _ptr(q_out), _ptr(q_scale_out),
-        _ptr(k_out), _ptr(k_scale_out), _ptr(gate_out), _stream(stream, qg))
+        qg.data_ptr(), ld_qg, k.data_ptr(), ld_k, q_w.data_ptr(), k_w.data_ptr(), T, Hq, Hk, D, eps, q_out.data_ptr(),
+        q_scale_out.data_ptr(), k_out.data_ptr(), k_scale_out.data_ptr(), gate_out.data_ptr(), _stream(stream, dev))
     if not _check(st, "qk_gemma_rmsnorm_gate_fp8"):
         return None
     return q_out, q_scale_out, k_out, k_scale_out, gate_out
@@ -377,9 +395,8 @@ def qk_gemma_rmsnorm_gate_mxfp4(qg, k, q_w, k_w, num_q_heads: int, num_k_heads: 
     """As qk_gemma_rmsnorm_gate, with q and k quantized to MXFP4 (head_dim a multiple of 32).
     -> (q [T, Hq, D/2] uint8 packed E2M1, q_scale [T, Hq, D/32] uint8 E8M0, k [T, Hk, D/2], k_scale [T, Hk, D/32],
         gate [T, Hq, D] bf16), or None."""
-    ld_qg, ld_k, T = _qk_inputs(qg, k, q_w, k_w, head_dim)
+    ld_qg, ld_k, T, dev = _qk_inputs(qg, k, q_w, k_w, head_dim)
     Hq, Hk, D = num_q_heads, num_k_heads, head_dim
-    dev = qg.device
     u8 = torch.uint8
     shapes = {"q_out": (T, Hq, D // 2), "q_scale_out": (T, Hq, max(D // 32, 1)), "k_out": (T, Hk, D // 2),
               "k_scale_out": (T, Hk, max(D // 32, 1)), "gate_out": (T, Hq, D)}
@@ -389,11 +406,11 @@ def qk_gemma_rmsnorm_gate_mxfp4(qg, k, q_w, k_w, num_q_heads: int, num_k_heads: 
     for name, shape in shapes.items():
         dt = torch.bfloat16 if name == "gate_out" else u8
         t = given[name]
-        outs[name] = torch.empty(shape, dtype=dt, device=dev) if t is None else _out(t, shape, (dt,), name, qg)
+        outs[name] = torch.empty(shape, dtype=dt, device=dev) if t is None else _out(t, shape, (dt,), name, dev)
     st = lib().qk_gemma_rmsnorm_gate_mxfp4(
-        _ptr(qg), ld_qg, _ptr(k), ld_k, _ptr(q_w), _ptr(k_w), T, Hq, Hk, D, eps, _ptr(outs["q_out"]),
-        _ptr(outs["q_scale_out"]), _ptr(outs["k_out"]), _ptr(outs["k_scale_out"]), _ptr(outs["gate_out"]),
-        _stream(stream, qg))
+        qg.data_ptr(), ld_qg, k.data_ptr(), ld_k, q_w.data_ptr(), k_w.data_ptr(), T, Hq, Hk, D, eps,
+        outs["q_out"].data_ptr(), outs["q_scale_out"].data_ptr(), outs["k_out"].data_ptr(),
+        outs["k_scale_out"].data_ptr(), outs["gate_out"].data_ptr(), _stream(stream, dev))
     if not _check(st, "qk_gemma_rmsnorm_gate_mxfp4"):
         return None
     return outs["q_out"], outs["q_scale_out"], outs["k_out"], outs["k_scale_out"], outs["gate_out"]
@@ -404,58 +421,56 @@ def qk_gemma_rmsnorm_gate_mxfp4(qg, k, q_w, k_w, num_q_heads: int, num_k_heads: 
 def rmsnorm_residual_bf16(x, residual, weight, eps: float = 1e-6, *, residual_out=None, y_out=None, stream=None):
     """-> (residual_out [M, H] bf16, y [M, H] bf16), or None."""
     ldx, ldr = _rows(x, "x"), _rows(residual, "residual", x.dtype)
-    M, H, residual_out, y_out = _row_outputs(x, residual, weight, residual_out, y_out, True)
-    st = _fn("rmsnorm_residual", x.dtype)(_ptr(x), ldx, _ptr(residual), ldr, _ptr(weight), M, H, eps,
-                                     _ptr(residual_out), _ptr(y_out), _stream(stream, x))
+    M, H, dev, residual_out, y_out = _row_outputs(x, residual, weight, residual_out, y_out, True)
+    st = _fn("rmsnorm_residual", x.dtype)(x.data_ptr(), ldx, residual.data_ptr(), ldr, weight.data_ptr(), M, H, eps,
+                                          residual_out.data_ptr(), y_out.data_ptr(), _stream(stream, dev))
     if not _check(st, "rmsnorm_residual_bf16"):
         return None
     return residual_out, y_out
 
 
 def _quant_input(y):
+    """-> (ldy, M, H, device)."""
     ldy = _rows(y, "y")
-    return ldy, y.shape[0], y.shape[1]
+    M, H = y.shape
+    return ldy, M, H, y.device
 
 
 def quantize_fp8_per_token(y, *, q_out=None, scale_out=None, stream=None):
     """-> (q [M, H] float8_e4m3fn, scale [M, 1] fp32), or None."""
-    ldy, M, H = _quant_input(y)
-    q_out = torch.empty((M, H), dtype=torch.uint8, device=y.device) if q_out is None else \
-        _out(q_out, (M, H), _CODES8, "q_out", y)
-    if scale_out is None:
-        scale_out = torch.empty((M,), dtype=torch.float32, device=y.device)
-    elif tuple(scale_out.shape) not in ((M,), (M, 1)):
-        raise ValueError(f"scale_out must be a contiguous [{M}] or [{M}, 1] float32 tensor")
-    else:
-        _out(scale_out, scale_out.shape, (torch.float32,), "scale_out", y)
-    st = _fn("quantize_fp8_per_token", y.dtype)(_ptr(y), ldy, M, H, _ptr(q_out), _ptr(scale_out), _stream(stream, y))
+    ldy, M, H, dev = _quant_input(y)
+    q_out = torch.empty((M, H), dtype=_FP8, device=dev) if q_out is None else _out(q_out, (M, H), _CODES8, "q_out", dev)
+    scale_out = _token_scale(scale_out, M, dev)
+    st = _fn("quantize_fp8_per_token", y.dtype)(y.data_ptr(), ldy, M, H, q_out.data_ptr(), scale_out.data_ptr(),
+                                                _stream(stream, dev))
     if not _check(st, "quantize_fp8_per_token"):
         return None
-    return q_out.view(torch.float8_e4m3fn), scale_out.view(M, 1)
+    return _fp8(q_out), scale_out if scale_out.dim() == 2 else scale_out.view(M, 1)
 
 
 def quantize_fp8_per_group(y, group: int = 128, *, q_out=None, scale_out=None, stream=None):
     """-> (q [M, H] float8_e4m3fn, scale [M, H/group] fp32), or None."""
-    ldy, M, H = _quant_input(y)
+    ldy, M, H, dev = _quant_input(y)
     G = max(H // group, 1) if group > 0 else 1
-    q_out = torch.empty((M, H), dtype=torch.uint8, device=y.device) if q_out is None else \
-        _out(q_out, (M, H), _CODES8, "q_out", y)
-    scale_out = torch.empty((M, G), dtype=torch.float32, device=y.device) if scale_out is None else \
-        _out(scale_out, (M, G), (torch.float32,), "scale_out", y)
-    st = _fn("quantize_fp8_per_group", y.dtype)(_ptr(y), ldy, M, H, group, _ptr(q_out), _ptr(scale_out), _stream(stream, y))
+    q_out = torch.empty((M, H), dtype=_FP8, device=dev) if q_out is None else _out(q_out, (M, H), _CODES8, "q_out", dev)
+    scale_out = torch.empty((M, G), dtype=_F32, device=dev) if scale_out is None else \
+        _out(scale_out, (M, G), (_F32,), "scale_out", dev)
+    st = _fn("quantize_fp8_per_group", y.dtype)(y.data_ptr(), ldy, M, H, group, q_out.data_ptr(), scale_out.data_ptr(),
+                                                _stream(stream, dev))
     if not _check(st, "quantize_fp8_per_group"):
         return None
-    return q_out.view(torch.float8_e4m3fn), scale_out
+    return _fp8(q_out), scale_out
 
 
 def quantize_mxfp4(y, *, q_out=None, scale_out=None, stream=None):
     """-> (q [M, H/2] uint8 packed E2M1, scale [M, H/32] uint8 E8M0), or None."""
-    ldy, M, H = _quant_input(y)
-    q_out = torch.empty((M, H // 2), dtype=torch.uint8, device=y.device) if q_out is None else \
-        _out(q_out, (M, H // 2), (torch.uint8,), "q_out", y)
-    scale_out = torch.empty((M, max(H // 32, 1)), dtype=torch.uint8, device=y.device) if scale_out is None else \
-        _out(scale_out, (M, max(H // 32, 1)), (torch.uint8,), "scale_out", y)
-    st = _fn("quantize_mxfp4", y.dtype)(_ptr(y), ldy, M, H, _ptr(q_out), _ptr(scale_out), _stream(stream, y))
+    ldy, M, H, dev = _quant_input(y)
+    q_out = torch.empty((M, H // 2), dtype=_U8, device=dev) if q_out is None else \
+        _out(q_out, (M, H // 2), (_U8,), "q_out", dev)
+    scale_out = torch.empty((M, max(H // 32, 1)), dtype=_U8, device=dev) if scale_out is None else \
+        _out(scale_out, (M, max(H // 32, 1)), (_U8,), "scale_out", dev)
+    st = _fn("quantize_mxfp4", y.dtype)(y.data_ptr(), ldy, M, H, q_out.data_ptr(), scale_out.data_ptr(),
+                                        _stream(stream, dev))
     if not _check(st, "quantize_mxfp4"):
         return None
     return q_out, scale_out
