@@ -4,6 +4,7 @@ from __future__ import annotations
 
 import os
 import subprocess
+import sysconfig
 
 PKG = os.path.dirname(os.path.abspath(__file__))
 ROOT = os.path.dirname(PKG)
@@ -36,6 +37,33 @@ def build(output: str = LIBRARY, extra_flags: tuple[str, ...] = ()) -> str:
     if proc.returncode != 0:
         raise RuntimeError(f"hipcc failed ({proc.returncode}):\n{proc.stderr}")
     os.replace(tmp, output)
+    return output
+
+
+MARSHAL_SOURCE = os.path.join(PKG, "csrc", "marshal.cpp")
+
+
+def marshal_path() -> str:
+    """The CPython module of the binding's argument marshalling, in-tree."""
+    return os.path.join(PKG, "_marshal" + sysconfig.get_config_var("EXT_SUFFIX"))
+
+
+def build_marshal(output: str | None = None) -> str:
+    """The binding's marshalling module (host C++ against torch's headers, g++;
+    no device code)."""
+    import torch.utils.cpp_extension as ce
+
+    output = output or marshal_path()
+    torch_lib = ce.library_paths()[0]
+    cmd = ["g++", "-O2", "-std=c++17", "-fPIC", "-shared", "-D__HIP_PLATFORM_AMD__=1", "-DUSE_ROCM=1",
+           f"-D_GLIBCXX_USE_CXX11_ABI={int(__import__('torch')._C._GLIBCXX_USE_CXX11_ABI)}",
+           *[f"-I{p}" for p in ce.include_paths()], "-I", os.path.join(ROCM, "include"),
+           "-I", sysconfig.get_paths()["include"], MARSHAL_SOURCE, "-o", output + ".tmp",
+           f"-L{torch_lib}", "-ltorch", "-ltorch_cpu", "-lc10", "-lc10_hip", "-ltorch_python", f"-Wl,-rpath,{torch_lib}"]
+    proc = subprocess.run(cmd, capture_output=True, text=True)
+    if proc.returncode != 0:
+        raise RuntimeError(f"g++ failed ({proc.returncode}):\n{proc.stderr}")
+    os.replace(output + ".tmp", output)
     return output
 
 

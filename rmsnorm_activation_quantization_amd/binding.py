@@ -1,10 +1,16 @@
-"""Thin ctypes binding of librmsnorm_quant.so (argument marshalling only).
+"""Thin binding of librmsnorm_quant.so (argument marshalling only).
 
 Every entry point has the name of the C function it calls (include/rmsnorm_quant.h).
 torch supplies device memory and the current stream; every step of the
-computation runs in the library's HIP kernels.  There is no other code path:
-if the library is missing (RuntimeError at the first call) or the device is
-not an MI355X (RQ_ERR_DEVICE, RuntimeError), calls fail loudly.
+computation runs in the library's HIP kernels.  The fused row calls, the norm
+launch and the QK calls hand their tensors to the marshalling module built
+beside this file (csrc/marshal.cpp), which checks the arguments on torch's C++
+tensors, allocates missing outputs and calls the C entry point whose address
+this module resolves from the loaded library; the unfused quantize launches
+check their arguments here and call through ctypes.  There is no other code
+path: if the library or the marshalling module is missing (RuntimeError at the
+first call) or the device is not an MI355X (RQ_ERR_DEVICE, RuntimeError),
+calls fail loudly.
 
 bf16 and fp16 rows: every row function dispatches on the dtype of x (or y):
 bf16 tensors run the bf16 kernels, fp16 tensors the _f16 ones, and the row
@@ -85,6 +91,47 @@ def _fn(name: str, dtype):
     return fn
 
 
+def _entries(name: str) -> tuple:
+    """Addresses of the bf16 and fp16 C entry points of one row call in the
+    loaded library (bf16: name, or name_bf16 for the norm launch; fp16:
+    name_f16), for the marshalling module."""
+    key = ("addresses", name)
+    e = _FN_CACHE.get(key)
+    if e is None:
+        h = lib()
+        bf = getattr(h, name + ("_bf16" if name == "rmsnorm_residual" else ""))
+        e = (ctypes.cast(bf, ctypes.c_void_p).value, ctypes.cast(getattr(h, name + "_f16"), ctypes.c_void_p).value)
+        _FN_CACHE[key] = e
+    return e
+
+
+def _entry(name: str) -> int:
+    """Address of one C entry point of the loaded library."""
+    key = ("address", name)
+    e = _FN_CACHE.get(key)
+    if e is None:
+        e = _FN_CACHE[key] = ctypes.cast(getattr(lib(), name), ctypes.c_void_p).value
+    return e
+
+
+_marshal = None
+
+
+def _native():
+    """The marshalling module built beside this file (csrc/marshal.cpp): the
+    checks, output allocation and C call of the row and QK entry points, on
+    torch's C++ tensors.  Raises if it has not been built."""
+    global _marshal
+    if _marshal is None:
+        try:
+            from . import _marshal as m
+        except ImportError as e:
+            raise RuntimeError(f"{_build.marshal_path()} is missing or does not load ({e}): build it first "
+                               "(python -c 'import __graft_entry__ as g; g.build()')") from e
+        _marshal = m
+    return _marshal
+
+
 def library_path() -> str:
     return _build.LIBRARY
 
@@ -133,6 +180,13 @@ def _check(status: int, name: str):
     raise RuntimeError(msg)
 
 
+def _status(status: int, name: str):
+    """A marshalled call that did not return RQ_OK: None for 'cannot fuse',
+    raise for the rest (as _check)."""
+    _check(status, name)
+    return None
+
+
 def _ptr(t: torch.Tensor | None) -> int | None:
     return None if t is None else t.data_ptr()
 
@@ -177,30 +231,6 @@ def _same_device(like: torch.Tensor, **tensors) -> None:
             raise ValueError(f"{name} is on {t.device}; every tensor must be on {dev}")
 
 
-def _row_outputs(x, residual, weight, residual_out, y_out, emit_y):
-    """Checks the row inputs (one element type for all, one device) and the
-    caller's row outputs, and allocates the missing ones in that type.
-    -> (M, H, device, residual_out, y_out)."""
-    sh, dt = x.shape, x.dtype
-    M, H = sh
-    if residual.shape != sh or weight.shape != (H,) or residual.dtype is not dt or weight.dtype is not dt:
-        raise ValueError(f"residual must be [M, H] and weight [H], both {dt} like x")
-    if not weight.is_contiguous():
-        raise ValueError("weight must be contiguous")
-    dev = x.device
-    for name, t in (("residual", residual), ("weight", weight), ("residual_out", residual_out), ("y_out", y_out)):
-        if t is not None and t.device != dev:
-            raise ValueError(f"{name} is on {t.device}; every tensor must be on {dev}")
-    for name, t in (("residual_out", residual_out), ("y_out", y_out)):
-        if t is not None and (t.shape != sh or t.dtype is not dt or not t.is_contiguous()):
-            raise ValueError(f"{name} must be a contiguous [M, H] {dt} tensor")
-    if residual_out is None:
-        residual_out = torch.empty(sh, dtype=dt, device=dev)
-    if y_out is None and emit_y:
-        y_out = torch.empty(sh, dtype=dt, device=dev)
-    return M, H, dev, residual_out, y_out
-
-
 def _out(t, shape, dtypes, name, dev):
     """A caller-supplied output: the exact shape, one of the dtypes, contiguous,
     on device `dev`.  The library cannot see buffer sizes, so a wrong output
@@ -227,166 +257,77 @@ def _token_scale(scale_out, M, dev):
 
 _CODES8 = (torch.uint8, torch.float8_e4m3fn)
 
+# What the marshalling module's rows() and qk() run (csrc/marshal.cpp)
+_FP8_TOKEN, _FP8_GROUP, _MXFP4, _FP8_GROUP_TSCALE, _MXFP4_TSCALE, _NORM = range(6)
+_QK_BF16, _QK_FP8, _QK_MXFP4 = range(3)
+
 
 def rmsnorm_quant_fp8_per_token(x, residual, weight, eps: float = 1e-6, *, residual_out=None, q_out=None,
                                 scale_out=None, emit_y: bool = False, y_out=None, stream=None):
     """-> (q [M, H] float8_e4m3fn, residual_out [M, H] bf16, scale [M, 1] fp32, y or None), or None."""
-    ldx, ldr = _rows(x, "x"), _rows(residual, "residual", x.dtype)
-    M, H, dev, residual_out, y_out = _row_outputs(x, residual, weight, residual_out, y_out, emit_y)
-    q_out = torch.empty((M, H), dtype=_FP8, device=dev) if q_out is None else _out(q_out, (M, H), _CODES8, "q_out", dev)
-    scale_out = _token_scale(scale_out, M, dev)
-    st = _fn("rmsnorm_quant_fp8_per_token", x.dtype)(
-        x.data_ptr(), ldx, residual.data_ptr(), ldr, weight.data_ptr(), M, H, eps, residual_out.data_ptr(),
-        q_out.data_ptr(), scale_out.data_ptr(), _ptr(y_out), _stream(stream, dev))
-    if not _check(st, "rmsnorm_quant_fp8_per_token"):
-        return None
-    return _fp8(q_out), residual_out, scale_out if scale_out.dim() == 2 else scale_out.view(M, 1), y_out
+    r = _native().rows(_FP8_TOKEN, _entries("rmsnorm_quant_fp8_per_token"), x, residual, weight, eps, 0,
+                       residual_out, q_out, scale_out, emit_y, y_out, stream)
+    return r if r.__class__ is tuple else _status(r, "rmsnorm_quant_fp8_per_token")
 
 
 def rmsnorm_quant_fp8_per_group(x, residual, weight, eps: float = 1e-6, group: int = 128, *, residual_out=None,
                                 q_out=None, scale_out=None, emit_y: bool = False, y_out=None, stream=None):
     """-> (q [M, H] float8_e4m3fn, residual_out, scale [M, H/group] fp32, y or None), or None."""
-    ldx, ldr = _rows(x, "x"), _rows(residual, "residual", x.dtype)
-    M, H, dev, residual_out, y_out = _row_outputs(x, residual, weight, residual_out, y_out, emit_y)
-    G = max(H // group, 1) if group > 0 else 1
-    q_out = torch.empty((M, H), dtype=_FP8, device=dev) if q_out is None else _out(q_out, (M, H), _CODES8, "q_out", dev)
-    scale_out = torch.empty((M, G), dtype=_F32, device=dev) if scale_out is None else \
-        _out(scale_out, (M, G), (_F32,), "scale_out", dev)
-    st = _fn("rmsnorm_quant_fp8_per_group", x.dtype)(
-        x.data_ptr(), ldx, residual.data_ptr(), ldr, weight.data_ptr(), M, H, eps, group, residual_out.data_ptr(),
-        q_out.data_ptr(), scale_out.data_ptr(), _ptr(y_out), _stream(stream, dev))
-    if not _check(st, "rmsnorm_quant_fp8_per_group"):
-        return None
-    return _fp8(q_out), residual_out, scale_out, y_out
+    r = _native().rows(_FP8_GROUP, _entries("rmsnorm_quant_fp8_per_group"), x, residual, weight, eps, group,
+                       residual_out, q_out, scale_out, emit_y, y_out, stream)
+    return r if r.__class__ is tuple else _status(r, "rmsnorm_quant_fp8_per_group")
 
 
 def rmsnorm_quant_mxfp4(x, residual, weight, eps: float = 1e-6, *, residual_out=None, q_out=None,
                         scale_out=None, emit_y: bool = False, y_out=None, stream=None):
     """-> (q [M, H/2] uint8 packed E2M1, residual_out, scale [M, H/32] uint8 E8M0, y or None), or None."""
-    ldx, ldr = _rows(x, "x"), _rows(residual, "residual", x.dtype)
-    M, H, dev, residual_out, y_out = _row_outputs(x, residual, weight, residual_out, y_out, emit_y)
-    q_out = torch.empty((M, H // 2), dtype=_U8, device=dev) if q_out is None else \
-        _out(q_out, (M, H // 2), (_U8,), "q_out", dev)
-    scale_out = torch.empty((M, max(H // 32, 1)), dtype=_U8, device=dev) if scale_out is None else \
-        _out(scale_out, (M, max(H // 32, 1)), (_U8,), "scale_out", dev)
-    st = _fn("rmsnorm_quant_mxfp4", x.dtype)(
-        x.data_ptr(), ldx, residual.data_ptr(), ldr, weight.data_ptr(), M, H, eps, residual_out.data_ptr(),
-        q_out.data_ptr(), scale_out.data_ptr(), _ptr(y_out), _stream(stream, dev))
-    if not _check(st, "rmsnorm_quant_mxfp4"):
-        return None
-    return q_out, residual_out, scale_out, y_out
-
-
-def _tscale_out(scale_out, rows, M, dtype, dev):
-    """Column-major scales: a [rows, n >= M] tensor with unit column stride
-    (a view of a wider buffer is fine); its row stride is ld_scale."""
-    if scale_out is None:
-        return torch.empty((rows, max(M, 1)), dtype=dtype, device=dev), max(M, 1)
-    sh = scale_out.shape
-    st = scale_out.stride() if len(sh) == 2 else None
-    if (st is None or sh[0] != rows or sh[1] < M or scale_out.dtype is not dtype or (sh[1] > 1 and st[1] != 1)
-            or scale_out.device != dev):
-        raise ValueError(f"scale_out must be a [{rows}, >= {M}] {dtype} tensor with unit column stride")
-    return scale_out, st[0] if rows > 1 else max(sh[1], 1)
+    r = _native().rows(_MXFP4, _entries("rmsnorm_quant_mxfp4"), x, residual, weight, eps, 0,
+                       residual_out, q_out, scale_out, emit_y, y_out, stream)
+    return r if r.__class__ is tuple else _status(r, "rmsnorm_quant_mxfp4")
 
 
 def rmsnorm_quant_fp8_per_group_tscale(x, residual, weight, eps: float = 1e-6, group: int = 128, *,
                                        residual_out=None, q_out=None, scale_out=None, emit_y: bool = False,
                                        y_out=None, stream=None):
     """Per-group FP8 with column-major scales: scale of row m, group g at scale[g, m].
+    scale_out: [H/group, n >= M] fp32 with unit column stride (a view of a wider buffer is fine; its row
+    stride is the leading dimension), allocated [H/group, M] when None.
     -> (q [M, H] float8_e4m3fn, residual_out, scale [H/group, >= M] fp32, y or None), or None."""
-    ldx, ldr = _rows(x, "x"), _rows(residual, "residual", x.dtype)
-    M, H, dev, residual_out, y_out = _row_outputs(x, residual, weight, residual_out, y_out, emit_y)
-    G = max(H // group, 1) if group > 0 else 1
-    q_out = torch.empty((M, H), dtype=_FP8, device=dev) if q_out is None else _out(q_out, (M, H), _CODES8, "q_out", dev)
-    scale_out, ld = _tscale_out(scale_out, G, M, _F32, dev)
-    st = _fn("rmsnorm_quant_fp8_per_group_tscale", x.dtype)(
-        x.data_ptr(), ldx, residual.data_ptr(), ldr, weight.data_ptr(), M, H, eps, group, residual_out.data_ptr(),
-        q_out.data_ptr(), scale_out.data_ptr(), ld, _ptr(y_out), _stream(stream, dev))
-    if not _check(st, "rmsnorm_quant_fp8_per_group_tscale"):
-        return None
-    return _fp8(q_out), residual_out, scale_out, y_out
+    r = _native().rows(_FP8_GROUP_TSCALE, _entries("rmsnorm_quant_fp8_per_group_tscale"), x, residual, weight, eps,
+                       group, residual_out, q_out, scale_out, emit_y, y_out, stream)
+    return r if r.__class__ is tuple else _status(r, "rmsnorm_quant_fp8_per_group_tscale")
 
 
 def rmsnorm_quant_mxfp4_tscale(x, residual, weight, eps: float = 1e-6, *, residual_out=None, q_out=None,
                                scale_out=None, emit_y: bool = False, y_out=None, stream=None):
     """MXFP4 with column-major E8M0 scales: block b of row m at scale[b, m].
+    scale_out: [H/32, n >= M] uint8 with unit column stride, allocated [H/32, M] when None.
     -> (q [M, H/2] uint8 packed E2M1, residual_out, scale [H/32, >= M] uint8, y or None), or None."""
-    ldx, ldr = _rows(x, "x"), _rows(residual, "residual", x.dtype)
-    M, H, dev, residual_out, y_out = _row_outputs(x, residual, weight, residual_out, y_out, emit_y)
-    q_out = torch.empty((M, H // 2), dtype=_U8, device=dev) if q_out is None else \
-        _out(q_out, (M, H // 2), (_U8,), "q_out", dev)
-    scale_out, ld = _tscale_out(scale_out, max(H // 32, 1), M, _U8, dev)
-    st = _fn("rmsnorm_quant_mxfp4_tscale", x.dtype)(
-        x.data_ptr(), ldx, residual.data_ptr(), ldr, weight.data_ptr(), M, H, eps, residual_out.data_ptr(),
-        q_out.data_ptr(), scale_out.data_ptr(), ld, _ptr(y_out), _stream(stream, dev))
-    if not _check(st, "rmsnorm_quant_mxfp4_tscale"):
-        return None
-    return q_out, residual_out, scale_out, y_out
-
-
-def _qk_inputs(qg, k, q_w, k_w, head_dim: int):
-    """Checks of the QK inputs (bf16 only, one device) -> (ld_qg, ld_k, T, device)."""
-    ld_qg, ld_k = _rows(qg, "qg", _BF16), _rows(k, "k", _BF16)
-    T = qg.shape[0]
-    if k.shape[0] != T:
-        raise ValueError("qg and k must have the same number of tokens")
-    for name, w in (("q_w", q_w), ("k_w", k_w)):
-        if w.shape != (head_dim,) or w.dtype is not _BF16 or not w.is_contiguous():
-            raise ValueError(f"{name} must be a contiguous [head_dim] bfloat16 tensor")
-    _same_device(qg, k=k, q_w=q_w, k_w=k_w)
-    return ld_qg, ld_k, T, qg.device
+    r = _native().rows(_MXFP4_TSCALE, _entries("rmsnorm_quant_mxfp4_tscale"), x, residual, weight, eps, 0,
+                       residual_out, q_out, scale_out, emit_y, y_out, stream)
+    return r if r.__class__ is tuple else _status(r, "rmsnorm_quant_mxfp4_tscale")
 
 
 def qk_gemma_rmsnorm_gate(qg, k, q_w, k_w, num_q_heads: int, num_k_heads: int, head_dim: int,
                           eps: float = 1e-6, *, q_out=None, k_out=None, gate_out=None, stream=None):
-    """qg [T, >= 2*Hq*D] interleaved per head as [q | gate]; k [T, >= Hk*D] (row stride allowed).
+    """qg [T, >= 2*Hq*D] interleaved per head as [q | gate]; k [T, >= Hk*D] (row stride allowed); q_w and
+    k_w [D] bf16, all bf16 on one device.
     -> (q [T, Hq, D], k [T, Hk, D], gate [T, Hq, D]) contiguous bf16, or None."""
-    ld_qg, ld_k, T, dev = _qk_inputs(qg, k, q_w, k_w, head_dim)
-    Hq, Hk, D = num_q_heads, num_k_heads, head_dim
-    q_out = torch.empty((T, Hq, D), dtype=torch.bfloat16, device=dev) if q_out is None else q_out
-    k_out = torch.empty((T, Hk, D), dtype=torch.bfloat16, device=dev) if k_out is None else k_out
-    gate_out = torch.empty((T, Hq, D), dtype=torch.bfloat16, device=dev) if gate_out is None else gate_out
-    for name, t, h in (("q_out", q_out, Hq), ("k_out", k_out, Hk), ("gate_out", gate_out, Hq)):
-        if t.shape != (T, h, D) or t.dtype is not _BF16 or not t.is_contiguous():
-            raise ValueError(f"{name} must be a contiguous [T, heads, head_dim] bfloat16 tensor")
-    _same_device(qg, q_out=q_out, k_out=k_out, gate_out=gate_out)
-    st = lib().qk_gemma_rmsnorm_gate(
-        qg.data_ptr(), ld_qg, k.data_ptr(), ld_k, q_w.data_ptr(), k_w.data_ptr(), T, Hq, Hk, D, eps, q_out.data_ptr(),
-        k_out.data_ptr(), gate_out.data_ptr(), _stream(stream, dev))
-    if not _check(st, "qk_gemma_rmsnorm_gate"):
-        return None
-    return q_out, k_out, gate_out
+    r = _native().qk(_QK_BF16, _entry("qk_gemma_rmsnorm_gate"), qg, k, q_w, k_w, num_q_heads, num_k_heads,
+                     head_dim, eps, q_out, None, k_out, None, gate_out, stream)
+    return r if r.__class__ is tuple else _status(r, "qk_gemma_rmsnorm_gate")
 
 
 def qk_gemma_rmsnorm_gate_fp8(qg, k, q_w, k_w, num_q_heads: int, num_k_heads: int, head_dim: int,
                               eps: float = 1e-6, *, q_out=None, q_scale_out=None, k_out=None, k_scale_out=None,
                               gate_out=None, stream=None):
-    """As qk_gemma_rmsnorm_gate, with q and k quantized per head to FP8 E4M3FN.
+    """As qk_gemma_rmsnorm_gate, with q and k quantized per head to FP8 E4M3FN (caller code buffers may be
+    float8_e4m3fn or uint8, and come back as given).
     -> (q [T, Hq, D] float8_e4m3fn, q_scale [T, Hq] fp32, k [T, Hk, D] float8_e4m3fn, k_scale [T, Hk] fp32,
         gate [T, Hq, D] bf16), or None."""
-    ld_qg, ld_k, T, dev = _qk_inputs(qg, k, q_w, k_w, head_dim)
-    Hq, Hk, D = num_q_heads, num_k_heads, head_dim
-    fp8 = torch.float8_e4m3fn
-    q_out = torch.empty((T, Hq, D), dtype=fp8, device=dev) if q_out is None else q_out
-    k_out = torch.empty((T, Hk, D), dtype=fp8, device=dev) if k_out is None else k_out
-    q_scale_out = torch.empty((T, Hq), dtype=torch.float32, device=dev) if q_scale_out is None else q_scale_out
-    k_scale_out = torch.empty((T, Hk), dtype=torch.float32, device=dev) if k_scale_out is None else k_scale_out
-    gate_out = torch.empty((T, Hq, D), dtype=torch.bfloat16, device=dev) if gate_out is None else gate_out
-    for name, t, shape, dts in (("q_out", q_out, (T, Hq, D), (fp8, torch.uint8)),
-                                ("k_out", k_out, (T, Hk, D), (fp8, torch.uint8)),
-                                ("q_scale_out", q_scale_out, (T, Hq), (torch.float32,)),
-                                ("k_scale_out", k_scale_out, (T, Hk), (torch.float32,)),
-                                ("gate_out", gate_out, (T, Hq, D), (torch.bfloat16,))):
-        if t.shape != shape or t.dtype not in dts or not t.is_contiguous():
-            raise ValueError(f"{name} must be a contiguous {list(shape)} tensor of {dts[0]}")
-    _same_device(qg, q_out=q_out, k_out=k_out, q_scale_out=q_scale_out, k_scale_out=k_scale_out, gate_out=gate_out)
-    st = lib().qk_gemma_rmsnorm_gate_fp8(
-        qg.data_ptr(), ld_qg, k.data_ptr(), ld_k, q_w.data_ptr(), k_w.data_ptr(), T, Hq, Hk, D, eps, q_out.data_ptr(),
-        q_scale_out.data_ptr(), k_out.data_ptr(), k_scale_out.data_ptr(), gate_out.data_ptr(), _stream(stream, dev))
-    if not _check(st, "qk_gemma_rmsnorm_gate_fp8"):
-        return None
-    return q_out, q_scale_out, k_out, k_scale_out, gate_out
+    r = _native().qk(_QK_FP8, _entry("qk_gemma_rmsnorm_gate_fp8"), qg, k, q_w, k_w, num_q_heads, num_k_heads,
+                     head_dim, eps, q_out, q_scale_out, k_out, k_scale_out, gate_out, stream)
+    return r if r.__class__ is tuple else _status(r, "qk_gemma_rmsnorm_gate_fp8")
 
 
 def qk_gemma_rmsnorm_gate_mxfp4(qg, k, q_w, k_w, num_q_heads: int, num_k_heads: int, head_dim: int,
@@ -395,38 +336,18 @@ def qk_gemma_rmsnorm_gate_mxfp4(qg, k, q_w, k_w, num_q_heads: int, num_k_heads: 
     """As qk_gemma_rmsnorm_gate, with q and k quantized to MXFP4 (head_dim a multiple of 32).
     -> (q [T, Hq, D/2] uint8 packed E2M1, q_scale [T, Hq, D/32] uint8 E8M0, k [T, Hk, D/2], k_scale [T, Hk, D/32],
         gate [T, Hq, D] bf16), or None."""
-    ld_qg, ld_k, T, dev = _qk_inputs(qg, k, q_w, k_w, head_dim)
-    Hq, Hk, D = num_q_heads, num_k_heads, head_dim
-    u8 = torch.uint8
-    shapes = {"q_out": (T, Hq, D // 2), "q_scale_out": (T, Hq, max(D // 32, 1)), "k_out": (T, Hk, D // 2),
-              "k_scale_out": (T, Hk, max(D // 32, 1)), "gate_out": (T, Hq, D)}
-    given = {"q_out": q_out, "q_scale_out": q_scale_out, "k_out": k_out, "k_scale_out": k_scale_out,
-             "gate_out": gate_out}
-    outs = {}
-    for name, shape in shapes.items():
-        dt = torch.bfloat16 if name == "gate_out" else u8
-        t = given[name]
-        outs[name] = torch.empty(shape, dtype=dt, device=dev) if t is None else _out(t, shape, (dt,), name, dev)
-    st = lib().qk_gemma_rmsnorm_gate_mxfp4(
-        qg.data_ptr(), ld_qg, k.data_ptr(), ld_k, q_w.data_ptr(), k_w.data_ptr(), T, Hq, Hk, D, eps,
-        outs["q_out"].data_ptr(), outs["q_scale_out"].data_ptr(), outs["k_out"].data_ptr(),
-        outs["k_scale_out"].data_ptr(), outs["gate_out"].data_ptr(), _stream(stream, dev))
-    if not _check(st, "qk_gemma_rmsnorm_gate_mxfp4"):
-        return None
-    return outs["q_out"], outs["q_scale_out"], outs["k_out"], outs["k_scale_out"], outs["gate_out"]
+    r = _native().qk(_QK_MXFP4, _entry("qk_gemma_rmsnorm_gate_mxfp4"), qg, k, q_w, k_w, num_q_heads, num_k_heads,
+                     head_dim, eps, q_out, q_scale_out, k_out, k_scale_out, gate_out, stream)
+    return r if r.__class__ is tuple else _status(r, "qk_gemma_rmsnorm_gate_mxfp4")
 
 
 # ---- the unfused sequence, one launch per step ----
 
 def rmsnorm_residual_bf16(x, residual, weight, eps: float = 1e-6, *, residual_out=None, y_out=None, stream=None):
     """-> (residual_out [M, H] bf16, y [M, H] bf16), or None."""
-    ldx, ldr = _rows(x, "x"), _rows(residual, "residual", x.dtype)
-    M, H, dev, residual_out, y_out = _row_outputs(x, residual, weight, residual_out, y_out, True)
-    st = _fn("rmsnorm_residual", x.dtype)(x.data_ptr(), ldx, residual.data_ptr(), ldr, weight.data_ptr(), M, H, eps,
-                                          residual_out.data_ptr(), y_out.data_ptr(), _stream(stream, dev))
-    if not _check(st, "rmsnorm_residual_bf16"):
-        return None
-    return residual_out, y_out
+    r = _native().rows(_NORM, _entries("rmsnorm_residual"), x, residual, weight, eps, 0, residual_out, None, None,
+                       True, y_out, stream)
+    return r if r.__class__ is tuple else _status(r, "rmsnorm_residual_bf16")
 
 
 def _quant_input(y):
