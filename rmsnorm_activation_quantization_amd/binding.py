@@ -2,15 +2,13 @@
 
 Every entry point has the name of the C function it calls (include/rmsnorm_quant.h).
 torch supplies device memory and the current stream; every step of the
-computation runs in the library's HIP kernels.  The fused row calls, the norm
-launch and the QK calls hand their tensors to the marshalling module built
-beside this file (csrc/marshal.cpp), which checks the arguments on torch's C++
-tensors, allocates missing outputs and calls the C entry point whose address
-this module resolves from the loaded library; the unfused quantize launches
-check their arguments here and call through ctypes.  There is no other code
-path: if the library or the marshalling module is missing (RuntimeError at the
-first call) or the device is not an MI355X (RQ_ERR_DEVICE, RuntimeError),
-calls fail loudly.
+computation runs in the library's HIP kernels.  Every call hands its tensors
+to the marshalling module built beside this file (csrc/marshal.cpp), which
+checks the arguments on torch's C++ tensors, allocates missing outputs and
+calls the C entry point whose address this module resolves from the loaded
+library.  There is no other code path: if the library or the marshalling
+module is missing (RuntimeError at the first call) or the device is not an
+MI355X (RQ_ERR_DEVICE, RuntimeError), calls fail loudly.
 
 bf16 and fp16 rows: every row function dispatches on the dtype of x (or y):
 bf16 tensors run the bf16 kernels, fp16 tensors the _f16 ones, and the row
@@ -31,7 +29,7 @@ import ctypes
 import os
 import threading
 
-import torch
+import torch  # noqa: F401  (the marshalling module needs torch's Python bindings initialized)
 
 from . import _build
 
@@ -69,26 +67,9 @@ for _name in ("rmsnorm_quant_fp8_per_token", "rmsnorm_quant_fp8_per_group", "rms
     _SIGNATURES[_name + "_f16"] = _SIGNATURES[_name]
 _SIGNATURES["rmsnorm_residual_f16"] = _SIGNATURES["rmsnorm_residual_bf16"]
 
-_ELEMENT_TYPES = (torch.bfloat16, torch.float16)
-# dtypes are singletons: the checks below compare them by identity
-_BF16, _F16, _F32, _U8, _FP8 = torch.bfloat16, torch.float16, torch.float32, torch.uint8, torch.float8_e4m3fn
 
 
 _FN_CACHE: dict = {}
-
-
-def _fn(name: str, dtype):
-    """The C entry point for an element type: bf16 -> name (rmsnorm_residual_bf16
-    for the norm launch), fp16 -> name_f16."""
-    key = (name, dtype)
-    fn = _FN_CACHE.get(key)
-    if fn is None:
-        if dtype == torch.float16:
-            fn = getattr(lib(), name + "_f16")
-        else:
-            fn = getattr(lib(), name + ("_bf16" if name == "rmsnorm_residual" else ""))
-        _FN_CACHE[key] = fn
-    return fn
 
 
 def _entries(name: str) -> tuple:
@@ -187,77 +168,8 @@ def _status(status: int, name: str):
     return None
 
 
-def _ptr(t: torch.Tensor | None) -> int | None:
-    return None if t is None else t.data_ptr()
 
-
-# torch's current stream as a raw handle: the private accessor is ~30x cheaper
-# than building a Stream object, which matters for eager decode-sized calls.
-_raw_stream = getattr(torch._C, "_cuda_getCurrentRawStream", None)
-
-
-def _stream(stream, dev: torch.device) -> int:
-    if stream is not None:
-        return stream.cuda_stream
-    if _raw_stream is not None:
-        return _raw_stream(dev.index)
-    return torch.cuda.current_stream(dev).cuda_stream
-
-
-# The checks below read each tensor attribute once: every read is a call into
-# torch (0.1-0.4 us), and an eager decode-sized call is bound by this host time.
-
-def _rows(t: torch.Tensor, name: str, dtype=None) -> int:
-    """Row stride (elements) of a 2-D bf16 or fp16 CUDA tensor with unit column
-    stride (and the given dtype, when one is given)."""
-    sh, dt = t.shape, t.dtype
-    if len(sh) != 2 or (dt is not _BF16 and dt is not _F16) or not t.is_cuda:
-        raise ValueError(f"{name} must be a 2-D bfloat16 or float16 CUDA tensor")
-    if dtype is not None and dt is not dtype:
-        raise ValueError(f"{name} must have the dtype of x ({dtype})")
-    st = t.stride()
-    if sh[1] > 1 and st[1] != 1:
-        raise ValueError(f"{name} must have unit column stride")
-    return st[0] if sh[0] > 1 else sh[1]
-
-
-def _same_device(like: torch.Tensor, **tensors) -> None:
-    """Every given tensor (None skipped) on the device of `like`: the kernels
-    dereference every pointer on that device, so a host tensor or one on
-    another GPU is refused here."""
-    dev = like.device
-    for name, t in tensors.items():
-        if t is not None and t.device != dev:
-            raise ValueError(f"{name} is on {t.device}; every tensor must be on {dev}")
-
-
-def _out(t, shape, dtypes, name, dev):
-    """A caller-supplied output: the exact shape, one of the dtypes, contiguous,
-    on device `dev`.  The library cannot see buffer sizes, so a wrong output
-    tensor is refused here rather than written past its end."""
-    if t.shape != shape or t.dtype not in dtypes or not t.is_contiguous() or t.device != dev:
-        raise ValueError(f"{name} must be a contiguous {list(shape)} {dtypes[0]} tensor on {dev}")
-    return t
-
-
-def _fp8(q):
-    """Codes as float8_e4m3fn (a caller's uint8 buffer is viewed; a view costs
-    about 1 us, so fp8 buffers pass through)."""
-    return q if q.dtype is _FP8 else q.view(_FP8)
-
-
-def _token_scale(scale_out, M, dev):
-    """The per-token scale output: [M, 1] fp32, or the caller's [M] or [M, 1]."""
-    if scale_out is None:
-        return torch.empty((M, 1), dtype=_F32, device=dev)
-    if scale_out.shape != (M,) and scale_out.shape != (M, 1):
-        raise ValueError(f"scale_out must be a contiguous [{M}] or [{M}, 1] float32 tensor")
-    return _out(scale_out, scale_out.shape, (_F32,), "scale_out", dev)
-
-
-_CODES8 = (torch.uint8, torch.float8_e4m3fn)
-
-# What the marshalling module's rows() and qk() run (csrc/marshal.cpp)
+# What the marshalling module's rows(), quantize() and qk() run (csrc/marshal.cpp)
 _FP8_TOKEN, _FP8_GROUP, _MXFP4, _FP8_GROUP_TSCALE, _MXFP4_TSCALE, _NORM = range(6)
 _QK_BF16, _QK_FP8, _QK_MXFP4 = range(3)
 
@@ -350,51 +262,22 @@ def rmsnorm_residual_bf16(x, residual, weight, eps: float = 1e-6, *, residual_ou
     return r if r.__class__ is tuple else _status(r, "rmsnorm_residual_bf16")
 
 
-def _quant_input(y):
-    """-> (ldy, M, H, device)."""
-    ldy = _rows(y, "y")
-    M, H = y.shape
-    return ldy, M, H, y.device
-
-
 def quantize_fp8_per_token(y, *, q_out=None, scale_out=None, stream=None):
     """-> (q [M, H] float8_e4m3fn, scale [M, 1] fp32), or None."""
-    ldy, M, H, dev = _quant_input(y)
-    q_out = torch.empty((M, H), dtype=_FP8, device=dev) if q_out is None else _out(q_out, (M, H), _CODES8, "q_out", dev)
-    scale_out = _token_scale(scale_out, M, dev)
-    st = _fn("quantize_fp8_per_token", y.dtype)(y.data_ptr(), ldy, M, H, q_out.data_ptr(), scale_out.data_ptr(),
-                                                _stream(stream, dev))
-    if not _check(st, "quantize_fp8_per_token"):
-        return None
-    return _fp8(q_out), scale_out if scale_out.dim() == 2 else scale_out.view(M, 1)
+    r = _native().quantize(_FP8_TOKEN, _entries("quantize_fp8_per_token"), y, 0, q_out, scale_out, stream)
+    return r if r.__class__ is tuple else _status(r, "quantize_fp8_per_token")
 
 
 def quantize_fp8_per_group(y, group: int = 128, *, q_out=None, scale_out=None, stream=None):
     """-> (q [M, H] float8_e4m3fn, scale [M, H/group] fp32), or None."""
-    ldy, M, H, dev = _quant_input(y)
-    G = max(H // group, 1) if group > 0 else 1
-    q_out = torch.empty((M, H), dtype=_FP8, device=dev) if q_out is None else _out(q_out, (M, H), _CODES8, "q_out", dev)
-    scale_out = torch.empty((M, G), dtype=_F32, device=dev) if scale_out is None else \
-        _out(scale_out, (M, G), (_F32,), "scale_out", dev)
-    st = _fn("quantize_fp8_per_group", y.dtype)(y.data_ptr(), ldy, M, H, group, q_out.data_ptr(), scale_out.data_ptr(),
-                                                _stream(stream, dev))
-    if not _check(st, "quantize_fp8_per_group"):
-        return None
-    return _fp8(q_out), scale_out
+    r = _native().quantize(_FP8_GROUP, _entries("quantize_fp8_per_group"), y, group, q_out, scale_out, stream)
+    return r if r.__class__ is tuple else _status(r, "quantize_fp8_per_group")
 
 
 def quantize_mxfp4(y, *, q_out=None, scale_out=None, stream=None):
     """-> (q [M, H/2] uint8 packed E2M1, scale [M, H/32] uint8 E8M0), or None."""
-    ldy, M, H, dev = _quant_input(y)
-    q_out = torch.empty((M, H // 2), dtype=_U8, device=dev) if q_out is None else \
-        _out(q_out, (M, H // 2), (_U8,), "q_out", dev)
-    scale_out = torch.empty((M, max(H // 32, 1)), dtype=_U8, device=dev) if scale_out is None else \
-        _out(scale_out, (M, max(H // 32, 1)), (_U8,), "scale_out", dev)
-    st = _fn("quantize_mxfp4", y.dtype)(y.data_ptr(), ldy, M, H, q_out.data_ptr(), scale_out.data_ptr(),
-                                        _stream(stream, dev))
-    if not _check(st, "quantize_mxfp4"):
-        return None
-    return q_out, scale_out
+    r = _native().quantize(_MXFP4, _entries("quantize_mxfp4"), y, 0, q_out, scale_out, stream)
+    return r if r.__class__ is tuple else _status(r, "quantize_mxfp4")
 
 
 # The fp16 entry points under their C names.  Every function above already

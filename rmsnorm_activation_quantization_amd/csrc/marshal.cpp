@@ -1,5 +1,6 @@
-// Argument marshalling of the fused row calls and the QK calls for the Python
-// binding (the CPython module _marshal).
+// Argument marshalling of the library's entry points for the Python binding
+// (the CPython module _marshal): the fused row calls, the unfused sequence's
+// launches and the QK calls.
 //
 // The binding's checks, the allocation of missing outputs and the call of the
 // C entry point, done on torch's C++ tensors.  From Python every tensor
@@ -10,7 +11,7 @@
 // function pointers that the Python binding resolves from the library it has
 // loaded (so that a test can point the binding at another build of it).
 //
-// rows() and qk() return the outputs as a tuple when the C call returns RQ_OK
+// rows(), quantize() and qk() return the outputs as a tuple when the C call returns RQ_OK
 // and the status code (an int) otherwise; arguments the checks refuse raise
 // ValueError, with the Python binding's messages.
 
@@ -30,7 +31,8 @@
 
 namespace {
 
-// What rows() runs (the binding passes one of these with the entry points).
+// What rows() runs (the binding passes one of these with the entry points);
+// quantize() takes the first three.
 enum RowOp { kFp8Token = 0, kFp8Group = 1, kMxfp4 = 2, kFp8GroupT = 3, kMxfp4T = 4, kNorm = 5 };
 // What qk() runs.
 enum QkOp { kQkBf16 = 0, kQkFp8 = 1, kQkMxfp4 = 2 };
@@ -43,6 +45,8 @@ using RowTFn = int (*)(const void*, int64_t, const void*, int64_t, const void*, 
                        void*, int64_t, void*, void*);
 using RowGroupTFn = int (*)(const void*, int64_t, const void*, int64_t, const void*, int64_t, int64_t, float, int64_t,
                             void*, void*, void*, int64_t, void*, void*);
+using QuantFn = int (*)(const void*, int64_t, int64_t, int64_t, void*, void*, void*);
+using QuantGroupFn = int (*)(const void*, int64_t, int64_t, int64_t, int64_t, void*, void*, void*);
 using NormFn = int (*)(const void*, int64_t, const void*, int64_t, const void*, int64_t, int64_t, float, void*, void*,
                        void*);
 using QkFn = int (*)(const void*, int64_t, const void*, int64_t, const void*, const void*, int64_t, int64_t, int64_t,
@@ -126,6 +130,68 @@ void* stream_of(PyObject* stream, const c10::Device& dev) {
 
 PyObject* wrap(const at::Tensor& t) { return THPVariable_Wrap(t); }
 
+// The codes and scales outputs of a row format (kFp8Token ... kMxfp4T): the
+// caller's, checked, or new ones.  Column-major scales are [rows, n >= M]
+// with unit column stride (a view of a wider buffer is fine); their row
+// stride is ld_scale.
+struct Codes {
+  at::Tensor q, sc;
+  int64_t ld_scale = 0;
+};
+Codes codes_and_scales(int op, const at::Tensor* qo, const at::Tensor* so, int64_t M, int64_t H, int64_t group,
+                       const at::TensorOptions& opt, const c10::Device& dev) {
+  Codes c;
+  const int64_t G = group > 0 ? std::max<int64_t>(floordiv(H, group), 1) : 1;
+  const int64_t B = std::max<int64_t>(floordiv(H, 32), 1);
+  if (op == kFp8Token || op == kFp8Group || op == kFp8GroupT)
+    c.q = qo != nullptr ? checked_out(*qo, {M, H}, {at::kByte, at::kFloat8_e4m3fn}, "q_out", dev)
+                        : at::empty({M, H}, opt.dtype(at::kFloat8_e4m3fn));
+  else if (op == kMxfp4 || op == kMxfp4T)
+    c.q = qo != nullptr ? checked_out(*qo, {M, floordiv(H, 2)}, {at::kByte}, "q_out", dev)
+                        : at::empty({M, floordiv(H, 2)}, opt.dtype(at::kByte));
+  if (op == kFp8Token) {
+    if (so == nullptr) {
+      c.sc = at::empty({M, 1}, opt.dtype(at::kFloat));
+    } else {
+      const bool ok = (so->dim() == 1 && so->size(0) == M) || (so->dim() == 2 && so->size(0) == M && so->size(1) == 1);
+      if (!ok)
+        throw Refused{"scale_out must be a contiguous [" + std::to_string(M) + "] or [" + std::to_string(M) +
+                      ", 1] float32 tensor"};
+      c.sc = checked_out(*so, so->sizes(), {at::kFloat}, "scale_out", dev);
+    }
+  } else if (op == kFp8Group) {
+    c.sc = so != nullptr ? checked_out(*so, {M, G}, {at::kFloat}, "scale_out", dev)
+                         : at::empty({M, G}, opt.dtype(at::kFloat));
+  } else if (op == kMxfp4) {
+    c.sc = so != nullptr ? checked_out(*so, {M, B}, {at::kByte}, "scale_out", dev)
+                         : at::empty({M, B}, opt.dtype(at::kByte));
+  } else if (op == kFp8GroupT || op == kMxfp4T) {
+    const int64_t srows = op == kFp8GroupT ? G : B;
+    const c10::ScalarType sdt = op == kFp8GroupT ? at::kFloat : at::kByte;
+    if (so == nullptr) {
+      c.sc = at::empty({srows, std::max<int64_t>(M, 1)}, opt.dtype(sdt));
+      c.ld_scale = std::max<int64_t>(M, 1);
+    } else {
+      if (so->dim() != 2 || so->size(0) != srows || so->size(1) < M || so->scalar_type() != sdt ||
+          (so->size(1) > 1 && so->stride(1) != 1) || so->device() != dev)
+        throw Refused{"scale_out must be a [" + std::to_string(srows) + ", >= " + std::to_string(M) + "] " +
+                      dtype_name(sdt) + " tensor with unit column stride"};
+      c.sc = *so;
+      c.ld_scale = srows > 1 ? so->stride(0) : std::max<int64_t>(so->size(1), 1);
+    }
+  }
+  return c;
+}
+
+// FP8 codes come back as float8_e4m3fn (a caller's uint8 buffer is viewed),
+// per-token scales as [M, 1].
+PyObject* codes_tuple_items(int op, at::Tensor& q, at::Tensor& sc, int64_t M, PyObject** q_obj) {
+  if (q.scalar_type() == at::kByte && op != kMxfp4 && op != kMxfp4T) q = q.view(at::kFloat8_e4m3fn);
+  if (op == kFp8Token && sc.dim() == 1) sc = sc.view({M, 1});
+  *q_obj = wrap(q);
+  return wrap(sc);
+}
+
 PyObject* rows_impl(PyObject* const* a) {
   const int op = (int)PyLong_AsLong(a[0]);
   PyObject* fns = a[1];  // (bf16 entry point, fp16 entry point) as addresses
@@ -169,48 +235,10 @@ PyObject* rows_impl(PyObject* const* a) {
   else if (emit_y || op == kNorm)
     y_out = at::empty({M, H}, opt);
 
-  // codes and scales
-  at::Tensor q, sc;
-  int64_t ld_scale = 0;
-  const int64_t G = group > 0 ? std::max<int64_t>(floordiv(H, group), 1) : 1;
-  const int64_t B = std::max<int64_t>(floordiv(H, 32), 1);
-  if (op == kFp8Token || op == kFp8Group || op == kFp8GroupT)
-    q = qo != nullptr ? checked_out(*qo, {M, H}, {at::kByte, at::kFloat8_e4m3fn}, "q_out", dev)
-                      : at::empty({M, H}, opt.dtype(at::kFloat8_e4m3fn));
-  else if (op == kMxfp4 || op == kMxfp4T)
-    q = qo != nullptr ? checked_out(*qo, {M, floordiv(H, 2)}, {at::kByte}, "q_out", dev)
-                      : at::empty({M, floordiv(H, 2)}, opt.dtype(at::kByte));
-  if (op == kFp8Token) {
-    if (so == nullptr) {
-      sc = at::empty({M, 1}, opt.dtype(at::kFloat));
-    } else {
-      const bool ok = (so->dim() == 1 && so->size(0) == M) || (so->dim() == 2 && so->size(0) == M && so->size(1) == 1);
-      if (!ok)
-        throw Refused{"scale_out must be a contiguous [" + std::to_string(M) + "] or [" + std::to_string(M) +
-                      ", 1] float32 tensor"};
-      sc = checked_out(*so, so->sizes(), {at::kFloat}, "scale_out", dev);
-    }
-  } else if (op == kFp8Group) {
-    sc = so != nullptr ? checked_out(*so, {M, G}, {at::kFloat}, "scale_out", dev) : at::empty({M, G}, opt.dtype(at::kFloat));
-  } else if (op == kMxfp4) {
-    sc = so != nullptr ? checked_out(*so, {M, B}, {at::kByte}, "scale_out", dev) : at::empty({M, B}, opt.dtype(at::kByte));
-  } else if (op == kFp8GroupT || op == kMxfp4T) {
-    // column-major scales: [rows, n >= M] with unit column stride (a view of a
-    // wider buffer is fine); its row stride is ld_scale
-    const int64_t srows = op == kFp8GroupT ? G : B;
-    const c10::ScalarType sdt = op == kFp8GroupT ? at::kFloat : at::kByte;
-    if (so == nullptr) {
-      sc = at::empty({srows, std::max<int64_t>(M, 1)}, opt.dtype(sdt));
-      ld_scale = std::max<int64_t>(M, 1);
-    } else {
-      if (so->dim() != 2 || so->size(0) != srows || so->size(1) < M || so->scalar_type() != sdt ||
-          (so->size(1) > 1 && so->stride(1) != 1) || so->device() != dev)
-        throw Refused{"scale_out must be a [" + std::to_string(srows) + ", >= " + std::to_string(M) + "] " +
-                      dtype_name(sdt) + " tensor with unit column stride"};
-      sc = *so;
-      ld_scale = srows > 1 ? so->stride(0) : std::max<int64_t>(so->size(1), 1);
-    }
-  }
+  Codes c = codes_and_scales(op, qo, so, M, H, group, opt, dev);
+  at::Tensor& q = c.q;
+  at::Tensor& sc = c.sc;
+  const int64_t ld_scale = c.ld_scale;
 
   void* fn = PyLong_AsVoidPtr(PyTuple_GET_ITEM(fns, dt == at::kHalf ? 1 : 0));
   if (PyErr_Occurred()) return nullptr;
@@ -245,10 +273,39 @@ PyObject* rows_impl(PyObject* const* a) {
   }
   if (st != 0) return PyLong_FromLong(st);
   if (op == kNorm) return Py_BuildValue("(NN)", wrap(r_out), wrap(y_out));
-  if (q.scalar_type() == at::kByte && op != kMxfp4 && op != kMxfp4T) q = q.view(at::kFloat8_e4m3fn);
-  if (op == kFp8Token && sc.dim() == 1) sc = sc.view({M, 1});
+  PyObject* q_obj;
+  PyObject* sc_obj = codes_tuple_items(op, q, sc, M, &q_obj);
   PyObject* y_obj = y_out.defined() ? wrap(y_out) : (Py_INCREF(Py_None), Py_None);
-  return Py_BuildValue("(NNNN)", wrap(q), wrap(r_out), wrap(sc), y_obj);
+  return Py_BuildValue("(NNNN)", q_obj, wrap(r_out), sc_obj, y_obj);
+}
+
+// The quantize launch of the unfused sequence: y (a 2-D bf16 or fp16 tensor)
+// to codes and scales in one of the three row formats.
+PyObject* quantize_impl(PyObject* const* a) {
+  const int op = (int)PyLong_AsLong(a[0]);
+  PyObject* fns = a[1];
+  const at::Tensor& y = *tensor_arg(a[2], "y", false);
+  const int64_t group = PyLong_AsLongLong(a[3]);
+  const at::Tensor* qo = tensor_arg(a[4], "q_out", true);
+  const at::Tensor* so = tensor_arg(a[5], "scale_out", true);
+  if (PyErr_Occurred() || !PyTuple_Check(fns) || PyTuple_GET_SIZE(fns) != 2 || op < kFp8Token || op > kMxfp4) {
+    if (!PyErr_Occurred()) PyErr_SetString(PyExc_TypeError, "quantize: an operation and a pair of entry points");
+    return nullptr;
+  }
+  const int64_t ldy = row_stride(y, "y", nullptr);
+  const int64_t M = y.size(0), H = y.size(1);
+  const c10::Device dev = y.device();
+  Codes c = codes_and_scales(op, qo, so, M, H, group, y.options(), dev);
+  void* fn = PyLong_AsVoidPtr(PyTuple_GET_ITEM(fns, y.scalar_type() == at::kHalf ? 1 : 0));
+  if (PyErr_Occurred()) return nullptr;
+  void* stream = stream_of(a[6], dev);
+  const int st = op == kFp8Group
+      ? reinterpret_cast<QuantGroupFn>(fn)(y.data_ptr(), ldy, M, H, group, c.q.data_ptr(), c.sc.data_ptr(), stream)
+      : reinterpret_cast<QuantFn>(fn)(y.data_ptr(), ldy, M, H, c.q.data_ptr(), c.sc.data_ptr(), stream);
+  if (st != 0) return PyLong_FromLong(st);
+  PyObject* q_obj;
+  PyObject* sc_obj = codes_tuple_items(op, c.q, c.sc, M, &q_obj);
+  return Py_BuildValue("(NN)", q_obj, sc_obj);
 }
 
 PyObject* qk_impl(PyObject* const* a) {
@@ -359,12 +416,15 @@ PyMethodDef kMethods[] = {
     {"rows", reinterpret_cast<PyCFunction>(reinterpret_cast<void (*)(void)>(&entry<rows_impl, 13>)), METH_FASTCALL,
      "rows(op, (entry_bf16, entry_f16), x, residual, weight, eps, group, residual_out, q_out, scale_out, emit_y, "
      "y_out, stream) -> outputs tuple, or the status code"},
+    {"quantize", reinterpret_cast<PyCFunction>(reinterpret_cast<void (*)(void)>(&entry<quantize_impl, 7>)),
+     METH_FASTCALL, "quantize(op, (entry_bf16, entry_f16), y, group, q_out, scale_out, stream) -> (codes, scales), "
+     "or the status code"},
     {"qk", reinterpret_cast<PyCFunction>(reinterpret_cast<void (*)(void)>(&entry<qk_impl, 16>)), METH_FASTCALL,
      "qk(op, entry, qg, k, q_w, k_w, Hq, Hk, D, eps, q_out, q_scale_out, k_out, k_scale_out, gate_out, stream) "
      "-> outputs tuple, or the status code"},
     {nullptr, nullptr, 0, nullptr}};
 
-PyModuleDef kModule = {PyModuleDef_HEAD_INIT, "_marshal", "Argument marshalling of the row and QK calls.", -1,
+PyModuleDef kModule = {PyModuleDef_HEAD_INIT, "_marshal", "Argument marshalling of the library's entry points.", -1,
                        kMethods};
 
 }  // namespace

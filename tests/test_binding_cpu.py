@@ -49,14 +49,6 @@ def test_fp16_names_are_the_dispatching_functions():
     assert rq.quantize_mxfp4_f16 is rq.quantize_mxfp4
 
 
-def test_tensors_on_another_device_are_refused():
-    from rmsnorm_activation_quantization_amd import binding
-    like = torch.zeros(4, 256, dtype=torch.bfloat16)
-    binding._same_device(like, a=torch.zeros(3), b=None)
-    with pytest.raises(ValueError, match="weight is on meta"):
-        binding._same_device(like, weight=torch.empty(256, dtype=torch.bfloat16, device="meta"))
-
-
 def test_missing_library_fails_loudly(monkeypatch):
     """No other code path: without the built library every call raises."""
     from rmsnorm_activation_quantization_amd import binding
@@ -66,7 +58,33 @@ def test_missing_library_fails_loudly(monkeypatch):
     with pytest.raises(RuntimeError, match="missing"):
         binding.lib()
     with pytest.raises(RuntimeError, match="missing"):
-        binding._fn("rmsnorm_quant_mxfp4", torch.bfloat16)
+        rq.rmsnorm_quant_mxfp4(*rows())
+
+
+def test_missing_marshalling_module_fails_loudly(monkeypatch):
+    """No other code path: without the built marshalling module every call raises."""
+    import sys
+    from rmsnorm_activation_quantization_amd import binding
+    import rmsnorm_activation_quantization_amd as pkg
+    monkeypatch.setattr(binding, "_marshal", None)
+    monkeypatch.delattr(pkg, "_marshal", raising=False)  # else the import finds the loaded module on the package
+    monkeypatch.setitem(sys.modules, "rmsnorm_activation_quantization_amd._marshal", None)
+    with pytest.raises(RuntimeError, match="missing or does not load"):
+        rq.quantize_mxfp4(torch.zeros(4, 256, dtype=torch.bfloat16))
+
+
+def test_entry_point_addresses():
+    """The marshalling module calls the entry points the binding resolves from
+    the loaded library: the bf16 and fp16 row functions (the norm launch's
+    bf16 one under its _bf16 name), and the QK functions."""
+    import ctypes
+    from rmsnorm_activation_quantization_amd import binding
+    h = binding.lib()
+    addr = lambda f: ctypes.cast(f, ctypes.c_void_p).value
+    assert binding._entries("rmsnorm_quant_mxfp4") == (addr(h.rmsnorm_quant_mxfp4), addr(h.rmsnorm_quant_mxfp4_f16))
+    assert binding._entries("rmsnorm_residual") == (addr(h.rmsnorm_residual_bf16), addr(h.rmsnorm_residual_f16))
+    assert binding._entry("qk_gemma_rmsnorm_gate_fp8") == addr(h.qk_gemma_rmsnorm_gate_fp8)
+    assert len(set(binding._entries("quantize_fp8_per_group"))) == 2
 
 
 def test_status_mapping():
