@@ -1,5 +1,5 @@
 """GPU parity of the fused residual-add + RMSNorm + quantization entry points
-against the CPU oracle (calls go through the C ABI via the ctypes binding)."""
+against the CPU oracle (calls go through the C ABI via the binding)."""
 
 from __future__ import annotations
 
