@@ -24,7 +24,8 @@ roofline comes from these), [4096, 4096] in the three formats, decode-size
 microseconds per call (M = 16, H = 4096, all formats, C1, C3 and the QK
 variants; graph replay of back-to-back calls over rotating inputs, as the
 pages time kernels) next to the launch floor of a one-element kernel timed the
-same way, the unfused sequence, QK and its quantized variants at 8192 tokens,
+same way, and the host time of an eager call through the Python binding; the
+unfused sequence, QK and its quantized variants at 8192 tokens,
 column-major scales and fp16 rows at [8192, 4096] (each timed alternately with
 its bf16 row-major counterpart), and the CPU oracle timed on the host cores as
 the CPU baseline.
@@ -441,6 +442,39 @@ def measured_traffic(kernel: str):
     return None
 
 
+def eager_host_us(torch, rq, inputs, dev, n: int = 2000, reps: int = 5):
+    """Wall time per eager call (no graph) through the Python binding at [16, 4096], the outputs
+    given: median over `reps` loops of `n` calls.  The GPU keeps up (each call's kernel is shorter than
+    its host time), so this is the host cost an eager decode caller pays."""
+    import statistics
+    wl = inputs.DECODE_4096
+    d = inputs.row_inputs(wl)
+    x, r, w = (d[k].to(dev) for k in ("x", "residual", "weight"))
+    M, H = wl.M, wl.H
+    ro = torch.empty((M, H), dtype=torch.bfloat16, device=dev)
+    q8 = torch.empty((M, H), dtype=torch.float8_e4m3fn, device=dev)
+    q4 = torch.empty((M, H // 2), dtype=torch.uint8, device=dev)
+    st = torch.empty((M, 1), dtype=torch.float32, device=dev)
+    sm = torch.empty((M, H // 32), dtype=torch.uint8, device=dev)
+    calls = {"fp8_token": lambda: rq.rmsnorm_quant_fp8_per_token(x, r, w, wl.eps, residual_out=ro, q_out=q8,
+                                                                 scale_out=st),
+             "mxfp4": lambda: rq.rmsnorm_quant_mxfp4(x, r, w, wl.eps, residual_out=ro, q_out=q4, scale_out=sm)}
+    res = {}
+    for name, fn in calls.items():
+        for _ in range(100):
+            fn()
+        torch.cuda.synchronize()
+        times = []
+        for _ in range(reps):
+            t0 = time.perf_counter()
+            for _ in range(n):
+                fn()
+            times.append((time.perf_counter() - t0) / n * 1e6)
+            torch.cuda.synchronize()
+        res[f"{name}_{M}x{H}"] = round(statistics.median(times), 2)
+    return res
+
+
 def decode_latency(torch, rq, inputs, dev, calls: int = 200, replays: int = 7):
     """Per-call microseconds at decode sizes: a graph of `calls` back-to-back
     calls over rotating inputs (more bytes than the Infinity Cache), replayed;
@@ -531,6 +565,7 @@ def decode_latency(torch, rq, inputs, dev, calls: int = 200, replays: int = 7):
         lambda i: rq.qk_gemma_rmsnorm_gate_fp8(qg[i % nq], kk[i % nq], qd["q_w"], qd["k_w"], qw.Hq, qw.Hk, qw.D,
                                                qw.eps, q_out=o8[0], q_scale_out=o8[1], k_out=o8[2],
                                                k_scale_out=o8[3], gate_out=outs[2])), 3)
+    res["eager_host_us"] = eager_host_us(torch, rq, inputs, dev)
     # The pages' own MI355X figures, as context (other kernels, other machines' runs): the fused QK
     # norm + gate kernel per attention layer, the gfx950 launch floor, and the related FlyDSL hc_mix
     # gate at M = 1, 2, 4, 8, 16 (its Speed Tests table).
