@@ -1,10 +1,24 @@
 """Host-side argument checks of the Python binding (no GPU: every case is
 refused before the library is called)."""
 
+import os
+
 import pytest
 import torch
 
 import rmsnorm_activation_quantization_amd as rq
+
+
+@pytest.fixture(scope="module", autouse=True)
+def built():
+    """The checks run in the marshalling module, which the binding calls with
+    entry points of the loaded library: build both if a fresh checkout has
+    neither (the HIP library cross-compiles without a GPU)."""
+    from rmsnorm_activation_quantization_amd import _build
+    if not os.path.exists(_build.LIBRARY):
+        _build.build()
+    if not os.path.exists(_build.marshal_path()):
+        _build.build_marshal()
 
 
 def rows(M=4, H=256, dtype=torch.bfloat16):
