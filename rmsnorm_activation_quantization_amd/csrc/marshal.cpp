@@ -119,12 +119,25 @@ const at::Tensor& checked_out(const at::Tensor& t, at::IntArrayRef shape, std::i
   return t;
 }
 
+// The caller's stream (a torch.cuda.Stream, or anything with an integer
+// `cuda_stream`, on the tensors' device when it says which), else torch's
+// current stream on that device.
 void* stream_of(PyObject* stream, const c10::Device& dev) {
   if (stream == Py_None) return c10::hip::getCurrentHIPStream(dev.index()).stream();
   PyObject* s = PyObject_GetAttrString(stream, "cuda_stream");
-  if (s == nullptr) throw Refused{"stream must be a torch.cuda.Stream"};
-  void* p = PyLong_AsVoidPtr(s);
-  Py_DECREF(s);
+  void* p = s != nullptr ? PyLong_AsVoidPtr(s) : nullptr;
+  Py_XDECREF(s);
+  if (PyErr_Occurred()) {
+    PyErr_Clear();
+    throw Refused{"stream must be a torch.cuda.Stream"};
+  }
+  if (PyObject* d = PyObject_GetAttrString(stream, "device_index")) {
+    const long idx = PyLong_Check(d) ? PyLong_AsLong(d) : (long)dev.index();
+    Py_DECREF(d);
+    if (idx != (long)dev.index())
+      throw Refused{"stream is on cuda:" + std::to_string(idx) + "; every tensor is on " + dev.str()};
+  }
+  PyErr_Clear();  // no device_index: nothing to compare
   return p;
 }
 
@@ -326,6 +339,13 @@ PyObject* qk_impl(PyObject* const* a) {
   const int64_t ld_qg = row_stride(qg, "qg", &bf), ld_k = row_stride(k, "k", &bf);
   const int64_t T = qg.size(0);
   if (k.size(0) != T) throw Refused{"qg and k must have the same number of tokens"};
+  // The library sees row strides, not widths: a narrower view of a wider
+  // buffer would pass its stride check and be read past its last column.
+  int64_t hq_d = 0, wq = 0, wk = 0;
+  if (Hq > 0 && Hk > 0 && D > 0 && !__builtin_mul_overflow(Hq, D, &hq_d) && !__builtin_mul_overflow(hq_d, 2, &wq) &&
+      !__builtin_mul_overflow(Hk, D, &wk) && (qg.size(1) < wq || k.size(1) < wk))
+    throw Refused{"qg must have at least 2 * num_q_heads * head_dim columns (" + std::to_string(wq) + ") and k " +
+                  "num_k_heads * head_dim (" + std::to_string(wk) + ")"};
   for (const auto& [name, t] : {std::pair<const char*, const at::Tensor*>{"q_w", &q_w}, {"k_w", &k_w}}) {
     if (t->dim() != 1 || t->size(0) != D || t->scalar_type() != bf || !t->is_contiguous())
       throw Refused{std::string(name) + " must be a contiguous [head_dim] bfloat16 tensor"};

@@ -4,6 +4,8 @@ caller passes come back as the very same tensors."""
 
 from __future__ import annotations
 
+import types
+
 import pytest
 import torch
 
@@ -57,6 +59,11 @@ def test_row_inputs_refused(name):
         fn(x, r, w, y_out=torch.empty(M, H, dtype=torch.float16, device=DEV))
     with pytest.raises(ValueError, match="stream"):
         fn(x, r, w, stream=object())
+    with pytest.raises(ValueError, match="stream must be"):
+        fn(x, r, w, stream=types.SimpleNamespace(cuda_stream="s"))  # not an integer handle
+    here = torch.cuda.current_stream().cuda_stream
+    with pytest.raises(ValueError, match="stream is on cuda:1"):
+        fn(x, r, w, stream=types.SimpleNamespace(cuda_stream=here, device_index=1))
     torch.cuda.synchronize()
 
 
@@ -141,6 +148,17 @@ def test_qk_refused(name):
         fn(qg, k, wq, wq.half(), Hq, Hk, D)
     with pytest.raises(ValueError, match="dtype of x"):
         fn(qg.half(), k, wq, wq, Hq, Hk, D)
+    # narrower views of wider buffers: the row strides would pass the library's
+    # own check, the widths do not
+    wide_qg = torch.zeros(T, 4 * Hq * D, dtype=torch.bfloat16, device=DEV)
+    wide_k = torch.zeros(T, 4 * Hk * D, dtype=torch.bfloat16, device=DEV)
+    with pytest.raises(ValueError, match="columns"):
+        fn(wide_qg[:, : 2 * Hq * D - 8], k, wq, wq, Hq, Hk, D)
+    with pytest.raises(ValueError, match="columns"):
+        fn(qg, wide_k[:, : Hk * D - 8], wq, wq, Hq, Hk, D)
+    out = fn(wide_qg[:, : 2 * Hq * D], wide_k[:, : Hk * D], wq, wq, Hq, Hk, D)  # exactly wide enough
+    torch.cuda.synchronize()
+    assert out is not None
     with pytest.raises(ValueError, match="gate_out"):
         fn(qg, k, wq, wq, Hq, Hk, D, gate_out=torch.empty(T, Hq, D + 1, dtype=torch.bfloat16, device=DEV))
     gate = torch.empty(T, Hq, D, dtype=torch.bfloat16, device=DEV)
