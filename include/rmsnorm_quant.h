@@ -27,7 +27,9 @@
  *    allocates nothing, never synchronizes the host and keeps no state besides
  *    a per-device cache of the architecture check.  Every call only enqueues
  *    kernels on `stream` (a hipStream_t; NULL = the null stream), so calls may
- *    be captured into a hipGraph.
+ *    be captured into a hipGraph.  The architecture check reads the current
+ *    HIP device: the stream and every pointer must belong to that device
+ *    (the library cannot see where a pointer or a stream lives).
  *  - Inputs x and residual may be strided views (row stride ldx / ldr in
  *    elements); every output is contiguous, except the column-major scale
  *    arrays of the _tscale calls, which take a leading dimension.
