@@ -3,7 +3,8 @@
 // launches and the QK calls.
 //
 // The binding's checks, the allocation of missing outputs and the call of the
-// C entry point, done on torch's C++ tensors.  From Python every tensor
+// C entry point (with the tensors' device current, as torch's own operators
+// do), done on torch's C++ tensors.  From Python every tensor
 // attribute a check reads is a call into torch of 0.1-0.4 us, and an eager
 // decode-sized call is bound by that host time; here the same reads cost
 // nanoseconds.  Nothing here computes: every step of the method runs in the
@@ -19,6 +20,7 @@
 
 #include <ATen/core/Tensor.h>
 #include <ATen/ops/empty.h>
+#include <c10/core/DeviceGuard.h>
 #include <c10/hip/HIPStream.h>
 #include <torch/csrc/autograd/python_variable.h>
 
@@ -255,6 +257,7 @@ PyObject* rows_impl(PyObject* const* a) {
 
   void* fn = PyLong_AsVoidPtr(PyTuple_GET_ITEM(fns, dt == at::kHalf ? 1 : 0));
   if (PyErr_Occurred()) return nullptr;
+  const c10::DeviceGuard on_device(dev);  // the library checks and launches on the current device
   void* stream = stream_of(a[12], dev);
   const void *xp = x.data_ptr(), *rp = res.data_ptr(), *wp = w.data_ptr();
   void* rop = r_out.data_ptr();
@@ -311,6 +314,7 @@ PyObject* quantize_impl(PyObject* const* a) {
   Codes c = codes_and_scales(op, qo, so, M, H, group, y.options(), dev);
   void* fn = PyLong_AsVoidPtr(PyTuple_GET_ITEM(fns, y.scalar_type() == at::kHalf ? 1 : 0));
   if (PyErr_Occurred()) return nullptr;
+  const c10::DeviceGuard on_device(dev);
   void* stream = stream_of(a[6], dev);
   const int st = op == kFp8Group
       ? reinterpret_cast<QuantGroupFn>(fn)(y.data_ptr(), ldy, M, H, group, c.q.data_ptr(), c.sc.data_ptr(), stream)
@@ -398,6 +402,7 @@ PyObject* qk_impl(PyObject* const* a) {
     return nullptr;
   }
 
+  const c10::DeviceGuard on_device(dev);
   void* stream = stream_of(a[15], dev);
   const void *qgp = qg.data_ptr(), *kp = k.data_ptr(), *qwp = q_w.data_ptr(), *kwp = k_w.data_ptr();
   int st;
