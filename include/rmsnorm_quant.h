@@ -69,7 +69,15 @@
 extern "C" {
 #endif
 
+/* C++ includers see a fixed underlying type (int), so that any status value a
+ * C caller can hold (rq_status_string takes unknown codes too) is a valid
+ * value of the enumeration in C++ as well; the size and calling convention are
+ * those of the C enum. */
+#ifdef __cplusplus
+typedef enum rq_status : int {
+#else
 typedef enum rq_status {
+#endif
   RQ_OK = 0,
   RQ_ERR_INVALID = 1,
   RQ_ERR_UNSUPPORTED = 2,
