@@ -1,8 +1,15 @@
-"""The oracle built with UndefinedBehaviorSanitizer checks in trap mode
-(g++ -fsanitize=undefined,float-cast-overflow -fsanitize-undefined-trap-on-error:
-no runtime library; an undefined operation stops the process), and every pin
-run against that build in a process of its own.  Float division by zero is
-not trapped: the oracle's IEEE arithmetic relies on it (1/0 = inf)."""
+"""The oracle under sanitizers.
+
+- Built with UndefinedBehaviorSanitizer checks in trap mode (g++
+  -fsanitize=undefined,float-cast-overflow -fsanitize-undefined-trap-on-error:
+  no runtime library; an undefined operation stops the process), with every
+  pin run against that build in a process of its own.  Float division by zero
+  is not trapped: the oracle's IEEE arithmetic relies on it (1/0 = inf).
+- Built into an executable with AddressSanitizer and UndefinedBehaviorSanitizer
+  beside oracle_asan_driver.cpp, which calls every entry point on heap buffers
+  of exactly the extent its arguments describe.
+
+Each has a negative control that the sanitizer must catch."""
 
 import os
 import subprocess
@@ -52,3 +59,24 @@ def test_planted_signed_overflow_is_trapped(tmp_path):
     planted.write_text(src.replace(head, head + " { volatile int big = 2147483647; big = big + 1; }"))
     run = pins_with_ub_trapped(str(planted), str(tmp_path / "librq_oracle_planted.so"))
     assert run.returncode == -4, (run.returncode, run.stdout[-2000:])  # SIGILL from the trap
+
+
+def asan_driver(tmp_path, *args) -> subprocess.CompletedProcess:
+    exe = str(tmp_path / "oracle_asan")
+    flags = [f for f in oracle.CXXFLAGS if f not in ("-shared", "-fPIC") and not f.startswith("-O")]
+    build = subprocess.run(["g++", *flags, "-O1", "-g", "-fsanitize=address,undefined", "-fno-sanitize-recover=all",
+                            "-I", os.path.dirname(oracle.SOURCE), os.path.join(TESTS, "oracle_asan_driver.cpp"),
+                            oracle.SOURCE, "-o", exe], capture_output=True, text=True, timeout=600)
+    assert build.returncode == 0, build.stderr[-4000:]
+    return subprocess.run([exe, *args], capture_output=True, text=True, timeout=600)
+
+
+def test_oracle_on_exact_buffers_under_asan(tmp_path):
+    run = asan_driver(tmp_path, "300")
+    assert run.returncode == 0 and "clean" in run.stdout, (run.returncode, run.stderr[-4000:])
+
+
+def test_short_buffer_is_reported(tmp_path):
+    """Negative control: the weight buffer one element short."""
+    run = asan_driver(tmp_path, "300", "short")
+    assert run.returncode != 0 and "heap-buffer-overflow" in run.stderr, (run.returncode, run.stderr[-2000:])
