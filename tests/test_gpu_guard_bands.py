@@ -1,0 +1,138 @@
+"""No kernel writes outside its outputs.  Every output lives inside a larger
+buffer whose guard bands (4 KiB before and after) hold a byte pattern, and so
+do the padding columns between M and the leading dimension of column-major
+scales; every byte of the pattern must survive the call.  The shapes reach
+every tiling: one-wave rows (H <= 512, four a workgroup), multi-wave rows with
+one or two chunks a lane, 16-wave rows, a ragged last workgroup, column-major
+scales stored directly and staged (MXFP4 rows in turn, with a dead second
+turn), the unfused launches, fp16 rows and the three QK calls."""
+
+from __future__ import annotations
+
+import pytest
+import torch
+
+import rmsnorm_activation_quantization_amd as rq
+
+pytestmark = pytest.mark.gpu
+DEV = "cuda:0"
+GUARD = 4096
+PATTERN = 0xA5
+
+
+class Guarded:
+    """Output tensors carved out of one pattern-filled byte buffer each."""
+
+    def __init__(self, device=DEV):
+        self.device = device
+        self.bufs = []
+
+    def out(self, shape, dtype, ld=None):
+        """A contiguous [*shape] tensor, or with `ld` a [rows, ld] tensor whose
+        columns past shape[1] are padding (column-major scales)."""
+        rows, cols = (shape[0], ld) if ld is not None else (None, None)
+        full = (rows, cols) if ld is not None else tuple(shape)
+        n = 1
+        for s in full:
+            n *= s
+        nbytes = n * torch.tensor([], dtype=dtype).element_size()
+        base = torch.full((nbytes + 2 * GUARD,), PATTERN, dtype=torch.uint8, device=self.device)
+        t = base[GUARD:GUARD + nbytes].view(dtype).view(full)
+        self.bufs.append((base, nbytes, shape, ld, t))
+        return t
+
+    def check(self, what):
+        if torch.device(self.device).type == "cuda":
+            torch.cuda.synchronize()
+        for base, nbytes, shape, ld, t in self.bufs:
+            assert (base[:GUARD] == PATTERN).all(), f"{what}: write before an output of {tuple(t.shape)}"
+            assert (base[GUARD + nbytes:] == PATTERN).all(), f"{what}: write after an output of {tuple(t.shape)}"
+            if ld is not None and ld > shape[1]:
+                pad = t[:, shape[1]:].contiguous().view(torch.uint8)
+                assert (pad == PATTERN).all(), f"{what}: write into the padding columns of the column-major scales"
+
+
+def rows(M, H, dtype=torch.bfloat16, seed=0):
+    g = torch.Generator(device=DEV).manual_seed(seed + M * 131 + H)
+    x = torch.randn(M, H, generator=g, device=DEV).to(dtype)
+    r = torch.randn(M, H, generator=g, device=DEV).to(dtype)
+    w = (1 + 0.1 * torch.randn(H, generator=g, device=DEV)).to(dtype)
+    return x, r, w
+
+
+SHAPES = [(1, 256), (7, 512), (3, 1024), (17, 2048), (5, 4096), (1025, 4096), (2050, 4096), (9, 5120),
+          (1, 7168), (16, 7168), (1030, 7168), (3, 16384)]
+
+
+@pytest.mark.parametrize("M,H", SHAPES)
+@pytest.mark.parametrize("dtype", [torch.bfloat16, torch.float16])
+def test_row_calls_write_only_their_outputs(M, H, dtype):
+    x, r, w = rows(M, H, dtype)
+    for fmt in ("fp8_token", "fp8_group", "mxfp4"):
+        g = Guarded()
+        ro, y = g.out((M, H), dtype), g.out((M, H), dtype)
+        if fmt == "mxfp4":
+            q, s = g.out((M, H // 2), torch.uint8), g.out((M, H // 32), torch.uint8)
+            out = rq.rmsnorm_quant_mxfp4(x, r, w, 1e-6, q_out=q, residual_out=ro, scale_out=s, y_out=y)
+        elif fmt == "fp8_group":
+            q, s = g.out((M, H), torch.uint8), g.out((M, H // 128), torch.float32)
+            out = rq.rmsnorm_quant_fp8_per_group(x, r, w, 1e-6, 128, q_out=q, residual_out=ro, scale_out=s, y_out=y)
+        else:
+            q, s = g.out((M, H), torch.uint8), g.out((M, 1), torch.float32)
+            out = rq.rmsnorm_quant_fp8_per_token(x, r, w, 1e-6, q_out=q, residual_out=ro, scale_out=s, y_out=y)
+        assert out is not None
+        g.check(f"{fmt} [{M}, {H}] {dtype}")
+
+
+@pytest.mark.parametrize("M,H", SHAPES)
+def test_column_major_scales_write_only_their_columns(M, H):
+    x, r, w = rows(M, H)
+    for fmt in ("fp8_group", "mxfp4"):
+        for ld in (M, M + 24):
+            g = Guarded()
+            ro = g.out((M, H), torch.bfloat16)
+            if fmt == "mxfp4":
+                q = g.out((M, H // 2), torch.uint8)
+                s = g.out((H // 32, M), torch.uint8, ld=ld)
+                out = rq.rmsnorm_quant_mxfp4_tscale(x, r, w, 1e-6, q_out=q, residual_out=ro, scale_out=s)
+            else:
+                q = g.out((M, H), torch.uint8)
+                s = g.out((H // 128, M), torch.float32, ld=ld)
+                out = rq.rmsnorm_quant_fp8_per_group_tscale(x, r, w, 1e-6, 128, q_out=q, residual_out=ro, scale_out=s)
+            assert out is not None
+            g.check(f"{fmt} column-major [{M}, {H}] ld {ld}")
+
+
+@pytest.mark.parametrize("M,H", [(1, 256), (17, 2048), (1025, 4096), (16, 7168)])
+def test_unfused_launches_write_only_their_outputs(M, H):
+    x, r, w = rows(M, H)
+    g = Guarded()
+    ro, y = g.out((M, H), torch.bfloat16), g.out((M, H), torch.bfloat16)
+    assert rq.rmsnorm_residual_bf16(x, r, w, 1e-6, residual_out=ro, y_out=y) is not None
+    q8, st, sg = g.out((M, H), torch.uint8), g.out((M, 1), torch.float32), g.out((M, H // 128), torch.float32)
+    q4, sm = g.out((M, H // 2), torch.uint8), g.out((M, H // 32), torch.uint8)
+    assert rq.quantize_fp8_per_token(y, q_out=q8, scale_out=st) is not None
+    assert rq.quantize_fp8_per_group(y, 128, q_out=q8, scale_out=sg) is not None
+    assert rq.quantize_mxfp4(y, q_out=q4, scale_out=sm) is not None
+    g.check(f"unfused [{M}, {H}]")
+
+
+@pytest.mark.parametrize("T,Hq,Hk,D", [(1, 16, 2, 256), (64, 16, 2, 256), (7, 4, 1, 64), (257, 8, 8, 128),
+                                       (3, 2, 2, 512)])
+def test_qk_calls_write_only_their_outputs(T, Hq, Hk, D):
+    gen = torch.Generator(device=DEV).manual_seed(T * 7 + D)
+    qg = torch.randn(T, 2 * Hq * D, generator=gen, device=DEV).to(torch.bfloat16)
+    k = torch.randn(T, Hk * D, generator=gen, device=DEV).to(torch.bfloat16)
+    qw = (0.1 * torch.randn(D, generator=gen, device=DEV)).to(torch.bfloat16)
+    g = Guarded()
+    q, kk, gate = g.out((T, Hq, D), torch.bfloat16), g.out((T, Hk, D), torch.bfloat16), g.out((T, Hq, D), torch.bfloat16)
+    assert rq.qk_gemma_rmsnorm_gate(qg, k, qw, qw, Hq, Hk, D, q_out=q, k_out=kk, gate_out=gate) is not None
+    qc, qs = g.out((T, Hq, D), torch.uint8), g.out((T, Hq), torch.float32)
+    kc, ks = g.out((T, Hk, D), torch.uint8), g.out((T, Hk), torch.float32)
+    assert rq.qk_gemma_rmsnorm_gate_fp8(qg, k, qw, qw, Hq, Hk, D, q_out=qc, q_scale_out=qs, k_out=kc,
+                                        k_scale_out=ks, gate_out=gate) is not None
+    qc4, qs4 = g.out((T, Hq, D // 2), torch.uint8), g.out((T, Hq, D // 32), torch.uint8)
+    kc4, ks4 = g.out((T, Hk, D // 2), torch.uint8), g.out((T, Hk, D // 32), torch.uint8)
+    assert rq.qk_gemma_rmsnorm_gate_mxfp4(qg, k, qw, qw, Hq, Hk, D, q_out=qc4, q_scale_out=qs4, k_out=kc4,
+                                          k_scale_out=ks4, gate_out=gate) is not None
+    g.check(f"qk T={T} Hq={Hq} Hk={Hk} D={D}")
