@@ -1,11 +1,19 @@
-"""No kernel writes outside its outputs.  Every output lives inside a larger
+"""No kernel touches memory outside its tensors.
+
+Writes: no kernel writes outside its outputs.  Every output lives inside a larger
 buffer whose guard bands (4 KiB before and after) hold a byte pattern, and so
 do the padding columns between M and the leading dimension of column-major
 scales; every byte of the pattern must survive the call.  The shapes reach
 every tiling: one-wave rows (H <= 512, four a workgroup), multi-wave rows with
 one or two chunks a lane, 16-wave rows, a ragged last workgroup, column-major
 scales stored directly and staged (MXFP4 rows in turn, with a dead second
-turn), the unfused launches, fp16 rows and the three QK calls."""
+turn), the unfused launches, fp16 rows and the three QK calls.
+
+Reads: inputs embedded in NaN-filled buffers (NaN before and after each input,
+in the gap columns of strided rows, around the weights) give outputs
+bit-identical to those of clean contiguous copies, so no kernel uses a value
+outside its inputs' extent (a NaN read into a row's sum or maximum would show
+in every output of that row)."""
 
 from __future__ import annotations
 
@@ -136,3 +144,69 @@ def test_qk_calls_write_only_their_outputs(T, Hq, Hk, D):
     assert rq.qk_gemma_rmsnorm_gate_mxfp4(qg, k, qw, qw, Hq, Hk, D, q_out=qc4, q_scale_out=qs4, k_out=kc4,
                                           k_scale_out=ks4, gate_out=gate) is not None
     g.check(f"qk T={T} Hq={Hq} Hk={Hk} D={D}")
+
+
+NAN_LEAD, NAN_GAP = 64, 64  # elements: 128-byte offsets keep every row start 16-byte aligned
+
+
+def nan_embedded(t, device=DEV):
+    """The values of `t` ([H] or [M, H]) as a view inside a NaN-filled buffer:
+    NaN before and after, and (2-D) NaN in the gap columns of each row."""
+    if t.dim() == 1:
+        buf = torch.full((NAN_LEAD + t.numel() + NAN_LEAD,), float("nan"), dtype=t.dtype, device=device)
+        v = buf[NAN_LEAD:NAN_LEAD + t.numel()]
+    else:
+        M, H = t.shape
+        ld = H + NAN_GAP
+        buf = torch.full((NAN_LEAD + M * ld + NAN_LEAD,), float("nan"), dtype=t.dtype, device=device)
+        v = buf[NAN_LEAD:NAN_LEAD + M * ld].view(M, ld)[:, :H]
+    v.copy_(t)
+    return v
+
+
+def same_bits(a, b, what):
+    for i, (u, v) in enumerate(zip(a, b)):
+        if u is None:
+            assert v is None, what
+            continue
+        assert torch.equal(u.contiguous().view(torch.uint8), v.contiguous().view(torch.uint8)), f"{what}: output {i}"
+
+
+@pytest.mark.parametrize("M,H", SHAPES)
+@pytest.mark.parametrize("dtype", [torch.bfloat16, torch.float16])
+def test_row_calls_read_only_their_inputs(M, H, dtype):
+    x, r, w = rows(M, H, dtype, seed=1)
+    xn, rn, wn = nan_embedded(x), nan_embedded(r), nan_embedded(w)
+    calls = {
+        "fp8_token": lambda *a: rq.rmsnorm_quant_fp8_per_token(*a, 1e-6, emit_y=True),
+        "fp8_group": lambda *a: rq.rmsnorm_quant_fp8_per_group(*a, 1e-6, 128, emit_y=True),
+        "mxfp4": lambda *a: rq.rmsnorm_quant_mxfp4(*a, 1e-6, emit_y=True),
+    }
+    if dtype == torch.bfloat16:
+        calls["fp8_group_tscale"] = lambda *a: rq.rmsnorm_quant_fp8_per_group_tscale(*a, 1e-6, 128, emit_y=True)
+        calls["mxfp4_tscale"] = lambda *a: rq.rmsnorm_quant_mxfp4_tscale(*a, 1e-6, emit_y=True)
+        calls["norm"] = lambda *a: rq.rmsnorm_residual_bf16(*a, 1e-6)
+    for name, fn in calls.items():
+        same_bits(fn(x, r, w), fn(xn, rn, wn), f"{name} [{M}, {H}] {dtype}")
+    if dtype == torch.bfloat16:
+        y = rq.rmsnorm_residual_bf16(x, r, w, 1e-6)[1]
+        yn = nan_embedded(y)
+        for name in ("quantize_fp8_per_token", "quantize_mxfp4"):
+            same_bits(getattr(rq, name)(y), getattr(rq, name)(yn), f"{name} [{M}, {H}]")
+        same_bits(rq.quantize_fp8_per_group(y, 128), rq.quantize_fp8_per_group(yn, 128), f"quantize group [{M}, {H}]")
+    torch.cuda.synchronize()
+
+
+@pytest.mark.parametrize("T,Hq,Hk,D", [(1, 16, 2, 256), (64, 16, 2, 256), (7, 4, 1, 64), (257, 8, 8, 128),
+                                       (3, 2, 2, 512)])
+def test_qk_calls_read_only_their_inputs(T, Hq, Hk, D):
+    gen = torch.Generator(device=DEV).manual_seed(T * 11 + D)
+    qg = torch.randn(T, 2 * Hq * D, generator=gen, device=DEV).to(torch.bfloat16)
+    k = torch.randn(T, Hk * D, generator=gen, device=DEV).to(torch.bfloat16)
+    qw = (0.1 * torch.randn(D, generator=gen, device=DEV)).to(torch.bfloat16)
+    kw = (0.1 * torch.randn(D, generator=gen, device=DEV)).to(torch.bfloat16)
+    clean, embedded = (qg, k, qw, kw), tuple(nan_embedded(t) for t in (qg, k, qw, kw))
+    for name in ("qk_gemma_rmsnorm_gate", "qk_gemma_rmsnorm_gate_fp8", "qk_gemma_rmsnorm_gate_mxfp4"):
+        fn = getattr(rq, name)
+        same_bits(fn(*clean, Hq, Hk, D), fn(*embedded, Hq, Hk, D), f"{name} T={T} Hq={Hq} Hk={Hk} D={D}")
+    torch.cuda.synchronize()
