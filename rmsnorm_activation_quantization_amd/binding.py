@@ -256,7 +256,9 @@ def qk_gemma_rmsnorm_gate_mxfp4(qg, k, q_w, k_w, num_q_heads: int, num_k_heads: 
 # ---- the unfused sequence, one launch per step ----
 
 def rmsnorm_residual_bf16(x, residual, weight, eps: float = 1e-6, *, residual_out=None, y_out=None, stream=None):
-    """-> (residual_out [M, H] bf16, y [M, H] bf16), or None."""
+    """The norm launch of the unfused sequence (rmsnorm_residual_bf16, or
+    rmsnorm_residual_f16 for fp16 rows).
+    -> (residual_out [M, H], y [M, H]) in the dtype of x, or None."""
     r = _native().rows(_NORM, _entries("rmsnorm_residual"), x, residual, weight, eps, 0, residual_out, None, None,
                        True, y_out, stream)
     return r if r.__class__ is tuple else _status(r, "rmsnorm_residual_bf16")

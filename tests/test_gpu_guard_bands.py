@@ -93,12 +93,13 @@ def test_row_calls_write_only_their_outputs(M, H, dtype):
 
 
 @pytest.mark.parametrize("M,H", SHAPES)
-def test_column_major_scales_write_only_their_columns(M, H):
-    x, r, w = rows(M, H)
+@pytest.mark.parametrize("dtype", [torch.bfloat16, torch.float16])
+def test_column_major_scales_write_only_their_columns(M, H, dtype):
+    x, r, w = rows(M, H, dtype)
     for fmt in ("fp8_group", "mxfp4"):
         for ld in (M, M + 24):
             g = Guarded()
-            ro = g.out((M, H), torch.bfloat16)
+            ro = g.out((M, H), dtype)
             if fmt == "mxfp4":
                 q = g.out((M, H // 2), torch.uint8)
                 s = g.out((H // 32, M), torch.uint8, ld=ld)
@@ -108,21 +109,22 @@ def test_column_major_scales_write_only_their_columns(M, H):
                 s = g.out((H // 128, M), torch.float32, ld=ld)
                 out = rq.rmsnorm_quant_fp8_per_group_tscale(x, r, w, 1e-6, 128, q_out=q, residual_out=ro, scale_out=s)
             assert out is not None
-            g.check(f"{fmt} column-major [{M}, {H}] ld {ld}")
+            g.check(f"{fmt} column-major [{M}, {H}] ld {ld} {dtype}")
 
 
 @pytest.mark.parametrize("M,H", [(1, 256), (17, 2048), (1025, 4096), (16, 7168)])
-def test_unfused_launches_write_only_their_outputs(M, H):
-    x, r, w = rows(M, H)
+@pytest.mark.parametrize("dtype", [torch.bfloat16, torch.float16])
+def test_unfused_launches_write_only_their_outputs(M, H, dtype):
+    x, r, w = rows(M, H, dtype)
     g = Guarded()
-    ro, y = g.out((M, H), torch.bfloat16), g.out((M, H), torch.bfloat16)
+    ro, y = g.out((M, H), dtype), g.out((M, H), dtype)
     assert rq.rmsnorm_residual_bf16(x, r, w, 1e-6, residual_out=ro, y_out=y) is not None
     q8, st, sg = g.out((M, H), torch.uint8), g.out((M, 1), torch.float32), g.out((M, H // 128), torch.float32)
     q4, sm = g.out((M, H // 2), torch.uint8), g.out((M, H // 32), torch.uint8)
     assert rq.quantize_fp8_per_token(y, q_out=q8, scale_out=st) is not None
     assert rq.quantize_fp8_per_group(y, 128, q_out=q8, scale_out=sg) is not None
     assert rq.quantize_mxfp4(y, q_out=q4, scale_out=sm) is not None
-    g.check(f"unfused [{M}, {H}]")
+    g.check(f"unfused [{M}, {H}] {dtype}")
 
 
 @pytest.mark.parametrize("T,Hq,Hk,D", [(1, 16, 2, 256), (64, 16, 2, 256), (7, 4, 1, 64), (257, 8, 8, 128),
