@@ -17,6 +17,8 @@ in every output of that row)."""
 
 from __future__ import annotations
 
+import math
+
 import pytest
 import torch
 
@@ -38,12 +40,8 @@ class Guarded:
     def out(self, shape, dtype, ld=None):
         """A contiguous [*shape] tensor, or with `ld` a [rows, ld] tensor whose
         columns past shape[1] are padding (column-major scales)."""
-        rows, cols = (shape[0], ld) if ld is not None else (None, None)
-        full = (rows, cols) if ld is not None else tuple(shape)
-        n = 1
-        for s in full:
-            n *= s
-        nbytes = n * torch.tensor([], dtype=dtype).element_size()
+        full = (shape[0], ld) if ld is not None else tuple(shape)
+        nbytes = math.prod(full) * torch.empty((), dtype=dtype).element_size()
         base = torch.full((nbytes + 2 * GUARD,), PATTERN, dtype=torch.uint8, device=self.device)
         t = base[GUARD:GUARD + nbytes].view(dtype).view(full)
         self.bufs.append((base, nbytes, shape, ld, t))
