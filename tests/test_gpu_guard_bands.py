@@ -182,18 +182,16 @@ def test_row_calls_read_only_their_inputs(M, H, dtype):
         "fp8_group": lambda *a: rq.rmsnorm_quant_fp8_per_group(*a, 1e-6, 128, emit_y=True),
         "mxfp4": lambda *a: rq.rmsnorm_quant_mxfp4(*a, 1e-6, emit_y=True),
     }
-    if dtype == torch.bfloat16:
-        calls["fp8_group_tscale"] = lambda *a: rq.rmsnorm_quant_fp8_per_group_tscale(*a, 1e-6, 128, emit_y=True)
-        calls["mxfp4_tscale"] = lambda *a: rq.rmsnorm_quant_mxfp4_tscale(*a, 1e-6, emit_y=True)
-        calls["norm"] = lambda *a: rq.rmsnorm_residual_bf16(*a, 1e-6)
+    calls["fp8_group_tscale"] = lambda *a: rq.rmsnorm_quant_fp8_per_group_tscale(*a, 1e-6, 128, emit_y=True)
+    calls["mxfp4_tscale"] = lambda *a: rq.rmsnorm_quant_mxfp4_tscale(*a, 1e-6, emit_y=True)
+    calls["norm"] = lambda *a: rq.rmsnorm_residual_bf16(*a, 1e-6)  # the fp16 norm launch for fp16 rows
     for name, fn in calls.items():
         same_bits(fn(x, r, w), fn(xn, rn, wn), f"{name} [{M}, {H}] {dtype}")
-    if dtype == torch.bfloat16:
-        y = rq.rmsnorm_residual_bf16(x, r, w, 1e-6)[1]
-        yn = nan_embedded(y)
-        for name in ("quantize_fp8_per_token", "quantize_mxfp4"):
-            same_bits(getattr(rq, name)(y), getattr(rq, name)(yn), f"{name} [{M}, {H}]")
-        same_bits(rq.quantize_fp8_per_group(y, 128), rq.quantize_fp8_per_group(yn, 128), f"quantize group [{M}, {H}]")
+    y = rq.rmsnorm_residual_bf16(x, r, w, 1e-6)[1]
+    yn = nan_embedded(y)
+    for name in ("quantize_fp8_per_token", "quantize_mxfp4"):
+        same_bits(getattr(rq, name)(y), getattr(rq, name)(yn), f"{name} [{M}, {H}] {dtype}")
+    same_bits(rq.quantize_fp8_per_group(y, 128), rq.quantize_fp8_per_group(yn, 128), f"quantize group [{M}, {H}] {dtype}")
     torch.cuda.synchronize()
 
 
